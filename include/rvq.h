@@ -1,0 +1,140 @@
+/*
+ * rvq.h -- C ABI of the MI355X (gfx950) residual vector quantization library.
+ *
+ * Plain C99, extern "C", no HIP or torch types in any signature. Only the
+ * rvq_* symbols below are exported from librvq.so; everything else is built
+ * with hidden visibility.
+ *
+ * What the operations compute follows the "RVQ codec" section of the
+ * "Architecture" page (omnivoice.cpp port of OmniVoice / Higgs-Audio-v2):
+ *   - encode is the residual loop: for stage q = 0..Q-1, pick the codeword
+ *     of codebook q nearest (squared L2) to the current residual, emit its
+ *     index, subtract the codeword from the residual;
+ *   - decode is the per-codebook gather and accumulate: gather row
+ *     codes[n, q] of codebook q and add it to an accumulator, q ascending.
+ * The codebooks act directly on the D-dim latent (identity per-stage
+ * projections). The code layout is frame-major [N, Q], as in gotcha 8 of
+ * the "Maintainer's guide -- moss-tts.cpp" page ("ne0 = NQ, ne1 = T").
+ *
+ * Numerical contract:
+ *   - ties in distance go to the lowest codeword index;
+ *   - the pick of every stage equals the argmin of the float64 direct-form
+ *     distance sum_j (r_j - c_j)^2 (j ascending, one rounding per
+ *     operation) over all K codewords. Scores are computed on fp32 matrix
+ *     cores; every codeword whose fp32 score lies within a proven error
+ *     bound of the best is re-ranked with that float64 sum, so the fp32
+ *     rounding never decides a pick;
+ *   - residuals are float32, r <- fl32(r - c) per element;
+ *   - decode (and the reconstruction of rvq_roundtrip) is a float32 sum
+ *     that starts at +0 and adds stage 0 first.
+ *
+ * Memory, ownership, streams:
+ *   - every array argument is DEVICE memory owned by the caller (for
+ *     example a torch tensor's data pointer). The library never allocates,
+ *     frees or keeps a caller buffer, and keeps no state between calls;
+ *   - float arrays must be 16-byte aligned, int32 arrays 4-byte aligned;
+ *   - all arrays are dense row-major:
+ *       x, residual, recon, out   [n_frames, dim]          float32
+ *       codebooks                 [n_stages, n_codes, dim] float32
+ *       codes                     [n_frames, codes_ld]     int32, columns 0..n_stages-1 used
+ *     Passing n_stages smaller than the codebook tensor's stage count uses
+ *     its first n_stages codebooks (bitrate control: first k of Q stages);
+ *   - `stream` is a hipStream_t cast to void* (NULL = the default stream).
+ *     Calls enqueue work and return; results are ready once the stream has
+ *     been synchronised. Calls on different streams may overlap safely as
+ *     long as their output buffers do not alias;
+ *   - argument errors are reported synchronously, before anything is
+ *     enqueued. A failed kernel launch returns RVQ_ERR_DEVICE; faults inside
+ *     a kernel surface at the caller's next synchronisation.
+ *
+ * Supported shapes: dim == 64; n_codes >= 1; 1 <= n_stages <= 65536;
+ * n_frames >= 0 (0 is a no-op that returns RVQ_OK and touches nothing).
+ * Inputs must be finite; non-finite values give unspecified codes, but no
+ * out-of-bounds access.
+ */
+#ifndef RVQ_H
+#define RVQ_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define RVQ_API __attribute__((visibility("default")))
+#else
+#define RVQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RVQ_VERSION_MAJOR 0
+#define RVQ_VERSION_MINOR 1
+#define RVQ_VERSION_PATCH 0
+
+/* Status codes: 0 on success, negative on failure (no output written). */
+typedef enum rvq_status {
+    RVQ_OK = 0,
+    RVQ_ERR_INVALID_ARG = -1,  /* null pointer, negative size, codes_ld < n_stages, misalignment */
+    RVQ_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape (dim != 64, n_stages > 65536) */
+    RVQ_ERR_DEVICE = -3        /* the HIP runtime refused the launch or has no device */
+} rvq_status;
+
+/* Static string "MAJOR.MINOR.PATCH (gfx950)". Never NULL. */
+RVQ_API const char *rvq_version(void);
+
+/* Static, human-readable name of a status code. Never NULL. */
+RVQ_API const char *rvq_status_string(rvq_status status);
+
+/*
+ * rvq_encode -- greedy residual encode of n_frames latents.
+ *
+ *   x          [n_frames, dim] input latents (read only)
+ *   codebooks  [n_stages, n_codes, dim] (read only)
+ *   codes      [n_frames, codes_ld] output; column q receives stage q's pick
+ *   residual   [n_frames, dim] output, the residual left after the last
+ *              stage; NULL to skip it
+ *
+ * The "RVQ codec" section of the "Architecture" page: residual loop.
+ */
+RVQ_API rvq_status rvq_encode(const float *x, int64_t n_frames, int32_t dim,
+                              const float *codebooks, int32_t n_stages, int32_t n_codes,
+                              int32_t *codes, int32_t codes_ld,
+                              float *residual, void *stream);
+
+/*
+ * rvq_decode -- gather-sum decode.
+ *
+ *   codes      [n_frames, codes_ld] input; columns 0..n_stages-1 are read
+ *   codebooks  [n_stages, n_codes, dim] (read only)
+ *   out        [n_frames, dim] output, out[n] = sum_q codebooks[q, codes[n, q]]
+ *
+ * A code outside [0, n_codes) is a caller error: that frame's output row is
+ * all quiet NaN and nothing outside the codebooks is read.
+ *
+ * The "RVQ codec" section of the "Architecture" page: per-codebook
+ * get_rows, accumulated codebook 0 first.
+ */
+RVQ_API rvq_status rvq_decode(const int32_t *codes, int32_t codes_ld, int64_t n_frames,
+                              const float *codebooks, int32_t n_stages, int32_t n_codes,
+                              int32_t dim, float *out, void *stream);
+
+/*
+ * rvq_roundtrip -- encode, and reconstruct in the same pass.
+ *
+ * Same arguments as rvq_encode plus
+ *   recon      [n_frames, dim] output, equal bit for bit to what rvq_decode
+ *              returns for the codes written by this call.
+ * residual may be NULL. This is the encode-then-decode reconstruction that
+ * the moss-tts.cpp codec API calls "reconstruct" ("Maintainer's guide --
+ * moss-tts.cpp", layout section), done without a second pass over memory.
+ */
+RVQ_API rvq_status rvq_roundtrip(const float *x, int64_t n_frames, int32_t dim,
+                                 const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                 int32_t *codes, int32_t codes_ld,
+                                 float *recon, float *residual, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RVQ_H */

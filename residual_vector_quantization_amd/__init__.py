@@ -1,0 +1,181 @@
+"""Residual vector quantization on MI355X (gfx950): Python binding of librvq.
+
+Thin ctypes layer over the C ABI in ``include/rvq.h``. It checks tensor
+dtypes, devices and layouts, allocates outputs with ``torch.empty`` on the
+input's device, and passes raw device pointers plus the current HIP stream.
+Every step of encode and decode runs in the HIP kernels of ``librvq.so``;
+there is no CPU or PyTorch fallback. If the library is missing the import
+still works, but every call raises.
+
+Functions (same names as the C entry points):
+
+* ``rvq_encode(x, codebooks, n_stages=None, residual=True)``
+  -> ``(codes [N, Q] int32, residual [N, D] float32 or None)``
+* ``rvq_decode(codes, codebooks, n_stages=None)`` -> ``out [N, D] float32``
+* ``rvq_roundtrip(x, codebooks, n_stages=None, residual=True)``
+  -> ``(codes, recon, residual or None)``
+* ``rvq_version()``, ``rvq_status_string(status)``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "librvq.so")
+
+RVQ_OK = 0
+RVQ_ERR_INVALID_ARG = -1
+RVQ_ERR_UNSUPPORTED = -2
+RVQ_ERR_DEVICE = -3
+
+EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip")
+
+_lib = None
+
+
+class RVQError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {message} ({status})")
+        self.status = status
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Loads librvq.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing; build it with `python -m residual_vector_quantization_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.rvq_version.restype = ctypes.c_char_p
+    lib.rvq_version.argtypes = []
+    lib.rvq_status_string.restype = ctypes.c_char_p
+    lib.rvq_status_string.argtypes = [ctypes.c_int]
+    lib.rvq_encode.restype = ctypes.c_int
+    lib.rvq_encode.argtypes = [vp, i64, i32, vp, i32, i32, vp, i32, vp, vp]
+    lib.rvq_decode.restype = ctypes.c_int
+    lib.rvq_decode.argtypes = [vp, i32, i64, vp, i32, i32, i32, vp, vp]
+    lib.rvq_roundtrip.restype = ctypes.c_int
+    lib.rvq_roundtrip.argtypes = [vp, i64, i32, vp, i32, i32, vp, i32, vp, vp, vp]
+    _lib = lib
+    return lib
+
+
+def rvq_version() -> str:
+    return load().rvq_version().decode()
+
+
+def rvq_status_string(status: int) -> str:
+    return load().rvq_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != RVQ_OK:
+        raise RVQError(fn, status, rvq_status_string(status))
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require(t: torch.Tensor, name: str, dtype: torch.dtype, dims: int, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stages(codebooks: torch.Tensor, n_stages: Optional[int]) -> int:
+    q = codebooks.shape[0] if n_stages is None else int(n_stages)
+    if not 0 < q <= codebooks.shape[0]:
+        raise ValueError(f"n_stages={q} outside 1..{codebooks.shape[0]}")
+    return q
+
+
+def rvq_encode(x: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[int] = None,
+               residual: bool = True, codes: Optional[torch.Tensor] = None,
+               residual_out: Optional[torch.Tensor] = None):
+    """Greedy residual encode of ``x`` [N, D] against ``codebooks`` [Q, K, D].
+
+    Returns ``(codes [N, Q] int32, residual [N, D] float32 or None)``. ``codes``
+    may be a preallocated [N, L] int32 tensor with L >= Q (columns 0..Q-1 are
+    written); ``residual_out`` a preallocated [N, D] float32 tensor.
+    """
+    _require(x, "x", torch.float32, 2)
+    _require(codebooks, "codebooks", torch.float32, 3, x.device)
+    n, d = x.shape
+    q = _stages(codebooks, n_stages)
+    if codes is None:
+        codes = torch.empty((n, q), dtype=torch.int32, device=x.device)
+    _require(codes, "codes", torch.int32, 2, x.device)
+    if codes.shape[0] != n:
+        raise ValueError("codes must have one row per frame")
+    res = None
+    if residual:
+        res = residual_out if residual_out is not None else torch.empty_like(x)
+        _require(res, "residual", torch.float32, 2, x.device)
+        if res.shape != x.shape:
+            raise ValueError("residual must match x")
+    st = load().rvq_encode(_ptr(x), n, d, _ptr(codebooks), q, codebooks.shape[1],
+                           _ptr(codes), codes.shape[1], _ptr(res), _stream(x))
+    _check("rvq_encode", st)
+    return codes, res
+
+
+def rvq_decode(codes: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[int] = None,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Gather-sum decode: ``codes`` [N, L] int32 (first Q columns) -> [N, D] float32."""
+    _require(codes, "codes", torch.int32, 2)
+    _require(codebooks, "codebooks", torch.float32, 3, codes.device)
+    n = codes.shape[0]
+    q = codes.shape[1] if n_stages is None else int(n_stages)
+    if not 0 < q <= min(codes.shape[1], codebooks.shape[0]):
+        raise ValueError(f"n_stages={q} does not fit codes {tuple(codes.shape)} / codebooks")
+    d = codebooks.shape[2]
+    if out is None:
+        out = torch.empty((n, d), dtype=torch.float32, device=codes.device)
+    _require(out, "out", torch.float32, 2, codes.device)
+    if out.shape != (n, d):
+        raise ValueError("out must be [N, D]")
+    st = load().rvq_decode(_ptr(codes), codes.shape[1], n, _ptr(codebooks), q, codebooks.shape[1],
+                           d, _ptr(out), _stream(codes))
+    _check("rvq_decode", st)
+    return out
+
+
+def rvq_roundtrip(x: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[int] = None,
+                  residual: bool = True):
+    """Encode and reconstruct in one pass: ``(codes, recon, residual or None)``.
+
+    ``recon`` equals ``rvq_decode(codes, codebooks)`` bit for bit.
+    """
+    _require(x, "x", torch.float32, 2)
+    _require(codebooks, "codebooks", torch.float32, 3, x.device)
+    n, d = x.shape
+    q = _stages(codebooks, n_stages)
+    codes = torch.empty((n, q), dtype=torch.int32, device=x.device)
+    recon = torch.empty_like(x)
+    res = torch.empty_like(x) if residual else None
+    st = load().rvq_roundtrip(_ptr(x), n, d, _ptr(codebooks), q, codebooks.shape[1],
+                              _ptr(codes), q, _ptr(recon), _ptr(res), _stream(x))
+    _check("rvq_roundtrip", st)
+    return codes, recon, res

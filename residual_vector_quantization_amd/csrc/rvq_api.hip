@@ -1,0 +1,94 @@
+// C ABI of librvq: argument validation, then one kernel launch on the
+// caller's stream. Declarations, layouts and the numerical contract are in
+// include/rvq.h. No allocation, no global state.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "rvq.h"
+#include "rvq_internal.h"
+
+namespace {
+
+constexpr int32_t kMaxStages = 65536;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Shape checks shared by every entry point; pointers are checked by callers.
+rvq_status check_shape(int64_t n_frames, int32_t dim, int32_t n_stages, int32_t n_codes)
+{
+    if (n_frames < 0 || dim <= 0 || n_stages <= 0 || n_codes <= 0) return RVQ_ERR_INVALID_ARG;
+    if (dim != rvq::kDim || n_stages > kMaxStages) return RVQ_ERR_UNSUPPORTED;
+    return RVQ_OK;
+}
+
+rvq_status from_hip(hipError_t e) { return e == hipSuccess ? RVQ_OK : RVQ_ERR_DEVICE; }
+
+rvq_status encode_common(const float *x, int64_t n_frames, int32_t dim, const float *books,
+                         int32_t n_stages, int32_t n_codes, int32_t *codes, int32_t codes_ld,
+                         float *recon, bool want_recon, float *residual, void *stream)
+{
+    rvq_status st = check_shape(n_frames, dim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (codes_ld < n_stages) return RVQ_ERR_INVALID_ARG;
+    if (n_frames == 0) return RVQ_OK;
+    if (!x || !books || !codes || (want_recon && !recon)) return RVQ_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(books, 16) || !aligned(codes, 4) ||
+        (recon && !aligned(recon, 16)) || (residual && !aligned(residual, 16)))
+        return RVQ_ERR_INVALID_ARG;
+    return from_hip(rvq::launch_encode(x, n_frames, books, n_stages, n_codes, codes, codes_ld,
+                                       residual, recon, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+RVQ_API const char *rvq_version(void)
+{
+    return "0.1.0 (gfx950)";
+}
+
+RVQ_API const char *rvq_status_string(rvq_status status)
+{
+    switch (status) {
+    case RVQ_OK: return "ok";
+    case RVQ_ERR_INVALID_ARG: return "invalid argument";
+    case RVQ_ERR_UNSUPPORTED: return "unsupported shape";
+    case RVQ_ERR_DEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+RVQ_API rvq_status rvq_encode(const float *x, int64_t n_frames, int32_t dim,
+                              const float *codebooks, int32_t n_stages, int32_t n_codes,
+                              int32_t *codes, int32_t codes_ld, float *residual, void *stream)
+{
+    return encode_common(x, n_frames, dim, codebooks, n_stages, n_codes, codes, codes_ld,
+                         nullptr, false, residual, stream);
+}
+
+RVQ_API rvq_status rvq_roundtrip(const float *x, int64_t n_frames, int32_t dim,
+                                 const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                 int32_t *codes, int32_t codes_ld, float *recon,
+                                 float *residual, void *stream)
+{
+    return encode_common(x, n_frames, dim, codebooks, n_stages, n_codes, codes, codes_ld,
+                         recon, true, residual, stream);
+}
+
+RVQ_API rvq_status rvq_decode(const int32_t *codes, int32_t codes_ld, int64_t n_frames,
+                              const float *codebooks, int32_t n_stages, int32_t n_codes,
+                              int32_t dim, float *out, void *stream)
+{
+    rvq_status st = check_shape(n_frames, dim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (codes_ld < n_stages) return RVQ_ERR_INVALID_ARG;
+    if (n_frames == 0) return RVQ_OK;
+    if (!codes || !codebooks || !out) return RVQ_ERR_INVALID_ARG;
+    if (!aligned(codes, 4) || !aligned(codebooks, 16) || !aligned(out, 16)) return RVQ_ERR_INVALID_ARG;
+    return from_hip(rvq::launch_decode(codes, codes_ld, n_frames, codebooks, n_stages, n_codes, out,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Internal launch interface between the C ABI layer (rvq_api.hip) and the
+// kernels (encode.hip, decode.hip). Not installed, not exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rvq {
+
+// Latent / codeword dimension the kernels are built for.
+constexpr int kDim = 64;
+
+// Encode: frames per workgroup (4 wavefronts x 32 frames).
+constexpr int kEncodeFramesPerBlock = 128;
+constexpr int kEncodeThreads = 256;
+
+// Decode: 16 lanes per frame (one float4 each), 256 threads per workgroup.
+constexpr int kDecodeLanesPerFrame = 16;
+constexpr int kDecodeThreads = 256;
+
+// Launches the fused multi-stage encode. `residual` and `recon` may be null.
+hipError_t launch_encode(const float *x, int64_t n_frames, const float *books,
+                         int n_stages, int n_codes, int32_t *codes, int codes_ld,
+                         float *residual, float *recon, hipStream_t stream);
+
+// Launches the gather-sum decode.
+hipError_t launch_decode(const int32_t *codes, int codes_ld, int64_t n_frames,
+                         const float *books, int n_stages, int n_codes, float *out,
+                         hipStream_t stream);
+
+}  // namespace rvq

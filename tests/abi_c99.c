@@ -1,0 +1,44 @@
+/* Plain C99 consumer of include/rvq.h: compiled with -std=c99 -Wall -Werror
+ * -pedantic by tests/test_abi.py, and run on the CPU. Every call below takes
+ * an early-return path (argument checks or the n_frames == 0 no-op), so no
+ * GPU is touched. */
+#include <stdio.h>
+#include <string.h>
+
+#include "rvq.h"
+
+static int expect(const char *what, rvq_status got, rvq_status want)
+{
+    if (got != want) {
+        printf("FAIL %s: got %d (%s), want %d\n", what, (int)got, rvq_status_string(got), (int)want);
+        return 1;
+    }
+    return 0;
+}
+
+int main(void)
+{
+    int bad = 0;
+    float *fx = (float *)0x1000;  /* never dereferenced: each call fails validation first */
+    int32_t *ic = (int32_t *)0x2000;
+    if (strlen(rvq_version()) == 0) bad++;
+    bad += expect("status string", strcmp(rvq_status_string(RVQ_ERR_DEVICE), "device error") == 0 ? RVQ_OK : RVQ_ERR_INVALID_ARG, RVQ_OK);
+    bad += expect("encode null x", rvq_encode(NULL, 10, 64, fx, 8, 1024, ic, 8, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("encode n<0", rvq_encode(fx, -1, 64, fx, 8, 1024, ic, 8, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("encode dim 32", rvq_encode(fx, 10, 32, fx, 8, 1024, ic, 8, NULL, NULL), RVQ_ERR_UNSUPPORTED);
+    bad += expect("encode q 0", rvq_encode(fx, 10, 64, fx, 0, 1024, ic, 8, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("encode k 0", rvq_encode(fx, 10, 64, fx, 8, 0, ic, 8, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("encode ld<q", rvq_encode(fx, 10, 64, fx, 8, 1024, ic, 7, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("encode misaligned", rvq_encode(fx + 1, 10, 64, fx, 8, 1024, ic, 8, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("encode too many stages", rvq_encode(fx, 10, 64, fx, 70000, 1024, ic, 70000, NULL, NULL), RVQ_ERR_UNSUPPORTED);
+    bad += expect("encode empty", rvq_encode(NULL, 0, 64, NULL, 8, 1024, NULL, 8, NULL, NULL), RVQ_OK);
+    bad += expect("roundtrip null recon", rvq_roundtrip(fx, 10, 64, fx, 8, 1024, ic, 8, NULL, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("roundtrip empty", rvq_roundtrip(NULL, 0, 64, NULL, 8, 1024, NULL, 8, NULL, NULL, NULL), RVQ_OK);
+    bad += expect("decode null out", rvq_decode(ic, 8, 10, fx, 8, 1024, 64, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("decode dim 16", rvq_decode(ic, 8, 10, fx, 8, 1024, 16, fx, NULL), RVQ_ERR_UNSUPPORTED);
+    bad += expect("decode ld<q", rvq_decode(ic, 4, 10, fx, 8, 1024, 64, fx, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("decode misaligned out", rvq_decode(ic, 8, 10, fx, 8, 1024, 64, fx + 2, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("decode empty", rvq_decode(NULL, 8, 0, NULL, 8, 1024, 64, NULL, NULL), RVQ_OK);
+    printf("%s\n", bad ? "abi_c99: FAILED" : "abi_c99: ok");
+    return bad ? 1 : 0;
+}

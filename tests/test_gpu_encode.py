@@ -1,0 +1,168 @@
+"""GPU parity of rvq_encode / rvq_roundtrip against the CPU oracle."""
+
+import numpy as np
+import pytest
+
+import rvq_workloads as W
+from gpu_util import needs_gpu, check_encode, rvq, to_dev, host, announce
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _books(rng, q, k, d=64, decay=0.5):
+    return (rng.standard_normal((q, k, d)) * decay ** np.arange(q)[:, None, None]).astype(np.float32)
+
+
+def test_tiny_workload_recovers_construction():
+    w = W.WORKLOADS["tiny"]
+    books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
+    x, t = W.latents(w, books)
+    check_encode(x, books)
+    m = rvq()
+    codes, _ = m.rvq_encode(to_dev(x), to_dev(books))
+    np.testing.assert_array_equal(host(codes), t)
+
+
+def test_clip_workload_full():
+    w = W.WORKLOADS["clip"]
+    books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
+    x, _ = W.latents(w, books)
+    check_encode(x, books)
+
+
+@pytest.mark.parametrize("n", [1, 31, 129, 677])
+def test_ragged_frame_counts(n):
+    rng = np.random.default_rng(100 + n)
+    books = _books(rng, 8, 1024)
+    x = rng.standard_normal((n, 64)).astype(np.float32)
+    check_encode(x, books)
+
+
+@pytest.mark.parametrize("k", [1, 63, 64, 65, 100, 1000, 4096])
+def test_codebook_sizes(k):
+    rng = np.random.default_rng(200 + k)
+    q = 10 if k == 4096 else 3
+    books = _books(rng, q, k)
+    x = rng.standard_normal((300, 64)).astype(np.float32)
+    check_encode(x, books)
+
+
+@pytest.mark.parametrize("q,decay", [(1, 1.0), (32, 0.85), (64, 0.9)])
+def test_stage_counts(q, decay):
+    rng = np.random.default_rng(300 + q)
+    k = 256 if q == 64 else 1024
+    books = _books(rng, q, k, decay=decay)
+    x = rng.standard_normal((257, 64)).astype(np.float32)
+    check_encode(x, books)
+
+
+def test_partial_depth_prefix():
+    """Encoding with the first k of Q stages gives the first k codes (bitrate control)."""
+    rng = np.random.default_rng(7)
+    books = _books(rng, 8, 1024)
+    x = rng.standard_normal((400, 64)).astype(np.float32)
+    check_encode(x, books, n_stages=3)
+    m = rvq()
+    full, _ = m.rvq_encode(to_dev(x), to_dev(books))
+    part, _ = m.rvq_encode(to_dev(x), to_dev(books), n_stages=3)
+    np.testing.assert_array_equal(host(part), host(full)[:, :3])
+
+
+def test_exact_ties_integer_data():
+    """Small integers: exact scores, many exact ties and duplicated rows (lowest index wins)."""
+    rng = np.random.default_rng(8)
+    books = rng.integers(-3, 4, size=(4, 128, 64)).astype(np.float32)
+    books[:, 100:128] = books[:, 0:28]
+    x = rng.integers(-6, 7, size=(500, 64)).astype(np.float32)
+    check_encode(x, books)
+
+
+def test_all_rows_identical():
+    rng = np.random.default_rng(9)
+    books = np.repeat(rng.standard_normal((3, 1, 64)).astype(np.float32), 192, axis=1)
+    x = rng.standard_normal((130, 64)).astype(np.float32)
+    check_encode(x, books)
+    codes, _ = rvq().rvq_encode(to_dev(x), to_dev(books))
+    assert (host(codes) == 0).all()
+
+
+def test_zero_inputs_and_codebooks():
+    x = np.zeros((70, 64), np.float32)
+    books = np.zeros((2, 128, 64), np.float32)
+    check_encode(x, books)
+
+
+@pytest.mark.parametrize("scale", [1e-6, 1e6])
+def test_scaled_data(scale):
+    rng = np.random.default_rng(10)
+    books = (_books(rng, 4, 512) * scale).astype(np.float32)
+    x = (rng.standard_normal((200, 64)) * scale).astype(np.float32)
+    check_encode(x, books)
+
+
+def test_codes_leading_dimension():
+    rng = np.random.default_rng(11)
+    books = _books(rng, 4, 256)
+    x = rng.standard_normal((150, 64)).astype(np.float32)
+    import torch
+    m = rvq()
+    codes = torch.full((150, 7), -5, dtype=torch.int32, device="cuda:0")
+    m.rvq_encode(to_dev(x), to_dev(books), codes=codes)
+    ref, _ = m.rvq_encode(to_dev(x), to_dev(books))
+    c = host(codes)
+    np.testing.assert_array_equal(c[:, :4], host(ref))
+    assert (c[:, 4:] == -5).all()
+
+
+def test_deterministic_and_batch_invariant():
+    rng = np.random.default_rng(12)
+    books = _books(rng, 8, 1024)
+    x = rng.standard_normal((1000, 64)).astype(np.float32)
+    m = rvq()
+    a, ra = m.rvq_encode(to_dev(x), to_dev(books))
+    b, rb = m.rvq_encode(to_dev(x), to_dev(books))
+    np.testing.assert_array_equal(host(a), host(b))
+    np.testing.assert_array_equal(host(ra), host(rb))
+    perm = rng.permutation(1000)[:333]
+    c, rc = m.rvq_encode(to_dev(x[perm]), to_dev(books))
+    np.testing.assert_array_equal(host(c), host(a)[perm])
+    np.testing.assert_array_equal(host(rc), host(ra)[perm])
+
+
+def test_empty_batch_is_noop():
+    import torch
+    m = rvq()
+    books = to_dev(np.zeros((2, 64, 64), np.float32))
+    codes, res = m.rvq_encode(torch.empty((0, 64), device="cuda:0"), books)
+    assert codes.shape == (0, 2) and res.shape == (0, 64)
+    out = m.rvq_decode(torch.empty((0, 2), dtype=torch.int32, device="cuda:0"), books)
+    assert out.shape == (0, 64)
+
+
+@pytest.mark.parametrize("name,count", [("batched", 4096), ("deep", 2048)])
+def test_full_size_workloads_sampled(name, count):
+    """Full-size batches in the benchmark's launch configuration; oracle on a seeded sample."""
+    w = W.WORKLOADS[name]
+    books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
+    x, t = W.latents(w, books)
+    idx = W.sample_frames(w.n_frames, count, seed=3)
+    rep = check_encode(x, books, idx=idx)
+    announce("full-size report", **rep)
+    if w.constructed_from < w.n_frames:
+        m = rvq()
+        codes, _ = m.rvq_encode(to_dev(x), to_dev(books))
+        c = host(codes)[w.constructed_from:]
+        frac = (c == t[w.constructed_from:]).all(axis=1).mean()
+        announce("constructed recovery", frac=frac)
+
+
+def test_argument_errors():
+    import torch
+    m = rvq()
+    x = torch.zeros((10, 32), device="cuda:0")
+    books = torch.zeros((2, 64, 32), device="cuda:0")
+    with pytest.raises(m.RVQError) as e:
+        m.rvq_encode(x, books)
+    assert e.value.status == m.RVQ_ERR_UNSUPPORTED
+    assert m.rvq_encode(torch.zeros((10, 64), device="cuda:0"),
+                        torch.zeros((2, 64, 64), device="cuda:0"))[0].shape == (10, 2)
