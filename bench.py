@@ -43,7 +43,22 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU-oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain elementwise copy of 512 MiB (for HBM counter scaling)")
     return p.parse_args()
+
+
+def recorded_traffic(kernel_source, summary):
+    """HBM bytes per launch from a committed counter summary, or None if the kernel changed since."""
+    import hashlib
+    path = os.path.join(_ROOT, "profiles", summary)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc", kernel_source)
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("traffic_bytes_per_launch")
 
 
 def cpu_baseline(w, x, books, codes_gpu, target_s):
@@ -128,6 +143,13 @@ def main():
     dec_bytes = (4.0 * q + 4.0 * d) * n
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
 
+    if args.calibrate_copy:
+        a = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        del a, b
+
     codes_h = codes.cpu().numpy()
     rec = {
         "metric": METRIC,
@@ -149,11 +171,12 @@ def main():
         "decode_ms": dec_ms,
         "roofline": {"bound": "mfma", "kernel": "encode_kernel (fp32 v_mfma_f32_32x32x2_f32)",
                      "achieved": enc_tflops, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": enc_tflops / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                     "frac": enc_tflops / PEAK_FP32_MFMA_TFLOPS,
+                     "traffic": recorded_traffic("encode.hip", f"encode_{w.name}_hbm_counters.json"),
                      "work_per_launch": f"2*Q*K*D*N = {enc_flop:.4g} flop"},
         "decode_roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": dec_gbps,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
-                            "traffic": None,
+                            "traffic": recorded_traffic("decode.hip", f"decode_{w.name}_hbm_counters.json"),
                             "work_per_launch": f"(4Q+4D)*N = {dec_bytes:.4g} B"},
     }
     if not args.no_cpu_baseline:

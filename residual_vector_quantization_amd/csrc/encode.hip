@@ -9,7 +9,7 @@
 //     for all Q stages, so a frame's argmin never leaves its wavefront.
 //   * Residuals stay in VGPRs for the whole call. Lane l holds frame l%32;
 //     lanes 0-31 keep dims 0..31, lanes 32-63 keep dims 32..63.
-//   * Codebooks stream through LDS in chunks of 64 codewords (double
+//   * Codebooks stream through LDS in chunks of 128 codewords (double
 //     buffered, one barrier per chunk). While staging, each codeword is
 //     negated and 0.5*||c||^2 is computed beside it.
 //   * Scores on fp32 matrix cores: v_mfma_f32_32x32x2_f32 with codewords on
@@ -35,6 +35,8 @@
 #include <float.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include <hip/hip_runtime.h>
 
 #include "rvq_internal.h"
@@ -48,13 +50,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kFramesPerWave = 32;
-constexpr int kChunk = 64;          // codewords per LDS chunk
+constexpr int kChunk = 128;         // codewords per LDS chunk
 constexpr int kRow = kDim + 4;      // padded LDS row (floats): 8 lanes of a b128 read hit 32 banks
 constexpr int kBlocksPerChunk = kChunk / 32;
 
 static_assert(kThreads == kEncodeThreads, "thread count");
 static_assert(kWaves * kFramesPerWave == kEncodeFramesPerBlock, "frames per block");
-static_assert(kThreads == 4 * kChunk, "staging maps 4 threads to a codeword row");
+static_assert(kThreads == 2 * kChunk, "staging maps 2 threads to a codeword row");
 
 // gamma_n = n*u / (1 - n*u), u = 2^-24, n = 2D + 2 roundings bound one score.
 constexpr float kUnit = 5.9604644775390625e-08f;
@@ -119,10 +121,10 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
     const int n_chunks = (n_codes + kChunk - 1) / kChunk;
     const int total = n_stages * n_chunks;
 
-    // Staging role: thread -> (codeword row, 16-float slice of it).
-    const int srow = tid >> 2;
-    const int scol = (tid & 3) * 16;
-    f32x4 stage[4];
+    // Staging role: thread -> (codeword row, 32-float half of it).
+    const int srow = tid >> 1;
+    const int scol = (tid & 1) * 32;
+    f32x4 stage[8];
 
     auto fetch = [&](int g) {
         const int q = g / n_chunks;
@@ -131,31 +133,31 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
             const f32x4 *p = reinterpret_cast<const f32x4 *>(
                 books + (static_cast<int64_t>(q) * n_codes + k) * kDim + scol);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) stage[i] = p[i];
+            for (int i = 0; i < 8; ++i) stage[i] = p[i];
         } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) stage[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int i = 0; i < 8; ++i) stage[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     };
     auto commit = [&](int buf) {
         float s = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) s = s + stage[i][e] * stage[i][e];
         s = s + __shfl_xor(s, 1);
-        s = s + __shfl_xor(s, 2);
         float *dst = &s_book[buf][srow * kRow + scol];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(dst + 4 * i) = -stage[i];
-        if ((tid & 3) == 0) s_norm[buf][srow] = 0.5f * s;
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(dst + 4 * i) = -stage[i];
+        if ((tid & 1) == 0) s_norm[buf][srow] = 0.5f * s;
     };
 
     fetch(0);
     commit(0);
     __syncthreads();
 
-    float best = INFINITY, second = INFINITY, cmax = 0.0f;
+    float best = INFINITY, second = INFINITY;
+    unsigned cmax = 0u;       // bits of max 0.5*||c||^2 seen by this lane in this stage
     int best_k = 0;
 
     for (int g = 0; g < total; ++g) {
@@ -174,7 +176,9 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const f32x4 nv = *reinterpret_cast<const f32x4 *>(sn + b * 32 + 8 * m + 4 * half);
-                    cmax = fmaxf(cmax, fmaxf(fmaxf(nv[0], nv[1]), fmaxf(nv[2], nv[3])));
+                    // norms are >= 0, so their bit patterns order like the values
+                    cmax = max(cmax, max(max(__float_as_uint(nv[0]), __float_as_uint(nv[1])),
+                                         max(__float_as_uint(nv[2]), __float_as_uint(nv[3]))));
 #pragma unroll
                     for (int e = 0; e < 4; ++e) d[b][4 * m + e] = nv[e];
                 }
@@ -191,20 +195,31 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
                     for (int b = 0; b < kBlocksPerChunk; ++b)
                         d[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[b][e], r[4 * t + e], d[b], 0, 0, 0);
             }
-            const bool tail = (c + 1) * kChunk > n_codes;
+            // Running best / second-best over this lane's scores. The index is
+            // kept chunk-local (a compile-time constant per accumulator) and
+            // folded into best_k once per chunk.
+            auto update = [&](auto masked) {
+                int loc = -1;
 #pragma unroll
-            for (int b = 0; b < kBlocksPerChunk; ++b) {
+                for (int b = 0; b < kBlocksPerChunk; ++b) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    // accumulator v of this lane is codeword row 8*(v/4) + 4*half + v%4
-                    const int k = c * kChunk + b * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-                    float s = d[b][v];
-                    if (tail && k >= n_codes) s = INFINITY;
-                    second = __builtin_amdgcn_fmed3f(s, best, second);
-                    best_k = (s < best) ? k : best_k;
-                    best = fminf(best, s);
+                    for (int v = 0; v < 16; ++v) {
+                        // accumulator v of this lane is codeword row 8*(v/4) + 4*half + v%4
+                        const int lk = b * 32 + 8 * (v >> 2) + (v & 3);
+                        float sc = d[b][v];
+                        if (decltype(masked)::value && c * kChunk + lk + 4 * half >= n_codes) sc = INFINITY;
+                        second = __builtin_amdgcn_fmed3f(sc, best, second);
+                        const bool lt = sc < best;
+                        loc = lt ? lk : loc;
+                        best = lt ? sc : best;
+                    }
                 }
-            }
+                if (loc >= 0) best_k = c * kChunk + 4 * half + loc;
+            };
+            if ((c + 1) * kChunk > n_codes)
+                update(std::true_type{});
+            else
+                update(std::false_type{});
         }
 
         if (g + 1 < total) commit(buf ^ 1);
@@ -214,13 +229,13 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
             const float best_o = __shfl_xor(best, 32);
             const float second_o = __shfl_xor(second, 32);
             const int best_k_o = __shfl_xor(best_k, 32);
-            const float cmax_o = __shfl_xor(cmax, 32);
+            const unsigned cmax_o = __shfl_xor(cmax, 32);
             float rn = 0.0f;
 #pragma unroll
             for (int j = 0; j < 32; ++j) rn = rn + r[j] * r[j];
             rn = rn + __shfl_xor(rn, 32);
 
-            const float c2 = fmaxf(cmax, cmax_o);            // max_k 0.5*||c_k||^2
+            const float c2 = __uint_as_float(max(cmax, cmax_o));   // max_k 0.5*||c_k||^2
             const float bound = kSafety * kGamma * (c2 + sqrtf(rn) * sqrtf(2.0f * c2)) + kAbsSlack;
             const float m = fminf(best, best_o);
             const float lim = m + 2.0f * bound;
@@ -314,7 +329,7 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
             }
             best = INFINITY;
             second = INFINITY;
-            cmax = 0.0f;
+            cmax = 0u;
             best_k = 0;
         }
         __syncthreads();
