@@ -28,9 +28,9 @@
 //
 // Exactness
 //   The key of codeword k differs from the exact score by at most
-//       e = (gamma_{2D+2} * kSafety + 2^-17) * (0.5*||c_k||^2 + ||r||*||c_k||)
-//   (norm and dot product summed in fp32 in any order, plus the 6 bits the
-//   index replaces). Every codeword whose key lies within 2*e_max of the
+//       e = (2 * gamma_{2D+4} + 2^-17) * (0.5*||c_k||^2 + ||r||*||c_k||)
+//   (norm and dot product summed in fp32 in any order with at most 2u error
+//   per operation, plus the 6 bits the index replaces). Every codeword whose key lies within 2*e_max of the
 //   smallest key is a candidate for the true argmin, and nothing else can
 //   be. One candidate is the answer; two candidates (the two lane minima of
 //   the frame) are re-ranked with the float64 direct-form distance
@@ -62,11 +62,14 @@ static_assert(kThreads == kEncodeThreads, "thread count");
 static_assert(kWaves * kFramesPerWave == kEncodeFramesPerBlock, "frames per block");
 static_assert(kThreads == 2 * kChunk, "staging maps 2 threads to a codeword row");
 
-// gamma_n = n*u / (1 - n*u), u = 2^-24, n = 2D + 2 roundings bound one score.
+// gamma_n = n*u / (1 - n*u), u = 2^-24. A score is a D+1 term sum (norm
+// plus D products, each product rounded) started from a norm that is itself
+// a D-term fp32 sum: n = 2D + 4 roundings cover both.
 constexpr float kUnit = 5.9604644775390625e-08f;
-constexpr float kGamma = (2 * kDim + 2) * kUnit / (1.0f - (2 * kDim + 2) * kUnit);
-// Margin for matrix-core rounding that is not round-to-nearest per step.
-constexpr float kSafety = 4.0f;
+constexpr float kGamma = (2 * kDim + 4) * kUnit / (1.0f - (2 * kDim + 4) * kUnit);
+// Margin for matrix-core rounding that is not round-to-nearest: an error
+// of up to 2u per operation (truncation) is still covered.
+constexpr float kSafety = 2.0f;
 // Replacing the 6 low mantissa bits moves a value by less than 2^-17 of it.
 constexpr float kKeyError = 7.62939453125e-06f;
 constexpr float kBoundScale = kSafety * kGamma + kKeyError;
@@ -185,6 +188,7 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
     __shared__ __align__(16) float s_book[2][kChunk * kRow];
     __shared__ __align__(16) float s_norm[2][kChunk];
     __shared__ __align__(16) unsigned s_cmax[2][kWaves];   // per stage parity, per wavefront
+    __shared__ __align__(16) float s_frame[kWaves][kDim];  // rescan: one frame's residual
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -357,35 +361,53 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
                 if (rerank) pick = winner;
             }
 
-            // More than one candidate inside a lane: full float64 rescan.
+            // More than one candidate inside a lane: full float64 rescan of the
+            // frame by the whole wavefront, two codewords per lane at a time.
             uint64_t pending = __ballot(valid && overflow && half == 0);
             while (pending) {
                 const int f = __ffsll(static_cast<unsigned long long>(pending)) - 1;
                 pending &= pending - 1;
-                float rr[64];
+                // frame f's negated residual, broadcast through this wavefront's LDS row
+                if (col == f) {
 #pragma unroll
-                for (int j = 0; j < 32; ++j) {
-                    rr[j] = __shfl(n[j], f);
-                    rr[32 + j] = __shfl(n[j], f + 32);
+                    for (int t = 0; t < 8; ++t)
+                        *reinterpret_cast<f32x4 *>(&s_frame[wave][32 * half + 4 * t]) =
+                            f32x4{n[4 * t], n[4 * t + 1], n[4 * t + 2], n[4 * t + 3]};
                 }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                const float *rr = s_frame[wave];
                 double bd = INFINITY;
                 int bk = 0x7fffffff;
-                for (int k = lane; k < n_codes; k += 64) {
-                    const float *cw = books + (static_cast<int64_t>(q) * n_codes + k) * kDim;
-                    double s = 0.0;
-#pragma unroll
+                for (int k0 = lane; k0 < n_codes; k0 += 128) {
+                    const int k1 = k0 + 64;
+                    const bool has1 = k1 < n_codes;
+                    const float *c0 = books + (static_cast<int64_t>(q) * n_codes + k0) * kDim;
+                    const float *c1 = books + (static_cast<int64_t>(q) * n_codes + (has1 ? k1 : k0)) * kDim;
+                    double s0 = 0.0, s1 = 0.0;
+#pragma unroll 4
                     for (int t = 0; t < 16; ++t) {
-                        const f32x4 v = *reinterpret_cast<const f32x4 *>(cw + 4 * t);
+                        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(c0 + 4 * t);
+                        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(c1 + 4 * t);
+                        const f32x4 rv = *reinterpret_cast<const f32x4 *>(rr + 4 * t);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const double dd = __dadd_rn(static_cast<double>(rr[4 * t + e]),
-                                                        static_cast<double>(v[e]));
-                            s = __dadd_rn(s, __dmul_rn(dd, dd));
+                            const double rj = static_cast<double>(rv[e]);
+                            const double d0 = __dadd_rn(rj, static_cast<double>(v0[e]));
+                            const double d1 = __dadd_rn(rj, static_cast<double>(v1[e]));
+                            s0 = __dadd_rn(s0, __dmul_rn(d0, d0));
+                            s1 = __dadd_rn(s1, __dmul_rn(d1, d1));
                         }
                     }
-                    if (s < bd) {
-                        bd = s;
-                        bk = k;
+                    // k0 < k1 and both ascend, so strict "<" keeps the lowest index on ties
+                    if (s0 < bd) {
+                        bd = s0;
+                        bk = k0;
+                    }
+                    if (has1 && s1 < bd) {
+                        bd = s1;
+                        bk = k1;
                     }
                 }
 #pragma unroll
@@ -398,6 +420,9 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
                     }
                 }
                 if (col == f) pick = bk;
+                // all reads of s_frame[wave] are done before the next frame overwrites it
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_wave_barrier();
             }
 
             pick = min(max(pick, 0), n_codes - 1);
