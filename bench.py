@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain elementwise copy of 512 MiB (for HBM counter scaling)")
+    p.add_argument("--summarize-profiles", metavar="DIR",
+                   help="turn rocprofv3 CSV output under DIR (trace/, fetch/, write/, mfma/) into the "
+                        "summaries under profiles/, then exit")
     return p.parse_args()
 
 
@@ -59,6 +62,125 @@ def recorded_traffic(kernel_source, summary):
     if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp   # R = repository root
+rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o bench -- python3 $R/bench.py --workload {wl} --steps 20 --no-cpu-baseline
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
+rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
+python3 $R/bench.py --workload {wl} --summarize-profiles $R/gpurun_out/prof"""
+
+# MI355X: 8 XCDs, 256 CUs, 4 SIMDs per CU.
+N_XCD, N_SIMD = 8, 1024
+COPY_BYTES = 512 << 20
+
+
+def _csv(dirname, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(dirname, "**", f"*{suffix}"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {dirname}")
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def _kernel_of(name):
+    if "encode_kernel" in name:
+        return "encode"
+    if "decode_kernel" in name:
+        return "decode"
+    if "elementwise" in name and "MulFunctor" in name:
+        return "copy"
+    return None
+
+
+def _counter_means(rows, counter):
+    """Mean value of `counter` per dispatch, for each kernel kind (copy: the calibration mul)."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        kind = _kernel_of(r["Kernel_Name"])
+        if kind:
+            per.setdefault(kind, {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[kind][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def summarize_profiles(w, src_dir):
+    """Writes profiles/<kernel>_<workload>_* from the four rocprofv3 runs under src_dir."""
+    import hashlib
+    out_dir = os.path.join(_ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    cmds = PROFILE_COMMANDS.format(wl=w.name)
+    n, q, k, d = w.n_frames, w.n_stages, w.n_codes, w.dim
+
+    stats = _csv(os.path.join(src_dir, "trace"), "kernel_stats.csv")
+    lines = [f"# Kernel trace: encode + decode, workload `{w.name}`", "",
+             f"Workload: {w.description}.", "", "Commands (the summary is the last line's output):", "",
+             "```", cmds, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    avg = {}
+    for r in stats:
+        kind = _kernel_of(r["Name"]) or r["Name"][:40]
+        a = float(r["AverageNs"]) / 1e3
+        avg[kind] = a
+        lines.append(f"| {kind} | {r['Calls']} | {a:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    enc_flop = 2.0 * q * k * d * n
+    dec_bytes = (4.0 * q + 4.0 * d) * n
+    lines += ["", f"Encode: {enc_flop:.4g} algorithmic flop per launch (2QKD per frame) / "
+                  f"{avg['encode']:.1f} us = {enc_flop / avg['encode'] / 1e6:.1f} TFLOP/s "
+                  f"({enc_flop / avg['encode'] / 1e6 / PEAK_FP32_MFMA_TFLOPS:.1%} of {PEAK_FP32_MFMA_TFLOPS} fp32 MFMA).",
+              f"Decode: {dec_bytes:.4g} algorithmic bytes per launch ((4Q+4D) per frame) / "
+              f"{avg['decode']:.1f} us = {dec_bytes / avg['decode'] / 1e3:.0f} GB/s "
+              f"({dec_bytes / avg['decode'] / 1e3 / PEAK_HBM_GBPS:.1%} of {PEAK_HBM_GBPS:.0f} GB/s HBM)."]
+
+    fetch = _counter_means(_csv(os.path.join(src_dir, "fetch"), "counter_collection.csv"), "FETCH_SIZE")
+    write = _counter_means(_csv(os.path.join(src_dir, "write"), "counter_collection.csv"), "WRITE_SIZE")
+    f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
+    w_scale = COPY_BYTES / (write["copy"] * 1024.0)
+    algo = {"encode": (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d, "decode": dec_bytes + 4.0 * q * k * d}
+    lines += ["", "## HBM counters (per launch)", "",
+              f"A 512 MiB elementwise copy reads FETCH_SIZE = {fetch['copy']:.0f} KiB and WRITE_SIZE = "
+              f"{write['copy']:.0f} KiB, so counter readings are scaled by {f_scale:.3f} (fetch) and "
+              f"{w_scale:.3f} (write).", "",
+              "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB | algorithmic MB |",
+              "|---|---|---|---|---|---|"]
+    for kind, src in (("encode", "encode.hip"), ("decode", "decode.hip")):
+        rd = fetch[kind] * 1024.0 * f_scale
+        wr = write[kind] * 1024.0 * w_scale
+        lines.append(f"| {kind} | {fetch[kind]:.0f} | {write[kind]:.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+                     f"{algo[kind] / 1e6:.1f} |")
+        sha = hashlib.sha256(open(os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc", src),
+                                  "rb").read()).hexdigest()
+        json.dump({"kernel": kind, "workload": w.name, "source_sha256": sha,
+                   "fetch_kib": fetch[kind], "write_kib": write[kind],
+                   "copy_scale_fetch": f_scale, "copy_scale_write": w_scale,
+                   "traffic_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": algo[kind],
+                   "commands": cmds},
+                  open(os.path.join(out_dir, f"{kind}_{w.name}_hbm_counters.json"), "w"), indent=1)
+
+    mf = _csv(os.path.join(src_dir, "mfma"), "counter_collection.csv")
+    c = {name: _counter_means(mf, name).get("encode") for name in
+         ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU",
+          "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")}
+    active = c["GRBM_GUI_ACTIVE"] / N_XCD
+    lines += ["", "## Encode matrix-core counters (per launch)", "",
+              f"- MFMA busy: {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * N_SIMD):.1%} of SIMD cycles "
+              f"(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x {N_SIMD} SIMDs))",
+              f"- MFMA fp32 flop counted: {c['SQ_INSTS_VALU_MFMA_MOPS_F32'] * 512:.4g} "
+              f"(algorithmic {enc_flop:.4g})",
+              f"- VALU instructions (incl. MFMA): {c['SQ_INSTS_VALU']:.4g}",
+              f"- LDS bank-conflict cycles / LDS active cycles: "
+              f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1%}"]
+    path = os.path.join(out_dir, f"encode_decode_{w.name}_rocprof.md")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("wrote", path)
 
 
 def cpu_baseline(w, x, books, codes_gpu, target_s):
@@ -90,6 +212,9 @@ def cpu_baseline(w, x, books, codes_gpu, target_s):
 
 def main():
     args = parse()
+    if args.summarize_profiles:
+        summarize_profiles(W.WORKLOADS[args.workload], args.summarize_profiles)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(frames shard with no exchange, so N GPUs would each run this same kernel on N/G frames)",
