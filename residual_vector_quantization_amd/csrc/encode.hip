@@ -60,7 +60,7 @@ constexpr int kRow = kDim + 4;      // padded LDS row (floats): 8 lanes of a b12
 
 static_assert(kThreads == kEncodeThreads, "thread count");
 static_assert(kWaves * kFramesPerWave == kEncodeFramesPerBlock, "frames per block");
-static_assert(kThreads == 2 * kChunk, "staging maps 2 threads to a codeword row");
+static_assert(kWaves * 32 == kChunk, "staging maps each wavefront to 32 codeword rows");
 
 // gamma_n = n*u / (1 - n*u), u = 2^-24. A score is a D+1 term sum (norm
 // plus D products, each product rounded) started from a norm that is itself
@@ -219,9 +219,11 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
     const int n_chunks = (n_codes + kChunk - 1) / kChunk;
     const int total = n_stages * n_chunks;
 
-    // Staging role: thread -> (codeword row, 32-float half of it).
-    const int srow = tid >> 1;
-    const int scol = (tid & 1) * 32;
+    // Staging role: wavefront w stages rows 32w..32w+31; lane l takes row
+    // 32w + l%32 and its half l/32, so 8 consecutive lanes write 8 rows of
+    // the same half (row stride 68 floats: distinct LDS banks).
+    const int srow = wave * 32 + col;
+    const int scol = half * 32;
     f32x4 stage[8];
     bool stage_valid = false;
     unsigned stage_max = 0u;   // bits of the largest valid 0.5*||c||^2 staged in this stage
@@ -249,12 +251,12 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) s = __builtin_fmaf(stage[i][e], stage[i][e], s);
-        s = s + __shfl_xor(s, 1);
+        s = s + __shfl_xor(s, 32);
         const float hn = 0.5f * s;
         float *dst = &s_book[buf][srow * kRow + scol];
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(dst + 4 * i) = stage[i];
-        if ((tid & 1) == 0) s_norm[buf][srow] = stage_valid ? hn : kNoScore;
+        if (half == 0) s_norm[buf][srow] = stage_valid ? hn : kNoScore;
         if (stage_valid) stage_max = max(stage_max, __float_as_uint(hn));   // hn >= 0: bits order like values
         const int q = g / n_chunks;
         if (g - q * n_chunks == n_chunks - 1) {
