@@ -133,6 +133,34 @@ RVQ_API rvq_status rvq_roundtrip(const float *x, int64_t n_frames, int32_t dim,
                                  int32_t *codes, int32_t codes_ld,
                                  float *recon, float *residual, void *stream);
 
+/*
+ * rvq_project_roundtrip -- linear in, encode, decode, linear out.
+ *
+ * The "Audio tokenizer pipeline" section of the "Architecture" page puts a
+ * linear layer (fc) before the RVQ encode and one (fc2) after the decode.
+ * This runs, on `stream`, in order:
+ *   latent       = h W_in^T + b_in              [n_frames, dim]
+ *   codes        = encode(latent)               [n_frames, codes_ld]
+ *   latent_recon = decode(codes)                [n_frames, dim]
+ *   h_recon      = latent_recon W_out^T + b_out [n_frames, hidden]
+ *
+ *   h            [n_frames, hidden] input (read only)
+ *   w_in         [dim, hidden]  PyTorch (out, in) order; b_in [dim] or NULL
+ *   codebooks    [n_stages, n_codes, dim]
+ *   w_out        [hidden, dim]  PyTorch (out, in) order; b_out [hidden] or NULL
+ *   codes, latent, latent_recon, h_recon: caller-allocated outputs
+ *
+ * The linear layers are fp32 sums on the matrix cores (bias added last);
+ * encode and decode keep the contract above, applied to `latent`.
+ * hidden must be a positive multiple of 64 (RVQ_ERR_UNSUPPORTED otherwise).
+ */
+RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32_t hidden,
+                                         const float *w_in, const float *b_in,
+                                         const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                         int32_t dim, const float *w_out, const float *b_out,
+                                         int32_t *codes, int32_t codes_ld, float *latent,
+                                         float *latent_recon, float *h_recon, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

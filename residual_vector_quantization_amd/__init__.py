@@ -14,6 +14,8 @@ Functions (same names as the C entry points):
 * ``rvq_decode(codes, codebooks, n_stages=None)`` -> ``out [N, D] float32``
 * ``rvq_roundtrip(x, codebooks, n_stages=None, residual=True)``
   -> ``(codes, recon, residual or None)``
+* ``rvq_project_roundtrip(h, w_in, b_in, codebooks, w_out, b_out, n_stages=None)``
+  -> ``(codes, latent, latent_recon, h_recon)``
 * ``rvq_version()``, ``rvq_status_string(status)``
 """
 
@@ -33,7 +35,8 @@ RVQ_ERR_INVALID_ARG = -1
 RVQ_ERR_UNSUPPORTED = -2
 RVQ_ERR_DEVICE = -3
 
-EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip")
+EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip",
+            "rvq_project_roundtrip")
 
 _lib = None
 
@@ -64,6 +67,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.rvq_decode.argtypes = [vp, i32, i64, vp, i32, i32, i32, vp, vp]
     lib.rvq_roundtrip.restype = ctypes.c_int
     lib.rvq_roundtrip.argtypes = [vp, i64, i32, vp, i32, i32, vp, i32, vp, vp, vp]
+    lib.rvq_project_roundtrip.restype = ctypes.c_int
+    lib.rvq_project_roundtrip.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, vp,
+                                          vp, i32, vp, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -179,3 +185,42 @@ def rvq_roundtrip(x: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[i
                               _ptr(codes), q, _ptr(recon), _ptr(res), _stream(x))
     _check("rvq_roundtrip", st)
     return codes, recon, res
+
+
+def rvq_project_roundtrip(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[torch.Tensor],
+                          codebooks: torch.Tensor, w_out: torch.Tensor, b_out: Optional[torch.Tensor],
+                          n_stages: Optional[int] = None, out=None):
+    """fc -> encode -> decode -> fc2 on ``h`` [N, H].
+
+    ``w_in`` [D, H], ``w_out`` [H, D] in PyTorch (out, in) order, biases
+    [D] / [H] or None. Returns ``(codes [N, Q], latent [N, D],
+    latent_recon [N, D], h_recon [N, H])``; ``out`` may pass those four
+    tensors preallocated.
+    """
+    _require(h, "h", torch.float32, 2)
+    dev = h.device
+    _require(codebooks, "codebooks", torch.float32, 3, dev)
+    _require(w_in, "w_in", torch.float32, 2, dev)
+    _require(w_out, "w_out", torch.float32, 2, dev)
+    n, hid = h.shape
+    d = codebooks.shape[2]
+    if tuple(w_in.shape) != (d, hid) or tuple(w_out.shape) != (hid, d):
+        raise ValueError("w_in must be [D, H] and w_out [H, D]")
+    for b, name, size in ((b_in, "b_in", d), (b_out, "b_out", hid)):
+        if b is not None:
+            _require(b, name, torch.float32, 1, dev)
+            if b.shape[0] != size:
+                raise ValueError(f"{name} must have {size} entries")
+    q = _stages(codebooks, n_stages)
+    if out is None:
+        out = (torch.empty((n, q), dtype=torch.int32, device=dev),
+               torch.empty((n, d), dtype=torch.float32, device=dev),
+               torch.empty((n, d), dtype=torch.float32, device=dev),
+               torch.empty((n, hid), dtype=torch.float32, device=dev))
+    codes, latent, latent_recon, h_recon = out
+    st = load().rvq_project_roundtrip(_ptr(h), n, hid, _ptr(w_in), _ptr(b_in), _ptr(codebooks), q,
+                                      codebooks.shape[1], d, _ptr(w_out), _ptr(b_out), _ptr(codes),
+                                      codes.shape[1], _ptr(latent), _ptr(latent_recon), _ptr(h_recon),
+                                      _stream(h))
+    _check("rvq_project_roundtrip", st)
+    return codes, latent, latent_recon, h_recon

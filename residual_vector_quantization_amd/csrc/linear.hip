@@ -1,0 +1,267 @@
+// fp32 matrix-core linear layers around the quantizer, gfx950 (CDNA4).
+//
+// The "Audio tokenizer pipeline" section of the "Architecture" page
+// (omnivoice.cpp) puts a linear layer before the RVQ encode (fc) and one
+// after the decode (fc2). The projected workload uses fc: hidden -> 64 and
+// fc2: 64 -> hidden, weights in PyTorch (out, in) order:
+//
+//   linear_in : y[n, i]  = sum_k h[n, k] * W_in[i, k]  + b_in[i]   (i < 64)
+//   linear_out: o[n, i]  = sum_k x[n, k] * W_out[i, k] + b_out[i]  (k < 64)
+//
+// Both put weight rows on the M side and 32 frames per wavefront on the N
+// side of v_mfma_f32_32x32x2_f32, stream the weights through LDS (padded
+// rows, double buffered, shared by the 4 wavefronts of a workgroup) and
+// keep the frame operand in VGPRs. The contraction dimension is split the
+// same way as in the encode: lanes 0-31 supply one 32-wide half of each
+// 64-wide step, lanes 32-63 the other. Results are fp32 sums in the matrix
+// core's order, the bias added last.
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "rvq_internal.h"
+
+namespace rvq {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kFramesPerWave = 32;
+constexpr int kRow = 64 + 4;   // padded LDS row: 8 lanes of a b128 read hit 32 banks
+
+static_assert(kWaves * kFramesPerWave == kLinearFramesPerBlock, "frames per block");
+
+// ---- linear_in: [N, hidden] x [64, hidden]^T -> [N, 64] -------------------
+
+template <bool kBias>
+__global__ __launch_bounds__(kThreads)
+void linear_in_kernel(const float *__restrict__ h, int64_t n_frames, int hidden,
+                      const float *__restrict__ w, const float *__restrict__ bias,
+                      float *__restrict__ y)
+{
+    // one chunk = 64 weight rows (all outputs) x 64 columns of the hidden dim
+    __shared__ __align__(16) float s_w[2][kDim * kRow];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kLinearFramesPerBlock +
+                          wave * kFramesPerWave + col;
+    const bool valid = frame < n_frames;
+    const float *hrow = h + (valid ? frame : 0) * static_cast<int64_t>(hidden) + 32 * half;
+
+    // staging: wavefront w stages weight rows 16w..16w+15; lane -> (row, 16-column quarter)
+    const int srow = wave * 16 + (lane & 15);
+    const int scol = (lane >> 4) * 16;
+    const int n_chunks = hidden / 64;
+
+    f32x4 ws[4];
+    f32x4 hv[8];
+    auto fetch_w = [&](int c) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(w + static_cast<int64_t>(srow) * hidden + 64 * c + scol);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ws[i] = p[i];
+    };
+    auto commit_w = [&](int buf) {
+        float *dst = &s_w[buf][srow * kRow + scol];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(dst + 4 * i) = ws[i];
+    };
+    auto fetch_h = [&](int c) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(hrow + 64 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = p[i];
+    };
+
+    f32x16 acc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
+
+    fetch_w(0);
+    commit_w(0);
+    fetch_h(0);
+    __syncthreads();
+
+    for (int c = 0; c < n_chunks; ++c) {
+        const int buf = c & 1;
+        f32x4 cur[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cur[i] = hv[i];
+        if (c + 1 < n_chunks) {
+            fetch_w(c + 1);
+            fetch_h(c + 1);
+        }
+        const float *sb = s_w[buf];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            f32x4 a[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+                a[b] = *reinterpret_cast<const f32x4 *>(sb + (b * 32 + col) * kRow + 32 * half + 4 * t);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[b][e], cur[t][e], acc[b], 0, 0, 0);
+        }
+        if (c + 1 < n_chunks) commit_w(buf ^ 1);
+        __syncthreads();
+    }
+
+    if (valid) {
+        // accumulator v of block b in this lane is output 32b + 8*(v/4) + 4*half + v%4
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int i0 = 32 * b + 8 * m + 4 * half;
+                f32x4 o = {acc[b][4 * m], acc[b][4 * m + 1], acc[b][4 * m + 2], acc[b][4 * m + 3]};
+                if (kBias) {
+                    const f32x4 bb = *reinterpret_cast<const f32x4 *>(bias + i0);
+                    o = o + bb;
+                }
+                *reinterpret_cast<f32x4 *>(y + frame * kDim + i0) = o;
+            }
+        }
+    }
+}
+
+// ---- linear_out: [N, 64] x [hidden, 64]^T -> [N, hidden] ------------------
+
+constexpr int kOutChunk = 128;   // weight rows (outputs) per LDS chunk
+
+template <bool kBias>
+__global__ __launch_bounds__(kThreads)
+void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden,
+                       const float *__restrict__ w, const float *__restrict__ bias,
+                       float *__restrict__ out)
+{
+    __shared__ __align__(16) float s_w[2][kOutChunk * kRow];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kLinearFramesPerBlock +
+                          wave * kFramesPerWave + col;
+    const bool valid = frame < n_frames;
+
+    float xv[32];
+    if (valid) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(x + frame * kDim + 32 * half);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 v = src[t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xv[4 * t + e] = v[e];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) xv[j] = 0.0f;
+    }
+
+    // staging: wavefront w stages rows 32w..32w+31 of the chunk, lane -> (row, half)
+    const int srow = wave * 32 + col;
+    const int scol = half * 32;
+    const int n_chunks = (hidden + kOutChunk - 1) / kOutChunk;
+    f32x4 ws[8];
+    auto fetch_w = [&](int c) {
+        const int row = min(c * kOutChunk + srow, hidden - 1);
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(w + static_cast<int64_t>(row) * kDim + scol);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ws[i] = p[i];
+    };
+    auto commit_w = [&](int buf) {
+        float *dst = &s_w[buf][srow * kRow + scol];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<f32x4 *>(dst + 4 * i) = ws[i];
+    };
+
+    fetch_w(0);
+    commit_w(0);
+    __syncthreads();
+
+    float *orow = out + (valid ? frame : 0) * static_cast<int64_t>(hidden);
+    for (int c = 0; c < n_chunks; ++c) {
+        const int buf = c & 1;
+        if (c + 1 < n_chunks) fetch_w(c + 1);
+        const float *sb = s_w[buf];
+#pragma unroll
+        for (int pb = 0; pb < kOutChunk / 64; ++pb) {
+            const int row0 = c * kOutChunk + pb * 64;
+            if (row0 >= hidden) break;   // uniform: hidden is a multiple of 64
+            f32x16 acc[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[b][v] = 0.0f;
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                f32x4 a[2];
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+                    a[b] = *reinterpret_cast<const f32x4 *>(sb + (pb * 64 + b * 32 + col) * kRow + 32 * half + 4 * t);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[b][e], xv[4 * t + e], acc[b], 0, 0, 0);
+            }
+            if (valid) {
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int i0 = row0 + 32 * b + 8 * m + 4 * half;
+                        f32x4 o = {acc[b][4 * m], acc[b][4 * m + 1], acc[b][4 * m + 2], acc[b][4 * m + 3]};
+                        if (kBias) {
+                            const f32x4 bb = *reinterpret_cast<const f32x4 *>(bias + i0);
+                            o = o + bb;
+                        }
+                        *reinterpret_cast<f32x4 *>(orow + i0) = o;
+                    }
+                }
+            }
+        }
+        if (c + 1 < n_chunks) commit_w(buf ^ 1);
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+hipError_t launch_linear_in(const float *h, int64_t n_frames, int hidden, const float *w,
+                            const float *bias, float *y, hipStream_t stream)
+{
+    const int64_t blocks = (n_frames + kLinearFramesPerBlock - 1) / kLinearFramesPerBlock;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    if (bias)
+        hipLaunchKernelGGL((linear_in_kernel<true>), grid, block, 0, stream, h, n_frames, hidden, w, bias, y);
+    else
+        hipLaunchKernelGGL((linear_in_kernel<false>), grid, block, 0, stream, h, n_frames, hidden, w, bias, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const float *w,
+                             const float *bias, float *out, hipStream_t stream)
+{
+    const int64_t blocks = (n_frames + kLinearFramesPerBlock - 1) / kLinearFramesPerBlock;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    if (bias)
+        hipLaunchKernelGGL((linear_out_kernel<true>), grid, block, 0, stream, x, n_frames, hidden, w, bias, out);
+    else
+        hipLaunchKernelGGL((linear_out_kernel<false>), grid, block, 0, stream, x, n_frames, hidden, w, bias, out);
+    return hipGetLastError();
+}
+
+}  // namespace rvq

@@ -91,4 +91,32 @@ RVQ_API rvq_status rvq_decode(const int32_t *codes, int32_t codes_ld, int64_t n_
                                        static_cast<hipStream_t>(stream)));
 }
 
+RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32_t hidden,
+                                         const float *w_in, const float *b_in,
+                                         const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                         int32_t dim, const float *w_out, const float *b_out,
+                                         int32_t *codes, int32_t codes_ld, float *latent,
+                                         float *latent_recon, float *h_recon, void *stream)
+{
+    rvq_status st = check_shape(n_frames, dim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (hidden <= 0 || codes_ld < n_stages) return RVQ_ERR_INVALID_ARG;
+    if (hidden % 64 != 0) return RVQ_ERR_UNSUPPORTED;
+    if (n_frames == 0) return RVQ_OK;
+    if (!h || !w_in || !codebooks || !w_out || !codes || !latent || !latent_recon || !h_recon)
+        return RVQ_ERR_INVALID_ARG;
+    if (!aligned(h, 16) || !aligned(w_in, 16) || !aligned(codebooks, 16) || !aligned(w_out, 16) ||
+        !aligned(codes, 4) || !aligned(latent, 16) || !aligned(latent_recon, 16) || !aligned(h_recon, 16) ||
+        (b_in && !aligned(b_in, 16)) || (b_out && !aligned(b_out, 16)))
+        return RVQ_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = rvq::launch_linear_in(h, n_frames, hidden, w_in, b_in, latent, s);
+    if (e == hipSuccess)
+        e = rvq::launch_encode(latent, n_frames, codebooks, n_stages, n_codes, codes, codes_ld,
+                               nullptr, latent_recon, s);
+    if (e == hipSuccess)
+        e = rvq::launch_linear_out(latent_recon, n_frames, hidden, w_out, b_out, h_recon, s);
+    return from_hip(e);
+}
+
 }  // extern "C"

@@ -18,6 +18,9 @@ constexpr int kEncodeThreads = 256;
 constexpr int kDecodeLanesPerFrame = 16;
 constexpr int kDecodeThreads = 256;
 
+// Linear layers: frames per workgroup (4 wavefronts x 32 frames).
+constexpr int kLinearFramesPerBlock = 128;
+
 // Launches the fused multi-stage encode. `residual` and `recon` may be null.
 hipError_t launch_encode(const float *x, int64_t n_frames, const float *books,
                          int n_stages, int n_codes, int32_t *codes, int codes_ld,
@@ -27,5 +30,13 @@ hipError_t launch_encode(const float *x, int64_t n_frames, const float *books,
 hipError_t launch_decode(const int32_t *codes, int codes_ld, int64_t n_frames,
                          const float *books, int n_stages, int n_codes, float *out,
                          hipStream_t stream);
+
+// y[N, 64] = h[N, hidden] W[64, hidden]^T + bias (bias nullable); hidden % 64 == 0.
+hipError_t launch_linear_in(const float *h, int64_t n_frames, int hidden, const float *w,
+                            const float *bias, float *y, hipStream_t stream);
+
+// out[N, hidden] = x[N, 64] W[hidden, 64]^T + bias (bias nullable); hidden % 64 == 0.
+hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const float *w,
+                             const float *bias, float *out, hipStream_t stream);
 
 }  // namespace rvq

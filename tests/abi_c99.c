@@ -39,6 +39,14 @@ int main(void)
     bad += expect("decode ld<q", rvq_decode(ic, 4, 10, fx, 8, 1024, 64, fx, NULL), RVQ_ERR_INVALID_ARG);
     bad += expect("decode misaligned out", rvq_decode(ic, 8, 10, fx, 8, 1024, 64, fx + 2, NULL), RVQ_ERR_INVALID_ARG);
     bad += expect("decode empty", rvq_decode(NULL, 8, 0, NULL, 8, 1024, 64, NULL, NULL), RVQ_OK);
+    bad += expect("project hidden 100", rvq_project_roundtrip(fx, 10, 100, fx, NULL, fx, 8, 1024, 64, fx, NULL,
+                                                              ic, 8, fx, fx, fx, NULL), RVQ_ERR_UNSUPPORTED);
+    bad += expect("project null h_recon", rvq_project_roundtrip(fx, 10, 1024, fx, NULL, fx, 8, 1024, 64, fx, NULL,
+                                                                ic, 8, fx, fx, NULL, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("project misaligned bias", rvq_project_roundtrip(fx, 10, 1024, fx, fx + 1, fx, 8, 1024, 64, fx,
+                                                                   NULL, ic, 8, fx, fx, fx, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("project empty", rvq_project_roundtrip(NULL, 0, 1024, NULL, NULL, NULL, 8, 1024, 64, NULL, NULL,
+                                                         NULL, 8, NULL, NULL, NULL, NULL), RVQ_OK);
     printf("%s\n", bad ? "abi_c99: FAILED" : "abi_c99: ok");
     return bad ? 1 : 0;
 }

@@ -25,7 +25,7 @@ def declared():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == sorted(["rvq_decode", "rvq_encode", "rvq_roundtrip",
+    assert declared() == sorted(["rvq_decode", "rvq_encode", "rvq_project_roundtrip", "rvq_roundtrip",
                                  "rvq_status_string", "rvq_version"])
 
 
