@@ -20,10 +20,11 @@
  *   - ties in distance go to the lowest codeword index;
  *   - the pick of every stage equals the argmin of the float64 direct-form
  *     distance sum_j (r_j - c_j)^2 (j ascending, one rounding per
- *     operation) over all K codewords. Scores are computed on fp32 matrix
- *     cores; every codeword whose fp32 score lies within a proven error
- *     bound of the best is re-ranked with that float64 sum, so the fp32
- *     rounding never decides a pick;
+ *     operation) over all K codewords. Scores are computed on the matrix
+ *     cores (split-bf16 by default, or fp32, see rvq_encode_scored); every
+ *     codeword whose score lies within a proven error bound of the best is
+ *     re-ranked with that float64 sum, so score rounding never decides a
+ *     pick and both scorings give identical results;
  *   - residuals are float32, r <- fl32(r - c) per element;
  *   - decode (and the reconstruction of rvq_roundtrip) is a float32 sum
  *     that starts at +0 and adds stage 0 first.
@@ -79,6 +80,13 @@ typedef enum rvq_status {
     RVQ_ERR_DEVICE = -3        /* the HIP runtime refused the launch or has no device */
 } rvq_status;
 
+/* How encode scores codewords before the exact float64 decision. */
+typedef enum rvq_scoring {
+    RVQ_SCORING_DEFAULT = 0,  /* the fastest available: RVQ_SCORING_BF16X3 */
+    RVQ_SCORING_BF16X3 = 1,   /* split-bf16 (hi*hi + hi*lo + lo*hi) on bf16 matrix cores */
+    RVQ_SCORING_FP32 = 2      /* fp32 matrix cores */
+} rvq_scoring;
+
 /* Static string "MAJOR.MINOR.PATCH (gfx950)". Never NULL. */
 RVQ_API const char *rvq_version(void);
 
@@ -132,6 +140,18 @@ RVQ_API rvq_status rvq_roundtrip(const float *x, int64_t n_frames, int32_t dim,
                                  const float *codebooks, int32_t n_stages, int32_t n_codes,
                                  int32_t *codes, int32_t codes_ld,
                                  float *recon, float *residual, void *stream);
+
+/*
+ * rvq_encode_scored -- rvq_encode / rvq_roundtrip with an explicit scoring.
+ *
+ * recon and residual are both optional (NULL skips them). Any valid
+ * `scoring` returns the same codes, residual and recon bit for bit; only
+ * the speed differs. An unknown scoring value is RVQ_ERR_INVALID_ARG.
+ */
+RVQ_API rvq_status rvq_encode_scored(const float *x, int64_t n_frames, int32_t dim,
+                                     const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                     int32_t *codes, int32_t codes_ld,
+                                     float *recon, float *residual, rvq_scoring scoring, void *stream);
 
 /*
  * rvq_project_roundtrip -- linear in, encode, decode, linear out.

@@ -14,6 +14,8 @@ Functions (same names as the C entry points):
 * ``rvq_decode(codes, codebooks, n_stages=None)`` -> ``out [N, D] float32``
 * ``rvq_roundtrip(x, codebooks, n_stages=None, residual=True)``
   -> ``(codes, recon, residual or None)``
+* ``rvq_encode_scored(x, codebooks, scoring, n_stages=None, recon=True, residual=True)``
+  -> ``(codes, recon or None, residual or None)``; scoring "default", "bf16x3" or "fp32"
 * ``rvq_project_roundtrip(h, w_in, b_in, codebooks, w_out, b_out, n_stages=None)``
   -> ``(codes, latent, latent_recon, h_recon)``
 * ``rvq_version()``, ``rvq_status_string(status)``
@@ -36,7 +38,9 @@ RVQ_ERR_UNSUPPORTED = -2
 RVQ_ERR_DEVICE = -3
 
 EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip",
-            "rvq_project_roundtrip")
+            "rvq_encode_scored", "rvq_project_roundtrip")
+
+SCORING = {"default": 0, "bf16x3": 1, "fp32": 2}
 
 _lib = None
 
@@ -67,6 +71,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.rvq_decode.argtypes = [vp, i32, i64, vp, i32, i32, i32, vp, vp]
     lib.rvq_roundtrip.restype = ctypes.c_int
     lib.rvq_roundtrip.argtypes = [vp, i64, i32, vp, i32, i32, vp, i32, vp, vp, vp]
+    lib.rvq_encode_scored.restype = ctypes.c_int
+    lib.rvq_encode_scored.argtypes = [vp, i64, i32, vp, i32, i32, vp, i32, vp, vp, ctypes.c_int, vp]
     lib.rvq_project_roundtrip.restype = ctypes.c_int
     lib.rvq_project_roundtrip.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, vp,
                                           vp, i32, vp, vp, vp, vp]
@@ -185,6 +191,36 @@ def rvq_roundtrip(x: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[i
                               _ptr(codes), q, _ptr(recon), _ptr(res), _stream(x))
     _check("rvq_roundtrip", st)
     return codes, recon, res
+
+
+def rvq_encode_scored(x: torch.Tensor, codebooks: torch.Tensor, scoring: str = "default",
+                      n_stages: Optional[int] = None, recon: bool = True, residual: bool = True,
+                      out=None):
+    """Encode with an explicit scoring ("default", "bf16x3" or "fp32"); all give identical results.
+
+    Returns ``(codes, recon or None, residual or None)``; ``out`` may pass
+    ``(codes, recon, residual)`` preallocated (entries may be None).
+    """
+    _require(x, "x", torch.float32, 2)
+    _require(codebooks, "codebooks", torch.float32, 3, x.device)
+    if scoring not in SCORING:
+        raise ValueError(f"scoring must be one of {sorted(SCORING)}")
+    n, d = x.shape
+    q = _stages(codebooks, n_stages)
+    if out is None:
+        out = (torch.empty((n, q), dtype=torch.int32, device=x.device),
+               torch.empty_like(x) if recon else None, torch.empty_like(x) if residual else None)
+    codes, rec, res = out
+    _require(codes, "codes", torch.int32, 2, x.device)
+    for t, name in ((rec, "recon"), (res, "residual")):
+        if t is not None:
+            _require(t, name, torch.float32, 2, x.device)
+            if t.shape != x.shape:
+                raise ValueError(f"{name} must match x")
+    st = load().rvq_encode_scored(_ptr(x), n, d, _ptr(codebooks), q, codebooks.shape[1], _ptr(codes),
+                                  codes.shape[1], _ptr(rec), _ptr(res), SCORING[scoring], _stream(x))
+    _check("rvq_encode_scored", st)
+    return codes, rec, res
 
 
 def rvq_project_roundtrip(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[torch.Tensor],

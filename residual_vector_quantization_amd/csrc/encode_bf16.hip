@@ -1,0 +1,382 @@
+// Fused multi-stage residual vector quantization encode for gfx950 (CDNA4)
+// with split-bf16 scoring on the bf16 matrix cores.
+//
+// Computes the residual loop of the "RVQ codec" section of the
+// "Architecture" page (omnivoice.cpp): for q = 0..Q-1 pick
+// argmin_k ||r - C[q,k]||^2 (lowest k on ties), emit k, r <- r - C[q,k].
+// The pick is the same as the fp32-scored kernel's (encode.hip): both end
+// in the float64 direct form for every codeword that the fp32 or split-bf16
+// scores cannot separate from the best. This kernel only scores faster:
+// one v_mfma_f32_32x32x16_bf16 does the work of eight fp32 32x32x2 steps.
+//
+// Scoring: every fp32 value v is split as v = hi + lo + e with hi = bf16(v)
+// and lo = bf16(v - hi) (round to nearest even; v - hi is exact in fp32),
+// |e| <= 2^-16 |v|. The dot product n.c (n = -r) is computed as
+//     n_hi.c_lo + n_lo.c_hi + n_hi.c_hi
+// on the matrix cores (bf16 x bf16 products are exact in fp32), added to an
+// accumulator that starts at 0.5*||c||^2 (fp32, from the fp32 codeword).
+// The dropped terms n_lo.c_lo and the split remainders are at most
+// 3.2 * 2^-16 * |n_j c_j| per dimension; the fp32 accumulation of 3D + 1
+// terms plus the norm's own D-term sum adds at most 2*gamma_{3D+8} (2u per
+// operation) of 0.5*||c||^2 + sum_j |n_j c_j|; the packed key adds 2^-17 of
+// the score. So every key is within
+//     e = (3.2 * 2^-16 + 2*gamma_{3D+8} + 2^-17) * (0.5*||c||^2 + ||r|| ||c||)
+// of the exact score, and every codeword within 2*e_max of the smallest key
+// is a candidate for the true argmin.
+//
+// Work split as in encode.hip: 4 wavefronts x 32 frames per workgroup,
+// residual in VGPRs (negated, plus its bf16 split), codebooks streamed
+// through LDS in 128-codeword chunks (stored as hi/lo bf16, 8-dim groups),
+// scored as two 64-codeword groups of two interleaved MFMA chains. Because candidate sets are
+// wider than with fp32 scores, each lane keeps its best, second and third
+// keys and the indices of the first two: a frame resolves from up to four
+// candidates (two per half) with the float64 re-rank, and only a third
+// candidate inside one lane sends it to the full float64 rescan.
+#include "encode_common.h"
+
+namespace rvq {
+namespace {
+
+using namespace enc;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kFramesPerWave = 32;
+constexpr int kChunk = 128;              // codewords per LDS chunk
+constexpr int kRowH = 2 * kDim + 8;      // bf16 per LDS row: 8 groups of (8 hi, 8 lo) + 16 B pad
+constexpr float kSplitError = 3.2f * 1.52587890625e-05f;   // 3.2 * 2^-16
+constexpr float kBoundScale = kSplitError + 2.0f * gamma_n(3 * kDim + 8) + kKeyError;
+
+static_assert(kThreads == kEncodeThreads, "thread count");
+static_assert(kWaves * kFramesPerWave == kEncodeFramesPerBlock, "frames per block");
+static_assert(kWaves * 32 == kChunk, "staging maps each wavefront to 32 codeword rows");
+
+__device__ __forceinline__ void split8(const float *v, bf16x8 &hi, bf16x8 &lo)
+{
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        hi[e] = static_cast<__bf16>(v[e]);
+        lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(hi[e]));
+    }
+}
+
+// Key scan of a 64-codeword group (two blocks): running best, second and
+// third key of this lane. Local index of accumulator v of block b:
+// b*32 + 8*(v/4) + v%4, plus the lane's 4*half row offset.
+__device__ __forceinline__ void scan_group(const f32x16 (&d)[2], float &best, float &second, float &third)
+{
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const float key = make_key(d[b][v], b * 32 + 8 * (v >> 2) + (v & 3));
+            third = __builtin_amdgcn_fmed3f(key, second, third);
+            second = __builtin_amdgcn_fmed3f(key, best, second);
+            best = __builtin_amdgcn_fmed3f(key, best, -FLT_MAX);
+        }
+    }
+}
+
+// Index bookkeeping after scanning the group that starts at codeword `base`.
+// A changed second key is either the previous best (demoted) or a key of this
+// group; equal bit patterns from different groups also leave a third key with
+// the same value, which the decision treats as an unresolved candidate.
+__device__ __forceinline__ void fold_group(float best, float second, unsigned best_before,
+                                           unsigned second_before, int base, int half,
+                                           int &best_k, int &second_k)
+{
+    const unsigned bb = __float_as_uint(best), sb = __float_as_uint(second);
+    if (sb != second_before)
+        second_k = (bb != best_before && sb == best_before) ? best_k
+                                                            : base + 4 * half + static_cast<int>(sb & ~kKeyMask);
+    if (bb != best_before) best_k = base + 4 * half + static_cast<int>(bb & ~kKeyMask);
+}
+
+// Scores codewords 64*kG .. 64*kG+63 of the chunk in LDS (two 32-codeword
+// blocks, two interleaved MFMA chains of 12 steps) and folds them into this
+// lane's best / second / third keys.
+template <int kG>
+__device__ __forceinline__ void score_group(const __bf16 *sb, const float *sn, int col, int half,
+                                            const bf16x8 (&nh)[4], const bf16x8 (&nl)[4], int base,
+                                            float &best, float &second, float &third,
+                                            int &best_k, int &second_k)
+{
+    f32x16 d[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 nv = *reinterpret_cast<const f32x4 *>(sn + kG * 64 + b * 32 + 8 * m + 4 * half);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[b][4 * m + e] = nv[e];
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        bf16x8 ah[2], al[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const __bf16 *row = sb + (kG * 64 + b * 32 + col) * kRowH + 16 * (4 * half + s);
+            ah[b] = *reinterpret_cast<const bf16x8 *>(row);
+            al[b] = *reinterpret_cast<const bf16x8 *>(row + 8);
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) d[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[b], nl[s], d[b], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) d[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[b], nh[s], d[b], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) d[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[b], nh[s], d[b], 0, 0, 0);
+    }
+    const unsigned bb = __float_as_uint(best), sb0 = __float_as_uint(second);
+    scan_group(d, best, second, third);
+    fold_group(best, second, bb, sb0, base, half, best_k, second_k);
+}
+
+template <bool kRecon, bool kResidual>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
+                        const float *__restrict__ books, int n_stages, int n_codes,
+                        int32_t *__restrict__ codes, int codes_ld,
+                        float *__restrict__ residual, float *__restrict__ recon)
+{
+    __shared__ __align__(16) __bf16 s_book[2][kChunk * kRowH];
+    __shared__ __align__(16) float s_norm[2][kChunk];
+    __shared__ __align__(16) unsigned s_cmax[2][kWaves];   // per stage parity, per wavefront
+    __shared__ __align__(16) float s_frame[kWaves][kDim];  // rescan: one frame's residual
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kEncodeFramesPerBlock +
+                          wave * kFramesPerWave + col;
+    const bool valid = frame < n_frames;
+
+    float n[32];     // negated residual, dims 32*half .. 32*half+31
+    float acc[32];   // reconstruction (kRecon)
+    if (valid) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(x + frame * kDim + 32 * half);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 v = src[t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) n[4 * t + e] = -v[e];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) n[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+    bf16x8 nh[4], nl[4];   // split of n: step s holds dims 32*half + 8s .. +7
+
+    const int n_chunks = (n_codes + kChunk - 1) / kChunk;
+    const int total = n_stages * n_chunks;
+
+    // Staging: wavefront w stages rows 32w..32w+31, lane -> (row 32w + l%32, half l/32).
+    const int srow = wave * 32 + col;
+    f32x4 stage[8];
+    bool stage_valid = false;
+    unsigned stage_max = 0u;
+
+    auto fetch = [&](int g) {
+        const int q = g / n_chunks;
+        const int c = g - q * n_chunks;
+        const int k = c * kChunk + srow;
+        if (c == 0) stage_max = 0u;
+        // rows past n_codes load the last row again; their norm becomes kNoScore
+        stage_valid = k < n_codes;
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(
+            books + (static_cast<int64_t>(q) * n_codes + min(k, n_codes - 1)) * kDim + 32 * half);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) stage[i] = p[i];
+    };
+    auto commit = [&](int g) {
+        const int buf = g & 1;
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s = __builtin_fmaf(stage[i][e], stage[i][e], s);
+        s = s + __shfl_xor(s, 32);
+        const float hn = 0.5f * s;
+        __bf16 *dst = &s_book[buf][srow * kRowH];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = stage[2 * t][e];
+                v[4 + e] = stage[2 * t + 1][e];
+            }
+            bf16x8 hi, lo;
+            split8(v, hi, lo);
+            const int grp = 4 * half + t;
+            *reinterpret_cast<bf16x8 *>(dst + 16 * grp) = hi;
+            *reinterpret_cast<bf16x8 *>(dst + 16 * grp + 8) = lo;
+        }
+        if (half == 0) s_norm[buf][srow] = stage_valid ? hn : kNoScore;
+        if (stage_valid) stage_max = max(stage_max, __float_as_uint(hn));   // hn >= 0: bits order like values
+        const int q = g / n_chunks;
+        if (g - q * n_chunks == n_chunks - 1) {
+            unsigned m = stage_max;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1)
+                m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
+            if (lane == 0) s_cmax[q & 1][wave] = m;
+        }
+    };
+
+    fetch(0);
+    commit(0);
+    __syncthreads();
+
+    float best = kNoScore, second = kNoScore, third = kNoScore;
+    int best_k = 0, second_k = 0;
+
+    for (int g = 0; g < total; ++g) {
+        const int buf = g & 1;
+        const int q = g / n_chunks;
+        const int c = g - q * n_chunks;
+        if (g + 1 < total) fetch(g + 1);
+        if (c == 0) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) split8(&n[8 * s], nh[s], nl[s]);
+        }
+
+        {
+            const __bf16 *sb = s_book[buf];
+            const float *sn = s_norm[buf];
+            score_group<0>(sb, sn, col, half, nh, nl, c * kChunk, best, second, third, best_k, second_k);
+            score_group<1>(sb, sn, col, half, nh, nl, c * kChunk + 64, best, second, third, best_k, second_k);
+        }
+
+        if (g + 1 < total) commit(g + 1);
+
+        if (c == n_chunks - 1) {
+            // ---- stage q is scored for this wavefront's 32 frames: decide ----
+            const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
+            const float best_o = __shfl_xor(best, 32);
+            const float second_o = __shfl_xor(second, 32);
+            const float third_o = __shfl_xor(third, 32);
+            const int best_k_o = __shfl_xor(best_k, 32);
+            const int second_k_o = __shfl_xor(second_k, 32);
+            float rn = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) rn = __builtin_fmaf(n[j], n[j], rn);
+            rn = rn + __shfl_xor(rn, 32);
+
+            const uint4 cm = *reinterpret_cast<const uint4 *>(s_cmax[q & 1]);
+            const float c2 = __uint_as_float(max(max(cm.x, cm.y), max(cm.z, cm.w)));   // max_k 0.5||c_k||^2
+            const float bound = kBoundScale * (c2 + sqrtf(rn) * sqrtf(2.0f * c2)) + kAbsSlack;
+            const float lim = fminf(best, best_o) + 2.0f * bound;
+            const bool overflow = third <= lim || third_o <= lim ||
+                                  (second <= lim && second_k == best_k) ||
+                                  (second_o <= lim && second_k_o == best_k_o);
+            // candidate slots in frame order: half 0's best and second, then half 1's
+            const float sv[4] = {half ? best_o : best, half ? second_o : second,
+                                 half ? best : best_o, half ? second : second_o};
+            const int sk[4] = {half ? best_k_o : best_k, half ? second_k_o : second_k,
+                               half ? best_k : best_k_o, half ? second_k : second_k_o};
+            bool cf[4];
+            int ncand = 0, pick = sk[0];
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                cf[i] = sv[i] <= lim;
+                ncand += cf[i];
+                if (cf[i]) pick = sk[i];
+            }
+
+            // Two to four candidates: float64 re-rank (slot 0 is always a valid index).
+            const bool rerank = valid && !overflow && ncand >= 2;
+            if (__any(rerank)) {
+                double bd = INFINITY;
+                int bk = 0x7fffffff;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool use = rerank && cf[i];
+                    if (__any(use)) {
+                        const int k = use ? sk[i] : sk[0];
+                        const double dist = pair_distance(n, book, k, half);
+                        if (use && (dist < bd || (dist == bd && k < bk))) {
+                            bd = dist;
+                            bk = k;
+                        }
+                    }
+                }
+                if (rerank) pick = bk;
+            }
+
+            // A third candidate inside one lane (or ambiguous bookkeeping): full rescan.
+            uint64_t pending = __ballot(valid && overflow && half == 0);
+            while (pending) {
+                const int f = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+                pending &= pending - 1;
+                const int w = rescan_frame(n, s_frame[wave], book, n_codes, f, lane);
+                if (col == f) pick = w;
+            }
+
+            pick = min(max(pick, 0), n_codes - 1);
+            if (valid && half == 0) codes[frame * codes_ld + q] = pick;
+            const f32x4 *cw = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(pick) * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const f32x4 v = cw[t];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    n[4 * t + e] = n[4 * t + e] + v[e];   // = -(r - c), exactly
+                    if (kRecon) acc[4 * t + e] = acc[4 * t + e] + v[e];
+                }
+            }
+            best = kNoScore;
+            second = kNoScore;
+            third = kNoScore;
+            best_k = 0;
+            second_k = 0;
+        }
+        __syncthreads();
+    }
+
+    if (valid) {
+        if (kResidual) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(residual + frame * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dst[t] = f32x4{-n[4 * t], -n[4 * t + 1], -n[4 * t + 2], -n[4 * t + 3]};
+        }
+        if (kRecon) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(recon + frame * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                dst[t] = f32x4{acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_encode_bf16(const float *x, int64_t n_frames, const float *books,
+                              int n_stages, int n_codes, int32_t *codes, int codes_ld,
+                              float *residual, float *recon, hipStream_t stream)
+{
+    const int64_t blocks = (n_frames + kEncodeFramesPerBlock - 1) / kEncodeFramesPerBlock;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    if (recon && residual)
+        hipLaunchKernelGGL((encode_bf16_kernel<true, true>), grid, block, 0, stream,
+                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else if (recon)
+        hipLaunchKernelGGL((encode_bf16_kernel<true, false>), grid, block, 0, stream,
+                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else if (residual)
+        hipLaunchKernelGGL((encode_bf16_kernel<false, true>), grid, block, 0, stream,
+                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else
+        hipLaunchKernelGGL((encode_bf16_kernel<false, false>), grid, block, 0, stream,
+                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+    return hipGetLastError();
+}
+
+}  // namespace rvq

@@ -24,10 +24,22 @@ rvq_status check_shape(int64_t n_frames, int32_t dim, int32_t n_stages, int32_t 
 
 rvq_status from_hip(hipError_t e) { return e == hipSuccess ? RVQ_OK : RVQ_ERR_DEVICE; }
 
+hipError_t launch_scored(rvq_scoring scoring, const float *x, int64_t n_frames, const float *books,
+                         int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
+                         float *recon, hipStream_t stream)
+{
+    if (scoring == RVQ_SCORING_FP32)
+        return rvq::launch_encode(x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon, stream);
+    return rvq::launch_encode_bf16(x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon,
+                                   stream);
+}
+
 rvq_status encode_common(const float *x, int64_t n_frames, int32_t dim, const float *books,
                          int32_t n_stages, int32_t n_codes, int32_t *codes, int32_t codes_ld,
-                         float *recon, bool want_recon, float *residual, void *stream)
+                         float *recon, bool want_recon, float *residual, rvq_scoring scoring, void *stream)
 {
+    if (scoring != RVQ_SCORING_DEFAULT && scoring != RVQ_SCORING_BF16X3 && scoring != RVQ_SCORING_FP32)
+        return RVQ_ERR_INVALID_ARG;
     rvq_status st = check_shape(n_frames, dim, n_stages, n_codes);
     if (st != RVQ_OK) return st;
     if (codes_ld < n_stages) return RVQ_ERR_INVALID_ARG;
@@ -36,8 +48,8 @@ rvq_status encode_common(const float *x, int64_t n_frames, int32_t dim, const fl
     if (!aligned(x, 16) || !aligned(books, 16) || !aligned(codes, 4) ||
         (recon && !aligned(recon, 16)) || (residual && !aligned(residual, 16)))
         return RVQ_ERR_INVALID_ARG;
-    return from_hip(rvq::launch_encode(x, n_frames, books, n_stages, n_codes, codes, codes_ld,
-                                       residual, recon, static_cast<hipStream_t>(stream)));
+    return from_hip(launch_scored(scoring, x, n_frames, books, n_stages, n_codes, codes, codes_ld,
+                                  residual, recon, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -65,7 +77,7 @@ RVQ_API rvq_status rvq_encode(const float *x, int64_t n_frames, int32_t dim,
                               int32_t *codes, int32_t codes_ld, float *residual, void *stream)
 {
     return encode_common(x, n_frames, dim, codebooks, n_stages, n_codes, codes, codes_ld,
-                         nullptr, false, residual, stream);
+                         nullptr, false, residual, RVQ_SCORING_DEFAULT, stream);
 }
 
 RVQ_API rvq_status rvq_roundtrip(const float *x, int64_t n_frames, int32_t dim,
@@ -74,7 +86,16 @@ RVQ_API rvq_status rvq_roundtrip(const float *x, int64_t n_frames, int32_t dim,
                                  float *residual, void *stream)
 {
     return encode_common(x, n_frames, dim, codebooks, n_stages, n_codes, codes, codes_ld,
-                         recon, true, residual, stream);
+                         recon, true, residual, RVQ_SCORING_DEFAULT, stream);
+}
+
+RVQ_API rvq_status rvq_encode_scored(const float *x, int64_t n_frames, int32_t dim,
+                                     const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                     int32_t *codes, int32_t codes_ld, float *recon, float *residual,
+                                     rvq_scoring scoring, void *stream)
+{
+    return encode_common(x, n_frames, dim, codebooks, n_stages, n_codes, codes, codes_ld,
+                         recon, false, residual, scoring, stream);
 }
 
 RVQ_API rvq_status rvq_decode(const int32_t *codes, int32_t codes_ld, int64_t n_frames,
@@ -112,8 +133,8 @@ RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = rvq::launch_linear_in(h, n_frames, hidden, w_in, b_in, latent, s);
     if (e == hipSuccess)
-        e = rvq::launch_encode(latent, n_frames, codebooks, n_stages, n_codes, codes, codes_ld,
-                               nullptr, latent_recon, s);
+        e = launch_scored(RVQ_SCORING_DEFAULT, latent, n_frames, codebooks, n_stages, n_codes, codes,
+                          codes_ld, nullptr, latent_recon, s);
     if (e == hipSuccess)
         e = rvq::launch_linear_out(latent_recon, n_frames, hidden, w_out, b_out, h_recon, s);
     return from_hip(e);

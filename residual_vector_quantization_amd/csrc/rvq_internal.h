@@ -26,6 +26,11 @@ hipError_t launch_encode(const float *x, int64_t n_frames, const float *books,
                          int n_stages, int n_codes, int32_t *codes, int codes_ld,
                          float *residual, float *recon, hipStream_t stream);
 
+// Same contract and results, scores on the bf16 matrix cores (split-bf16).
+hipError_t launch_encode_bf16(const float *x, int64_t n_frames, const float *books,
+                              int n_stages, int n_codes, int32_t *codes, int codes_ld,
+                              float *residual, float *recon, hipStream_t stream);
+
 // Launches the gather-sum decode.
 hipError_t launch_decode(const int32_t *codes, int codes_ld, int64_t n_frames,
                          const float *books, int n_stages, int n_codes, float *out,

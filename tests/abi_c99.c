@@ -47,6 +47,10 @@ int main(void)
                                                                    NULL, ic, 8, fx, fx, fx, NULL), RVQ_ERR_INVALID_ARG);
     bad += expect("project empty", rvq_project_roundtrip(NULL, 0, 1024, NULL, NULL, NULL, 8, 1024, 64, NULL, NULL,
                                                          NULL, 8, NULL, NULL, NULL, NULL), RVQ_OK);
+    bad += expect("scored bad mode", rvq_encode_scored(fx, 10, 64, fx, 8, 1024, ic, 8, NULL, NULL, (rvq_scoring)7, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("scored empty", rvq_encode_scored(NULL, 0, 64, NULL, 8, 1024, NULL, 8, NULL, NULL, RVQ_SCORING_FP32, NULL),
+                  RVQ_OK);
     printf("%s\n", bad ? "abi_c99: FAILED" : "abi_c99: ok");
     return bad ? 1 : 0;
 }

@@ -31,21 +31,31 @@ def announce(what, **shape):
     print(f"[gpu case] {what} " + " ".join(f"{k}={v}" for k, v in shape.items()), flush=True)
 
 
-def check_encode(x, books, n_stages=None, idx=None, roundtrip=True):
+SCORINGS = ["default", "fp32"]
+
+
+def check_encode(x, books, n_stages=None, idx=None, roundtrip=True, scoring="default"):
     """Runs the HIP encode (and roundtrip) and compares with the oracle.
 
-    ``idx``: compare only those frames (the oracle runs on x[idx]); the GPU
-    still encodes every frame. Codes must be identical; residual and recon
-    bit-identical (they are deterministic float32 functions of the codes).
-    Returns a small report dict.
+    ``scoring`` "default" goes through rvq_encode / rvq_roundtrip, any other
+    value through rvq_encode_scored. ``idx``: compare only those frames (the
+    oracle runs on x[idx]); the GPU still encodes every frame. Codes must be
+    identical; residual and recon bit-identical (they are deterministic
+    float32 functions of the codes). Returns a small report dict.
     """
     m = rvq()
     q = books.shape[0] if n_stages is None else n_stages
-    announce("encode", n=x.shape[0], q=q, k=books.shape[1])
+    announce("encode", n=x.shape[0], q=q, k=books.shape[1], scoring=scoring)
     xg, bg = to_dev(x), to_dev(books)
-    codes, res = m.rvq_encode(xg, bg, n_stages=q)
+    if scoring == "default":
+        codes, res = m.rvq_encode(xg, bg, n_stages=q)
+    else:
+        codes, _, res = m.rvq_encode_scored(xg, bg, scoring, n_stages=q, recon=False)
     if roundtrip:
-        codes2, recon, res2 = m.rvq_roundtrip(xg, bg, n_stages=q)
+        if scoring == "default":
+            codes2, recon, res2 = m.rvq_roundtrip(xg, bg, n_stages=q)
+        else:
+            codes2, recon, res2 = m.rvq_encode_scored(xg, bg, scoring, n_stages=q)
         out = m.rvq_decode(codes2, bg)
     torch.cuda.synchronize()
     codes, res = host(codes), host(res)

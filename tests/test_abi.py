@@ -25,8 +25,8 @@ def declared():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == sorted(["rvq_decode", "rvq_encode", "rvq_project_roundtrip", "rvq_roundtrip",
-                                 "rvq_status_string", "rvq_version"])
+    assert declared() == sorted(["rvq_decode", "rvq_encode", "rvq_encode_scored", "rvq_project_roundtrip",
+                                 "rvq_roundtrip", "rvq_status_string", "rvq_version"])
 
 
 def test_library_exports_every_declared_symbol(libpath):

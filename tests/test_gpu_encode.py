@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import rvq_workloads as W
-from gpu_util import needs_gpu, check_encode, rvq, to_dev, host, announce
+from gpu_util import SCORINGS, needs_gpu, check_encode, rvq, to_dev, host, announce
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -13,47 +13,52 @@ def _books(rng, q, k, d=64, decay=0.5):
     return (rng.standard_normal((q, k, d)) * decay ** np.arange(q)[:, None, None]).astype(np.float32)
 
 
-def test_tiny_workload_recovers_construction():
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_tiny_workload_recovers_construction(scoring):
     w = W.WORKLOADS["tiny"]
     books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
     x, t = W.latents(w, books)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
     m = rvq()
     codes, _ = m.rvq_encode(to_dev(x), to_dev(books))
     np.testing.assert_array_equal(host(codes), t)
 
 
-def test_clip_workload_full():
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_clip_workload_full(scoring):
     w = W.WORKLOADS["clip"]
     books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
     x, _ = W.latents(w, books)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
 
 
 @pytest.mark.parametrize("n", [1, 31, 129, 677])
-def test_ragged_frame_counts(n):
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_ragged_frame_counts(n, scoring):
     rng = np.random.default_rng(100 + n)
     books = _books(rng, 8, 1024)
     x = rng.standard_normal((n, 64)).astype(np.float32)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
 
 
 @pytest.mark.parametrize("k", [1, 63, 64, 65, 100, 1000, 4096])
-def test_codebook_sizes(k):
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_codebook_sizes(k, scoring):
     rng = np.random.default_rng(200 + k)
     q = 10 if k == 4096 else 3
     books = _books(rng, q, k)
     x = rng.standard_normal((300, 64)).astype(np.float32)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
 
 
 @pytest.mark.parametrize("q,decay", [(1, 1.0), (32, 0.85), (64, 0.9)])
-def test_stage_counts(q, decay):
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_stage_counts(q, decay, scoring):
     rng = np.random.default_rng(300 + q)
     k = 256 if q == 64 else 1024
     books = _books(rng, q, k, decay=decay)
     x = rng.standard_normal((257, 64)).astype(np.float32)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
 
 
 def test_partial_depth_prefix():
@@ -68,36 +73,40 @@ def test_partial_depth_prefix():
     np.testing.assert_array_equal(host(part), host(full)[:, :3])
 
 
-def test_exact_ties_integer_data():
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_exact_ties_integer_data(scoring):
     """Small integers: exact scores, many exact ties and duplicated rows (lowest index wins)."""
     rng = np.random.default_rng(8)
     books = rng.integers(-3, 4, size=(4, 128, 64)).astype(np.float32)
     books[:, 100:128] = books[:, 0:28]
     x = rng.integers(-6, 7, size=(500, 64)).astype(np.float32)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
 
 
-def test_all_rows_identical():
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_all_rows_identical(scoring):
     rng = np.random.default_rng(9)
     books = np.repeat(rng.standard_normal((3, 1, 64)).astype(np.float32), 192, axis=1)
     x = rng.standard_normal((130, 64)).astype(np.float32)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
     codes, _ = rvq().rvq_encode(to_dev(x), to_dev(books))
     assert (host(codes) == 0).all()
 
 
-def test_zero_inputs_and_codebooks():
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_zero_inputs_and_codebooks(scoring):
     x = np.zeros((70, 64), np.float32)
     books = np.zeros((2, 128, 64), np.float32)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
 
 
 @pytest.mark.parametrize("scale", [1e-6, 1e6])
-def test_scaled_data(scale):
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_scaled_data(scale, scoring):
     rng = np.random.default_rng(10)
     books = (_books(rng, 4, 512) * scale).astype(np.float32)
     x = (rng.standard_normal((200, 64)) * scale).astype(np.float32)
-    check_encode(x, books)
+    check_encode(x, books, scoring=scoring)
 
 
 def test_codes_leading_dimension():
@@ -140,13 +149,14 @@ def test_empty_batch_is_noop():
 
 
 @pytest.mark.parametrize("name,count", [("batched", 4096), ("deep", 2048)])
-def test_full_size_workloads_sampled(name, count):
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_full_size_workloads_sampled(name, count, scoring):
     """Full-size batches in the benchmark's launch configuration; oracle on a seeded sample."""
     w = W.WORKLOADS[name]
     books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
     x, t = W.latents(w, books)
     idx = W.sample_frames(w.n_frames, count, seed=3)
-    rep = check_encode(x, books, idx=idx)
+    rep = check_encode(x, books, idx=idx, scoring=scoring)
     announce("full-size report", **rep)
     if w.constructed_from < w.n_frames:
         m = rvq()
@@ -166,3 +176,25 @@ def test_argument_errors():
     assert e.value.status == m.RVQ_ERR_UNSUPPORTED
     assert m.rvq_encode(torch.zeros((10, 64), device="cuda:0"),
                         torch.zeros((2, 64, 64), device="cuda:0"))[0].shape == (10, 2)
+
+
+@pytest.mark.parametrize("name", ["batched", "deep"])
+def test_scorings_agree_at_full_size(name):
+    """Split-bf16 and fp32 scoring give identical codes, residuals and reconstructions."""
+    w = W.WORKLOADS[name]
+    books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
+    x, _ = W.latents(w, books)
+    m = rvq()
+    xg, bg = to_dev(x), to_dev(books)
+    announce("scorings agree", name=name)
+    a = [host(t) for t in m.rvq_encode_scored(xg, bg, "bf16x3")]
+    b = [host(t) for t in m.rvq_encode_scored(xg, bg, "fp32")]
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_unknown_scoring_rejected():
+    m = rvq()
+    import torch
+    with pytest.raises(ValueError):
+        m.rvq_encode_scored(torch.zeros((4, 64), device="cuda:0"), torch.zeros((1, 64, 64), device="cuda:0"), "fp8")
