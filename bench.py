@@ -2,20 +2,25 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
 
-One step = ``rvq_encode`` (codes + final residual) followed by
-``rvq_decode`` (codes -> reconstruction) over the whole batch, inputs and
-outputs resident in HBM. W untimed steps, then K timed steps between
-``torch.cuda.synchronize()`` calls. Per-launch kernel times come from HIP
-events recorded on the stream the kernels run on (torch's current stream,
-which is the stream handed to the C ABI).
+One step = ``rvq_encode`` (codes + final residual, default split-bf16
+scoring) followed by ``rvq_decode`` (codes -> reconstruction) over the whole
+batch, inputs and outputs resident in HBM. W untimed steps, then K timed
+steps between ``torch.cuda.synchronize()`` calls. Per-launch kernel times
+come from HIP events recorded on the stream the kernels run on (torch's
+current stream, which is the stream handed to the C ABI).
 
 Prints one JSON line with the throughput, the roofline of the dominant
-kernel (encode, fp32 matrix cores), the decode's HBM roofline, sampled
-parity against the CPU oracle, and the oracle's own throughput on a bounded
-sample of the same workload (``cpu_baseline``).
+kernel (the split-bf16 encode on the bf16 matrix cores), the same encode
+with fp32 scores against the fp32 matrix-core roofline, the decode's HBM
+roofline, sampled parity against the CPU oracle, and the oracle's own
+throughput on a bounded sample of the same workload (``cpu_baseline``).
+
+``--summarize-profiles DIR`` turns the rocprofv3 runs listed in
+PROFILE_COMMANDS into the summaries under ``profiles/``.
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,7 +36,18 @@ import rvq_workloads as W  # noqa: E402
 
 METRIC = "RVQ encode + decode frames/sec (Q=8,K=1024,D=64 fp32); % MFMA / HBM roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
+N_XCD, N_SIMD = 8, 1024            # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+COPY_BYTES = 512 << 20             # size of the counter-calibration copy
+
+CSRC = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc")
+# kernel kind -> sources whose text defines it (hashed to detect stale counters)
+KERNEL_SOURCES = {
+    "encode_bf16": ["encode_bf16.hip", "encode_common.h"],
+    "encode_fp32": ["encode.hip"],
+    "decode": ["decode.hip"],
+}
 
 
 def parse():
@@ -40,6 +56,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="batched", choices=list(W.WORKLOADS))
+    p.add_argument("--fp32-steps", type=int, default=5,
+                   help="launches of the fp32-scored encode timed after the main steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU-oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -51,29 +69,32 @@ def parse():
     return p.parse_args()
 
 
-def recorded_traffic(kernel_source, summary):
+def source_hash(kind):
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kind, workload):
     """HBM bytes per launch from a committed counter summary, or None if the kernel changed since."""
-    import hashlib
-    path = os.path.join(_ROOT, "profiles", summary)
+    path = os.path.join(_ROOT, "profiles", f"{kind}_{workload}_hbm_counters.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc", kernel_source)
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+    if rec.get("source_sha256") != source_hash(kind):
         return None
     return rec.get("traffic_bytes_per_launch")
 
+
+# ---------------------------------------------------------------- profiles
 
 PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp   # R = repository root
 rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o bench -- python3 $R/bench.py --workload {wl} --steps 20 --no-cpu-baseline
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
-rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_BUSY_CU_CYCLES SQ_INSTS_VALU SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
 python3 $R/bench.py --workload {wl} --summarize-profiles $R/gpurun_out/prof"""
-
-# MI355X: 8 XCDs, 256 CUs, 4 SIMDs per CU.
-N_XCD, N_SIMD = 8, 1024
-COPY_BYTES = 512 << 20
 
 
 def _csv(dirname, suffix):
@@ -89,8 +110,10 @@ def _csv(dirname, suffix):
 
 
 def _kernel_of(name):
+    if "encode_bf16_kernel" in name:
+        return "encode_bf16"
     if "encode_kernel" in name:
-        return "encode"
+        return "encode_fp32"
     if "decode_kernel" in name:
         return "decode"
     if "elementwise" in name and "MulFunctor" in name:
@@ -112,17 +135,19 @@ def _counter_means(rows, counter):
 
 
 def summarize_profiles(w, src_dir):
-    """Writes profiles/<kernel>_<workload>_* from the four rocprofv3 runs under src_dir."""
-    import hashlib
+    """Writes profiles/encode_decode_<workload>_rocprof.md and <kernel>_<workload>_hbm_counters.json."""
     out_dir = os.path.join(_ROOT, "profiles")
     os.makedirs(out_dir, exist_ok=True)
     cmds = PROFILE_COMMANDS.format(wl=w.name)
     n, q, k, d = w.n_frames, w.n_stages, w.n_codes, w.dim
+    enc_flop = 2.0 * q * k * d * n
+    dec_bytes = (4.0 * q + 4.0 * d) * n
 
     stats = _csv(os.path.join(src_dir, "trace"), "kernel_stats.csv")
-    lines = [f"# Kernel trace: encode + decode, workload `{w.name}`", "",
+    lines = [f"# rocprofv3: encode + decode, workload `{w.name}`", "",
              f"Workload: {w.description}.", "", "Commands (the summary is the last line's output):", "",
              "```", cmds, "```", "",
+             "## Kernel trace", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     avg = {}
     for r in stats:
@@ -131,34 +156,45 @@ def summarize_profiles(w, src_dir):
         avg[kind] = a
         lines.append(f"| {kind} | {r['Calls']} | {a:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    enc_flop = 2.0 * q * k * d * n
-    dec_bytes = (4.0 * q + 4.0 * d) * n
-    lines += ["", f"Encode: {enc_flop:.4g} algorithmic flop per launch (2QKD per frame) / "
-                  f"{avg['encode']:.1f} us = {enc_flop / avg['encode'] / 1e6:.1f} TFLOP/s "
-                  f"({enc_flop / avg['encode'] / 1e6 / PEAK_FP32_MFMA_TFLOPS:.1%} of {PEAK_FP32_MFMA_TFLOPS} fp32 MFMA).",
-              f"Decode: {dec_bytes:.4g} algorithmic bytes per launch ((4Q+4D) per frame) / "
-              f"{avg['decode']:.1f} us = {dec_bytes / avg['decode'] / 1e3:.0f} GB/s "
-              f"({dec_bytes / avg['decode'] / 1e3 / PEAK_HBM_GBPS:.1%} of {PEAK_HBM_GBPS:.0f} GB/s HBM)."]
+    lines.append("")
+    if "encode_bf16" in avg:
+        t = avg["encode_bf16"]
+        lines.append(f"- encode_bf16: {3 * enc_flop:.4g} bf16 matrix flop per launch (3 x 2QKD per frame) / "
+                     f"{t:.1f} us = {3 * enc_flop / t / 1e6:.1f} TFLOP/s "
+                     f"({3 * enc_flop / t / 1e6 / PEAK_BF16_MFMA_TFLOPS:.1%} of {PEAK_BF16_MFMA_TFLOPS:.0f} bf16); "
+                     f"fp32-equivalent {enc_flop / t / 1e6:.1f} TFLOP/s "
+                     f"({enc_flop / t / 1e6 / PEAK_FP32_MFMA_TFLOPS:.1%} of {PEAK_FP32_MFMA_TFLOPS} fp32).")
+    if "encode_fp32" in avg:
+        t = avg["encode_fp32"]
+        lines.append(f"- encode_fp32: {enc_flop:.4g} flop per launch (2QKD per frame) / {t:.1f} us = "
+                     f"{enc_flop / t / 1e6:.1f} TFLOP/s ({enc_flop / t / 1e6 / PEAK_FP32_MFMA_TFLOPS:.1%} "
+                     f"of {PEAK_FP32_MFMA_TFLOPS} fp32 MFMA).")
+    if "decode" in avg:
+        t = avg["decode"]
+        lines.append(f"- decode: {dec_bytes:.4g} bytes per launch ((4Q+4D) per frame) / {t:.1f} us = "
+                     f"{dec_bytes / t / 1e3:.0f} GB/s ({dec_bytes / t / 1e3 / PEAK_HBM_GBPS:.1%} of "
+                     f"{PEAK_HBM_GBPS:.0f} GB/s HBM).")
 
     fetch = _counter_means(_csv(os.path.join(src_dir, "fetch"), "counter_collection.csv"), "FETCH_SIZE")
     write = _counter_means(_csv(os.path.join(src_dir, "write"), "counter_collection.csv"), "WRITE_SIZE")
     f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
     w_scale = COPY_BYTES / (write["copy"] * 1024.0)
-    algo = {"encode": (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d, "decode": dec_bytes + 4.0 * q * k * d}
+    enc_algo = (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d
+    algo = {"encode_bf16": enc_algo, "encode_fp32": enc_algo, "decode": dec_bytes + 4.0 * q * k * d}
     lines += ["", "## HBM counters (per launch)", "",
               f"A 512 MiB elementwise copy reads FETCH_SIZE = {fetch['copy']:.0f} KiB and WRITE_SIZE = "
-              f"{write['copy']:.0f} KiB, so counter readings are scaled by {f_scale:.3f} (fetch) and "
+              f"{write['copy']:.0f} KiB, so readings are scaled by {f_scale:.3f} (fetch) and "
               f"{w_scale:.3f} (write).", "",
               "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB | algorithmic MB |",
               "|---|---|---|---|---|---|"]
-    for kind, src in (("encode", "encode.hip"), ("decode", "decode.hip")):
+    for kind in KERNEL_SOURCES:
+        if kind not in fetch or kind not in write:
+            continue
         rd = fetch[kind] * 1024.0 * f_scale
         wr = write[kind] * 1024.0 * w_scale
         lines.append(f"| {kind} | {fetch[kind]:.0f} | {write[kind]:.0f} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
                      f"{algo[kind] / 1e6:.1f} |")
-        sha = hashlib.sha256(open(os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc", src),
-                                  "rb").read()).hexdigest()
-        json.dump({"kernel": kind, "workload": w.name, "source_sha256": sha,
+        json.dump({"kernel": kind, "workload": w.name, "source_sha256": source_hash(kind),
                    "fetch_kib": fetch[kind], "write_kib": write[kind],
                    "copy_scale_fetch": f_scale, "copy_scale_write": w_scale,
                    "traffic_bytes_per_launch": rd + wr, "algorithmic_bytes_per_launch": algo[kind],
@@ -166,22 +202,29 @@ def summarize_profiles(w, src_dir):
                   open(os.path.join(out_dir, f"{kind}_{w.name}_hbm_counters.json"), "w"), indent=1)
 
     mf = _csv(os.path.join(src_dir, "mfma"), "counter_collection.csv")
-    c = {name: _counter_means(mf, name).get("encode") for name in
-         ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_VALU",
-          "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")}
-    active = c["GRBM_GUI_ACTIVE"] / N_XCD
-    lines += ["", "## Encode matrix-core counters (per launch)", "",
-              f"- MFMA busy: {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * N_SIMD):.1%} of SIMD cycles "
-              f"(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x {N_SIMD} SIMDs))",
-              f"- MFMA fp32 flop counted: {c['SQ_INSTS_VALU_MFMA_MOPS_F32'] * 512:.4g} "
-              f"(algorithmic {enc_flop:.4g})",
-              f"- VALU instructions (incl. MFMA): {c['SQ_INSTS_VALU']:.4g}",
-              f"- LDS bank-conflict cycles / LDS active cycles: "
-              f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1%}"]
+    names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+             "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
+    means = {name: _counter_means(mf, name) for name in names}
+    lines += ["", "## Matrix-core counters (per launch)", ""]
+    for kind in ("encode_bf16", "encode_fp32"):
+        c = {name: means[name].get(kind) for name in names}
+        if c["GRBM_GUI_ACTIVE"] is None:
+            continue
+        active = c["GRBM_GUI_ACTIVE"] / N_XCD
+        lines += [f"{kind}:",
+                  f"- MFMA busy: {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * N_SIMD):.1%} of SIMD cycles "
+                  f"(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x {N_SIMD} SIMDs))",
+                  f"- MFMA flop counted: fp32 {c['SQ_INSTS_VALU_MFMA_MOPS_F32'] * 512:.4g}, "
+                  f"bf16 {c['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g} (algorithmic 2QKD = {enc_flop:.4g})",
+                  f"- instructions: VALU {c['SQ_INSTS_VALU']:.4g} of which MFMA {c['SQ_INSTS_MFMA']:.4g}",
+                  f"- LDS bank-conflict cycles / LDS active cycles: "
+                  f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1%}", ""]
     path = os.path.join(out_dir, f"encode_decode_{w.name}_rocprof.md")
     open(path, "w").write("\n".join(lines) + "\n")
     print("wrote", path)
 
+
+# ------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(w, x, books, codes_gpu, target_s):
     """Times the CPU oracle (encode + decode) on a seeded frame sample; also checks parity there."""
@@ -210,8 +253,10 @@ def cpu_baseline(w, x, books, codes_gpu, target_s):
     return base, parity
 
 
+# --------------------------------------------------------------- benches
+
 def bench_projected(args, w):
-    """fc -> encode -> decode -> fc2 per step (rvq_project_roundtrip); all three kernels are fp32 MFMA."""
+    """fc -> encode -> decode -> fc2 per step (rvq_project_roundtrip)."""
     import torch
     import residual_vector_quantization_amd as rvq
     books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
@@ -240,18 +285,16 @@ def bench_projected(args, w):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev[0].elapsed_time(ev[1]) / args.steps
-    flop = (2.0 * q * k * d + 2 * 2.0 * hid * d) * n
-    tflops = flop / (ms * 1e-3) / 1e12
+    lin_flop = 2 * 2.0 * hid * d * n
+    enc_flop = 2.0 * q * k * d * n
     rec = {"metric": "RVQ projected round trip frames/sec (fc 1024->64, Q=8 K=1024 D=64 RVQ, fc2 64->1024; fp32)",
            "value": n * args.steps / wall, "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": w.name, "frames": n, "hidden": hid, "Q": q, "K": k, "D": d,
                       "recipe": w.description},
-           "roofline": {"bound": "mfma", "kernel": "linear_in + encode + linear_out (fp32 MFMA)",
-                        "achieved": tflops, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                        "frac": tflops / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
-                        "work_per_launch": f"(2QKD + 4*H*D)*N = {flop:.4g} flop"}}
+           "step_ms_events": ms,
+           "fp32_equivalent_tflops": (lin_flop + enc_flop) / (ms * 1e-3) / 1e12}
     print(json.dumps(rec), flush=True)
 
 
@@ -306,23 +349,39 @@ def main():
     wall = time.perf_counter() - t0
     enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    codes_h = codes.cpu().numpy()
 
-    n, q, k, d = w.n_frames, w.n_stages, w.n_codes, w.dim
-    ms_per_step = wall * 1e3 / args.steps
-    value = n * args.steps / wall
-    enc_flop = 2.0 * q * k * d * n
-    enc_tflops = enc_flop / (enc_ms * 1e-3) / 1e12
-    dec_bytes = (4.0 * q + 4.0 * d) * n
-    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    # the same encode with fp32 matrix-core scores (identical results), timed separately
+    fp32_ms = None
+    if args.fp32_steps > 0:
+        c32 = torch.empty_like(codes)
+        r32 = torch.empty_like(xg)
+        rvq.rvq_encode_scored(xg, bg, "fp32", out=(c32, None, r32))
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for _ in range(args.fp32_steps):
+            rvq.rvq_encode_scored(xg, bg, "fp32", out=(c32, None, r32))
+        ev[1].record()
+        torch.cuda.synchronize()
+        fp32_ms = ev[0].elapsed_time(ev[1]) / args.fp32_steps
+        if not torch.equal(c32, codes):
+            raise SystemExit("fp32 and split-bf16 scorings disagree")
 
     if args.calibrate_copy:
-        a = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+        a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         b = torch.empty_like(a)
         torch.mul(a, 1.0, out=b)
         torch.cuda.synchronize()
         del a, b
 
-    codes_h = codes.cpu().numpy()
+    n, q, k, d = w.n_frames, w.n_stages, w.n_codes, w.dim
+    ms_per_step = wall * 1e3 / args.steps
+    value = n * args.steps / wall
+    enc_flop = 2.0 * q * k * d * n
+    bf16_tflops = 3 * enc_flop / (enc_ms * 1e-3) / 1e12
+    dec_bytes = (4.0 * q + 4.0 * d) * n
+    dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": value,
@@ -336,21 +395,30 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "frames": n, "Q": q, "K": k, "D": d,
+        "config": {"workload": w.name, "frames": n, "Q": q, "K": k, "D": d, "scoring": "split-bf16",
                    "recipe": w.description},
         "audio_seconds_per_s": value / w.frame_rate_hz,
         "encode_ms": enc_ms,
         "decode_ms": dec_ms,
-        "roofline": {"bound": "mfma", "kernel": "encode_kernel (fp32 v_mfma_f32_32x32x2_f32)",
-                     "achieved": enc_tflops, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": enc_tflops / PEAK_FP32_MFMA_TFLOPS,
-                     "traffic": recorded_traffic("encode.hip", f"encode_{w.name}_hbm_counters.json"),
-                     "work_per_launch": f"2*Q*K*D*N = {enc_flop:.4g} flop"},
+        "roofline": {"bound": "mfma", "kernel": "encode_bf16_kernel (v_mfma_f32_32x32x16_bf16, 3 split products)",
+                     "achieved": bf16_tflops, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": bf16_tflops / PEAK_BF16_MFMA_TFLOPS,
+                     "traffic": recorded_traffic("encode_bf16", w.name),
+                     "work_per_launch": f"3*2*Q*K*D*N = {3 * enc_flop:.4g} bf16 flop"},
+        "encode_fp32_equivalent": {"achieved": enc_flop / (enc_ms * 1e-3) / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
+                                   "unit": "TFLOP/s", "work_per_launch": f"2*Q*K*D*N = {enc_flop:.4g} flop"},
         "decode_roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": dec_gbps,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
-                            "traffic": recorded_traffic("decode.hip", f"decode_{w.name}_hbm_counters.json"),
+                            "traffic": recorded_traffic("decode", w.name),
                             "work_per_launch": f"(4Q+4D)*N = {dec_bytes:.4g} B"},
     }
+    if fp32_ms is not None:
+        t32 = enc_flop / (fp32_ms * 1e-3) / 1e12
+        rec["encode_fp32_scoring"] = {"kernel": "encode_kernel (v_mfma_f32_32x32x2_f32)", "ms": fp32_ms,
+                                      "bound": "mfma", "achieved": t32, "peak": PEAK_FP32_MFMA_TFLOPS,
+                                      "unit": "TFLOP/s", "frac": t32 / PEAK_FP32_MFMA_TFLOPS,
+                                      "traffic": recorded_traffic("encode_fp32", w.name),
+                                      "codes_equal_to_default": True}
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, x, books, codes_h, args.cpu_seconds)
         rec["cpu_baseline"] = base
