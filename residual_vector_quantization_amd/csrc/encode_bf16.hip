@@ -53,13 +53,26 @@ static_assert(kThreads == kEncodeThreads, "thread count");
 static_assert(kWaves * kFramesPerWave == kEncodeFramesPerBlock, "frames per block");
 static_assert(kWaves * 32 == kChunk, "staging maps each wavefront to 32 codeword rows");
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// hi = bf16(v), lo = bf16(v - hi), both round to nearest even, converted in
+// pairs (one v_cvt_pk_bf16_f32 per two values); hi is widened back to fp32 by
+// placing its 16 bits at the top of a word, and v - hi is exact in fp32.
 __device__ __forceinline__ void split8(const float *v, bf16x8 &hi, bf16x8 &lo)
 {
+    u32x4 hp, lp;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        hi[e] = static_cast<__bf16>(v[e]);
-        lo[e] = static_cast<__bf16>(v[e] - static_cast<float>(hi[e]));
+    for (int p = 0; p < 4; ++p) {
+        const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{v[2 * p], v[2 * p + 1]}, bf16x2));
+        const float r0 = v[2 * p] - __uint_as_float(h << 16);
+        const float r1 = v[2 * p + 1] - __uint_as_float(h & 0xFFFF0000u);
+        hp[p] = h;
+        lp[p] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
     }
+    hi = __builtin_bit_cast(bf16x8, hp);
+    lo = __builtin_bit_cast(bf16x8, lp);
 }
 
 // Key scan of a 64-codeword group (two blocks): running best, second and
