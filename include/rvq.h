@@ -154,6 +154,32 @@ RVQ_API rvq_status rvq_encode_scored(const float *x, int64_t n_frames, int32_t d
                                      float *recon, float *residual, rvq_scoring scoring, void *stream);
 
 /*
+ * Prepared codebooks: the split-bf16 layout of a codebook tensor, computed
+ * once (codebooks are model constants) so that each encode only copies rows.
+ *
+ * rvq_prepared_bytes returns the size of the buffer for the given shape
+ * (a negative rvq_status for invalid or unsupported shapes).
+ * rvq_prepare_codebooks writes it on `stream` into caller-allocated device
+ * memory `prepared` (16-byte aligned, at least rvq_prepared_bytes bytes).
+ * Per stage it holds: each codeword as bf16 hi = bf16(c) and lo = bf16(c -
+ * hi) in 8-dim groups, 0.5*||c||^2 in fp32, and the stage's largest
+ * 0.5*||c||^2. The buffer depends only on the codebook values.
+ *
+ * rvq_encode_prepared is rvq_encode_scored with split-bf16 scoring, reading
+ * the split rows from `prepared` (which must have been prepared from the same
+ * `codebooks` with at least `n_stages` stages and the same n_codes and dim;
+ * the library cannot check this). Results are identical to rvq_encode.
+ */
+RVQ_API int64_t rvq_prepared_bytes(int32_t n_stages, int32_t n_codes, int32_t dim);
+RVQ_API rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                         int32_t dim, void *prepared, int64_t prepared_bytes, void *stream);
+RVQ_API rvq_status rvq_encode_prepared(const float *x, int64_t n_frames, int32_t dim,
+                                       const float *codebooks, const void *prepared,
+                                       int32_t n_stages, int32_t n_codes,
+                                       int32_t *codes, int32_t codes_ld,
+                                       float *recon, float *residual, void *stream);
+
+/*
  * rvq_project_roundtrip -- linear in, encode, decode, linear out.
  *
  * The "Audio tokenizer pipeline" section of the "Architecture" page puts a

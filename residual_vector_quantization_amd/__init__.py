@@ -16,6 +16,10 @@ Functions (same names as the C entry points):
   -> ``(codes, recon, residual or None)``
 * ``rvq_encode_scored(x, codebooks, scoring, n_stages=None, recon=True, residual=True)``
   -> ``(codes, recon or None, residual or None)``; scoring "default", "bf16x3" or "fp32"
+* ``rvq_prepared_bytes(n_stages, n_codes, dim)`` -> int;
+  ``rvq_prepare_codebooks(codebooks)`` -> uint8 device tensor;
+  ``rvq_encode_prepared(x, codebooks, prepared, n_stages=None, recon=False, residual=True)``
+  -> ``(codes, recon or None, residual or None)``
 * ``rvq_project_roundtrip(h, w_in, b_in, codebooks, w_out, b_out, n_stages=None)``
   -> ``(codes, latent, latent_recon, h_recon)``
 * ``rvq_version()``, ``rvq_status_string(status)``
@@ -38,7 +42,8 @@ RVQ_ERR_UNSUPPORTED = -2
 RVQ_ERR_DEVICE = -3
 
 EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip",
-            "rvq_encode_scored", "rvq_project_roundtrip")
+            "rvq_encode_scored", "rvq_prepared_bytes", "rvq_prepare_codebooks", "rvq_encode_prepared",
+            "rvq_project_roundtrip")
 
 SCORING = {"default": 0, "bf16x3": 1, "fp32": 2}
 
@@ -73,6 +78,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.rvq_roundtrip.argtypes = [vp, i64, i32, vp, i32, i32, vp, i32, vp, vp, vp]
     lib.rvq_encode_scored.restype = ctypes.c_int
     lib.rvq_encode_scored.argtypes = [vp, i64, i32, vp, i32, i32, vp, i32, vp, vp, ctypes.c_int, vp]
+    lib.rvq_prepared_bytes.restype = ctypes.c_int64
+    lib.rvq_prepared_bytes.argtypes = [i32, i32, i32]
+    lib.rvq_prepare_codebooks.restype = ctypes.c_int
+    lib.rvq_prepare_codebooks.argtypes = [vp, i32, i32, i32, vp, i64, vp]
+    lib.rvq_encode_prepared.restype = ctypes.c_int
+    lib.rvq_encode_prepared.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, i32, vp, vp, vp]
     lib.rvq_project_roundtrip.restype = ctypes.c_int
     lib.rvq_project_roundtrip.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, vp,
                                           vp, i32, vp, vp, vp, vp]
@@ -220,6 +231,54 @@ def rvq_encode_scored(x: torch.Tensor, codebooks: torch.Tensor, scoring: str = "
     st = load().rvq_encode_scored(_ptr(x), n, d, _ptr(codebooks), q, codebooks.shape[1], _ptr(codes),
                                   codes.shape[1], _ptr(rec), _ptr(res), SCORING[scoring], _stream(x))
     _check("rvq_encode_scored", st)
+    return codes, rec, res
+
+
+def rvq_prepared_bytes(n_stages: int, n_codes: int, dim: int) -> int:
+    size = load().rvq_prepared_bytes(n_stages, n_codes, dim)
+    if size < 0:
+        raise RVQError("rvq_prepared_bytes", size, rvq_status_string(size))
+    return size
+
+
+def rvq_prepare_codebooks(codebooks: torch.Tensor, prepared: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Split-bf16 layout of ``codebooks`` [Q, K, D] (a uint8 tensor on the same device)."""
+    _require(codebooks, "codebooks", torch.float32, 3)
+    q, k, d = codebooks.shape
+    size = rvq_prepared_bytes(q, k, d)
+    if prepared is None:
+        prepared = torch.empty(size, dtype=torch.uint8, device=codebooks.device)
+    _require(prepared, "prepared", torch.uint8, 1, codebooks.device)
+    st = load().rvq_prepare_codebooks(_ptr(codebooks), q, k, d, _ptr(prepared), prepared.numel(),
+                                      _stream(codebooks))
+    _check("rvq_prepare_codebooks", st)
+    return prepared
+
+
+def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torch.Tensor,
+                        n_stages: Optional[int] = None, recon: bool = False, residual: bool = True,
+                        out=None):
+    """Split-bf16 encode from prepared codebooks: ``(codes, recon or None, residual or None)``."""
+    _require(x, "x", torch.float32, 2)
+    _require(codebooks, "codebooks", torch.float32, 3, x.device)
+    _require(prepared, "prepared", torch.uint8, 1, x.device)
+    n, d = x.shape
+    q = _stages(codebooks, n_stages)
+    if prepared.numel() < rvq_prepared_bytes(q, codebooks.shape[1], d):
+        raise ValueError("prepared buffer is too small for these codebooks")
+    if out is None:
+        out = (torch.empty((n, q), dtype=torch.int32, device=x.device),
+               torch.empty_like(x) if recon else None, torch.empty_like(x) if residual else None)
+    codes, rec, res = out
+    _require(codes, "codes", torch.int32, 2, x.device)
+    for t, name in ((rec, "recon"), (res, "residual")):
+        if t is not None:
+            _require(t, name, torch.float32, 2, x.device)
+            if t.shape != x.shape:
+                raise ValueError(f"{name} must match x")
+    st = load().rvq_encode_prepared(_ptr(x), n, d, _ptr(codebooks), _ptr(prepared), q, codebooks.shape[1],
+                                    _ptr(codes), codes.shape[1], _ptr(rec), _ptr(res), _stream(x))
+    _check("rvq_encode_prepared", st)
     return codes, rec, res
 
 

@@ -147,10 +147,24 @@ __device__ __forceinline__ void score_group(const __bf16 *sb, const float *sn, i
     fold_group(best, second, bb, sb0, base, half, best_k, second_k);
 }
 
-template <bool kRecon, bool kResidual>
+// Prepared codebooks (rvq_prepare_codebooks): per stage one block of
+//   rows  [Kp][256 B]  16-byte segments (8 bf16 hi, 8 bf16 lo) per 8-dim group
+//   norms [Kp] fp32    0.5*||c||^2, kNoScore for rows k >= n_codes
+//   max   uint32       bits of the largest valid 0.5*||c||^2
+// with Kp = n_codes rounded up to kChunk, blocks kStageAlign-aligned.
+constexpr int64_t kStageAlign = 256;
+__host__ __device__ inline int64_t padded_codes(int n_codes) { return (n_codes + kChunk - 1) / kChunk * kChunk; }
+__host__ __device__ inline int64_t stage_bytes(int n_codes)
+{
+    const int64_t kp = padded_codes(n_codes);
+    return (kp * 260 + 4 + kStageAlign - 1) / kStageAlign * kStageAlign;
+}
+
+template <bool kRecon, bool kResidual, bool kPrepared>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
-                        const float *__restrict__ books, int n_stages, int n_codes,
+                        const float *__restrict__ books, const uint8_t *__restrict__ prepared,
+                        int n_stages, int n_codes,
                         int32_t *__restrict__ codes, int codes_ld,
                         float *__restrict__ residual, float *__restrict__ recon)
 {
@@ -195,10 +209,22 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
     bool stage_valid = false;
     unsigned stage_max = 0u;
 
+    const int64_t kp = padded_codes(n_codes);
+    const int64_t sbytes = stage_bytes(n_codes);
+    float stage_norm = 0.0f;   // prepared mode: this row's 0.5*||c||^2
+
     auto fetch = [&](int g) {
         const int q = g / n_chunks;
         const int c = g - q * n_chunks;
         const int k = c * kChunk + srow;
+        if (kPrepared) {
+            const uint8_t *blk = prepared + q * sbytes;
+            const f32x4 *p = reinterpret_cast<const f32x4 *>(blk + static_cast<int64_t>(k) * 256 + 128 * half);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) stage[i] = p[i];
+            if (half == 0) stage_norm = reinterpret_cast<const float *>(blk + kp * 256)[k];
+            return;
+        }
         if (c == 0) stage_max = 0u;
         // rows past n_codes load the last row again; their norm becomes kNoScore
         stage_valid = k < n_codes;
@@ -209,6 +235,13 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
     };
     auto commit = [&](int g) {
         const int buf = g & 1;
+        if (kPrepared) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(&s_book[buf][srow * kRowH + 64 * half]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) dst[i] = stage[i];
+            if (half == 0) s_norm[buf][srow] = stage_norm;
+            return;
+        }
         float s = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -282,8 +315,13 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
             for (int j = 0; j < 32; ++j) rn = __builtin_fmaf(n[j], n[j], rn);
             rn = rn + __shfl_xor(rn, 32);
 
-            const uint4 cm = *reinterpret_cast<const uint4 *>(s_cmax[q & 1]);
-            const float c2 = __uint_as_float(max(max(cm.x, cm.y), max(cm.z, cm.w)));   // max_k 0.5||c_k||^2
+            float c2;   // max_k 0.5||c_k||^2 over the stage
+            if (kPrepared) {
+                c2 = *reinterpret_cast<const float *>(prepared + q * sbytes + kp * 260);
+            } else {
+                const uint4 cm = *reinterpret_cast<const uint4 *>(s_cmax[q & 1]);
+                c2 = __uint_as_float(max(max(cm.x, cm.y), max(cm.z, cm.w)));
+            }
             const float bound = kBoundScale * (c2 + sqrtf(rn) * sqrtf(2.0f * c2)) + kAbsSlack;
             const float lim = fminf(best, best_o) + 2.0f * bound;
             const bool overflow = third <= lim || third_o <= lim ||
@@ -368,28 +406,114 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
     }
 }
 
-}  // namespace
+// One thread per (stage, padded row): hi/lo split and half-norm of the row.
+__global__ __launch_bounds__(256)
+void prepare_rows_kernel(const float *__restrict__ books, int n_stages, int n_codes, uint8_t *__restrict__ prepared)
+{
+    const int64_t kp = padded_codes(n_codes);
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (i >= kp * n_stages) return;
+    const int q = static_cast<int>(i / kp);
+    const int k = static_cast<int>(i - q * kp);
+    uint8_t *blk = prepared + q * stage_bytes(n_codes);
+    bf16x8 *row = reinterpret_cast<bf16x8 *>(blk + static_cast<int64_t>(k) * 256);
+    float *norms = reinterpret_cast<float *>(blk + kp * 256);
+    if (k >= n_codes) {
+        const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+#pragma unroll
+        for (int j = 0; j < 16; ++j) row[j] = z;
+        norms[k] = kNoScore;
+        return;
+    }
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(books + (static_cast<int64_t>(q) * n_codes + k) * kDim);
+    float s = 0.0f;
+#pragma unroll
+    for (int grp = 0; grp < 8; ++grp) {
+        const f32x4 a = src[2 * grp], b = src[2 * grp + 1];
+        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s = __builtin_fmaf(v[e], v[e], s);
+        bf16x8 hi, lo;
+        split8(v, hi, lo);
+        row[2 * grp] = hi;
+        row[2 * grp + 1] = lo;
+    }
+    norms[k] = 0.5f * s;
+}
 
-hipError_t launch_encode_bf16(const float *x, int64_t n_frames, const float *books,
-                              int n_stages, int n_codes, int32_t *codes, int codes_ld,
-                              float *residual, float *recon, hipStream_t stream)
+// One workgroup per stage: the largest valid half-norm (bits; values >= 0).
+__global__ __launch_bounds__(256)
+void prepare_max_kernel(int n_codes, uint8_t *__restrict__ prepared)
+{
+    __shared__ unsigned s_m[4];
+    const int64_t kp = padded_codes(n_codes);
+    uint8_t *blk = prepared + static_cast<int64_t>(blockIdx.x) * stage_bytes(n_codes);
+    const float *norms = reinterpret_cast<const float *>(blk + kp * 256);
+    unsigned m = 0u;
+    for (int k = threadIdx.x; k < n_codes; k += 256) m = max(m, __float_as_uint(norms[k]));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
+    if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *reinterpret_cast<unsigned *>(blk + kp * 260) = max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3]));
+}
+
+template <bool kPrepared>
+hipError_t launch_variant(const float *x, int64_t n_frames, const float *books, const uint8_t *prepared,
+                          int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
+                          float *recon, hipStream_t stream)
 {
     const int64_t blocks = (n_frames + kEncodeFramesPerBlock - 1) / kEncodeFramesPerBlock;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
     if (recon && residual)
-        hipLaunchKernelGGL((encode_bf16_kernel<true, true>), grid, block, 0, stream,
-                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+        hipLaunchKernelGGL((encode_bf16_kernel<true, true, kPrepared>), grid, block, 0, stream,
+                           x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
     else if (recon)
-        hipLaunchKernelGGL((encode_bf16_kernel<true, false>), grid, block, 0, stream,
-                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+        hipLaunchKernelGGL((encode_bf16_kernel<true, false, kPrepared>), grid, block, 0, stream,
+                           x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
     else if (residual)
-        hipLaunchKernelGGL((encode_bf16_kernel<false, true>), grid, block, 0, stream,
-                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+        hipLaunchKernelGGL((encode_bf16_kernel<false, true, kPrepared>), grid, block, 0, stream,
+                           x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
     else
-        hipLaunchKernelGGL((encode_bf16_kernel<false, false>), grid, block, 0, stream,
-                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+        hipLaunchKernelGGL((encode_bf16_kernel<false, false, kPrepared>), grid, block, 0, stream,
+                           x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
     return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t prepared_bytes(int n_stages, int n_codes) { return stage_bytes(n_codes) * n_stages; }
+
+hipError_t launch_prepare(const float *books, int n_stages, int n_codes, void *prepared, hipStream_t stream)
+{
+    const int64_t rows = padded_codes(n_codes) * n_stages;
+    const int64_t blocks = (rows + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    uint8_t *p = static_cast<uint8_t *>(prepared);
+    hipLaunchKernelGGL(prepare_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                       books, n_stages, n_codes, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prepare_max_kernel, dim3(n_stages), dim3(256), 0, stream, n_codes, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_bf16(const float *x, int64_t n_frames, const float *books,
+                              int n_stages, int n_codes, int32_t *codes, int codes_ld,
+                              float *residual, float *recon, hipStream_t stream)
+{
+    return launch_variant<false>(x, n_frames, books, nullptr, n_stages, n_codes, codes, codes_ld, residual,
+                                 recon, stream);
+}
+
+hipError_t launch_encode_prepared(const float *x, int64_t n_frames, const float *books, const void *prepared,
+                                  int n_stages, int n_codes, int32_t *codes, int codes_ld,
+                                  float *residual, float *recon, hipStream_t stream)
+{
+    return launch_variant<true>(x, n_frames, books, static_cast<const uint8_t *>(prepared), n_stages, n_codes,
+                                codes, codes_ld, residual, recon, stream);
 }
 
 }  // namespace rvq

@@ -112,6 +112,40 @@ RVQ_API rvq_status rvq_decode(const int32_t *codes, int32_t codes_ld, int64_t n_
                                        static_cast<hipStream_t>(stream)));
 }
 
+RVQ_API int64_t rvq_prepared_bytes(int32_t n_stages, int32_t n_codes, int32_t dim)
+{
+    const rvq_status st = check_shape(0, dim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    return rvq::prepared_bytes(n_stages, n_codes);
+}
+
+RVQ_API rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                         int32_t dim, void *prepared, int64_t prepared_bytes, void *stream)
+{
+    const rvq_status st = check_shape(0, dim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (!codebooks || !prepared || !aligned(codebooks, 16) || !aligned(prepared, 16)) return RVQ_ERR_INVALID_ARG;
+    if (prepared_bytes < rvq::prepared_bytes(n_stages, n_codes)) return RVQ_ERR_INVALID_ARG;
+    return from_hip(rvq::launch_prepare(codebooks, n_stages, n_codes, prepared, static_cast<hipStream_t>(stream)));
+}
+
+RVQ_API rvq_status rvq_encode_prepared(const float *x, int64_t n_frames, int32_t dim, const float *codebooks,
+                                       const void *prepared, int32_t n_stages, int32_t n_codes,
+                                       int32_t *codes, int32_t codes_ld, float *recon, float *residual,
+                                       void *stream)
+{
+    rvq_status st = check_shape(n_frames, dim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (codes_ld < n_stages) return RVQ_ERR_INVALID_ARG;
+    if (n_frames == 0) return RVQ_OK;
+    if (!x || !codebooks || !prepared || !codes) return RVQ_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(codebooks, 16) || !aligned(prepared, 16) || !aligned(codes, 4) ||
+        (recon && !aligned(recon, 16)) || (residual && !aligned(residual, 16)))
+        return RVQ_ERR_INVALID_ARG;
+    return from_hip(rvq::launch_encode_prepared(x, n_frames, codebooks, prepared, n_stages, n_codes, codes,
+                                                codes_ld, residual, recon, static_cast<hipStream_t>(stream)));
+}
+
 RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32_t hidden,
                                          const float *w_in, const float *b_in,
                                          const float *codebooks, int32_t n_stages, int32_t n_codes,

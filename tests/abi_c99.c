@@ -51,6 +51,14 @@ int main(void)
                   RVQ_ERR_INVALID_ARG);
     bad += expect("scored empty", rvq_encode_scored(NULL, 0, 64, NULL, 8, 1024, NULL, 8, NULL, NULL, RVQ_SCORING_FP32, NULL),
                   RVQ_OK);
+    bad += expect("prepared bytes dim", (rvq_status)rvq_prepared_bytes(8, 1024, 16), RVQ_ERR_UNSUPPORTED);
+    if (rvq_prepared_bytes(8, 1024, 64) <= 0) bad++;
+    bad += expect("prepare too small", rvq_prepare_codebooks(fx, 8, 1024, 64, fx, 16, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("prepare null", rvq_prepare_codebooks(NULL, 8, 1024, 64, fx, 1 << 30, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("encode prepared null", rvq_encode_prepared(fx, 10, 64, fx, NULL, 8, 1024, ic, 8, NULL, NULL, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("encode prepared empty", rvq_encode_prepared(NULL, 0, 64, NULL, NULL, 8, 1024, NULL, 8, NULL, NULL, NULL),
+                  RVQ_OK);
     printf("%s\n", bad ? "abi_c99: FAILED" : "abi_c99: ok");
     return bad ? 1 : 0;
 }

@@ -31,7 +31,7 @@ def announce(what, **shape):
     print(f"[gpu case] {what} " + " ".join(f"{k}={v}" for k, v in shape.items()), flush=True)
 
 
-SCORINGS = ["default", "fp32"]
+SCORINGS = ["default", "fp32", "prepared"]
 
 
 def check_encode(x, books, n_stages=None, idx=None, roundtrip=True, scoring="default"):
@@ -47,13 +47,18 @@ def check_encode(x, books, n_stages=None, idx=None, roundtrip=True, scoring="def
     q = books.shape[0] if n_stages is None else n_stages
     announce("encode", n=x.shape[0], q=q, k=books.shape[1], scoring=scoring)
     xg, bg = to_dev(x), to_dev(books)
+    prep = m.rvq_prepare_codebooks(bg) if scoring == "prepared" else None
     if scoring == "default":
         codes, res = m.rvq_encode(xg, bg, n_stages=q)
+    elif scoring == "prepared":
+        codes, _, res = m.rvq_encode_prepared(xg, bg, prep, n_stages=q)
     else:
         codes, _, res = m.rvq_encode_scored(xg, bg, scoring, n_stages=q, recon=False)
     if roundtrip:
         if scoring == "default":
             codes2, recon, res2 = m.rvq_roundtrip(xg, bg, n_stages=q)
+        elif scoring == "prepared":
+            codes2, recon, res2 = m.rvq_encode_prepared(xg, bg, prep, n_stages=q, recon=True)
         else:
             codes2, recon, res2 = m.rvq_encode_scored(xg, bg, scoring, n_stages=q)
         out = m.rvq_decode(codes2, bg)

@@ -25,7 +25,8 @@ def declared():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == sorted(["rvq_decode", "rvq_encode", "rvq_encode_scored", "rvq_project_roundtrip",
+    assert declared() == sorted(["rvq_decode", "rvq_encode", "rvq_encode_prepared", "rvq_encode_scored",
+                                 "rvq_prepare_codebooks", "rvq_prepared_bytes", "rvq_project_roundtrip",
                                  "rvq_roundtrip", "rvq_status_string", "rvq_version"])
 
 
@@ -65,3 +66,13 @@ def test_status_strings(libpath):
     assert rvq.rvq_status_string(0) == "ok"
     assert rvq.rvq_status_string(-2) == "unsupported shape"
     assert "gfx950" in rvq.rvq_version()
+
+
+def test_prepared_bytes_shape_rules(libpath):
+    import residual_vector_quantization_amd as rvq
+    a = rvq.rvq_prepared_bytes(8, 1024, 64)
+    assert a > 8 * 1024 * 256 and a % 256 == 0
+    assert rvq.rvq_prepared_bytes(8, 1000, 64) == a   # rows are padded to whole chunks
+    assert rvq.rvq_prepared_bytes(1, 1, 64) > 0
+    with pytest.raises(rvq.RVQError):
+        rvq.rvq_prepared_bytes(8, 1024, 32)
