@@ -2,9 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
 
-One step = ``rvq_encode`` (codes + final residual, default split-bf16
-scoring) followed by ``rvq_decode`` (codes -> reconstruction) over the whole
-batch, inputs and outputs resident in HBM. W untimed steps, then K timed
+One step = ``rvq_prepare_codebooks`` (codebooks split into bf16 halves with
+their half-norms), ``rvq_encode_prepared`` (codes + final residual, split-bf16
+scoring) and ``rvq_decode`` (codes -> reconstruction) over the whole batch,
+inputs and outputs resident in HBM. W untimed steps, then K timed
 steps between ``torch.cuda.synchronize()`` calls. Per-launch kernel times
 come from HIP events recorded on the stream the kernels run on (torch's
 current stream, which is the stream handed to the C ABI).
@@ -40,12 +41,16 @@ PEAK_BF16_MFMA_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 N_XCD, N_SIMD = 8, 1024            # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 COPY_BYTES = 512 << 20             # size of the counter-calibration copy
+# Rate of random 256 B codebook-row gathers out of L2 / MALL that the decode
+# reaches at best over codebook sizes from 0.25 to 16 MiB (--gather-sweep);
+# the decode's row gathers are bound by it, not by HBM.
+GATHER_CEILING_TBPS = 21.9
 
 CSRC = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc")
 # kernel kind -> sources whose text defines it (hashed to detect stale counters)
 KERNEL_SOURCES = {
     "encode_bf16": ["encode_bf16.hip", "encode_common.h"],
-    "encode_fp32": ["encode.hip"],
+    "encode_fp32": ["encode.hip", "encode_common.h"],
     "decode": ["decode.hip"],
 }
 
@@ -63,6 +68,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain elementwise copy of 512 MiB (for HBM counter scaling)")
+    p.add_argument("--gather-sweep", metavar="OUT_MD",
+                   help="time rvq_decode at Q=32, N=720000 over codebook sizes 0.25..16 MiB, write a "
+                        "summary of the row-gather rates to OUT_MD, then exit")
     p.add_argument("--summarize-profiles", metavar="DIR",
                    help="turn rocprofv3 CSV output under DIR (trace/, fetch/, write/, mfma/) into the "
                         "summaries under profiles/, then exit")
@@ -111,11 +119,17 @@ def _csv(dirname, suffix):
 
 def _kernel_of(name):
     if "encode_bf16_kernel" in name:
-        return "encode_bf16"
+        # template arguments <recon, residual, prepared>: the timed step runs the prepared one
+        prepared = name.split("encode_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")[-1].strip()
+        return "encode_bf16" if prepared == "true" else "encode_bf16_onthefly"
     if "encode_kernel" in name:
         return "encode_fp32"
-    if "decode_kernel" in name:
+    if "decode_kernel" in name or "decode_tiled_kernel" in name:
         return "decode"
+    if "prepare_rows_kernel" in name:
+        return "prepare_rows"
+    if "prepare_max_kernel" in name:
+        return "prepare_max"
     if "elementwise" in name and "MulFunctor" in name:
         return "copy"
     return None
@@ -159,7 +173,8 @@ def summarize_profiles(w, src_dir):
     lines.append("")
     if "encode_bf16" in avg:
         t = avg["encode_bf16"]
-        lines.append(f"- encode_bf16: {3 * enc_flop:.4g} bf16 matrix flop per launch (3 x 2QKD per frame) / "
+        lines.append(f"- encode_bf16 (prepared codebooks): {3 * enc_flop:.4g} bf16 matrix flop per launch "
+                     f"(3 x 2QKD per frame) / "
                      f"{t:.1f} us = {3 * enc_flop / t / 1e6:.1f} TFLOP/s "
                      f"({3 * enc_flop / t / 1e6 / PEAK_BF16_MFMA_TFLOPS:.1%} of {PEAK_BF16_MFMA_TFLOPS:.0f} bf16); "
                      f"fp32-equivalent {enc_flop / t / 1e6:.1f} TFLOP/s "
@@ -180,7 +195,11 @@ def summarize_profiles(w, src_dir):
     f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
     w_scale = COPY_BYTES / (write["copy"] * 1024.0)
     enc_algo = (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d
-    algo = {"encode_bf16": enc_algo, "encode_fp32": enc_algo, "decode": dec_bytes + 4.0 * q * k * d}
+    # the prepared encode reads the split-bf16 codebook rows (256 B), norms and stage maxima instead
+    kp = -(-k // 128) * 128
+    prep_bytes = q * (-(-(kp * 260 + 4) // 256) * 256)
+    algo = {"encode_bf16": enc_algo - 4.0 * q * k * d + prep_bytes, "encode_fp32": enc_algo,
+            "decode": dec_bytes + 4.0 * q * k * d}
     lines += ["", "## HBM counters (per launch)", "",
               f"A 512 MiB elementwise copy reads FETCH_SIZE = {fetch['copy']:.0f} KiB and WRITE_SIZE = "
               f"{write['copy']:.0f} KiB, so readings are scaled by {f_scale:.3f} (fetch) and "
@@ -222,6 +241,51 @@ def summarize_profiles(w, src_dir):
     path = os.path.join(out_dir, f"encode_decode_{w.name}_rocprof.md")
     open(path, "w").write("\n".join(lines) + "\n")
     print("wrote", path)
+
+
+# ------------------------------------------------------------ gather sweep
+
+def gather_sweep(out_md):
+    """Decode time vs codebook footprint at a fixed number of row gathers (Q=32 x 720000 frames)."""
+    import torch
+    import residual_vector_quantization_amd as rvq
+    dev = torch.device("cuda:0")
+    n, q = 720000, 32
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rows = []
+    for k in (32, 128, 256, 512, 1024, 2048):
+        books = torch.from_numpy(W.codebooks(q, k, 64, 0.85, 1)).to(dev)
+        codes = torch.from_numpy(W.random_codes(n, q, k, seed=3)).to(dev)
+        out = torch.empty((n, 64), dtype=torch.float32, device=dev)
+        ts = []
+        for rep in range(10):
+            torch.cuda.synchronize()
+            ev[0].record()
+            rvq.rvq_decode(codes, books, out=out)
+            ev[1].record()
+            torch.cuda.synchronize()
+            if rep >= 2:
+                ts.append(ev[0].elapsed_time(ev[1]))
+        ms = float(np.median(ts))
+        kernel = "decode_tiled_kernel" if q * k * 256 >= 4 << 20 else "decode_kernel"
+        rec = {"K": k, "codebook_MiB": q * k * 256 / 2 ** 20, "kernel": kernel, "ms": ms,
+               "gather_TBps": n * q * 256 / (ms * 1e-3) / 1e12,
+               "hbm_GBps": (4.0 * q + 256.0) * n / (ms * 1e-3) / 1e9}
+        print(json.dumps(rec), flush=True)
+        rows.append(rec)
+    lines = ["# Decode row-gather rate vs codebook size", "",
+             "Q = 32 stages, N = 720000 frames, D = 64, uniform random codes (seed 3); every frame "
+             "gathers Q rows of 256 B, so each launch moves 5.9 GB of codebook rows out of L2 / MALL "
+             "and 0.28 GB to and from HBM (codes in, reconstruction out). Median of 8 timed launches "
+             "(HIP events).", "",
+             "Command: `python3 bench.py --gather-sweep gpurun_out/decode_gather_sweep.md`", "",
+             "| K | codebook MiB | kernel | ms | row gathers TB/s | HBM GB/s |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['K']} | {r['codebook_MiB']:.2f} | {r['kernel']} | {r['ms']:.3f} | "
+                     f"{r['gather_TBps']:.1f} | {r['hbm_GBps']:.0f} |")
+    lines += ["", f"Best row-gather rate: {max(r['gather_TBps'] for r in rows):.1f} TB/s."]
+    os.makedirs(os.path.dirname(os.path.abspath(out_md)), exist_ok=True)
+    open(out_md, "w").write("\n".join(lines) + "\n")
 
 
 # ------------------------------------------------------------ CPU baseline
@@ -303,6 +367,9 @@ def main():
     if args.summarize_profiles:
         summarize_profiles(W.WORKLOADS[args.workload], args.summarize_profiles)
         return
+    if args.gather_sweep:
+        gather_sweep(args.gather_sweep)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(frames shard with no exchange, so N GPUs would each run this same kernel on N/G frames)",
@@ -326,29 +393,37 @@ def main():
     out = torch.empty_like(xg)
     torch.cuda.synchronize()
 
+    prepared = torch.empty(rvq.rvq_prepared_bytes(w.n_stages, w.n_codes, w.dim), dtype=torch.uint8,
+                           device=dev)
+
     def step(ev=None):
+        # codebook split into bf16 halves (every step), encode from it, decode the codes
         if ev is not None:
             ev[0].record()
-        rvq.rvq_encode(xg, bg, codes=codes, residual_out=residual)
+        rvq.rvq_prepare_codebooks(bg, prepared)
         if ev is not None:
             ev[1].record()
-        rvq.rvq_decode(codes, bg, out=out)
+        rvq.rvq_encode_prepared(xg, bg, prepared, out=(codes, None, residual))
         if ev is not None:
             ev[2].record()
+        rvq.rvq_decode(codes, bg, out=out)
+        if ev is not None:
+            ev[3].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    dec_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    enc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
     codes_h = codes.cpu().numpy()
 
     # the same encode with fp32 matrix-core scores (identical results), timed separately
@@ -367,6 +442,10 @@ def main():
         fp32_ms = ev[0].elapsed_time(ev[1]) / args.fp32_steps
         if not torch.equal(c32, codes):
             raise SystemExit("fp32 and split-bf16 scorings disagree")
+        rvq.rvq_encode(xg, bg, codes=c32, residual_out=r32)
+        torch.cuda.synchronize()
+        if not torch.equal(c32, codes):
+            raise SystemExit("rvq_encode and rvq_encode_prepared disagree")
 
     if args.calibrate_copy:
         a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
@@ -382,6 +461,8 @@ def main():
     bf16_tflops = 3 * enc_flop / (enc_ms * 1e-3) / 1e12
     dec_bytes = (4.0 * q + 4.0 * d) * n
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
+    gather_tbps = 4.0 * d * q * n / (dec_ms * 1e-3) / 1e12
+    dec_kernel = "decode_tiled_kernel" if 4 * q * k * d >= 4 << 20 else "decode_kernel"
     rec = {
         "metric": METRIC,
         "value": value,
@@ -398,19 +479,25 @@ def main():
         "config": {"workload": w.name, "frames": n, "Q": q, "K": k, "D": d, "scoring": "split-bf16",
                    "recipe": w.description},
         "audio_seconds_per_s": value / w.frame_rate_hz,
+        "prepare_ms": prep_ms,
         "encode_ms": enc_ms,
         "decode_ms": dec_ms,
-        "roofline": {"bound": "mfma", "kernel": "encode_bf16_kernel (v_mfma_f32_32x32x16_bf16, 3 split products)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "encode_bf16_kernel, prepared codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)",
                      "achieved": bf16_tflops, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": bf16_tflops / PEAK_BF16_MFMA_TFLOPS,
                      "traffic": recorded_traffic("encode_bf16", w.name),
                      "work_per_launch": f"3*2*Q*K*D*N = {3 * enc_flop:.4g} bf16 flop"},
         "encode_fp32_equivalent": {"achieved": enc_flop / (enc_ms * 1e-3) / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
                                    "unit": "TFLOP/s", "work_per_launch": f"2*Q*K*D*N = {enc_flop:.4g} flop"},
-        "decode_roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": dec_gbps,
+        "decode_roofline": {"bound": "hbm", "kernel": dec_kernel, "achieved": dec_gbps,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
                             "traffic": recorded_traffic("decode", w.name),
-                            "work_per_launch": f"(4Q+4D)*N = {dec_bytes:.4g} B"},
+                            "work_per_launch": f"(4Q+4D)*N = {dec_bytes:.4g} B",
+                            "row_gathers": {"achieved": gather_tbps, "ceiling": GATHER_CEILING_TBPS,
+                                            "unit": "TB/s", "frac": gather_tbps / GATHER_CEILING_TBPS,
+                                            "work_per_launch": f"4*D*Q*N = {4.0 * d * q * n:.4g} B "
+                                                               "of codebook rows from L2 / MALL"}},
     }
     if fp32_ms is not None:
         t32 = enc_flop / (fp32_ms * 1e-3) / 1e12

@@ -17,6 +17,8 @@ constexpr int kEncodeThreads = 256;
 // Decode: 16 lanes per frame (one float4 each), 256 threads per workgroup.
 constexpr int kDecodeLanesPerFrame = 16;
 constexpr int kDecodeThreads = 256;
+// Codebooks from this size on (one XCD's L2) take the stage-ordered decode.
+constexpr int64_t kDecodeTiledMinBookBytes = int64_t(4) << 20;
 
 // Linear layers: frames per workgroup (4 wavefronts x 32 frames).
 constexpr int kLinearFramesPerBlock = 128;

@@ -56,6 +56,25 @@ def test_decode_partial_depth_and_leading_dim():
     np.testing.assert_array_equal(out, oracle.get().decode(np.ascontiguousarray(codes[:, :3]), books[:3]))
 
 
+# Codebooks of 4 MiB and more take the stage-ordered kernel: wavefront tiles
+# of 32 frames, codes staged 32 stages at a time. Cases cross both.
+@pytest.mark.parametrize("n,q,k,ld", [(1, 16, 1024, 16), (31, 33, 1024, 33), (129, 40, 512, 41),
+                                      (4099, 64, 256, 64), (700, 8, 4096, 12)])
+def test_decode_large_codebook(n, q, k, ld):
+    rng = np.random.default_rng(n * 7 + q)
+    books = rng.standard_normal((q, k, 64)).astype(np.float32)
+    codes = np.full((n, ld), -5, np.int32)   # columns past q are never read
+    codes[:, :q] = W.random_codes(n, q, k, seed=n + 1)
+    bad = sorted({0, n // 2, n - 1})
+    for j, f in enumerate(bad):
+        codes[f, (q - 1) if j == 0 else (j * 13) % q] = k if j % 2 == 0 else -1
+    announce("decode large codebook", n=n, q=q, k=k, ld=ld)
+    out = host(rvq().rvq_decode(to_dev(codes), to_dev(books), n_stages=q))
+    assert np.isnan(out[bad]).all()
+    good = np.setdiff1d(np.arange(n), bad)
+    np.testing.assert_array_equal(out[good], oracle.get().decode(np.ascontiguousarray(codes[good, :q]), books))
+
+
 @pytest.mark.parametrize("name", ["batched", "deep"])
 def test_full_size_decode_sampled(name):
     w = W.WORKLOADS[name]
