@@ -70,7 +70,7 @@ class Workload:
         return self.hidden > 0
 
 
-# The five workloads. Sizes and recipes as the codec shapes dictate; the
+# The six workloads. Sizes and recipes as the codec shapes dictate; the
 # description strings state them for result lines.
 WORKLOADS = {
     "tiny": Workload(
@@ -90,6 +90,11 @@ WORKLOADS = {
         "deep", 720_000, 32, 1024, 64, 0.85, 720_000, 0.0, 12.5,
         description="16 clips x 45000 frames (1 h at 12.5 Hz) = 720000 frames ~ N(0,1); "
                     "C[q] ~ N(0,1)*0.85^q, Q=32, K=1024, D=64; seed 0"),
+    "large": Workload(
+        "large", 192_000, 10, 4096, 64, 0.5, 192_000, 0.0, 44100.0 / 2048.0,
+        description="96 clips x 2000 frames = 192000 frames (44.1 kHz, 2048 samples per frame) "
+                    "~ N(0,1); C[q] ~ N(0,1)*0.5^q, Q=10, K=4096, D=64 (codebook dim assumed); "
+                    "seed 0"),
     "projected": Workload(
         "projected", 1_000_000, 8, 1024, 64, 0.5, 1_000_000, 0.0, 25.0, hidden=1024,
         description="1e6 hidden vectors [1e6,1024] ~ N(0,1); fc 1024->64 W ~ N(0, var 1/1024), "

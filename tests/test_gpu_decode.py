@@ -75,7 +75,7 @@ def test_decode_large_codebook(n, q, k, ld):
     np.testing.assert_array_equal(out[good], oracle.get().decode(np.ascontiguousarray(codes[good, :q]), books))
 
 
-@pytest.mark.parametrize("name", ["batched", "deep"])
+@pytest.mark.parametrize("name", ["batched", "deep", "large"])
 def test_full_size_decode_sampled(name):
     w = W.WORKLOADS[name]
     books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)

@@ -148,7 +148,7 @@ def test_empty_batch_is_noop():
     assert out.shape == (0, 64)
 
 
-@pytest.mark.parametrize("name,count", [("batched", 4096), ("deep", 2048)])
+@pytest.mark.parametrize("name,count", [("batched", 4096), ("deep", 2048), ("large", 2048)])
 @pytest.mark.parametrize("scoring", SCORINGS)
 def test_full_size_workloads_sampled(name, count, scoring):
     """Full-size batches in the benchmark's launch configuration; oracle on a seeded sample."""
@@ -178,7 +178,7 @@ def test_argument_errors():
                         torch.zeros((2, 64, 64), device="cuda:0"))[0].shape == (10, 2)
 
 
-@pytest.mark.parametrize("name", ["batched", "deep"])
+@pytest.mark.parametrize("name", ["batched", "deep", "large"])
 def test_scorings_agree_at_full_size(name):
     """Split-bf16 and fp32 scoring give identical codes, residuals and reconstructions."""
     w = W.WORKLOADS[name]
