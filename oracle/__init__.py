@@ -65,6 +65,16 @@ class Oracle:
         lib.oracle_linear.argtypes = [
             _F32P, ctypes.c_int64, ctypes.c_int32, _F32P, ctypes.c_void_p, ctypes.c_int32,
             _F32P, ctypes.c_int]
+        lib.oracle_projected_encode.restype = ctypes.c_int
+        lib.oracle_projected_encode.argtypes = [
+            _F32P, ctypes.c_int64, ctypes.c_int32, _F32P, ctypes.c_void_p, _F32P, ctypes.c_int32,
+            ctypes.c_int32, ctypes.c_int32, _F32P, ctypes.c_void_p, ctypes.c_void_p, _I32P,
+            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int]
+        lib.oracle_projected_decode.restype = ctypes.c_int
+        lib.oracle_projected_decode.argtypes = [
+            _I32P, ctypes.c_int32, ctypes.c_int64, _F32P, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_int32, _F32P, ctypes.c_void_p, ctypes.c_int32, _F32P, ctypes.c_int]
         self.lib = lib
         self.last_threads = 0
 
@@ -124,6 +134,71 @@ class Oracle:
         y = np.empty((n, o), np.float32)
         self.last_threads = self.lib.oracle_linear(h, n, i, w, self._ptr(b), o, y, int(threads))
         return y
+
+    @staticmethod
+    def _projected_shapes(books, w_in, b_in, w_out, b_out, n_stages):
+        books = np.ascontiguousarray(books, dtype=np.float32)
+        qn, k, d = books.shape
+        q = qn if n_stages is None else int(n_stages)
+        assert 0 < q <= qn
+        w_out = np.ascontiguousarray(w_out, dtype=np.float32)
+        assert w_out.shape[0] >= q and w_out.shape[2] == d
+        hidden = w_out.shape[1]
+        if w_in is not None:
+            w_in = np.ascontiguousarray(w_in, dtype=np.float32)
+            assert w_in.shape[0] >= q and w_in.shape[1:] == (d, hidden)
+        if b_in is not None:
+            b_in = np.ascontiguousarray(b_in, dtype=np.float32)
+            assert b_in.shape[0] >= q and b_in.shape[1] == d
+        if b_out is not None:
+            b_out = np.ascontiguousarray(b_out, dtype=np.float32)
+            assert b_out.shape[0] >= q and b_out.shape[1] == hidden
+        return books, w_in, b_in, w_out, b_out, q, k, d, hidden
+
+    def projected_encode(self, h: np.ndarray, w_in: np.ndarray, b_in: Optional[np.ndarray],
+                         books: np.ndarray, w_out: np.ndarray, b_out: Optional[np.ndarray],
+                         n_stages: Optional[int] = None, e_given: Optional[np.ndarray] = None,
+                         threads: int = 0):
+        """Per-stage projected encode (each codebook with its own project_in / project_out).
+
+        ``h`` [N, hidden]; ``w_in`` [Q, D, hidden], ``b_in`` [Q, D] or None;
+        ``books`` [Q, K, D]; ``w_out`` [Q, hidden, D], ``b_out`` [Q, hidden]
+        or None. With ``e_given`` [Q, N, D] the argmin of stage q is taken on
+        ``e_given[q]`` instead of the oracle's own projection. Returns
+        ``(codes [N, Q], e [Q, N, D] (the oracle's own projections),
+        residual [N, hidden], best [N, Q], second [N, Q])``.
+        """
+        books, w_in, b_in, w_out, b_out, q, k, d, hidden = self._projected_shapes(
+            books, w_in, b_in, w_out, b_out, n_stages)
+        h = np.ascontiguousarray(h, dtype=np.float32)
+        n = h.shape[0]
+        assert h.shape[1] == hidden
+        assert np.isfinite(h).all(), "oracle inputs must be finite"
+        if e_given is not None:
+            e_given = np.ascontiguousarray(e_given, dtype=np.float32)
+            assert e_given.shape == (q, n, d)
+        codes = np.zeros((n, q), np.int32)
+        e = np.empty((q, n, d), np.float32)
+        residual = np.empty((n, hidden), np.float32)
+        best = np.empty((n, q), np.float64)
+        second = np.empty((n, q), np.float64)
+        self.last_threads = self.lib.oracle_projected_encode(
+            h, n, hidden, w_in, self._ptr(b_in), books, q, k, d, w_out, self._ptr(b_out),
+            self._ptr(e_given), codes, q, self._ptr(e), self._ptr(residual), self._ptr(best),
+            self._ptr(second), int(threads))
+        return codes, e, residual, best, second
+
+    def projected_decode(self, codes: np.ndarray, books: np.ndarray, w_out: np.ndarray,
+                         b_out: Optional[np.ndarray], threads: int = 0) -> np.ndarray:
+        """Sum over stages of W_out[q] C[q, code] + b_out[q]: [N, Q] codes -> [N, hidden]."""
+        codes = np.ascontiguousarray(codes, dtype=np.int32)
+        n, q = codes.shape
+        books, _, _, w_out, b_out, q, k, d, hidden = self._projected_shapes(
+            books, None, None, w_out, b_out, q)
+        out = np.empty((n, hidden), np.float32)
+        self.last_threads = self.lib.oracle_projected_decode(
+            codes, q, n, books, q, k, d, w_out, self._ptr(b_out), hidden, out, int(threads))
+        return out
 
     def roundtrip(self, x: np.ndarray, books: np.ndarray, threads: int = 0):
         """Encode then decode: returns ``(codes, recon, residual, best, second)``."""

@@ -19,13 +19,19 @@
  *   - Linear: y = W h + b with W in PyTorch (out, in) order, used for the
  *     fc 1024->64 prologue and fc2 64->1024 epilogue of the projected
  *     workload.
+ *   - Per-stage projected encode and decode: the same section's loop with
+ *     each codebook's own project_in (hidden -> dim, with bias) before the
+ *     argmin and project_out (dim -> hidden, with bias) applied to the
+ *     picked codeword before it is subtracted from the hidden-width
+ *     residual; decode sums the projected codewords, stage 0 first.
  *
  * Precision (the pages fix only that the codec is kept in F32):
  *   - distances: float64, direct form sum_j (r_j - c_j)^2, j ascending,
  *     one rounding per operation (built with -ffp-contract=off);
  *   - residual: float32, r_j <- fl32(r_j - c_j);
  *   - decode accumulator: float32, stage order ascending;
- *   - linear: float64 sum, i ascending, bias added last, rounded once.
+ *   - linear (and both per-stage projections): float64 sum, i ascending,
+ *     bias added last, rounded once to float32.
  *
  * The best and second-best distances of every stage are reported too, so
  * a caller can classify near-ties (gap <= 1e-5 * best).
@@ -52,6 +58,44 @@ static double sq_dist(const float *r, const float *c, int32_t dim)
     return s;
 }
 
+/* Index of the codeword of `book` [n_codes, dim] nearest to v, the lowest
+ * index on ties (strict "<" while k ascends); *best and *second receive the
+ * smallest and second-smallest distance. */
+static int32_t nearest(const float *v, const float *book, int32_t n_codes, int32_t dim,
+                       double *best, double *second)
+{
+    int32_t k1 = 0;
+    double d1 = sq_dist(v, book, dim);
+    double d2 = INFINITY;
+    for (int32_t k = 1; k < n_codes; ++k) {
+        double dk = sq_dist(v, book + (int64_t)k * dim, dim);
+        if (dk < d1) {
+            d2 = d1;
+            d1 = dk;
+            k1 = k;
+        } else if (dk < d2) {
+            d2 = dk;
+        }
+    }
+    *best = d1;
+    *second = d2;
+    return k1;
+}
+
+/* y = W v + b for one vector: W [out_dim, in_dim] row-major, b nullable;
+ * float64 sum over i ascending, bias added last, rounded once. */
+static void linear_row(const float *w, const float *b, const float *v,
+                       int32_t in_dim, int32_t out_dim, float *y)
+{
+    for (int32_t o = 0; o < out_dim; ++o) {
+        const float *wo = w + (int64_t)o * in_dim;
+        double s = 0.0;
+        for (int32_t i = 0; i < in_dim; ++i) s = s + (double)v[i] * (double)wo[i];
+        if (b) s = s + (double)b[o];
+        y[o] = (float)s;
+    }
+}
+
 typedef struct {
     const float *x;
     const float *books;
@@ -71,19 +115,8 @@ static void encode_frames(const encode_job *jb)
         memcpy(r, jb->x + n * jb->dim, sizeof(float) * (size_t)jb->dim);
         for (int32_t q = 0; q < jb->n_stages; ++q) {
             const float *book = jb->books + (int64_t)q * jb->n_codes * jb->dim;
-            int32_t k1 = 0;
-            double d1 = sq_dist(r, book, jb->dim);
-            double d2 = INFINITY;
-            for (int32_t k = 1; k < jb->n_codes; ++k) {
-                double dk = sq_dist(r, book + (int64_t)k * jb->dim, jb->dim);
-                if (dk < d1) {
-                    d2 = d1;
-                    d1 = dk;
-                    k1 = k;
-                } else if (dk < d2) {
-                    d2 = dk;
-                }
-            }
+            double d1, d2;
+            int32_t k1 = nearest(r, book, jb->n_codes, jb->dim, &d1, &d2);
             jb->codes[n * jb->codes_ld + q] = k1;
             if (jb->best) jb->best[n * jb->n_stages + q] = d1;
             if (jb->second) jb->second[n * jb->n_stages + q] = d2;
@@ -132,21 +165,103 @@ typedef struct {
 
 static void linear_rows(const linear_job *jb)
 {
+    for (int64_t n = jb->begin; n < jb->end; ++n)
+        linear_row(jb->w, jb->b, jb->h + n * jb->in_dim, jb->in_dim, jb->out_dim,
+                   jb->y + n * jb->out_dim);
+}
+
+typedef struct {
+    const float *h;
+    int32_t hidden, dim, n_stages, n_codes;
+    const float *w_in, *b_in;    /* [Q, dim, hidden], [Q, dim] (nullable) */
+    const float *books;          /* [Q, K, dim] */
+    const float *w_out, *b_out;  /* [Q, hidden, dim], [Q, hidden] (nullable) */
+    const float *e_given;        /* nullable [Q, N, dim] */
+    int32_t *codes;
+    int32_t codes_ld;
+    float *e_out;                /* nullable [Q, N, dim] */
+    float *residual;             /* nullable [N, hidden] */
+    double *best, *second;       /* nullable [N, Q] */
+    int64_t n_frames;
+    int64_t begin, end;
+} projected_job;
+
+/* Per-stage projected encode of frames [begin, end). For each stage q the
+ * projection e = W_in[q] r + b_in[q] is computed; the argmin is taken on it,
+ * or on e_given[q, n] when e_given is set (the residual chain then follows
+ * those picks); the picked codeword is projected back with W_out[q] and
+ * b_out[q] and subtracted from the hidden-width residual in float32. */
+static void projected_frames(const projected_job *jb)
+{
+    const int32_t hid = jb->hidden, dim = jb->dim;
+    float *r = (float *)malloc(sizeof(float) * (size_t)hid);
+    float *p = (float *)malloc(sizeof(float) * (size_t)hid);
+    float *e = (float *)malloc(sizeof(float) * (size_t)dim);
     for (int64_t n = jb->begin; n < jb->end; ++n) {
-        const float *hn = jb->h + n * jb->in_dim;
-        for (int32_t o = 0; o < jb->out_dim; ++o) {
-            const float *wo = jb->w + (int64_t)o * jb->in_dim;
-            double s = 0.0;
-            for (int32_t i = 0; i < jb->in_dim; ++i) s = s + (double)hn[i] * (double)wo[i];
-            if (jb->b) s = s + (double)jb->b[o];
-            jb->y[n * jb->out_dim + o] = (float)s;
+        memcpy(r, jb->h + n * hid, sizeof(float) * (size_t)hid);
+        for (int32_t q = 0; q < jb->n_stages; ++q) {
+            const float *b_in = jb->b_in ? jb->b_in + (int64_t)q * dim : NULL;
+            linear_row(jb->w_in + (int64_t)q * dim * hid, b_in, r, hid, dim, e);
+            const int64_t at = ((int64_t)q * jb->n_frames + n) * dim;
+            if (jb->e_out) memcpy(jb->e_out + at, e, sizeof(float) * (size_t)dim);
+            const float *pick_on = jb->e_given ? jb->e_given + at : e;
+            const float *stage_book = jb->books + (int64_t)q * jb->n_codes * dim;
+            double d1, d2;
+            int32_t k1 = nearest(pick_on, stage_book, jb->n_codes, dim, &d1, &d2);
+            const int64_t nq = n * jb->n_stages + q;
+            jb->codes[n * jb->codes_ld + q] = k1;
+            if (jb->best) jb->best[nq] = d1;
+            if (jb->second) jb->second[nq] = d2;
+            const float *b_out = jb->b_out ? jb->b_out + (int64_t)q * hid : NULL;
+            linear_row(jb->w_out + (int64_t)q * hid * dim, b_out, stage_book + (int64_t)k1 * dim, dim, hid, p);
+            for (int32_t i = 0; i < hid; ++i) r[i] = (float)(r[i] - p[i]);
+        }
+        if (jb->residual) memcpy(jb->residual + n * hid, r, sizeof(float) * (size_t)hid);
+    }
+    free(e);
+    free(p);
+    free(r);
+}
+
+typedef struct {
+    const int32_t *codes;
+    int32_t codes_ld;
+    const float *books;          /* [Q, K, dim] */
+    const float *w_out, *b_out;  /* [Q, hidden, dim], [Q, hidden] (nullable) */
+    int32_t n_stages, n_codes, dim, hidden;
+    float *out;                  /* [N, hidden] */
+    int64_t begin, end;
+} projected_decode_job;
+
+/* out[n] = sum_q (W_out[q] C[q, codes[n, q]] + b_out[q]): each stage's
+ * projected codeword rounded to float32, then added to a float32
+ * accumulator that starts at +0, stage 0 first. A code outside [0, K)
+ * gives a NaN frame. */
+static void projected_decode_frames(const projected_decode_job *jb)
+{
+    const int32_t hid = jb->hidden, dim = jb->dim;
+    float *p = (float *)malloc(sizeof(float) * (size_t)hid);
+    for (int64_t n = jb->begin; n < jb->end; ++n) {
+        float *acc = jb->out + n * hid;
+        for (int32_t i = 0; i < hid; ++i) acc[i] = 0.0f;
+        for (int32_t q = 0; q < jb->n_stages; ++q) {
+            int32_t code = jb->codes[n * jb->codes_ld + q];
+            if (code < 0 || code >= jb->n_codes) {
+                for (int32_t i = 0; i < hid; ++i) acc[i] = NAN;
+                break;
+            }
+            const float *b_out = jb->b_out ? jb->b_out + (int64_t)q * hid : NULL;
+            linear_row(jb->w_out + (int64_t)q * hid * dim, b_out,
+                       jb->books + ((int64_t)q * jb->n_codes + code) * dim, dim, hid, p);
+            for (int32_t i = 0; i < hid; ++i) acc[i] = (float)(acc[i] + p[i]);
         }
     }
+    free(p);
 }
 
 /* ---- threading: contiguous frame ranges, one pthread each ------------- */
 
-enum { JOB_ENCODE, JOB_DECODE, JOB_LINEAR };
+enum { JOB_ENCODE, JOB_DECODE, JOB_LINEAR, JOB_PROJECTED, JOB_PROJECTED_DECODE };
 
 typedef struct {
     int kind;
@@ -154,6 +269,8 @@ typedef struct {
         encode_job e;
         decode_job d;
         linear_job l;
+        projected_job p;
+        projected_decode_job pd;
     } u;
 } any_job;
 
@@ -162,7 +279,9 @@ static void *run_job(void *p)
     any_job *j = (any_job *)p;
     if (j->kind == JOB_ENCODE) encode_frames(&j->u.e);
     else if (j->kind == JOB_DECODE) decode_frames(&j->u.d);
-    else linear_rows(&j->u.l);
+    else if (j->kind == JOB_LINEAR) linear_rows(&j->u.l);
+    else if (j->kind == JOB_PROJECTED) projected_frames(&j->u.p);
+    else projected_decode_frames(&j->u.pd);
     return NULL;
 }
 
@@ -194,7 +313,9 @@ static int run_parallel(any_job proto, int64_t n, int t)
         jobs[i] = proto;
         if (proto.kind == JOB_ENCODE) { jobs[i].u.e.begin = b; jobs[i].u.e.end = e; }
         else if (proto.kind == JOB_DECODE) { jobs[i].u.d.begin = b; jobs[i].u.d.end = e; }
-        else { jobs[i].u.l.begin = b; jobs[i].u.l.end = e; }
+        else if (proto.kind == JOB_LINEAR) { jobs[i].u.l.begin = b; jobs[i].u.l.end = e; }
+        else if (proto.kind == JOB_PROJECTED) { jobs[i].u.p.begin = b; jobs[i].u.p.end = e; }
+        else { jobs[i].u.pd.begin = b; jobs[i].u.pd.end = e; }
         started[i] = (t > 1) && pthread_create(&tids[i], NULL, run_job, &jobs[i]) == 0;
         if (!started[i]) run_job(&jobs[i]);
     }
@@ -248,4 +369,44 @@ int oracle_linear(const float *h, int64_t n_rows, int32_t in_dim,
     p.u.l.h = h; p.u.l.in_dim = in_dim; p.u.l.out_dim = out_dim;
     p.u.l.w = w; p.u.l.b = b; p.u.l.y = y;
     return run_parallel(p, n_rows, pick_threads(threads, n_rows));
+}
+
+/* Per-stage projected encode of frames [0, n_frames); see projected_frames.
+ * e_given, e_out, residual, best and second are nullable. */
+int oracle_projected_encode(const float *h, int64_t n_frames, int32_t hidden,
+                            const float *w_in, const float *b_in,
+                            const float *books, int32_t n_stages, int32_t n_codes, int32_t dim,
+                            const float *w_out, const float *b_out, const float *e_given,
+                            int32_t *codes, int32_t codes_ld, float *e_out, float *residual,
+                            double *best, double *second, int threads)
+{
+    if (n_frames <= 0) return 0;
+    any_job p;
+    memset(&p, 0, sizeof p);
+    p.kind = JOB_PROJECTED;
+    p.u.p.h = h; p.u.p.hidden = hidden; p.u.p.dim = dim;
+    p.u.p.n_stages = n_stages; p.u.p.n_codes = n_codes;
+    p.u.p.w_in = w_in; p.u.p.b_in = b_in; p.u.p.books = books;
+    p.u.p.w_out = w_out; p.u.p.b_out = b_out; p.u.p.e_given = e_given;
+    p.u.p.codes = codes; p.u.p.codes_ld = codes_ld; p.u.p.e_out = e_out;
+    p.u.p.residual = residual; p.u.p.best = best; p.u.p.second = second;
+    p.u.p.n_frames = n_frames;
+    return run_parallel(p, n_frames, pick_threads(threads, n_frames));
+}
+
+/* Per-stage projected decode of frames [0, n_frames) into out [N, hidden]. */
+int oracle_projected_decode(const int32_t *codes, int32_t codes_ld, int64_t n_frames,
+                            const float *books, int32_t n_stages, int32_t n_codes, int32_t dim,
+                            const float *w_out, const float *b_out, int32_t hidden,
+                            float *out, int threads)
+{
+    if (n_frames <= 0) return 0;
+    any_job p;
+    memset(&p, 0, sizeof p);
+    p.kind = JOB_PROJECTED_DECODE;
+    p.u.pd.codes = codes; p.u.pd.codes_ld = codes_ld; p.u.pd.books = books;
+    p.u.pd.w_out = w_out; p.u.pd.b_out = b_out;
+    p.u.pd.n_stages = n_stages; p.u.pd.n_codes = n_codes; p.u.pd.dim = dim; p.u.pd.hidden = hidden;
+    p.u.pd.out = out;
+    return run_parallel(p, n_frames, pick_threads(threads, n_frames));
 }

@@ -24,7 +24,14 @@ What pins what:
   recon + residual == x exactly);
 * invariants: prefix consistency, frame permutation, decode of one stage is
   a row gather, out-of-range codes give a NaN frame;
-* linear layer against numpy's float64 matmul.
+* linear layer against numpy's float64 matmul;
+* per-stage projected encode / decode: a hand-worked 2-stage case with a
+  three-way tie (tests/golden/projected_handworked.txt); identity
+  projections reduce it to the plain encode / decode; small-integer data
+  against an exact integer re-derivation with numpy (argmin first
+  occurrence); the argmin follows given encodings (checked with cdist);
+  prefix consistency; the float32, stage-0-first decode order; NaN frames
+  for bad codes.
 """
 
 import numpy as np
@@ -199,6 +206,128 @@ def pin_linear(o):
     np.testing.assert_array_equal(o.linear(hi, wi), hi @ wi.T)
 
 
+def _projected_case(name):
+    p, frames = golden_io.read_projected(name)
+    h = np.array([f["h"] for f in frames], np.float32)
+    return p, frames, h
+
+
+def pin_projected_handworked(o):
+    p, frames, h = _projected_case("projected_handworked.txt")
+    q, _, d = p["books"].shape
+    codes, e, residual, best, second = o.projected_encode(h, p["w_in"], p["b_in"], p["books"],
+                                                          p["w_out"], p["b_out"])
+    np.testing.assert_array_equal(codes, np.array([f["codes"] for f in frames], np.int32))
+    np.testing.assert_array_equal(e.transpose(1, 0, 2).reshape(len(frames), q * d),
+                                  np.array([f["e"] for f in frames], np.float32))
+    np.testing.assert_array_equal(best, np.array([f["best"] for f in frames]))
+    np.testing.assert_array_equal(second, np.array([f["second"] for f in frames]))
+    np.testing.assert_array_equal(residual, np.array([f["residual"] for f in frames], np.float32))
+    recon = o.projected_decode(codes, p["books"], p["w_out"], p["b_out"])
+    np.testing.assert_array_equal(recon, np.array([f["recon"] for f in frames], np.float32))
+
+
+def pin_projected_identity_is_plain_rvq(o):
+    rng = np.random.default_rng(21)
+    q, k, d, n = 4, 96, 16, 150
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    books = _random_books(rng, q, k, d)
+    eye = np.broadcast_to(np.eye(d, dtype=np.float32), (q, d, d))
+    zeros_in, zeros_out = np.zeros((q, d), np.float32), np.zeros((q, d), np.float32)
+    codes, e, residual, best, second = o.projected_encode(x, eye, zeros_in, books, eye, zeros_out)
+    c0, r0, b0, s0 = o.encode(x, books)
+    np.testing.assert_array_equal(codes, c0)
+    np.testing.assert_array_equal(residual, r0)
+    np.testing.assert_array_equal(best, b0)
+    np.testing.assert_array_equal(second, s0)
+    np.testing.assert_array_equal(e[0], x)
+    for s in range(1, q):
+        _, rs, _, _ = o.encode(x, books, n_stages=s)
+        np.testing.assert_array_equal(e[s], rs)
+    np.testing.assert_array_equal(o.projected_decode(codes, books, eye, None), o.decode(codes, books))
+
+
+def pin_projected_integer_exact(o):
+    rng = np.random.default_rng(22)
+    q, k, d, hid, n = 3, 12, 3, 7, 400
+    books = rng.integers(-3, 4, size=(q, k, d)).astype(np.float32)
+    books[:, 9:12] = books[:, 2:5]          # duplicated rows: lower copy must win
+    w_in = rng.integers(-2, 3, size=(q, d, hid)).astype(np.float32)
+    b_in = rng.integers(-2, 3, size=(q, d)).astype(np.float32)
+    w_out = rng.integers(-2, 3, size=(q, hid, d)).astype(np.float32)
+    b_out = rng.integers(-2, 3, size=(q, hid)).astype(np.float32)
+    h = rng.integers(-5, 6, size=(n, hid)).astype(np.float32)
+    codes, e, residual, best, second = o.projected_encode(h, w_in, b_in, books, w_out, b_out)
+    r = h.astype(np.int64)
+    recon = np.zeros((n, hid), np.int64)
+    for s in range(q):
+        es = r @ w_in[s].astype(np.int64).T + b_in[s].astype(np.int64)
+        np.testing.assert_array_equal(e[s], es.astype(np.float32))
+        dist = ((es[:, None, :] - books[s].astype(np.int64)[None]) ** 2).sum(axis=2)
+        np.testing.assert_array_equal(codes[:, s], np.argmin(dist, axis=1))
+        np.testing.assert_array_equal(best[:, s], dist.min(axis=1).astype(np.float64))
+        np.testing.assert_array_equal(second[:, s], np.sort(dist, axis=1)[:, 1].astype(np.float64))
+        ps = books[s].astype(np.int64)[codes[:, s]] @ w_out[s].astype(np.int64).T + b_out[s].astype(np.int64)
+        r = r - ps
+        recon = recon + ps
+    np.testing.assert_array_equal(residual, r.astype(np.float32))
+    out = o.projected_decode(codes, books, w_out, b_out)
+    np.testing.assert_array_equal(out, recon.astype(np.float32))
+    np.testing.assert_array_equal(out + residual, h)
+
+
+def pin_projected_follows_given_encodings(o):
+    rng = np.random.default_rng(23)
+    q, k, d, hid, n = 3, 64, 8, 48, 200
+    books = _random_books(rng, q, k, d)
+    w_in = (rng.standard_normal((q, d, hid)) / np.sqrt(hid)).astype(np.float32)
+    w_out = (rng.standard_normal((q, hid, d)) / np.sqrt(d)).astype(np.float32)
+    b_in = (0.1 * rng.standard_normal((q, d))).astype(np.float32)
+    b_out = (0.1 * rng.standard_normal((q, hid))).astype(np.float32)
+    h = rng.standard_normal((n, hid)).astype(np.float32)
+    given = rng.standard_normal((q, n, d)).astype(np.float32)
+    codes, e, residual, best, _ = o.projected_encode(h, w_in, b_in, books, w_out, b_out, e_given=given)
+    r = h.astype(np.float64)
+    for s in range(q):
+        dist = cdist(given[s].astype(np.float64), books[s].astype(np.float64), "sqeuclidean")
+        _check_nn(codes[:, s], dist, f"stage {s}")
+        np.testing.assert_allclose(best[:, s], dist.min(axis=1), rtol=1e-12, atol=0)
+        # the oracle's own projection is taken on the residual that the given picks leave
+        np.testing.assert_allclose(e[s], r @ w_in[s].astype(np.float64).T + b_in[s], rtol=0, atol=1e-5)
+        r = r - (books[s][codes[:, s]].astype(np.float64) @ w_out[s].astype(np.float64).T + b_out[s])
+    np.testing.assert_allclose(residual, r, rtol=0, atol=1e-5)
+    # without given encodings the picks are made on the oracle's own projections
+    c_own, e_own, _, _, _ = o.projected_encode(h, w_in, b_in, books, w_out, b_out)
+    c_again, _, _, _, _ = o.projected_encode(h, w_in, b_in, books, w_out, b_out, e_given=e_own)
+    np.testing.assert_array_equal(c_again, c_own)
+    assert (c_own != codes).any(), "random given encodings should change some picks"
+
+
+def pin_projected_prefix_and_decode(o):
+    rng = np.random.default_rng(24)
+    q, k, d, hid, n = 5, 64, 8, 32, 120
+    books = _random_books(rng, q, k, d)
+    w_in = (rng.standard_normal((q, d, hid)) / np.sqrt(hid)).astype(np.float32)
+    w_out = (rng.standard_normal((q, hid, d)) / np.sqrt(d)).astype(np.float32)
+    h = rng.standard_normal((n, hid)).astype(np.float32)
+    codes, e, _, best, _ = o.projected_encode(h, w_in, None, books, w_out, None)
+    c2, e2, _, b2, _ = o.projected_encode(h, w_in, None, books, w_out, None, n_stages=2)
+    np.testing.assert_array_equal(c2, codes[:, :2])
+    np.testing.assert_array_equal(e2, e[:2])
+    np.testing.assert_array_equal(b2, best[:, :2])
+    # decode: float32 accumulation, stage 0 first (rows 1, 1e8, -1e8 give 0)
+    books3 = np.zeros((3, 1, 1), np.float32)
+    books3[:, 0, 0] = (1.0, 1e8, -1e8)
+    one = np.ones((3, 1, 1), np.float32)
+    out = o.projected_decode(np.zeros((4, 3), np.int32), books3, one, None)
+    assert (out == 0.0).all()
+    bad = codes.copy()
+    bad[3, 1] = k
+    bad[7, 4] = -1
+    out = o.projected_decode(bad, books, w_out, None)
+    assert np.isnan(out[[3, 7]]).all() and np.isfinite(np.delete(out, [3, 7], axis=0)).all()
+
+
 ALL_PINS = [
     pin_handworked,
     pin_decode_order,
@@ -210,4 +339,9 @@ ALL_PINS = [
     pin_prefix_and_permutation,
     pin_decode_gather,
     pin_linear,
+    pin_projected_handworked,
+    pin_projected_identity_is_plain_rvq,
+    pin_projected_integer_exact,
+    pin_projected_follows_given_encodings,
+    pin_projected_prefix_and_decode,
 ]

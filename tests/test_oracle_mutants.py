@@ -29,17 +29,17 @@ MUTANTS = [
     ("distance with a wrong sign",
      "double t = (double)r[j] - (double)c[j];", "double t = (double)r[j] + (double)c[j];"),
     ("transposed codebook row stride",
-     "double dk = sq_dist(r, book + (int64_t)k * jb->dim, jb->dim);",
-     "double dk = sq_dist(r, book + (int64_t)k, jb->dim);"),
+     "double dk = sq_dist(v, book + (int64_t)k * dim, dim);",
+     "double dk = sq_dist(v, book + (int64_t)k, dim);"),
     ("residual subtracts the wrong row",
      "const float *c = book + (int64_t)k1 * jb->dim;", "const float *c = book + (int64_t)k1;"),
     ("second-best not shifted on a new best",
-     "                    d2 = d1;\n", ""),
+     "            d2 = d1;\n", ""),
     ("best and second swapped in the report",
      "if (jb->best) jb->best[n * jb->n_stages + q] = d1;",
      "if (jb->best) jb->best[n * jb->n_stages + q] = d2;"),
     ("first codeword never compared",
-     "double d1 = sq_dist(r, book, jb->dim);", "double d1 = INFINITY;"),
+     "double d1 = sq_dist(v, book, dim);", "double d1 = INFINITY;"),
     ("decode stage order reversed",
      "            int32_t k = jb->codes[n * jb->codes_ld + q];\n"
      "            if (k < 0 || k >= jb->n_codes) {",
@@ -53,13 +53,52 @@ MUTANTS = [
      "                for (int32_t j = 0; j < jb->dim; ++j) o[j] = NAN;\n                break;",
      "                k = 0;"),
     ("linear drops the bias",
-     "if (jb->b) s = s + (double)jb->b[o];", ""),
+     "if (b) s = s + (double)b[o];", ""),
     ("linear uses the transposed weight",
-     "for (int32_t i = 0; i < jb->in_dim; ++i) s = s + (double)hn[i] * (double)wo[i];",
-     "for (int32_t i = 0; i < jb->in_dim; ++i) s = s + (double)hn[i] * (double)jb->w[(int64_t)i * jb->out_dim + o];"),
+     "for (int32_t i = 0; i < in_dim; ++i) s = s + (double)v[i] * (double)wo[i];",
+     "for (int32_t i = 0; i < in_dim; ++i) s = s + (double)v[i] * (double)w[(int64_t)i * out_dim + o];"),
     ("linear accumulates in float32",
-     "double s = 0.0;\n            for (int32_t i = 0; i < jb->in_dim; ++i)",
-     "float s = 0.0f;\n            for (int32_t i = 0; i < jb->in_dim; ++i)"),
+     "double s = 0.0;\n        for (int32_t i = 0; i < in_dim; ++i)",
+     "float s = 0.0f;\n        for (int32_t i = 0; i < in_dim; ++i)"),
+    ("projected: every stage projects with stage 0's W_in",
+     "linear_row(jb->w_in + (int64_t)q * dim * hid, b_in, r, hid, dim, e);",
+     "linear_row(jb->w_in, b_in, r, hid, dim, e);"),
+    ("projected: b_in dropped",
+     "const float *b_in = jb->b_in ? jb->b_in + (int64_t)q * dim : NULL;",
+     "const float *b_in = NULL;"),
+    ("projected: given encodings ignored",
+     "const float *pick_on = jb->e_given ? jb->e_given + at : e;",
+     "const float *pick_on = e;"),
+    ("projected: encodings reported frame-major",
+     "const int64_t at = ((int64_t)q * jb->n_frames + n) * dim;",
+     "const int64_t at = (n * jb->n_stages + q) * dim;"),
+    ("projected: every stage searches codebook 0",
+     "const float *stage_book = jb->books + (int64_t)q * jb->n_codes * dim;",
+     "const float *stage_book = jb->books;"),
+    ("projected: out-projection with stage 0's W_out",
+     "linear_row(jb->w_out + (int64_t)q * hid * dim, b_out, stage_book + (int64_t)k1 * dim, dim, hid, p);",
+     "linear_row(jb->w_out, b_out, stage_book + (int64_t)k1 * dim, dim, hid, p);"),
+    ("projected: out-projection of the wrong codeword row",
+     "linear_row(jb->w_out + (int64_t)q * hid * dim, b_out, stage_book + (int64_t)k1 * dim, dim, hid, p);",
+     "linear_row(jb->w_out + (int64_t)q * hid * dim, b_out, stage_book + (int64_t)k1, dim, hid, p);"),
+    ("projected: residual adds the projected codeword",
+     "for (int32_t i = 0; i < hid; ++i) r[i] = (float)(r[i] - p[i]);",
+     "for (int32_t i = 0; i < hid; ++i) r[i] = (float)(r[i] + p[i]);"),
+    ("projected: b_out dropped in the encode",
+     "const float *b_out = jb->b_out ? jb->b_out + (int64_t)q * hid : NULL;\n            linear_row(jb->w_out + (int64_t)q * hid * dim, b_out, stage_book",
+     "const float *b_out = NULL;\n            linear_row(jb->w_out + (int64_t)q * hid * dim, b_out, stage_book"),
+    ("projected decode: b_out dropped",
+     "const float *b_out = jb->b_out ? jb->b_out + (int64_t)q * hid : NULL;\n            linear_row(jb->w_out + (int64_t)q * hid * dim, b_out,\n",
+     "const float *b_out = NULL;\n            linear_row(jb->w_out + (int64_t)q * hid * dim, b_out,\n"),
+    ("projected decode: stage q's code looked up in codebook 0",
+     "jb->books + ((int64_t)q * jb->n_codes + code) * dim, dim, hid, p);",
+     "jb->books + ((int64_t)0 * jb->n_codes + code) * dim, dim, hid, p);"),
+    ("projected decode: stage order reversed",
+     "            int32_t code = jb->codes[n * jb->codes_ld + q];",
+     "            int32_t code = jb->codes[n * jb->codes_ld + (jb->n_stages - 1 - q)];"),
+    ("projected decode: bad codes read row 0",
+     "                for (int32_t i = 0; i < hid; ++i) acc[i] = NAN;\n                break;",
+     "                code = 0;"),
 ]
 
 
