@@ -207,6 +207,60 @@ RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32
                                          int32_t *codes, int32_t codes_ld, float *latent,
                                          float *latent_recon, float *h_recon, void *stream);
 
+/*
+ * Per-stage projected RVQ -- the codec quantizer of the "RVQ codec" section
+ * of the "Architecture" page, where codebook q has its own project_in
+ * (hidden -> dim, with bias) and project_out (dim -> hidden, with bias) and
+ * the residual has the hidden width:
+ *
+ *   r = h;  for q: e_q = W_in[q] r + b_in[q];
+ *                  k_q = argmin_i ||e_q - C[q,i]||^2 (lowest i on ties);
+ *                  r   = r - (W_out[q] C[q,k_q] + b_out[q])
+ *   decode: out = sum_q (W_out[q] C[q,k_q] + b_out[q]), stage 0 first
+ *
+ * Weights are in PyTorch (out, in) order and stacked over the stages:
+ *   w_in [n_stages, dim, hidden], b_in [n_stages, dim] or NULL,
+ *   w_out [n_stages, hidden, dim], b_out [n_stages, hidden] or NULL.
+ * dim must be 64 and hidden a positive multiple of 64 (RVQ_ERR_UNSUPPORTED
+ * otherwise). All pointers are caller-owned device memory, 16-byte aligned
+ * (codes 4-byte); calls enqueue on `stream` and return.
+ *
+ * rvq_projected_prepare writes the table of projected codewords
+ *   table [n_stages, n_codes, hidden] float32,
+ *   table[q,k,i] = float32(sum_j W_out[q,i,j] C[q,k,j] + b_out[q,i]),
+ * each entry a float64 sum over j ascending with the bias added last,
+ * rounded once. It depends only on the weights and codebooks.
+ *
+ * rvq_projected_encode runs the loop above on n_frames hidden vectors h
+ * [n_frames, hidden], reading the out-projections from `table` (prepared
+ * from the same codebooks and weights; the library cannot check this):
+ *   codes    [n_frames, codes_ld] output, column q = k_q
+ *   latent   [n_stages, n_frames, dim] output, latent[q] = e_q, computed as
+ *            fp32 sums on the matrix cores (bias added last); the argmin of
+ *            stage q is exact for these values
+ *   residual [n_frames, hidden] output, the residual after the last stage,
+ *            each update r_i = float32(r_i - table[q,k_q,i]); it is also the
+ *            working buffer between stages and may be h itself (h is then
+ *            overwritten).
+ * latent must not overlap h, residual or codes.
+ *
+ * rvq_projected_decode: out [n_frames, hidden] = sum_q table[q, codes[n,q]],
+ * a float32 accumulator from +0, stage 0 first; a code outside
+ * [0, n_codes) gives a NaN row.
+ */
+RVQ_API rvq_status rvq_projected_prepare(const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                         int32_t dim, const float *w_out, const float *b_out,
+                                         int32_t hidden, float *table, void *stream);
+RVQ_API rvq_status rvq_projected_encode(const float *h, int64_t n_frames, int32_t hidden,
+                                        const float *w_in, const float *b_in,
+                                        const float *codebooks, const float *table,
+                                        int32_t n_stages, int32_t n_codes, int32_t dim,
+                                        int32_t *codes, int32_t codes_ld,
+                                        float *latent, float *residual, void *stream);
+RVQ_API rvq_status rvq_projected_decode(const int32_t *codes, int32_t codes_ld, int64_t n_frames,
+                                        const float *table, int32_t n_stages, int32_t n_codes,
+                                        int32_t hidden, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

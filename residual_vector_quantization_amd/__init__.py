@@ -43,7 +43,7 @@ RVQ_ERR_DEVICE = -3
 
 EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip",
             "rvq_encode_scored", "rvq_prepared_bytes", "rvq_prepare_codebooks", "rvq_encode_prepared",
-            "rvq_project_roundtrip")
+            "rvq_project_roundtrip", "rvq_projected_prepare", "rvq_projected_encode", "rvq_projected_decode")
 
 SCORING = {"default": 0, "bf16x3": 1, "fp32": 2}
 
@@ -87,6 +87,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.rvq_project_roundtrip.restype = ctypes.c_int
     lib.rvq_project_roundtrip.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, vp,
                                           vp, i32, vp, vp, vp, vp]
+    lib.rvq_projected_prepare.restype = ctypes.c_int
+    lib.rvq_projected_prepare.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
+    lib.rvq_projected_encode.restype = ctypes.c_int
+    lib.rvq_projected_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.rvq_projected_decode.restype = ctypes.c_int
+    lib.rvq_projected_decode.argtypes = [vp, i32, i64, vp, i32, i32, i32, vp, vp]
     _lib = lib
     return lib
 
@@ -319,3 +325,96 @@ def rvq_project_roundtrip(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[to
                                       _stream(h))
     _check("rvq_project_roundtrip", st)
     return codes, latent, latent_recon, h_recon
+
+
+def rvq_projected_prepare(codebooks: torch.Tensor, w_out: torch.Tensor, b_out: Optional[torch.Tensor] = None,
+                          table: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Table of projected codewords ``[Q, K, H]``: ``W_out[q] C[q, k] + b_out[q]``.
+
+    ``codebooks`` [Q, K, D], ``w_out`` [Q, H, D] (PyTorch (out, in) order per
+    stage), ``b_out`` [Q, H] or None.
+    """
+    _require(codebooks, "codebooks", torch.float32, 3)
+    dev = codebooks.device
+    _require(w_out, "w_out", torch.float32, 3, dev)
+    q, k, d = codebooks.shape
+    if w_out.shape[0] != q or w_out.shape[2] != d:
+        raise ValueError("w_out must be [Q, H, D]")
+    hid = w_out.shape[1]
+    if b_out is not None:
+        _require(b_out, "b_out", torch.float32, 2, dev)
+        if tuple(b_out.shape) != (q, hid):
+            raise ValueError("b_out must be [Q, H]")
+    if table is None:
+        table = torch.empty((q, k, hid), dtype=torch.float32, device=dev)
+    _require(table, "table", torch.float32, 3, dev)
+    if tuple(table.shape) != (q, k, hid):
+        raise ValueError("table must be [Q, K, H]")
+    st = load().rvq_projected_prepare(_ptr(codebooks), q, k, d, _ptr(w_out), _ptr(b_out), hid, _ptr(table),
+                                      _stream(codebooks))
+    _check("rvq_projected_prepare", st)
+    return table
+
+
+def rvq_projected_encode(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[torch.Tensor],
+                         codebooks: torch.Tensor, table: torch.Tensor, n_stages: Optional[int] = None,
+                         out=None):
+    """Per-stage projected encode of ``h`` [N, H].
+
+    ``w_in`` [Q, D, H], ``b_in`` [Q, D] or None, ``table`` from
+    ``rvq_projected_prepare``. Returns ``(codes [N, Q], latent [Q, N, D],
+    residual [N, H])``; ``out`` may pass those three tensors preallocated
+    (codes may be [N, L] with L >= Q).
+    """
+    _require(h, "h", torch.float32, 2)
+    dev = h.device
+    _require(codebooks, "codebooks", torch.float32, 3, dev)
+    _require(w_in, "w_in", torch.float32, 3, dev)
+    _require(table, "table", torch.float32, 3, dev)
+    n, hid = h.shape
+    qn, k, d = codebooks.shape
+    q = _stages(codebooks, n_stages)
+    if w_in.shape[0] < q or tuple(w_in.shape[1:]) != (d, hid):
+        raise ValueError("w_in must be [Q, D, H]")
+    if b_in is not None:
+        _require(b_in, "b_in", torch.float32, 2, dev)
+        if b_in.shape[0] < q or b_in.shape[1] != d:
+            raise ValueError("b_in must be [Q, D]")
+    if table.shape[0] < q or tuple(table.shape[1:]) != (k, hid):
+        raise ValueError("table must be [Q, K, H]")
+    if out is None:
+        out = (torch.empty((n, q), dtype=torch.int32, device=dev),
+               torch.empty((q, n, d), dtype=torch.float32, device=dev),
+               torch.empty((n, hid), dtype=torch.float32, device=dev))
+    codes, latent, residual = out
+    _require(codes, "codes", torch.int32, 2, dev)
+    _require(latent, "latent", torch.float32, 3, dev)
+    _require(residual, "residual", torch.float32, 2, dev)
+    if codes.shape[0] != n or codes.shape[1] < q or latent.shape[0] < q or tuple(latent.shape[1:]) != (n, d) \
+            or residual.shape != h.shape:
+        raise ValueError("output shapes do not match")
+    st = load().rvq_projected_encode(_ptr(h), n, hid, _ptr(w_in), _ptr(b_in), _ptr(codebooks), _ptr(table), q, k,
+                                     d, _ptr(codes), codes.shape[1], _ptr(latent), _ptr(residual), _stream(h))
+    _check("rvq_projected_encode", st)
+    return codes, latent, residual
+
+
+def rvq_projected_decode(codes: torch.Tensor, table: torch.Tensor, n_stages: Optional[int] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Sum of projected codewords: ``codes`` [N, L] (first Q columns) -> [N, H]."""
+    _require(codes, "codes", torch.int32, 2)
+    _require(table, "table", torch.float32, 3, codes.device)
+    n = codes.shape[0]
+    q = table.shape[0] if n_stages is None else int(n_stages)
+    if not 0 < q <= min(codes.shape[1], table.shape[0]):
+        raise ValueError(f"n_stages={q} does not fit codes {tuple(codes.shape)} / table")
+    k, hid = table.shape[1], table.shape[2]
+    if out is None:
+        out = torch.empty((n, hid), dtype=torch.float32, device=codes.device)
+    _require(out, "out", torch.float32, 2, codes.device)
+    if tuple(out.shape) != (n, hid):
+        raise ValueError("out must be [N, H]")
+    st = load().rvq_projected_decode(_ptr(codes), codes.shape[1], n, _ptr(table), q, k, hid, _ptr(out),
+                                     _stream(codes))
+    _check("rvq_projected_decode", st)
+    return out

@@ -174,4 +174,70 @@ RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32
     return from_hip(e);
 }
 
+RVQ_API rvq_status rvq_projected_prepare(const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                         int32_t dim, const float *w_out, const float *b_out,
+                                         int32_t hidden, float *table, void *stream)
+{
+    const rvq_status st = check_shape(0, dim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (hidden <= 0) return RVQ_ERR_INVALID_ARG;
+    if (hidden % 64 != 0) return RVQ_ERR_UNSUPPORTED;
+    if (!codebooks || !w_out || !table) return RVQ_ERR_INVALID_ARG;
+    if (!aligned(codebooks, 16) || !aligned(w_out, 16) || !aligned(table, 16) || (b_out && !aligned(b_out, 16)))
+        return RVQ_ERR_INVALID_ARG;
+    return from_hip(rvq::launch_projected_table(codebooks, n_stages, n_codes, w_out, b_out, hidden, table,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+RVQ_API rvq_status rvq_projected_encode(const float *h, int64_t n_frames, int32_t hidden,
+                                        const float *w_in, const float *b_in,
+                                        const float *codebooks, const float *table,
+                                        int32_t n_stages, int32_t n_codes, int32_t dim,
+                                        int32_t *codes, int32_t codes_ld,
+                                        float *latent, float *residual, void *stream)
+{
+    const rvq_status st = check_shape(n_frames, dim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (hidden <= 0 || codes_ld < n_stages) return RVQ_ERR_INVALID_ARG;
+    if (hidden % 64 != 0) return RVQ_ERR_UNSUPPORTED;
+    if (n_frames == 0) return RVQ_OK;
+    if (!h || !w_in || !codebooks || !table || !codes || !latent || !residual) return RVQ_ERR_INVALID_ARG;
+    if (!aligned(h, 16) || !aligned(w_in, 16) || !aligned(codebooks, 16) || !aligned(table, 16) ||
+        !aligned(codes, 4) || !aligned(latent, 16) || !aligned(residual, 16) || (b_in && !aligned(b_in, 16)))
+        return RVQ_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    for (int32_t q = 0; q < n_stages && e == hipSuccess; ++q) {
+        // stage q reads the hidden input itself at q = 0, the residual buffer afterwards
+        const float *src = q == 0 ? h : residual;
+        float *lat = latent + static_cast<int64_t>(q) * n_frames * rvq::kDim;
+        const float *book = codebooks + static_cast<int64_t>(q) * n_codes * rvq::kDim;
+        e = rvq::launch_linear_in(src, n_frames, hidden, w_in + static_cast<int64_t>(q) * rvq::kDim * hidden,
+                                  b_in ? b_in + static_cast<int64_t>(q) * rvq::kDim : nullptr, lat, s);
+        if (e == hipSuccess)
+            e = launch_scored(RVQ_SCORING_DEFAULT, lat, n_frames, book, 1, n_codes, codes + q, codes_ld,
+                              nullptr, nullptr, s);
+        if (e == hipSuccess)
+            e = rvq::launch_projected_update(src, codes + q, codes_ld, n_frames,
+                                             table + static_cast<int64_t>(q) * n_codes * hidden, n_codes,
+                                             hidden, residual, s);
+    }
+    return from_hip(e);
+}
+
+RVQ_API rvq_status rvq_projected_decode(const int32_t *codes, int32_t codes_ld, int64_t n_frames,
+                                        const float *table, int32_t n_stages, int32_t n_codes,
+                                        int32_t hidden, float *out, void *stream)
+{
+    const rvq_status st = check_shape(n_frames, rvq::kDim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (hidden <= 0 || codes_ld < n_stages) return RVQ_ERR_INVALID_ARG;
+    if (hidden % 64 != 0) return RVQ_ERR_UNSUPPORTED;
+    if (n_frames == 0) return RVQ_OK;
+    if (!codes || !table || !out) return RVQ_ERR_INVALID_ARG;
+    if (!aligned(codes, 4) || !aligned(table, 16) || !aligned(out, 16)) return RVQ_ERR_INVALID_ARG;
+    return from_hip(rvq::launch_projected_decode(codes, codes_ld, n_frames, table, n_stages, n_codes, hidden,
+                                                 out, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -57,4 +57,18 @@ hipError_t launch_linear_in(const float *h, int64_t n_frames, int hidden, const 
 hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const float *w,
                              const float *bias, float *out, hipStream_t stream);
 
+// Per-stage projected RVQ (projected.hip). Table of projected codewords
+// P[q, k, :] = W_out[q] C[q, k] + b_out[q] (float64 sums, rounded once);
+// w_out [Q, hidden, 64], b_out [Q, hidden] (nullable), table [Q, K, hidden].
+hipError_t launch_projected_table(const float *books, int n_stages, int n_codes, const float *w_out,
+                                  const float *b_out, int hidden, float *table, hipStream_t stream);
+
+// dst[n] = src[n] - table[codes[n * ld]] for one stage (src may be dst).
+hipError_t launch_projected_update(const float *src, const int32_t *codes, int codes_ld, int64_t n_frames,
+                                   const float *table, int n_codes, int hidden, float *dst, hipStream_t stream);
+
+// out[n] = sum_q table[q, codes[n, q]], float32 from +0, stage 0 first.
+hipError_t launch_projected_decode(const int32_t *codes, int codes_ld, int64_t n_frames, const float *table,
+                                   int n_stages, int n_codes, int hidden, float *out, hipStream_t stream);
+
 }  // namespace rvq

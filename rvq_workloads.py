@@ -17,7 +17,9 @@ projection matrix is drawn from a seeded PCG64 generator. Each kind of
 draw has its own stream, so changing one size never shifts another draw:
 
     codebook = 1, latents = 2, code indices = 3, noise = 4,
-    fc (1024 -> 64) weights = 5, fc2 (64 -> 1024) weights = 6.
+    fc (1024 -> 64) weights = 5, fc2 (64 -> 1024) weights = 6,
+    per-stage project_in weights = 7, project_out weights = 8,
+    project_in biases = 9, project_out biases = 10.
 
 Readings of the recipe that the pages leave open:
 
@@ -28,6 +30,10 @@ Readings of the recipe that the pages leave open:
 * ``N(0, 1/fan_in)`` for linear weights names a variance (std 1/32 for
   fc, 1/8 for fc2), the usual 1/fan_in scaling that keeps outputs near
   unit scale.
+* Per-stage projections ("RVQ codec" section: project_in / project_out of
+  every codebook, both with bias) use the same 1/fan_in variances; the
+  pages give no values for their biases, so they are drawn small,
+  N(0, 0.05^2), to exercise the bias path.
 * Frames built as "sums of random codewords plus noise" are summed in
   float64 and rounded once to float32. That is input synthesis, done at a
   higher precision than the method's own float32 arithmetic.
@@ -46,6 +52,10 @@ STREAM_CODES = 3
 STREAM_NOISE = 4
 STREAM_FC_IN = 5
 STREAM_FC_OUT = 6
+STREAM_STAGE_IN = 7
+STREAM_STAGE_OUT = 8
+STREAM_STAGE_IN_BIAS = 9
+STREAM_STAGE_OUT_BIAS = 10
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,15 +72,16 @@ class Workload:
     noise_sigma: float     # std of the additive noise on constructed frames
     frame_rate_hz: float   # for seconds-of-audio figures
     hidden: int = 0        # >0: projected workload with fc hidden->dim and fc2 dim->hidden
+    per_stage: bool = False  # projections per codebook (project_in / project_out) instead of fc / fc2
     seed: int = 0
     description: str = ""
 
     @property
     def projected(self) -> bool:
-        return self.hidden > 0
+        return self.hidden > 0 and not self.per_stage
 
 
-# The six workloads. Sizes and recipes as the codec shapes dictate; the
+# The seven workloads. Sizes and recipes as the codec shapes dictate; the
 # description strings state them for result lines.
 WORKLOADS = {
     "tiny": Workload(
@@ -100,6 +111,12 @@ WORKLOADS = {
         description="1e6 hidden vectors [1e6,1024] ~ N(0,1); fc 1024->64 W ~ N(0, var 1/1024), "
                     "b = 0; RVQ Q=8, K=1024, D=64, C[q] ~ N(0,1)*0.5^q; fc2 64->1024 "
                     "W ~ N(0, var 1/64), b = 0; seed 0"),
+    "stage_projected": Workload(
+        "stage_projected", 192_000, 8, 1024, 64, 0.5, 192_000, 0.0, 25.0, hidden=1024, per_stage=True,
+        description="256 clips x 750 frames = 192000 hidden vectors [N,1024] ~ N(0,1); per stage q < 8: "
+                    "project_in W_in[q] [64,1024] ~ N(0, var 1/1024), b_in[q] ~ N(0, 0.05^2); "
+                    "C[q] [1024,64] ~ N(0,1)*0.5^q; project_out W_out[q] [1024,64] ~ N(0, var 1/64), "
+                    "b_out[q] ~ N(0, 0.05^2); seed 0"),
 }
 
 
@@ -158,6 +175,18 @@ def projection_weights(w: Workload):
     w_in = (_rng(w.seed, STREAM_FC_IN).standard_normal((d, h)) * (1.0 / np.sqrt(h))).astype(np.float32)
     w_out = (_rng(w.seed, STREAM_FC_OUT).standard_normal((h, d)) * (1.0 / np.sqrt(d))).astype(np.float32)
     return w_in, np.zeros(d, np.float32), w_out, np.zeros(h, np.float32)
+
+
+def stage_projection_weights(w: Workload):
+    """Per-stage projections, PyTorch (out, in) order, stacked over the Q stages:
+    ``w_in`` [Q, D, H] (var 1/H), ``b_in`` [Q, D], ``w_out`` [Q, H, D] (var 1/D),
+    ``b_out`` [Q, H]; biases N(0, 0.05^2)."""
+    q, h, d = w.n_stages, w.hidden, w.dim
+    w_in = (_rng(w.seed, STREAM_STAGE_IN).standard_normal((q, d, h)) * (1.0 / np.sqrt(h))).astype(np.float32)
+    w_out = (_rng(w.seed, STREAM_STAGE_OUT).standard_normal((q, h, d)) * (1.0 / np.sqrt(d))).astype(np.float32)
+    b_in = (0.05 * _rng(w.seed, STREAM_STAGE_IN_BIAS).standard_normal((q, d))).astype(np.float32)
+    b_out = (0.05 * _rng(w.seed, STREAM_STAGE_OUT_BIAS).standard_normal((q, h))).astype(np.float32)
+    return w_in, b_in, w_out, b_out
 
 
 def hidden_states(w: Workload, rows: Optional[int] = None) -> np.ndarray:

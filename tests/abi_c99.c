@@ -59,6 +59,25 @@ int main(void)
                   RVQ_ERR_INVALID_ARG);
     bad += expect("encode prepared empty", rvq_encode_prepared(NULL, 0, 64, NULL, NULL, 8, 1024, NULL, 8, NULL, NULL, NULL),
                   RVQ_OK);
+    bad += expect("projected prepare hidden 96", rvq_projected_prepare(fx, 8, 1024, 64, fx, NULL, 96, fx, NULL),
+                  RVQ_ERR_UNSUPPORTED);
+    bad += expect("projected prepare null table", rvq_projected_prepare(fx, 8, 1024, 64, fx, NULL, 1024, NULL, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("projected prepare misaligned bias", rvq_projected_prepare(fx, 8, 1024, 64, fx, fx + 1, 1024, fx, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("projected encode null latent", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, fx, 8, 1024, 64,
+                                                                       ic, 8, NULL, fx, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("projected encode dim 32", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, fx, 8, 1024, 32,
+                                                                  ic, 8, fx, fx, NULL), RVQ_ERR_UNSUPPORTED);
+    bad += expect("projected encode ld<q", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, fx, 8, 1024, 64,
+                                                                ic, 7, fx, fx, NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("projected encode empty", rvq_projected_encode(NULL, 0, 1024, NULL, NULL, NULL, NULL, 8, 1024, 64,
+                                                                 NULL, 8, NULL, NULL, NULL), RVQ_OK);
+    bad += expect("projected decode null out", rvq_projected_decode(ic, 8, 10, fx, 8, 1024, 1024, NULL, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("projected decode hidden 0", rvq_projected_decode(ic, 8, 10, fx, 8, 1024, 0, fx, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("projected decode empty", rvq_projected_decode(NULL, 8, 0, NULL, 8, 1024, 1024, NULL, NULL), RVQ_OK);
     printf("%s\n", bad ? "abi_c99: FAILED" : "abi_c99: ok");
     return bad ? 1 : 0;
 }
