@@ -36,11 +36,25 @@ static_assert(kWaves * kFramesPerWave == kLinearFramesPerBlock, "frames per bloc
 
 // ---- linear_in: [N, hidden] x [64, hidden]^T -> [N, 64] -------------------
 
-template <bool kBias>
+// The residual update of the previous stage of a per-stage projected
+// quantizer can ride along (kUpdate): each lane subtracts the table row of
+// its frame's previous code from the hidden-width chunk it loads,
+// r <- fl32(r - P[code]), stores the result to `dst` (which may be `h`
+// itself: every element is loaded, then stored, by the same lane) and feeds
+// it to the matrix cores. A code outside [0, n_codes) makes the row NaN.
+struct Update {
+    const int32_t *codes;   // previous stage's column; row n at codes[n * ld]
+    int ld;
+    const float *table;     // previous stage's [n_codes, hidden] projected codewords
+    int n_codes;
+    float *dst;             // [N, hidden] updated residual
+};
+
+template <bool kBias, bool kUpdate>
 __global__ __launch_bounds__(kThreads)
-void linear_in_kernel(const float *__restrict__ h, int64_t n_frames, int hidden,
+void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
                       const float *__restrict__ w, const float *__restrict__ bias,
-                      float *__restrict__ y)
+                      float *__restrict__ y, Update up)
 {
     // one chunk = 64 weight rows (all outputs) x 64 columns of the hidden dim
     __shared__ __align__(16) float s_w[2][kDim * kRow];
@@ -54,6 +68,16 @@ void linear_in_kernel(const float *__restrict__ h, int64_t n_frames, int hidden,
                           wave * kFramesPerWave + col;
     const bool valid = frame < n_frames;
     const float *hrow = h + (valid ? frame : 0) * static_cast<int64_t>(hidden) + 32 * half;
+    const float *prow = nullptr;   // previous code's table row (kUpdate)
+    float *drow = nullptr;
+    bool code_ok = true;
+    if (kUpdate) {
+        int k = up.codes[(valid ? frame : 0) * up.ld];
+        code_ok = static_cast<unsigned>(k) < static_cast<unsigned>(up.n_codes);
+        k = code_ok ? k : 0;
+        prow = up.table + static_cast<int64_t>(k) * hidden + 32 * half;
+        drow = up.dst + (valid ? frame : 0) * static_cast<int64_t>(hidden) + 32 * half;
+    }
 
     // staging: wavefront w stages weight rows 16w..16w+15; lane -> (row, 16-column quarter)
     const int srow = wave * 16 + (lane & 15);
@@ -72,10 +96,30 @@ void linear_in_kernel(const float *__restrict__ h, int64_t n_frames, int hidden,
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(dst + 4 * i) = ws[i];
     };
+    f32x4 pv[8];
     auto fetch_h = [&](int c) {
         const f32x4 *p = reinterpret_cast<const f32x4 *>(hrow + 64 * c);
 #pragma unroll
         for (int i = 0; i < 8; ++i) hv[i] = p[i];
+        if (kUpdate) {
+            const f32x4 *t = reinterpret_cast<const f32x4 *>(prow + 64 * c);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pv[i] = t[i];
+        }
+    };
+    // r - P[code] for the chunk in hv/pv, stored to dst and kept for the product
+    auto update_h = [&](int c, f32x4 (&cur)[8]) {
+        const float nan = __builtin_nanf("");
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cur[i][e] = code_ok ? hv[i][e] - pv[i][e] : nan;
+        }
+        if (valid) {
+            f32x4 *d = reinterpret_cast<f32x4 *>(drow + 64 * c);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d[i] = cur[i];
+        }
     };
 
     f32x16 acc[2];
@@ -92,8 +136,12 @@ void linear_in_kernel(const float *__restrict__ h, int64_t n_frames, int hidden,
     for (int c = 0; c < n_chunks; ++c) {
         const int buf = c & 1;
         f32x4 cur[8];
+        if (kUpdate) {
+            update_h(c, cur);
+        } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cur[i] = hv[i];
+            for (int i = 0; i < 8; ++i) cur[i] = hv[i];
+        }
         if (c + 1 < n_chunks) {
             fetch_w(c + 1);
             fetch_h(c + 1);
@@ -244,10 +292,30 @@ hipError_t launch_linear_in(const float *h, int64_t n_frames, int hidden, const 
     const int64_t blocks = (n_frames + kLinearFramesPerBlock - 1) / kLinearFramesPerBlock;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    const Update none = {nullptr, 0, nullptr, 0, nullptr};
     if (bias)
-        hipLaunchKernelGGL((linear_in_kernel<true>), grid, block, 0, stream, h, n_frames, hidden, w, bias, y);
+        hipLaunchKernelGGL((linear_in_kernel<true, false>), grid, block, 0, stream, h, n_frames, hidden, w, bias,
+                           y, none);
     else
-        hipLaunchKernelGGL((linear_in_kernel<false>), grid, block, 0, stream, h, n_frames, hidden, w, bias, y);
+        hipLaunchKernelGGL((linear_in_kernel<false, false>), grid, block, 0, stream, h, n_frames, hidden, w, bias,
+                           y, none);
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_in_update(const float *src, const int32_t *codes, int codes_ld, const float *table,
+                                   int n_codes, float *dst, int64_t n_frames, int hidden, const float *w,
+                                   const float *bias, float *y, hipStream_t stream)
+{
+    const int64_t blocks = (n_frames + kLinearFramesPerBlock - 1) / kLinearFramesPerBlock;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    const Update up = {codes, codes_ld, table, n_codes, dst};
+    if (bias)
+        hipLaunchKernelGGL((linear_in_kernel<true, true>), grid, block, 0, stream, src, n_frames, hidden, w, bias,
+                           y, up);
+    else
+        hipLaunchKernelGGL((linear_in_kernel<false, true>), grid, block, 0, stream, src, n_frames, hidden, w, bias,
+                           y, up);
     return hipGetLastError();
 }
 

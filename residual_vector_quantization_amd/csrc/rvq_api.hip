@@ -207,21 +207,28 @@ RVQ_API rvq_status rvq_projected_encode(const float *h, int64_t n_frames, int32_
         return RVQ_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
+    const int64_t table_stage = static_cast<int64_t>(n_codes) * hidden;
     for (int32_t q = 0; q < n_stages && e == hipSuccess; ++q) {
-        // stage q reads the hidden input itself at q = 0, the residual buffer afterwards
-        const float *src = q == 0 ? h : residual;
         float *lat = latent + static_cast<int64_t>(q) * n_frames * rvq::kDim;
         const float *book = codebooks + static_cast<int64_t>(q) * n_codes * rvq::kDim;
-        e = rvq::launch_linear_in(src, n_frames, hidden, w_in + static_cast<int64_t>(q) * rvq::kDim * hidden,
-                                  b_in ? b_in + static_cast<int64_t>(q) * rvq::kDim : nullptr, lat, s);
+        const float *wq = w_in + static_cast<int64_t>(q) * rvq::kDim * hidden;
+        const float *bq = b_in ? b_in + static_cast<int64_t>(q) * rvq::kDim : nullptr;
+        if (q == 0) {
+            e = rvq::launch_linear_in(h, n_frames, hidden, wq, bq, lat, s);
+        } else {
+            // stage q - 1's residual update rides along with stage q's in-projection:
+            // it reads h at q = 1 and the residual buffer afterwards
+            e = rvq::launch_linear_in_update(q == 1 ? h : residual, codes + (q - 1), codes_ld,
+                                             table + (q - 1) * table_stage, n_codes, residual, n_frames,
+                                             hidden, wq, bq, lat, s);
+        }
         if (e == hipSuccess)
             e = launch_scored(RVQ_SCORING_DEFAULT, lat, n_frames, book, 1, n_codes, codes + q, codes_ld,
                               nullptr, nullptr, s);
-        if (e == hipSuccess)
-            e = rvq::launch_projected_update(src, codes + q, codes_ld, n_frames,
-                                             table + static_cast<int64_t>(q) * n_codes * hidden, n_codes,
-                                             hidden, residual, s);
     }
+    if (e == hipSuccess)
+        e = rvq::launch_projected_update(n_stages == 1 ? h : residual, codes + (n_stages - 1), codes_ld, n_frames,
+                                         table + (n_stages - 1) * table_stage, n_codes, hidden, residual, s);
     return from_hip(e);
 }
 

@@ -53,6 +53,13 @@ hipError_t launch_decode(const int32_t *codes, int codes_ld, int64_t n_frames,
 hipError_t launch_linear_in(const float *h, int64_t n_frames, int hidden, const float *w,
                             const float *bias, float *y, hipStream_t stream);
 
+// linear_in on r = fl32(src - table[codes[n * ld]]) (the previous stage's
+// residual update of a per-stage projected quantizer), also storing r to dst
+// (dst may be src).
+hipError_t launch_linear_in_update(const float *src, const int32_t *codes, int codes_ld, const float *table,
+                                   int n_codes, float *dst, int64_t n_frames, int hidden, const float *w,
+                                   const float *bias, float *y, hipStream_t stream);
+
 // out[N, hidden] = x[N, 64] W[hidden, 64]^T + bias (bias nullable); hidden % 64 == 0.
 hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const float *w,
                              const float *bias, float *out, hipStream_t stream);
