@@ -70,7 +70,7 @@ class Oracle:
             _F32P, ctypes.c_int64, ctypes.c_int32, _F32P, ctypes.c_void_p, _F32P, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, _F32P, ctypes.c_void_p, ctypes.c_void_p, _I32P,
             ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-            ctypes.c_int]
+            ctypes.c_int, ctypes.c_int]
         lib.oracle_projected_decode.restype = ctypes.c_int
         lib.oracle_projected_decode.argtypes = [
             _I32P, ctypes.c_int32, ctypes.c_int64, _F32P, ctypes.c_int32, ctypes.c_int32,
@@ -158,13 +158,15 @@ class Oracle:
     def projected_encode(self, h: np.ndarray, w_in: np.ndarray, b_in: Optional[np.ndarray],
                          books: np.ndarray, w_out: np.ndarray, b_out: Optional[np.ndarray],
                          n_stages: Optional[int] = None, e_given: Optional[np.ndarray] = None,
-                         threads: int = 0):
+                         normalize: bool = False, threads: int = 0):
         """Per-stage projected encode (each codebook with its own project_in / project_out).
 
         ``h`` [N, hidden]; ``w_in`` [Q, D, hidden], ``b_in`` [Q, D] or None;
         ``books`` [Q, K, D]; ``w_out`` [Q, hidden, D], ``b_out`` [Q, hidden]
         or None. With ``e_given`` [Q, N, D] the argmin of stage q is taken on
-        ``e_given[q]`` instead of the oracle's own projection. Returns
+        ``e_given[q]`` instead of the oracle's own projection. With
+        ``normalize`` the argmin compares the encoding and the codewords
+        scaled to unit L2 norm (float64, norm floored at 1e-12). Returns
         ``(codes [N, Q], e [Q, N, D] (the oracle's own projections),
         residual [N, hidden], best [N, Q], second [N, Q])``.
         """
@@ -185,7 +187,7 @@ class Oracle:
         self.last_threads = self.lib.oracle_projected_encode(
             h, n, hidden, w_in, self._ptr(b_in), books, q, k, d, w_out, self._ptr(b_out),
             self._ptr(e_given), codes, q, self._ptr(e), self._ptr(residual), self._ptr(best),
-            self._ptr(second), int(threads))
+            self._ptr(second), int(bool(normalize)), int(threads))
         return codes, e, residual, best, second
 
     def projected_decode(self, codes: np.ndarray, books: np.ndarray, w_out: np.ndarray,

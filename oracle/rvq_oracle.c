@@ -24,6 +24,11 @@
  *     argmin and project_out (dim -> hidden, with bias) applied to the
  *     picked codeword before it is subtracted from the hidden-width
  *     residual; decode sums the projected codewords, stage 0 first.
+ *   - Normalized (cosine) variant of it: the quantizer of the
+ *     "Maintainer's guide -- moss-tts.cpp" page (gotchas, item 9) scales
+ *     the projected encoding and every codeword to unit L2 norm (dividing by
+ *     max(norm, 1e-12)) before the argmin; the decode and the residual
+ *     update use the stored codeword, unscaled.
  *
  * Precision (the pages fix only that the codec is kept in F32):
  *   - distances: float64, direct form sum_j (r_j - c_j)^2, j ascending,
@@ -31,7 +36,10 @@
  *   - residual: float32, r_j <- fl32(r_j - c_j);
  *   - decode accumulator: float32, stage order ascending;
  *   - linear (and both per-stage projections): float64 sum, i ascending,
- *     bias added last, rounded once to float32.
+ *     bias added last, rounded once to float32;
+ *   - normalization: float64 throughout (squares summed j ascending, sqrt,
+ *     one division per element), distances in float64 on the normalized
+ *     vectors, direct form.
  *
  * The best and second-best distances of every stage are reported too, so
  * a caller can classify near-ties (gap <= 1e-5 * best).
@@ -80,6 +88,43 @@ static int32_t nearest(const float *v, const float *book, int32_t n_codes, int32
     *best = d1;
     *second = d2;
     return k1;
+}
+
+/* out = v / max(||v||_2, 1e-12), all in float64. */
+static void unit_vector(const float *v, int32_t dim, double *out)
+{
+    double ss = 0.0;
+    for (int32_t j = 0; j < dim; ++j) ss = ss + (double)v[j] * (double)v[j];
+    double norm = sqrt(ss);
+    if (norm < 1e-12) norm = 1e-12;
+    for (int32_t j = 0; j < dim; ++j) out[j] = (double)v[j] / norm;
+}
+
+/* As `nearest`, on float64 vectors: `units` [n_codes, dim] are the
+ * normalized codewords, u the normalized encoding. */
+static int32_t nearest_unit(const double *u, const double *units, int32_t n_codes, int32_t dim,
+                            double *best, double *second)
+{
+    int32_t pick = 0;
+    double lo = INFINITY, next = INFINITY;
+    for (int32_t k = 0; k < n_codes; ++k) {
+        const double *ck = units + (int64_t)k * dim;
+        double acc = 0.0;
+        for (int32_t j = 0; j < dim; ++j) {
+            const double t = u[j] - ck[j];
+            acc = acc + t * t;
+        }
+        if (acc < lo) {
+            next = lo;
+            lo = acc;
+            pick = k;
+        } else if (acc < next) {
+            next = acc;
+        }
+    }
+    *best = lo;
+    *second = next;
+    return pick;
 }
 
 /* y = W v + b for one vector: W [out_dim, in_dim] row-major, b nullable;
@@ -177,6 +222,7 @@ typedef struct {
     const float *books;          /* [Q, K, dim] */
     const float *w_out, *b_out;  /* [Q, hidden, dim], [Q, hidden] (nullable) */
     const float *e_given;        /* nullable [Q, N, dim] */
+    const double *units;         /* nullable [Q, K, dim]: normalized codewords (cosine variant) */
     int32_t *codes;
     int32_t codes_ld;
     float *e_out;                /* nullable [Q, N, dim] */
@@ -197,6 +243,7 @@ static void projected_frames(const projected_job *jb)
     float *r = (float *)malloc(sizeof(float) * (size_t)hid);
     float *p = (float *)malloc(sizeof(float) * (size_t)hid);
     float *e = (float *)malloc(sizeof(float) * (size_t)dim);
+    double *u = (double *)malloc(sizeof(double) * (size_t)dim);
     for (int64_t n = jb->begin; n < jb->end; ++n) {
         memcpy(r, jb->h + n * hid, sizeof(float) * (size_t)hid);
         for (int32_t q = 0; q < jb->n_stages; ++q) {
@@ -207,7 +254,13 @@ static void projected_frames(const projected_job *jb)
             const float *pick_on = jb->e_given ? jb->e_given + at : e;
             const float *stage_book = jb->books + (int64_t)q * jb->n_codes * dim;
             double d1, d2;
-            int32_t k1 = nearest(pick_on, stage_book, jb->n_codes, dim, &d1, &d2);
+            int32_t k1;
+            if (jb->units) {
+                unit_vector(pick_on, dim, u);
+                k1 = nearest_unit(u, jb->units + (int64_t)q * jb->n_codes * dim, jb->n_codes, dim, &d1, &d2);
+            } else {
+                k1 = nearest(pick_on, stage_book, jb->n_codes, dim, &d1, &d2);
+            }
             const int64_t nq = n * jb->n_stages + q;
             jb->codes[n * jb->codes_ld + q] = k1;
             if (jb->best) jb->best[nq] = d1;
@@ -218,6 +271,7 @@ static void projected_frames(const projected_job *jb)
         }
         if (jb->residual) memcpy(jb->residual + n * hid, r, sizeof(float) * (size_t)hid);
     }
+    free(u);
     free(e);
     free(p);
     free(r);
@@ -372,15 +426,23 @@ int oracle_linear(const float *h, int64_t n_rows, int32_t in_dim,
 }
 
 /* Per-stage projected encode of frames [0, n_frames); see projected_frames.
- * e_given, e_out, residual, best and second are nullable. */
+ * e_given, e_out, residual, best and second are nullable. With `normalize`
+ * set, every argmin is taken between the normalized encoding and the
+ * normalized codewords (best / second are then those distances). */
 int oracle_projected_encode(const float *h, int64_t n_frames, int32_t hidden,
                             const float *w_in, const float *b_in,
                             const float *books, int32_t n_stages, int32_t n_codes, int32_t dim,
                             const float *w_out, const float *b_out, const float *e_given,
                             int32_t *codes, int32_t codes_ld, float *e_out, float *residual,
-                            double *best, double *second, int threads)
+                            double *best, double *second, int normalize, int threads)
 {
     if (n_frames <= 0) return 0;
+    double *units = NULL;
+    if (normalize) {
+        const int64_t rows = (int64_t)n_stages * n_codes;
+        units = (double *)malloc(sizeof(double) * (size_t)(rows * dim));
+        for (int64_t k = 0; k < rows; ++k) unit_vector(books + k * dim, dim, units + k * dim);
+    }
     any_job p;
     memset(&p, 0, sizeof p);
     p.kind = JOB_PROJECTED;
@@ -391,7 +453,10 @@ int oracle_projected_encode(const float *h, int64_t n_frames, int32_t hidden,
     p.u.p.codes = codes; p.u.p.codes_ld = codes_ld; p.u.p.e_out = e_out;
     p.u.p.residual = residual; p.u.p.best = best; p.u.p.second = second;
     p.u.p.n_frames = n_frames;
-    return run_parallel(p, n_frames, pick_threads(threads, n_frames));
+    p.u.p.units = units;
+    const int used = run_parallel(p, n_frames, pick_threads(threads, n_frames));
+    free(units);
+    return used;
 }
 
 /* Per-stage projected decode of frames [0, n_frames) into out [N, hidden]. */

@@ -31,7 +31,12 @@ What pins what:
   against an exact integer re-derivation with numpy (argmin first
   occurrence); the argmin follows given encodings (checked with cdist);
   prefix consistency; the float32, stage-0-first decode order; NaN frames
-  for bad codes.
+  for bad codes;
+* normalized (cosine) variant: a hand-worked 2-stage case where the
+  normalization decides a pick (tests/golden/cosine_handworked.txt); the
+  argmin equals scipy's cosine-distance argmin; scaling an encoding or a
+  codeword by a positive factor changes nothing; the zero encoding and a
+  zero codeword follow the 1e-12 norm floor.
 """
 
 import numpy as np
@@ -328,6 +333,58 @@ def pin_projected_prefix_and_decode(o):
     assert np.isnan(out[[3, 7]]).all() and np.isfinite(np.delete(out, [3, 7], axis=0)).all()
 
 
+def pin_cosine_handworked(o):
+    p, frames, h = _projected_case("cosine_handworked.txt")
+    q, _, d = p["books"].shape
+    codes, e, residual, best, second = o.projected_encode(h, p["w_in"], p["b_in"], p["books"],
+                                                          p["w_out"], p["b_out"], normalize=True)
+    np.testing.assert_array_equal(codes, np.array([f["codes"] for f in frames], np.int32))
+    np.testing.assert_array_equal(e.transpose(1, 0, 2).reshape(len(frames), q * d),
+                                  np.array([f["e"] for f in frames], np.float32))
+    np.testing.assert_allclose(best, np.array([f["best"] for f in frames]), rtol=1e-9, atol=1e-15)
+    np.testing.assert_allclose(second, np.array([f["second"] for f in frames]), rtol=1e-9, atol=1e-15)
+    np.testing.assert_array_equal(residual, np.array([f["residual"] for f in frames], np.float32))
+    recon = o.projected_decode(codes, p["books"], p["w_out"], p["b_out"])
+    np.testing.assert_array_equal(recon, np.array([f["recon"] for f in frames], np.float32))
+
+
+def pin_cosine_against_cdist(o):
+    rng = np.random.default_rng(25)
+    q, k, d, hid, n = 3, 200, 8, 40, 300
+    books = rng.standard_normal((q, k, d)).astype(np.float32)
+    w_in = (rng.standard_normal((q, d, hid)) / np.sqrt(hid)).astype(np.float32)
+    w_out = (rng.standard_normal((q, hid, d)) / np.sqrt(d)).astype(np.float32)
+    b_in = (0.05 * rng.standard_normal((q, d))).astype(np.float32)
+    h = rng.standard_normal((n, hid)).astype(np.float32)
+    codes, e, _, best, _ = o.projected_encode(h, w_in, b_in, books, w_out, None, normalize=True)
+    for s in range(q):
+        cosd = cdist(e[s].astype(np.float64), books[s].astype(np.float64), "cosine")   # 1 - cos
+        _check_nn(codes[:, s], cosd, f"stage {s}")
+        np.testing.assert_allclose(best[:, s], 2.0 * cosd.min(axis=1), rtol=1e-9, atol=1e-12)
+    # a positive scale of an encoding or of a codeword changes no pick
+    scaled = books * rng.uniform(0.1, 10.0, size=(q, k, 1)).astype(np.float32)
+    given = e * rng.uniform(0.1, 10.0, size=(q, n, 1)).astype(np.float32)
+    c2, _, _, _, _ = o.projected_encode(h, w_in, b_in, scaled, w_out, None, e_given=given, normalize=True)
+    np.testing.assert_array_equal(c2[:, 0], codes[:, 0])
+    # without normalization the picks differ on these codebooks
+    c_plain, _, _, _, _ = o.projected_encode(h, w_in, b_in, books, w_out, None)
+    assert (c_plain[:, 0] != codes[:, 0]).any()
+
+
+def pin_cosine_norm_floor(o):
+    # codewords (2,0), (0,3), (0,0): a zero encoding stays zero, so every distance is |v_k|^2 =
+    # 1, 1, 0 and the zero codeword wins; a nonzero encoding is at distance 1 from the zero codeword
+    books = np.array([[[2.0, 0.0], [0.0, 3.0], [0.0, 0.0]]], np.float32)
+    eye = np.eye(2, dtype=np.float32)[None]
+    h = np.array([[0.0, 0.0], [5.0, 0.0], [-1.0, -1.0], [1e-30, 0.0]], np.float32)
+    codes, _, _, best, second = o.projected_encode(h, eye, None, books, eye, None, normalize=True)
+    # frame 2: u = -(1,1)/sqrt2, so |u|^2 = 1 and |u - v_0|^2 = |u - v_1|^2 = 2 + sqrt2;
+    # frame 3: |e| = 1e-30 is floored to 1e-12, so u = (1e-18, 0) and the zero codeword is at 1e-36
+    np.testing.assert_array_equal(codes[:, 0], [2, 0, 2, 2])
+    np.testing.assert_allclose(best[:, 0], [0.0, 0.0, 1.0, 1e-36], rtol=1e-7, atol=0)
+    np.testing.assert_allclose(second[:, 0], [1.0, 1.0, 2.0 + np.sqrt(2.0), 1.0], rtol=1e-15, atol=0)
+
+
 ALL_PINS = [
     pin_handworked,
     pin_decode_order,
@@ -344,4 +401,7 @@ ALL_PINS = [
     pin_projected_integer_exact,
     pin_projected_follows_given_encodings,
     pin_projected_prefix_and_decode,
+    pin_cosine_handworked,
+    pin_cosine_against_cdist,
+    pin_cosine_norm_floor,
 ]

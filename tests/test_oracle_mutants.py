@@ -96,6 +96,21 @@ MUTANTS = [
     ("projected decode: stage order reversed",
      "            int32_t code = jb->codes[n * jb->codes_ld + q];",
      "            int32_t code = jb->codes[n * jb->codes_ld + (jb->n_stages - 1 - q)];"),
+    ("cosine: the encoding is not normalized",
+     "                unit_vector(pick_on, dim, u);\n",
+     "                for (int32_t j = 0; j < dim; ++j) u[j] = pick_on[j];\n"),
+    ("cosine: codewords are not normalized",
+     "for (int64_t k = 0; k < rows; ++k) unit_vector(books + k * dim, dim, units + k * dim);",
+     "for (int64_t k = 0; k < rows * dim; ++k) units[k] = books[k];"),
+    ("cosine: no norm floor",
+     "    if (norm < 1e-12) norm = 1e-12;\n", ""),
+    ("cosine: every stage searches normalized codebook 0",
+     "k1 = nearest_unit(u, jb->units + (int64_t)q * jb->n_codes * dim, jb->n_codes, dim, &d1, &d2);",
+     "k1 = nearest_unit(u, jb->units, jb->n_codes, dim, &d1, &d2);"),
+    ("cosine: ties go to the highest index",
+     "        if (acc < lo) {", "        if (acc <= lo) {"),
+    ("cosine: norm without the square root",
+     "double norm = sqrt(ss);", "double norm = ss;"),
     ("projected decode: bad codes read row 0",
      "                for (int32_t i = 0; i < hid; ++i) acc[i] = NAN;\n                break;",
      "                code = 0;"),
