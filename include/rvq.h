@@ -221,8 +221,8 @@ RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32
  * Weights are in PyTorch (out, in) order and stacked over the stages:
  *   w_in [n_stages, dim, hidden], b_in [n_stages, dim] or NULL,
  *   w_out [n_stages, hidden, dim], b_out [n_stages, hidden] or NULL.
- * dim must be 64 and hidden a positive multiple of 64 (RVQ_ERR_UNSUPPORTED
- * otherwise). All pointers are caller-owned device memory, 16-byte aligned
+ * dim must be 64 (8 for the table of the normalized quantizer below) and
+ * hidden a positive multiple of 64 (RVQ_ERR_UNSUPPORTED otherwise). All pointers are caller-owned device memory, 16-byte aligned
  * (codes 4-byte); calls enqueue on `stream` and return.
  *
  * rvq_projected_prepare writes the table of projected codewords
@@ -260,6 +260,39 @@ RVQ_API rvq_status rvq_projected_encode(const float *h, int64_t n_frames, int32_
 RVQ_API rvq_status rvq_projected_decode(const int32_t *codes, int32_t codes_ld, int64_t n_frames,
                                         const float *table, int32_t n_stages, int32_t n_codes,
                                         int32_t hidden, float *out, void *stream);
+
+/*
+ * Normalized (cosine) per-stage projected RVQ -- the quantizer of the
+ * "Maintainer's guide -- moss-tts.cpp" page (gotchas, item 9): the same
+ * loop as rvq_projected_encode with an 8-dim codebook space, where the
+ * argmin compares the projection and the codewords scaled to unit L2 norm:
+ *
+ *   u = e_q / max(|e_q|, 1e-12),  v_k = C[q,k] / max(|C[q,k]|, 1e-12),
+ *   k_q = argmin_k sum_j (u_j - v_kj)^2   (lowest k on ties)
+ *
+ * decided exactly as in float64 (a frame the fp32 scores cannot separate
+ * is rescanned in float64). The residual update and the decode use the
+ * stored, unscaled codeword: table from rvq_projected_prepare with dim 8,
+ * decode with rvq_projected_decode.
+ *
+ * rvq_cosine_prepare writes units [n_stages, n_codes, 8] float64 (16-byte
+ * aligned, caller-owned), the unit codewords v computed in float64
+ * (squares summed in order, sqrt, one division per element).
+ *
+ * rvq_cosine_encode: arguments as rvq_projected_encode, with dim == 8,
+ * hidden a multiple of 64 and at most 1024 (RVQ_ERR_UNSUPPORTED otherwise),
+ * `units` from rvq_cosine_prepare and `table` from rvq_projected_prepare
+ * (both from the same codebooks and weights), latent [n_stages, n_frames, 8]
+ * the fp32 projections e_q (bias added last).
+ */
+RVQ_API rvq_status rvq_cosine_prepare(const float *codebooks, int32_t n_stages, int32_t n_codes, int32_t dim,
+                                      double *units, void *stream);
+RVQ_API rvq_status rvq_cosine_encode(const float *h, int64_t n_frames, int32_t hidden,
+                                     const float *w_in, const float *b_in,
+                                     const double *units, const float *table,
+                                     int32_t n_stages, int32_t n_codes, int32_t dim,
+                                     int32_t *codes, int32_t codes_ld,
+                                     float *latent, float *residual, void *stream);
 
 #ifdef __cplusplus
 }

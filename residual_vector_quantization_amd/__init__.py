@@ -43,7 +43,8 @@ RVQ_ERR_DEVICE = -3
 
 EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip",
             "rvq_encode_scored", "rvq_prepared_bytes", "rvq_prepare_codebooks", "rvq_encode_prepared",
-            "rvq_project_roundtrip", "rvq_projected_prepare", "rvq_projected_encode", "rvq_projected_decode")
+            "rvq_project_roundtrip", "rvq_projected_prepare", "rvq_projected_encode", "rvq_projected_decode",
+            "rvq_cosine_prepare", "rvq_cosine_encode")
 
 SCORING = {"default": 0, "bf16x3": 1, "fp32": 2}
 
@@ -93,6 +94,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.rvq_projected_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.rvq_projected_decode.restype = ctypes.c_int
     lib.rvq_projected_decode.argtypes = [vp, i32, i64, vp, i32, i32, i32, vp, vp]
+    lib.rvq_cosine_prepare.restype = ctypes.c_int
+    lib.rvq_cosine_prepare.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.rvq_cosine_encode.restype = ctypes.c_int
+    lib.rvq_cosine_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     _lib = lib
     return lib
 
@@ -339,7 +344,7 @@ def rvq_projected_prepare(codebooks: torch.Tensor, w_out: torch.Tensor, b_out: O
     _require(w_out, "w_out", torch.float32, 3, dev)
     q, k, d = codebooks.shape
     if w_out.shape[0] != q or w_out.shape[2] != d:
-        raise ValueError("w_out must be [Q, H, D]")
+        raise ValueError("w_out must be [Q, H, D] (D = 64, or 8 for the normalized quantizer)")
     hid = w_out.shape[1]
     if b_out is not None:
         _require(b_out, "b_out", torch.float32, 2, dev)
@@ -418,3 +423,61 @@ def rvq_projected_decode(codes: torch.Tensor, table: torch.Tensor, n_stages: Opt
                                      _stream(codes))
     _check("rvq_projected_decode", st)
     return out
+
+
+def rvq_cosine_prepare(codebooks: torch.Tensor, units: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Unit codewords ``[Q, K, 8]`` float64 of 8-dim ``codebooks`` [Q, K, 8] (norm floor 1e-12)."""
+    _require(codebooks, "codebooks", torch.float32, 3)
+    q, k, d = codebooks.shape
+    if units is None:
+        units = torch.empty((q, k, d), dtype=torch.float64, device=codebooks.device)
+    _require(units, "units", torch.float64, 3, codebooks.device)
+    if tuple(units.shape) != (q, k, d):
+        raise ValueError("units must be [Q, K, D]")
+    st = load().rvq_cosine_prepare(_ptr(codebooks), q, k, d, _ptr(units), _stream(codebooks))
+    _check("rvq_cosine_prepare", st)
+    return units
+
+
+def rvq_cosine_encode(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[torch.Tensor], units: torch.Tensor,
+                      table: torch.Tensor, n_stages: Optional[int] = None, out=None):
+    """Normalized (cosine) per-stage projected encode of ``h`` [N, H].
+
+    ``w_in`` [Q, 8, H], ``b_in`` [Q, 8] or None, ``units`` from
+    ``rvq_cosine_prepare``, ``table`` from ``rvq_projected_prepare`` (8-dim
+    codebooks). Returns ``(codes [N, Q], latent [Q, N, 8], residual [N, H])``;
+    ``out`` may pass those three tensors preallocated.
+    """
+    _require(h, "h", torch.float32, 2)
+    dev = h.device
+    _require(w_in, "w_in", torch.float32, 3, dev)
+    _require(units, "units", torch.float64, 3, dev)
+    _require(table, "table", torch.float32, 3, dev)
+    n, hid = h.shape
+    qn, k, d = units.shape
+    q = qn if n_stages is None else int(n_stages)
+    if not 0 < q <= qn:
+        raise ValueError(f"n_stages={q} outside 1..{qn}")
+    if w_in.shape[0] < q or tuple(w_in.shape[1:]) != (d, hid):
+        raise ValueError("w_in must be [Q, D, H]")
+    if b_in is not None:
+        _require(b_in, "b_in", torch.float32, 2, dev)
+        if b_in.shape[0] < q or b_in.shape[1] != d:
+            raise ValueError("b_in must be [Q, D]")
+    if table.shape[0] < q or tuple(table.shape[1:]) != (k, hid):
+        raise ValueError("table must be [Q, K, H]")
+    if out is None:
+        out = (torch.empty((n, q), dtype=torch.int32, device=dev),
+               torch.empty((q, n, d), dtype=torch.float32, device=dev),
+               torch.empty((n, hid), dtype=torch.float32, device=dev))
+    codes, latent, residual = out
+    _require(codes, "codes", torch.int32, 2, dev)
+    _require(latent, "latent", torch.float32, 3, dev)
+    _require(residual, "residual", torch.float32, 2, dev)
+    if codes.shape[0] != n or codes.shape[1] < q or latent.shape[0] < q or tuple(latent.shape[1:]) != (n, d) \
+            or residual.shape != h.shape:
+        raise ValueError("output shapes do not match")
+    st = load().rvq_cosine_encode(_ptr(h), n, hid, _ptr(w_in), _ptr(b_in), _ptr(units), _ptr(table), q, k, d,
+                                  _ptr(codes), codes.shape[1], _ptr(latent), _ptr(residual), _stream(h))
+    _check("rvq_cosine_encode", st)
+    return codes, latent, residual

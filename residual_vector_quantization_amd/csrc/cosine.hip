@@ -1,0 +1,342 @@
+// Normalized (cosine) per-stage projected residual vector quantization for
+// gfx950 (CDNA4): the quantizer of the "Maintainer's guide -- moss-tts.cpp"
+// page (gotchas, item 9). Each stage projects the hidden-width residual into
+// an 8-dim codebook space (project_in, with bias), scales the projection and
+// every codeword to unit L2 norm (dividing by max(norm, 1e-12)), picks the
+// nearest unit codeword, and subtracts the projected-back stored codeword
+// (project_out, with bias) from the residual -- the loop of the "RVQ codec"
+// section of the "Architecture" page. The residual update and the decode
+// use the table of projected codewords of projected.hip.
+//
+// Exactness. The oracle decides each pick in float64: u = e / max(|e|,
+// 1e-12), v_k = c_k / max(|c_k|, 1e-12), d_k = sum_j (u_j - v_kj)^2 (j
+// ascending), lowest k on ties. Here the unit codewords v_k are prepared
+// once in exactly that float64 arithmetic (double sqrt and division are
+// correctly rounded on gfx950). Scores are fp32:
+//     s_k = 0.5 |v32_k|^2 - u32 . v32_k,   d_k = |u|^2 + 2 s_k (exact reals),
+// with u32 normalized in fp32 and v32 = fp32(v_k). Every |u| and |v_k| is at
+// most 1, so the normalization (<= 8u per element), the rounding of v, the
+// 8-term dot product and the half-norm keep each s_k within kScoreError of
+// its exact value (24u is the worst case; 96u is used). When the two lowest
+// fp32 scores are more than 2 kScoreError + 1e-13 apart the fp32 winner is
+// the float64 winner (float64 distances are within 1e-14 of exact);
+// otherwise the frame is rescanned over all codewords in float64 by its
+// whole wavefront with the oracle's formula.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "rvq_internal.h"
+
+namespace rvq {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kCosDim = 8;
+constexpr float kUnit = 5.9604644775390625e-08f;       // 2^-24
+constexpr float kScoreError = 96.0f * kUnit;
+constexpr float kAmbiguous = 2.0f * kScoreError + 1e-13f;
+constexpr int kArgChunk = 256;                          // unit codewords per LDS chunk
+constexpr int kProjWaves = 4;
+
+// v = c / max(|c|, 1e-12) in float64 for every codeword of every stage.
+__global__ __launch_bounds__(256)
+void units_kernel(const float *__restrict__ books, int64_t rows, double *__restrict__ units)
+{
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (r >= rows) return;
+    const float *c = books + r * kCosDim;
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < kCosDim; ++j)
+        ss = __dadd_rn(ss, __dmul_rn(static_cast<double>(c[j]), static_cast<double>(c[j])));
+    double norm = __builtin_sqrt(ss);
+    if (norm < 1e-12) norm = 1e-12;
+#pragma unroll
+    for (int j = 0; j < kCosDim; ++j) units[r * kCosDim + j] = static_cast<double>(c[j]) / norm;
+}
+
+struct Update8 {
+    const int32_t *codes;   // previous stage's column; row n at codes[n * ld]
+    int ld;
+    const float *table;     // previous stage's [n_codes, hidden] projected codewords
+    int n_codes;
+    float *dst;             // [N, hidden] updated residual
+};
+
+// y[n, 0..7] = W r_n + bias, W [8, hidden]; one wavefront per frame with
+// lanes over float4 columns of the row (fully coalesced), W held in VGPRs
+// (kT float4 columns per lane, hidden <= 256 kT), partial sums reduced by a
+// butterfly that halves the number of outputs each lane carries. With
+// kUpdate the previous stage's residual update is applied first:
+// r = fl32(src - table[code]) is stored to up.dst (which may be src) and
+// projected. Waves stride over the frames, so W is read once per wave.
+template <int kT, bool kBias, bool kUpdate>
+__global__ __launch_bounds__(64 * kProjWaves)
+void proj8_kernel(const float *src, int64_t n_frames, int hidden, const float *__restrict__ w,
+                  const float *__restrict__ bias, float *__restrict__ y, Update8 up)
+{
+    const int lane = threadIdx.x & 63;
+    const int cols = hidden >> 2;   // float4 columns per row
+    f32x4 wr[kT][kCosDim];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
+        const int col = lane + 64 * t;
+#pragma unroll
+        for (int o = 0; o < kCosDim; ++o)
+            wr[t][o] = col < cols ? *reinterpret_cast<const f32x4 *>(w + static_cast<int64_t>(o) * hidden + 4 * col)
+                                  : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    const int out_id = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+    const float b_out = kBias ? bias[out_id] : 0.0f;
+    const float nan = __builtin_nanf("");
+
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kProjWaves;
+    for (int64_t n = static_cast<int64_t>(blockIdx.x) * kProjWaves + (threadIdx.x >> 6); n < n_frames; n += stride) {
+        const float *row = src + n * hidden;
+        f32x4 r[kT];
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            const int col = lane + 64 * t;
+            r[t] = col < cols ? *reinterpret_cast<const f32x4 *>(row + 4 * col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (kUpdate) {
+            int k = up.codes[n * up.ld];
+            const bool ok = static_cast<unsigned>(k) < static_cast<unsigned>(up.n_codes);
+            k = ok ? k : 0;
+            const float *prow = up.table + static_cast<int64_t>(k) * hidden;
+            float *drow = up.dst + n * hidden;
+#pragma unroll
+            for (int t = 0; t < kT; ++t) {
+                const int col = lane + 64 * t;
+                if (col < cols) {
+                    const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * col);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[t][e] = ok ? r[t][e] - p[e] : nan;
+                    *reinterpret_cast<f32x4 *>(drow + 4 * col) = r[t];
+                }
+            }
+        }
+        float a[kCosDim];
+#pragma unroll
+        for (int o = 0; o < kCosDim; ++o) {
+            float s = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kT; ++t)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s = __builtin_fmaf(wr[t][o][e], r[t][e], s);
+            a[o] = s;
+        }
+        // butterfly: after the xor-32, -16 and -8 steps lane l carries output out_id(l) only
+        float b[4], c[2];
+        const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float give = hi32 ? a[i] : a[i + 4];
+            const float got = __shfl_xor(give, 32);
+            b[i] = (hi32 ? a[i + 4] : a[i]) + got;
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const float give = hi16 ? b[i] : b[i + 2];
+            const float got = __shfl_xor(give, 16);
+            c[i] = (hi16 ? b[i + 2] : b[i]) + got;
+        }
+        float d;
+        {
+            const float give = hi8 ? c[0] : c[1];
+            const float got = __shfl_xor(give, 8);
+            d = (hi8 ? c[1] : c[0]) + got;
+        }
+        d += __shfl_xor(d, 4);
+        d += __shfl_xor(d, 2);
+        d += __shfl_xor(d, 1);
+        if ((lane & 7) == 0) y[n * kCosDim + out_id] = kBias ? d + b_out : d;
+    }
+}
+
+// Float64 distance of the unit encoding u to unit codeword k, the oracle's form.
+__device__ inline double unit_distance(const double (&u)[kCosDim], const double *units, int k)
+{
+    const double *v = units + static_cast<int64_t>(k) * kCosDim;
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < kCosDim; ++j) {
+        const double t = __dadd_rn(u[j], -v[j]);
+        acc = __dadd_rn(acc, __dmul_rn(t, t));
+    }
+    return acc;
+}
+
+// One frame per thread: fp32 scores against the stage's unit codewords
+// (staged through LDS), then a float64 rescan by the whole wavefront for
+// every frame whose two lowest scores are too close to call.
+__global__ __launch_bounds__(256)
+void cosine_argmin_kernel(const float *__restrict__ lat, int64_t n_frames, const double *__restrict__ units,
+                          int n_codes, int32_t *__restrict__ codes, int codes_ld)
+{
+    __shared__ __align__(16) float s_v[kArgChunk * kCosDim];
+    __shared__ float s_hn[kArgChunk];
+    const int lane = threadIdx.x & 63;
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const bool valid = frame < n_frames;
+    float e[kCosDim];
+    {
+        const float *p = lat + (valid ? frame : 0) * kCosDim;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(p);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(p + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            e[j] = lo[j];
+            e[j + 4] = hi[j];
+        }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kCosDim; ++j) ss = __builtin_fmaf(e[j], e[j], ss);
+    // outside this range the fp32 norm may under- or overflow: decide in float64
+    const bool norm_ok = ss >= 1e-30f && ss <= 1e30f;
+    const float inv = 1.0f / fmaxf(__builtin_sqrtf(ss), 1e-12f);
+    float nu[kCosDim];   // -u32
+#pragma unroll
+    for (int j = 0; j < kCosDim; ++j) nu[j] = -(e[j] * inv);
+
+    float best = INFINITY, second = INFINITY;
+    int bk = 0;
+    for (int k0 = 0; k0 < n_codes; k0 += kArgChunk) {
+        const int kn = min(kArgChunk, n_codes - k0);
+        __syncthreads();   // the previous chunk is no longer read
+        if (threadIdx.x < kn) {
+            const double *v = units + static_cast<int64_t>(k0 + threadIdx.x) * kCosDim;
+            float hn = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kCosDim; ++j) {
+                const float vj = static_cast<float>(v[j]);
+                s_v[threadIdx.x * kCosDim + j] = vj;
+                hn = __builtin_fmaf(vj, vj, hn);
+            }
+            s_hn[threadIdx.x] = 0.5f * hn;
+        }
+        __syncthreads();
+        for (int kk = 0; kk < kn; ++kk) {
+            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&s_v[kk * kCosDim]);
+            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&s_v[kk * kCosDim + 4]);
+            float s = s_hn[kk];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s = __builtin_fmaf(nu[j], v0[j], s);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s = __builtin_fmaf(nu[j + 4], v1[j], s);
+            if (s < best) {
+                second = best;
+                best = s;
+                bk = k0 + kk;
+            } else if (s < second) {
+                second = s;
+            }
+        }
+    }
+    bool ambiguous = valid && (!norm_ok || !(second - best > kAmbiguous));
+
+    // float64 rescan, one ambiguous frame at a time, by the whole wavefront
+    uint64_t mask = __ballot(ambiguous);
+    while (mask) {
+        const int srcl = __builtin_ctzll(mask);
+        mask &= mask - 1;
+        double u[kCosDim];
+        double uss = 0.0;
+#pragma unroll
+        for (int j = 0; j < kCosDim; ++j) {
+            const double ej = static_cast<double>(__shfl(e[j], srcl));
+            u[j] = ej;
+            uss = __dadd_rn(uss, __dmul_rn(ej, ej));
+        }
+        double norm = __builtin_sqrt(uss);
+        if (norm < 1e-12) norm = 1e-12;
+#pragma unroll
+        for (int j = 0; j < kCosDim; ++j) u[j] = u[j] / norm;
+        double bd = INFINITY;
+        int bi = 0x7fffffff;
+        for (int k = lane; k < n_codes; k += 64) {   // k ascends per lane: strict "<" keeps the lowest
+            const double d = unit_distance(u, units, k);
+            if (d < bd) {
+                bd = d;
+                bi = k;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const double od = __shfl_xor(bd, off);
+            const int oi = __shfl_xor(bi, off);
+            if (od < bd || (od == bd && oi < bi)) {
+                bd = od;
+                bi = oi;
+            }
+        }
+        if (lane == srcl) bk = bi;
+    }
+    if (valid) codes[frame * codes_ld] = bk;
+}
+
+template <int kT>
+hipError_t launch_proj8_t(const float *src, int64_t n_frames, int hidden, const float *w, const float *bias,
+                          float *y, const Update8 &up, bool update, hipStream_t stream)
+{
+    const int64_t waves = (n_frames + 7) / 8;   // about 8 frames per wavefront, capped below
+    int64_t blocks = (waves + kProjWaves - 1) / kProjWaves;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kProjWaves);
+    if (update) {
+        if (bias)
+            hipLaunchKernelGGL((proj8_kernel<kT, true, true>), grid, block, 0, stream, src, n_frames, hidden, w, bias, y, up);
+        else
+            hipLaunchKernelGGL((proj8_kernel<kT, false, true>), grid, block, 0, stream, src, n_frames, hidden, w, bias, y, up);
+    } else {
+        if (bias)
+            hipLaunchKernelGGL((proj8_kernel<kT, true, false>), grid, block, 0, stream, src, n_frames, hidden, w, bias, y, up);
+        else
+            hipLaunchKernelGGL((proj8_kernel<kT, false, false>), grid, block, 0, stream, src, n_frames, hidden, w, bias, y, up);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cosine_units(const float *books, int n_stages, int n_codes, double *units, hipStream_t stream)
+{
+    const int64_t rows = static_cast<int64_t>(n_stages) * n_codes;
+    const int64_t blocks = (rows + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(units_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, books, rows, units);
+    return hipGetLastError();
+}
+
+hipError_t launch_proj8(const float *src, const int32_t *prev_codes, int codes_ld, const float *prev_table,
+                        int n_codes, float *dst, int64_t n_frames, int hidden, const float *w, const float *bias,
+                        float *y, hipStream_t stream)
+{
+    const Update8 up = {prev_codes, codes_ld, prev_table, n_codes, dst};
+    const bool update = prev_codes != nullptr;
+    const int t = (hidden + 255) / 256;
+    switch (t) {
+    case 1: return launch_proj8_t<1>(src, n_frames, hidden, w, bias, y, up, update, stream);
+    case 2: return launch_proj8_t<2>(src, n_frames, hidden, w, bias, y, up, update, stream);
+    case 3: return launch_proj8_t<3>(src, n_frames, hidden, w, bias, y, up, update, stream);
+    case 4: return launch_proj8_t<4>(src, n_frames, hidden, w, bias, y, up, update, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_cosine_argmin(const float *lat, int64_t n_frames, const double *units, int n_codes,
+                                int32_t *codes, int codes_ld, hipStream_t stream)
+{
+    const int64_t blocks = (n_frames + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(cosine_argmin_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream, lat,
+                       n_frames, units, n_codes, codes, codes_ld);
+    return hipGetLastError();
+}
+
+}  // namespace rvq

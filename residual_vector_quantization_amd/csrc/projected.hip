@@ -11,8 +11,9 @@
 //
 // The out-projection depends only on (q, k), so it is tabulated once per set
 // of weights: P[q,k,:] = W_out[q] C[q,k] + b_out[q] (K x hidden floats per
-// stage, 4 MiB at K = hidden = 1024), every entry a float64 sum over the 64
-// codeword dims in ascending order with the bias added last, rounded once --
+// stage, 4 MiB at K = hidden = 1024), every entry a float64 sum over the
+// codeword dims (64, or 8 for the normalized quantizer of cosine.hip) in
+// ascending order with the bias added last, rounded once --
 // the value a per-frame evaluation in that precision gives. The residual
 // update and the decode are then gathers of table rows with no matrix work
 // per frame: r <- fl32(r - P[q,k]) and out <- fl32(out + P[q,k]) from +0.
@@ -38,18 +39,19 @@ constexpr int kTableRows = 16;    // codewords per workgroup step
 constexpr int kRowFrames = 4;     // frames per workgroup in the row kernels (one per wavefront)
 
 // table[k, i] = fl32(sum_j C[k, j] W_out[i, j] (float64, j ascending) + b_out[i])
-// for one stage; grid-strides over blocks of kTableRows codewords.
+// for one stage, codeword dim kD; grid-strides over blocks of kTableRows codewords.
+template <int kD>
 __global__ __launch_bounds__(kTableCols)
 void table_kernel(const float *__restrict__ book, const float *__restrict__ w_out,
                   const float *__restrict__ b_out, int n_codes, int hidden, float *__restrict__ table)
 {
-    __shared__ float s_c[kTableRows * kDim];
+    __shared__ float s_c[kTableRows * kD];
     const int i = blockIdx.x * kTableCols + threadIdx.x;
     const bool active = i < hidden;
-    float w[kDim];
-    const float *wi = w_out + static_cast<int64_t>(active ? i : 0) * kDim;
+    float w[kD];
+    const float *wi = w_out + static_cast<int64_t>(active ? i : 0) * kD;
 #pragma unroll
-    for (int t = 0; t < kDim / 4; ++t) {
+    for (int t = 0; t < kD / 4; ++t) {
         const f32x4 v = *reinterpret_cast<const f32x4 *>(wi + 4 * t);
         w[4 * t] = v[0];
         w[4 * t + 1] = v[1];
@@ -61,15 +63,15 @@ void table_kernel(const float *__restrict__ book, const float *__restrict__ w_ou
     for (int k0 = blockIdx.y * kTableRows; k0 < n_codes; k0 += gridDim.y * kTableRows) {
         const int kn = min(kTableRows, n_codes - k0);
         __syncthreads();   // the previous block of rows is no longer read
-        for (int t = threadIdx.x; t < kn * kDim; t += kTableCols)
-            s_c[t] = book[static_cast<int64_t>(k0) * kDim + t];
+        for (int t = threadIdx.x; t < kn * kD; t += kTableCols)
+            s_c[t] = book[static_cast<int64_t>(k0) * kD + t];
         __syncthreads();
         if (!active) continue;
         for (int r = 0; r < kn; ++r) {
             double s = 0.0;
 #pragma unroll
-            for (int j = 0; j < kDim; ++j)
-                s = __dadd_rn(s, __dmul_rn(static_cast<double>(s_c[r * kDim + j]), static_cast<double>(w[j])));
+            for (int j = 0; j < kD; ++j)
+                s = __dadd_rn(s, __dmul_rn(static_cast<double>(s_c[r * kD + j]), static_cast<double>(w[j])));
             if (b_out) s = __dadd_rn(s, bias);
             table[static_cast<int64_t>(k0 + r) * hidden + i] = static_cast<float>(s);
         }
@@ -142,17 +144,23 @@ void projected_decode_kernel(const int32_t *__restrict__ codes, int codes_ld, in
 
 }  // namespace
 
-hipError_t launch_projected_table(const float *books, int n_stages, int n_codes, const float *w_out,
+hipError_t launch_projected_table(const float *books, int n_stages, int n_codes, int dim, const float *w_out,
                                   const float *b_out, int hidden, float *table, hipStream_t stream)
 {
+    if (dim != 8 && dim != kDim) return hipErrorInvalidValue;
     const unsigned gx = static_cast<unsigned>((hidden + kTableCols - 1) / kTableCols);
     const unsigned gy = static_cast<unsigned>(min((n_codes + kTableRows - 1) / kTableRows, 4096));
     for (int q = 0; q < n_stages; ++q) {
-        hipLaunchKernelGGL(table_kernel, dim3(gx, gy), dim3(kTableCols), 0, stream,
-                           books + static_cast<int64_t>(q) * n_codes * kDim,
-                           w_out + static_cast<int64_t>(q) * hidden * kDim,
-                           b_out ? b_out + static_cast<int64_t>(q) * hidden : nullptr, n_codes, hidden,
-                           table + static_cast<int64_t>(q) * n_codes * hidden);
+        const float *bq = books + static_cast<int64_t>(q) * n_codes * dim;
+        const float *wq = w_out + static_cast<int64_t>(q) * hidden * dim;
+        const float *biq = b_out ? b_out + static_cast<int64_t>(q) * hidden : nullptr;
+        float *tq = table + static_cast<int64_t>(q) * n_codes * hidden;
+        if (dim == 8)
+            hipLaunchKernelGGL(table_kernel<8>, dim3(gx, gy), dim3(kTableCols), 0, stream, bq, wq, biq, n_codes,
+                               hidden, tq);
+        else
+            hipLaunchKernelGGL(table_kernel<kDim>, dim3(gx, gy), dim3(kTableCols), 0, stream, bq, wq, biq, n_codes,
+                               hidden, tq);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

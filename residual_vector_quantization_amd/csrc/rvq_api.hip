@@ -11,6 +11,8 @@
 namespace {
 
 constexpr int32_t kMaxStages = 65536;
+constexpr int32_t kCosineDim = 8;          // codebook dim of the normalized quantizer
+constexpr int32_t kCosineMaxHidden = 1024;
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -178,14 +180,15 @@ RVQ_API rvq_status rvq_projected_prepare(const float *codebooks, int32_t n_stage
                                          int32_t dim, const float *w_out, const float *b_out,
                                          int32_t hidden, float *table, void *stream)
 {
-    const rvq_status st = check_shape(0, dim, n_stages, n_codes);
+    // codeword dim 64 (per-stage projected RVQ) or 8 (normalized quantizer)
+    const rvq_status st = check_shape(0, dim == kCosineDim ? rvq::kDim : dim, n_stages, n_codes);
     if (st != RVQ_OK) return st;
     if (hidden <= 0) return RVQ_ERR_INVALID_ARG;
     if (hidden % 64 != 0) return RVQ_ERR_UNSUPPORTED;
     if (!codebooks || !w_out || !table) return RVQ_ERR_INVALID_ARG;
     if (!aligned(codebooks, 16) || !aligned(w_out, 16) || !aligned(table, 16) || (b_out && !aligned(b_out, 16)))
         return RVQ_ERR_INVALID_ARG;
-    return from_hip(rvq::launch_projected_table(codebooks, n_stages, n_codes, w_out, b_out, hidden, table,
+    return from_hip(rvq::launch_projected_table(codebooks, n_stages, n_codes, dim, w_out, b_out, hidden, table,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -245,6 +248,55 @@ RVQ_API rvq_status rvq_projected_decode(const int32_t *codes, int32_t codes_ld, 
     if (!aligned(codes, 4) || !aligned(table, 16) || !aligned(out, 16)) return RVQ_ERR_INVALID_ARG;
     return from_hip(rvq::launch_projected_decode(codes, codes_ld, n_frames, table, n_stages, n_codes, hidden,
                                                  out, static_cast<hipStream_t>(stream)));
+}
+
+RVQ_API rvq_status rvq_cosine_prepare(const float *codebooks, int32_t n_stages, int32_t n_codes, int32_t dim,
+                                      double *units, void *stream)
+{
+    const rvq_status st = check_shape(0, rvq::kDim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (dim <= 0) return RVQ_ERR_INVALID_ARG;
+    if (dim != kCosineDim) return RVQ_ERR_UNSUPPORTED;
+    if (!codebooks || !units || !aligned(codebooks, 16) || !aligned(units, 16)) return RVQ_ERR_INVALID_ARG;
+    return from_hip(rvq::launch_cosine_units(codebooks, n_stages, n_codes, units, static_cast<hipStream_t>(stream)));
+}
+
+RVQ_API rvq_status rvq_cosine_encode(const float *h, int64_t n_frames, int32_t hidden,
+                                     const float *w_in, const float *b_in,
+                                     const double *units, const float *table,
+                                     int32_t n_stages, int32_t n_codes, int32_t dim,
+                                     int32_t *codes, int32_t codes_ld,
+                                     float *latent, float *residual, void *stream)
+{
+    const rvq_status st = check_shape(n_frames, rvq::kDim, n_stages, n_codes);
+    if (st != RVQ_OK) return st;
+    if (dim <= 0 || hidden <= 0 || codes_ld < n_stages) return RVQ_ERR_INVALID_ARG;
+    if (dim != kCosineDim || hidden % 64 != 0 || hidden > kCosineMaxHidden) return RVQ_ERR_UNSUPPORTED;
+    if (n_frames == 0) return RVQ_OK;
+    if (!h || !w_in || !units || !table || !codes || !latent || !residual) return RVQ_ERR_INVALID_ARG;
+    if (!aligned(h, 16) || !aligned(w_in, 16) || !aligned(units, 16) || !aligned(table, 16) ||
+        !aligned(codes, 4) || !aligned(latent, 16) || !aligned(residual, 16) || (b_in && !aligned(b_in, 16)))
+        return RVQ_ERR_INVALID_ARG;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    const int64_t table_stage = static_cast<int64_t>(n_codes) * hidden;
+    for (int32_t q = 0; q < n_stages && e == hipSuccess; ++q) {
+        float *lat = latent + static_cast<int64_t>(q) * n_frames * kCosineDim;
+        const float *wq = w_in + static_cast<int64_t>(q) * kCosineDim * hidden;
+        const float *bq = b_in ? b_in + static_cast<int64_t>(q) * kCosineDim : nullptr;
+        if (q == 0)
+            e = rvq::launch_proj8(h, nullptr, codes_ld, nullptr, n_codes, nullptr, n_frames, hidden, wq, bq, lat, s);
+        else
+            e = rvq::launch_proj8(q == 1 ? h : residual, codes + (q - 1), codes_ld, table + (q - 1) * table_stage,
+                                  n_codes, residual, n_frames, hidden, wq, bq, lat, s);
+        if (e == hipSuccess)
+            e = rvq::launch_cosine_argmin(lat, n_frames, units + static_cast<int64_t>(q) * n_codes * kCosineDim,
+                                          n_codes, codes + q, codes_ld, s);
+    }
+    if (e == hipSuccess)
+        e = rvq::launch_projected_update(n_stages == 1 ? h : residual, codes + (n_stages - 1), codes_ld, n_frames,
+                                         table + (n_stages - 1) * table_stage, n_codes, hidden, residual, s);
+    return from_hip(e);
 }
 
 }  // extern "C"

@@ -66,8 +66,9 @@ hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const
 
 // Per-stage projected RVQ (projected.hip). Table of projected codewords
 // P[q, k, :] = W_out[q] C[q, k] + b_out[q] (float64 sums, rounded once);
-// w_out [Q, hidden, 64], b_out [Q, hidden] (nullable), table [Q, K, hidden].
-hipError_t launch_projected_table(const float *books, int n_stages, int n_codes, const float *w_out,
+// w_out [Q, hidden, dim], b_out [Q, hidden] (nullable), table [Q, K, hidden];
+// dim 64 or 8.
+hipError_t launch_projected_table(const float *books, int n_stages, int n_codes, int dim, const float *w_out,
                                   const float *b_out, int hidden, float *table, hipStream_t stream);
 
 // dst[n] = src[n] - table[codes[n * ld]] for one stage (src may be dst).
@@ -77,5 +78,19 @@ hipError_t launch_projected_update(const float *src, const int32_t *codes, int c
 // out[n] = sum_q table[q, codes[n, q]], float32 from +0, stage 0 first.
 hipError_t launch_projected_decode(const int32_t *codes, int codes_ld, int64_t n_frames, const float *table,
                                    int n_stages, int n_codes, int hidden, float *out, hipStream_t stream);
+
+// Normalized (cosine) quantizer, codebook dim 8 (cosine.hip).
+// units[q, k, :] = C[q, k] / max(|C[q, k]|, 1e-12) in float64.
+hipError_t launch_cosine_units(const float *books, int n_stages, int n_codes, double *units, hipStream_t stream);
+
+// y[N, 8] = W r + bias with W [8, hidden], hidden <= 1024; with prev_codes
+// set, r = fl32(src - prev_table[prev_codes[n * ld]]) is also stored to dst.
+hipError_t launch_proj8(const float *src, const int32_t *prev_codes, int codes_ld, const float *prev_table,
+                        int n_codes, float *dst, int64_t n_frames, int hidden, const float *w, const float *bias,
+                        float *y, hipStream_t stream);
+
+// codes[n * ld] = argmin_k |u_n - units[k]|^2 with u_n = lat[n] / max(|lat[n]|, 1e-12), exact.
+hipError_t launch_cosine_argmin(const float *lat, int64_t n_frames, const double *units, int n_codes,
+                                int32_t *codes, int codes_ld, hipStream_t stream);
 
 }  // namespace rvq

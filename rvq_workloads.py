@@ -34,6 +34,9 @@ Readings of the recipe that the pages leave open:
   every codebook, both with bias) use the same 1/fan_in variances; the
   pages give no values for their biases, so they are drawn small,
   N(0, 0.05^2), to exercise the bias path.
+* The normalized quantizer ("Maintainer's guide -- moss-tts.cpp": 32
+  codebooks at 12.5 Hz, 1024 entries each behind 1025-wide heads, 8-dim
+  codebook space) takes a 1024-wide input here; the page does not state it.
 * Frames built as "sums of random codewords plus noise" are summed in
   float64 and rounded once to float32. That is input synthesis, done at a
   higher precision than the method's own float32 arithmetic.
@@ -73,6 +76,7 @@ class Workload:
     frame_rate_hz: float   # for seconds-of-audio figures
     hidden: int = 0        # >0: projected workload with fc hidden->dim and fc2 dim->hidden
     per_stage: bool = False  # projections per codebook (project_in / project_out) instead of fc / fc2
+    normalized: bool = False  # argmin between unit-norm projection and unit-norm codewords
     seed: int = 0
     description: str = ""
 
@@ -81,7 +85,7 @@ class Workload:
         return self.hidden > 0 and not self.per_stage
 
 
-# The seven workloads. Sizes and recipes as the codec shapes dictate; the
+# The eight workloads. Sizes and recipes as the codec shapes dictate; the
 # description strings state them for result lines.
 WORKLOADS = {
     "tiny": Workload(
@@ -117,6 +121,13 @@ WORKLOADS = {
                     "project_in W_in[q] [64,1024] ~ N(0, var 1/1024), b_in[q] ~ N(0, 0.05^2); "
                     "C[q] [1024,64] ~ N(0,1)*0.5^q; project_out W_out[q] [1024,64] ~ N(0, var 1/64), "
                     "b_out[q] ~ N(0, 0.05^2); seed 0"),
+    "cosine": Workload(
+        "cosine", 180_000, 32, 1024, 8, 0.85, 180_000, 0.0, 12.5, hidden=1024, per_stage=True, normalized=True,
+        description="16 clips x 11250 frames (4 h at 12.5 Hz) = 180000 hidden vectors [N,1024] ~ N(0,1) "
+                    "(input width assumed); per stage q < 32: project_in W_in[q] [8,1024] ~ N(0, var 1/1024), "
+                    "b_in[q] ~ N(0, 0.05^2); C[q] [1024,8] ~ N(0,1)*0.85^q; project_out W_out[q] [1024,8] "
+                    "~ N(0, var 1/8), b_out[q] ~ N(0, 0.05^2); argmin on unit-norm projection and codewords; "
+                    "seed 0"),
 }
 
 

@@ -78,6 +78,23 @@ int main(void)
     bad += expect("projected decode hidden 0", rvq_projected_decode(ic, 8, 10, fx, 8, 1024, 0, fx, NULL),
                   RVQ_ERR_INVALID_ARG);
     bad += expect("projected decode empty", rvq_projected_decode(NULL, 8, 0, NULL, 8, 1024, 1024, NULL, NULL), RVQ_OK);
+    {
+        double *ud = (double *)0x3000;
+        bad += expect("cosine prepare dim 64", rvq_cosine_prepare(fx, 32, 1024, 64, ud, NULL), RVQ_ERR_UNSUPPORTED);
+        bad += expect("cosine prepare null", rvq_cosine_prepare(fx, 32, 1024, 8, NULL, NULL), RVQ_ERR_INVALID_ARG);
+        bad += expect("cosine encode hidden 2048", rvq_cosine_encode(fx, 10, 2048, fx, NULL, ud, fx, 32, 1024, 8,
+                                                                     ic, 32, fx, fx, NULL), RVQ_ERR_UNSUPPORTED);
+        bad += expect("cosine encode dim 64", rvq_cosine_encode(fx, 10, 1024, fx, NULL, ud, fx, 32, 1024, 64,
+                                                                ic, 32, fx, fx, NULL), RVQ_ERR_UNSUPPORTED);
+        bad += expect("cosine encode null units", rvq_cosine_encode(fx, 10, 1024, fx, NULL, NULL, fx, 32, 1024, 8,
+                                                                    ic, 32, fx, fx, NULL), RVQ_ERR_INVALID_ARG);
+        bad += expect("cosine encode empty", rvq_cosine_encode(NULL, 0, 1024, NULL, NULL, NULL, NULL, 32, 1024, 8,
+                                                               NULL, 32, NULL, NULL, NULL), RVQ_OK);
+        bad += expect("projected prepare dim 8 hidden 96", rvq_projected_prepare(fx, 32, 1024, 8, fx, NULL, 96, fx, NULL),
+                      RVQ_ERR_UNSUPPORTED);
+        bad += expect("projected prepare dim 16", rvq_projected_prepare(fx, 32, 1024, 16, fx, NULL, 1024, fx, NULL),
+                      RVQ_ERR_UNSUPPORTED);
+    }
     printf("%s\n", bad ? "abi_c99: FAILED" : "abi_c99: ok");
     return bad ? 1 : 0;
 }
