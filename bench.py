@@ -376,6 +376,7 @@ def bench_stage_projected(args, w):
          dict(h=h, w_in=w_in, b_in=b_in, w_out=w_out, b_out=b_out, books=books).items()}
     n, q, k, d, hid = w.n_frames, w.n_stages, w.n_codes, w.dim, w.hidden
     table = torch.empty((q, k, hid), device=dev)
+    units = torch.empty((q, k, d), dtype=torch.float64, device=dev) if w.normalized else None
     out = (torch.empty((n, q), dtype=torch.int32, device=dev), torch.empty((q, n, d), device=dev),
            torch.empty((n, hid), device=dev))
     recon = torch.empty((n, hid), device=dev)
@@ -384,9 +385,14 @@ def bench_stage_projected(args, w):
         if ev is not None:
             ev[0].record()
         rvq.rvq_projected_prepare(t["books"], t["w_out"], t["b_out"], table)
+        if w.normalized:
+            rvq.rvq_cosine_prepare(t["books"], units)
         if ev is not None:
             ev[1].record()
-        rvq.rvq_projected_encode(t["h"], t["w_in"], t["b_in"], t["books"], table, out=out)
+        if w.normalized:
+            rvq.rvq_cosine_encode(t["h"], t["w_in"], t["b_in"], units, table, out=out)
+        else:
+            rvq.rvq_projected_encode(t["h"], t["w_in"], t["b_in"], t["books"], table, out=out)
         if ev is not None:
             ev[2].record()
         rvq.rvq_projected_decode(out[0], table, out=recon)
@@ -407,7 +413,10 @@ def bench_stage_projected(args, w):
     # HBM per frame and stage: residual read + write and one gathered table row (H floats each)
     proj_flop = 2.0 * q * hid * d * n
     score_flop = 2.0 * q * k * d * n
-    rec = {"metric": "RVQ per-stage projected encode + decode frames/sec (H=1024, Q=8, K=1024, D=64; fp32)",
+    metric = (f"RVQ normalized (cosine) per-stage projected encode + decode frames/sec (H={hid}, Q={q}, K={k}, "
+              f"D={d}; fp32)" if w.normalized else
+              f"RVQ per-stage projected encode + decode frames/sec (H={hid}, Q={q}, K={k}, D={d}; fp32)")
+    rec = {"metric": metric,
            "value": n * args.steps / wall, "unit": "frames/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
@@ -423,11 +432,12 @@ def bench_stage_projected(args, w):
         o = oracle.get()
         probe = W.sample_frames(n, 256, seed=7)
         t1 = time.perf_counter()
-        o.projected_encode(h[probe], w_in, b_in, books, w_out, b_out)
+        o.projected_encode(h[probe], w_in, b_in, books, w_out, b_out, normalize=w.normalized)
         rate = probe.size / max(time.perf_counter() - t1, 1e-6)
         idx = W.sample_frames(n, int(min(n, max(probe.size, rate * args.cpu_seconds))), seed=8)
         t1 = time.perf_counter()
-        oc, _, _, best, second = o.projected_encode(h[idx], w_in, b_in, books, w_out, b_out)
+        oc, _, _, best, second = o.projected_encode(h[idx], w_in, b_in, books, w_out, b_out,
+                                                    normalize=w.normalized)
         o.projected_decode(oc, books, w_out, b_out)
         dt = time.perf_counter() - t1
         mism = (codes_h[idx] != oc).any(axis=1)
@@ -439,7 +449,8 @@ def bench_stage_projected(args, w):
         rec["cpu_baseline"] = {"value": idx.size / dt, "unit": "frames/s", "cores": int(o.last_threads),
                                "kind": "oracle",
                                "sample": f"{idx.size} of {n} frames (seeded uniform sample incl. first/last 64), "
-                                         f"projected encode + decode, {dt:.1f} s wall"}
+                                         f"{'normalized ' if w.normalized else ''}projected encode + decode, "
+                                         f"{dt:.1f} s wall"}
         rec["parity_sample"] = {"frames_checked": int(idx.size), "code_mismatch_frames": int(mism.sum()),
                                 "mismatch_first_stage_near_tie": exempt,
                                 "near_tie_frames_in_sample": int(ties.any(axis=1).sum()),

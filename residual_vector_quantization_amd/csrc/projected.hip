@@ -142,6 +142,68 @@ void projected_decode_kernel(const int32_t *__restrict__ codes, int codes_ld, in
     }
 }
 
+// Stage-ordered decode for tables larger than an XCD's L2: each wavefront
+// owns kF frames with their hidden-width accumulators in VGPRs (hidden <=
+// 1024) and adds stage q's rows for all of them before stage q+1, so the
+// resident wavefronts sweep the stages together and gather from one or two
+// stage tables at a time (4 MiB each at K = hidden = 1024) instead of the
+// whole table. Per element the sum is the same: +0, stage 0 first.
+constexpr int kTiledFrames = 4;
+constexpr int kTiledCols = 4;   // float4 columns per lane (hidden <= 1024)
+
+__global__ __launch_bounds__(64 * kRowFrames)
+void projected_decode_tiled_kernel(const int32_t *__restrict__ codes, int codes_ld, int64_t n_frames,
+                                   const float *__restrict__ table, int n_stages, int n_codes, int hidden,
+                                   float *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63;
+    const int cols = hidden >> 2;
+    const int64_t frame0 = (static_cast<int64_t>(blockIdx.x) * kRowFrames + (threadIdx.x >> 6)) * kTiledFrames;
+    const int64_t stage_floats = static_cast<int64_t>(n_codes) * hidden;
+    f32x4 acc[kTiledFrames][kTiledCols];
+#pragma unroll
+    for (int f = 0; f < kTiledFrames; ++f)
+#pragma unroll
+        for (int t = 0; t < kTiledCols; ++t) acc[f][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    unsigned bad = 0u;   // bit f: frame f has a code outside [0, n_codes)
+    for (int q = 0; q < n_stages; ++q) {
+        const float *tq = table + q * stage_floats;
+#pragma unroll
+        for (int f = 0; f < kTiledFrames; ++f) {
+            const int64_t fr = frame0 + f;
+            int k = fr < n_frames ? codes[fr * codes_ld + q] : 0;
+            const bool ok = static_cast<unsigned>(k) < static_cast<unsigned>(n_codes);
+            bad |= ok ? 0u : (1u << f);
+            k = ok ? k : 0;
+            const float *row = tq + static_cast<int64_t>(k) * hidden;
+#pragma unroll
+            for (int t = 0; t < kTiledCols; ++t) {
+                const int col = lane + 64 * t;
+                if (col < cols) {
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(row + 4 * col);
+                    acc[f][t][0] = acc[f][t][0] + v[0];
+                    acc[f][t][1] = acc[f][t][1] + v[1];
+                    acc[f][t][2] = acc[f][t][2] + v[2];
+                    acc[f][t][3] = acc[f][t][3] + v[3];
+                }
+            }
+        }
+    }
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int f = 0; f < kTiledFrames; ++f) {
+        const int64_t fr = frame0 + f;
+        if (fr >= n_frames) continue;
+        float *o = out + fr * hidden;
+#pragma unroll
+        for (int t = 0; t < kTiledCols; ++t) {
+            const int col = lane + 64 * t;
+            if (col < cols)
+                *reinterpret_cast<f32x4 *>(o + 4 * col) = ((bad >> f) & 1u) ? f32x4{nan, nan, nan, nan} : acc[f][t];
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_projected_table(const float *books, int n_stages, int n_codes, int dim, const float *w_out,
@@ -180,6 +242,15 @@ hipError_t launch_projected_update(const float *src, const int32_t *codes, int c
 hipError_t launch_projected_decode(const int32_t *codes, int codes_ld, int64_t n_frames, const float *table,
                                    int n_stages, int n_codes, int hidden, float *out, hipStream_t stream)
 {
+    const int64_t table_bytes = static_cast<int64_t>(n_stages) * n_codes * hidden * sizeof(float);
+    if (table_bytes >= kDecodeTiledMinBookBytes && hidden <= 256 * kTiledCols) {
+        const int64_t per_block = static_cast<int64_t>(kRowFrames) * kTiledFrames;
+        const int64_t tb = (n_frames + per_block - 1) / per_block;
+        if (tb > 0x7fffffff) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(projected_decode_tiled_kernel, dim3(static_cast<unsigned>(tb)), dim3(64 * kRowFrames), 0,
+                           stream, codes, codes_ld, n_frames, table, n_stages, n_codes, hidden, out);
+        return hipGetLastError();
+    }
     const int64_t blocks = (n_frames + kRowFrames - 1) / kRowFrames;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(projected_decode_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64 * kRowFrames), 0,

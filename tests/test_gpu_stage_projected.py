@@ -127,17 +127,23 @@ def test_stage_projected_identity_is_plain_rvq():
     np.testing.assert_array_equal(host(m.rvq_projected_decode(codes, table)), host(m.rvq_decode(codes, bg)))
 
 
-def test_stage_projected_decode_bad_codes():
-    rng = np.random.default_rng(43)
-    books, _, _, w_out, b_out = _weights(rng, 3, 128, 192, True)
+# tables of 4 MiB and more (with hidden <= 1024) take the stage-ordered decode
+@pytest.mark.parametrize("n,hidden,q,k", [(40, 192, 3, 128), (41, 1024, 4, 1024), (203, 448, 9, 300),
+                                          (37, 1280, 2, 1024)])
+def test_stage_projected_decode_bad_codes(n, hidden, q, k):
+    rng = np.random.default_rng(43 + n)
+    books, _, _, w_out, b_out = _weights(rng, q, k, hidden, True)
     m = rvq()
+    announce("projected decode", n=n, hidden=hidden, q=q, k=k)
     table = m.rvq_projected_prepare(to_dev(books), to_dev(w_out), to_dev(b_out))
-    codes = W.random_codes(40, 3, 128, seed=5)
-    codes[4, 1] = 128
-    codes[9, 2] = -1
+    codes = W.random_codes(n, q, k, seed=5)
+    codes[4, 1] = k
+    codes[9, q - 1] = -1
+    codes[n - 1, 0] = k + 7
+    bad = [4, 9, n - 1]
     out = host(m.rvq_projected_decode(to_dev(codes), table))
-    assert np.isnan(out[[4, 9]]).all()
-    good = np.setdiff1d(np.arange(40), [4, 9])
+    assert np.isnan(out[bad]).all()
+    good = np.setdiff1d(np.arange(n), bad)
     np.testing.assert_array_equal(out[good], oracle.get().projected_decode(codes[good], books, w_out, b_out))
 
 
