@@ -36,12 +36,16 @@ static_assert(kWaves * kFramesPerWave == kLinearFramesPerBlock, "frames per bloc
 
 // ---- linear_in: [N, hidden] x [64, hidden]^T -> [N, 64] -------------------
 
-// The residual update of the previous stage of a per-stage projected
-// quantizer can ride along (kUpdate): each lane subtracts the table row of
-// its frame's previous code from the hidden-width chunk it loads,
-// r <- fl32(r - P[code]), stores the result to `dst` (which may be `h`
-// itself: every element is loaded, then stored, by the same lane) and feeds
-// it to the matrix cores. A code outside [0, n_codes) makes the row NaN.
+// Each wavefront loads its 32 frames chunk by chunk (64 columns) with
+// coalesced 1 KiB row loads into a padded LDS tile, and reads the tile back
+// in the matrix-core operand layout (lane (col, half): frame col, columns
+// 32 half .. 32 half + 31 of the chunk). The residual update of the
+// previous stage of a per-stage projected quantizer can ride along
+// (kUpdate): the table row of each frame's previous code is subtracted
+// from the loaded chunk, r <- fl32(r - P[code]), and the result is stored
+// to `dst` (which may be `h` itself: every element is loaded, then stored,
+// by the same lane) and used as the operand. A code outside [0, n_codes)
+// makes the row NaN.
 struct Update {
     const int32_t *codes;   // previous stage's column; row n at codes[n * ld]
     int ld;
@@ -58,25 +62,37 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
 {
     // one chunk = 64 weight rows (all outputs) x 64 columns of the hidden dim
     __shared__ __align__(16) float s_w[2][kDim * kRow];
+    // per wavefront: its 32 frames x 64 columns of the current chunk
+    __shared__ __align__(16) float s_h[kWaves][kFramesPerWave * kRow];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kLinearFramesPerBlock +
-                          wave * kFramesPerWave + col;
+    const int64_t frame0 = static_cast<int64_t>(blockIdx.x) * kLinearFramesPerBlock + wave * kFramesPerWave;
+    const int64_t frame = frame0 + col;
     const bool valid = frame < n_frames;
-    const float *hrow = h + (valid ? frame : 0) * static_cast<int64_t>(hidden) + 32 * half;
-    const float *prow = nullptr;   // previous code's table row (kUpdate)
-    float *drow = nullptr;
-    bool code_ok = true;
-    if (kUpdate) {
-        int k = up.codes[(valid ? frame : 0) * up.ld];
-        code_ok = static_cast<unsigned>(k) < static_cast<unsigned>(up.n_codes);
-        k = code_ok ? k : 0;
-        prow = up.table + static_cast<int64_t>(k) * hidden + 32 * half;
-        drow = up.dst + (valid ? frame : 0) * static_cast<int64_t>(hidden) + 32 * half;
+
+    // Tile loads are coalesced: load i covers frames 4i .. 4i+3 of the
+    // wavefront, 16 lanes per frame, one float4 each (a 256 B row chunk).
+    const int trow = lane >> 4;
+    const int tc4 = lane & 15;
+    int64_t roff[8];     // element offset of this lane's row in h / dst
+    bool rvalid[8];
+    const float *prow[8];   // kUpdate: table row of the frame's previous code
+    unsigned bad = 0u;      // kUpdate: bit i: frame 4i + trow has a code outside [0, n_codes)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t fr = frame0 + 4 * i + trow;
+        rvalid[i] = fr < n_frames;
+        roff[i] = (rvalid[i] ? fr : 0) * static_cast<int64_t>(hidden) + 4 * tc4;
+        if (kUpdate) {
+            int k = up.codes[(rvalid[i] ? fr : 0) * up.ld];
+            const bool ok = static_cast<unsigned>(k) < static_cast<unsigned>(up.n_codes);
+            bad |= ok ? 0u : (1u << i);
+            prow[i] = up.table + static_cast<int64_t>(ok ? k : 0) * hidden + 4 * tc4;
+        }
     }
 
     // staging: wavefront w stages weight rows 16w..16w+15; lane -> (row, 16-column quarter)
@@ -85,7 +101,7 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
     const int n_chunks = hidden / 64;
 
     f32x4 ws[4];
-    f32x4 hv[8];
+    f32x4 hv[8], pv[8];
     auto fetch_w = [&](int c) {
         const f32x4 *p = reinterpret_cast<const f32x4 *>(w + static_cast<int64_t>(srow) * hidden + 64 * c + scol);
 #pragma unroll
@@ -96,29 +112,11 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(dst + 4 * i) = ws[i];
     };
-    f32x4 pv[8];
     auto fetch_h = [&](int c) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(hrow + 64 * c);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hv[i] = p[i];
-        if (kUpdate) {
-            const f32x4 *t = reinterpret_cast<const f32x4 *>(prow + 64 * c);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) pv[i] = t[i];
-        }
-    };
-    // r - P[code] for the chunk in hv/pv, stored to dst and kept for the product
-    auto update_h = [&](int c, f32x4 (&cur)[8]) {
-        const float nan = __builtin_nanf("");
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) cur[i][e] = code_ok ? hv[i][e] - pv[i][e] : nan;
-        }
-        if (valid) {
-            f32x4 *d = reinterpret_cast<f32x4 *>(drow + 64 * c);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) d[i] = cur[i];
+            hv[i] = *reinterpret_cast<const f32x4 *>(h + roff[i] + 64 * c);
+            if (kUpdate) pv[i] = *reinterpret_cast<const f32x4 *>(prow[i] + 64 * c);
         }
     };
 
@@ -133,15 +131,28 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
     fetch_h(0);
     __syncthreads();
 
+    float *tile = s_h[wave];
+    const float nan = __builtin_nanf("");
     for (int c = 0; c < n_chunks; ++c) {
         const int buf = c & 1;
-        f32x4 cur[8];
-        if (kUpdate) {
-            update_h(c, cur);
-        } else {
+        // this chunk's rows (updated: r - P[code], stored back) into the wavefront's tile
 #pragma unroll
-            for (int i = 0; i < 8; ++i) cur[i] = hv[i];
+        for (int i = 0; i < 8; ++i) {
+            f32x4 r = hv[i];
+            if (kUpdate) {
+                const bool ok = !((bad >> i) & 1u);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[e] = ok ? r[e] - pv[i][e] : nan;
+                if (rvalid[i]) *reinterpret_cast<f32x4 *>(up.dst + roff[i] + 64 * c) = r;
+            }
+            *reinterpret_cast<f32x4 *>(&tile[(4 * i + trow) * kRow + 4 * tc4]) = r;
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        f32x4 cur[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) cur[t] = *reinterpret_cast<const f32x4 *>(&tile[col * kRow + 32 * half + 4 * t]);
         if (c + 1 < n_chunks) {
             fetch_w(c + 1);
             fetch_h(c + 1);
@@ -160,6 +171,7 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
                     acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[b][e], cur[t][e], acc[b], 0, 0, 0);
         }
         if (c + 1 < n_chunks) commit_w(buf ^ 1);
+        // every lane has read the tile (and the weight buffer) before they are overwritten
         __syncthreads();
     }
 
