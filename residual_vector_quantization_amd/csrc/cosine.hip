@@ -67,41 +67,54 @@ struct Update8 {
 };
 
 // y[n, 0..7] = W r_n + bias, W [8, hidden]; one wavefront per frame with
-// lanes over float4 columns of the row (fully coalesced), W held in VGPRs
-// (kT float4 columns per lane, hidden <= 256 kT), partial sums reduced by a
-// butterfly that halves the number of outputs each lane carries. With
-// kUpdate the previous stage's residual update is applied first:
-// r = fl32(src - table[code]) is stored to up.dst (which may be src) and
-// projected. Waves stride over the frames, so W is read once per wave.
+// lanes over float4 columns of the row (fully coalesced 1 KiB loads). W is
+// staged once per workgroup in LDS (32 KiB at hidden 1024) and read per
+// frame as contiguous 1 KiB rows (conflict-free), which keeps the kernel at
+// about 50 VGPRs so that many wavefronts hide the memory latency of the
+// residual rows. Partial sums are reduced by a butterfly that halves the
+// number of outputs each lane carries. With kUpdate the previous stage's
+// residual update is applied first: r = fl32(src - table[code]) is stored
+// to up.dst (which may be src) and projected. Waves stride over the frames.
+constexpr int kProjMaxHidden = 1024;
+
 template <int kT, bool kBias, bool kUpdate>
-__global__ __launch_bounds__(64 * kProjWaves)
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kProjWaves, 64 * kProjWaves),
+                          amdgpu_waves_per_eu(5)))   // 5 workgroups of 32 KiB LDS per CU
 void proj8_kernel(const float *src, int64_t n_frames, int hidden, const float *__restrict__ w,
                   const float *__restrict__ bias, float *__restrict__ y, Update8 up)
 {
+    // W rows at a fixed stride, zero past `hidden`, so a lane's 8 reads per
+    // column block differ only by immediate offsets and need no guard
+    __shared__ __align__(16) float s_w[kCosDim * kProjMaxHidden];
+    {
+        const int c4s = hidden >> 2;
+        for (int i = threadIdx.x; i < kCosDim * 64 * kT; i += 64 * kProjWaves) {
+            const int o = i / (64 * kT), c4 = i - o * (64 * kT);
+            *reinterpret_cast<f32x4 *>(&s_w[o * kProjMaxHidden + 4 * c4]) =
+                c4 < c4s ? reinterpret_cast<const f32x4 *>(w)[o * c4s + c4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+    __syncthreads();
+
     const int lane = threadIdx.x & 63;
     const int cols = hidden >> 2;   // float4 columns per row
-    f32x4 wr[kT][kCosDim];
-#pragma unroll
-    for (int t = 0; t < kT; ++t) {
-        const int col = lane + 64 * t;
-#pragma unroll
-        for (int o = 0; o < kCosDim; ++o)
-            wr[t][o] = col < cols ? *reinterpret_cast<const f32x4 *>(w + static_cast<int64_t>(o) * hidden + 4 * col)
-                                  : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
     const int out_id = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
     const float b_out = kBias ? bias[out_id] : 0.0f;
     const float nan = __builtin_nanf("");
+    // column of block t: lane + 64 t; past the row it reads the last column
+    // (always in bounds) and contributes 0
+    int ccol[kT];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) ccol[t] = min(lane + 64 * t, cols - 1);
 
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kProjWaves;
     for (int64_t n = static_cast<int64_t>(blockIdx.x) * kProjWaves + (threadIdx.x >> 6); n < n_frames; n += stride) {
+        // keeps the W reads inside the loop: hoisted, they would pin 32 kT VGPRs
+        asm volatile("" ::: "memory");
         const float *row = src + n * hidden;
         f32x4 r[kT];
 #pragma unroll
-        for (int t = 0; t < kT; ++t) {
-            const int col = lane + 64 * t;
-            r[t] = col < cols ? *reinterpret_cast<const f32x4 *>(row + 4 * col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+        for (int t = 0; t < kT; ++t) r[t] = *reinterpret_cast<const f32x4 *>(row + 4 * ccol[t]);
         if (kUpdate) {
             int k = up.codes[n * up.ld];
             const bool ok = static_cast<unsigned>(k) < static_cast<unsigned>(up.n_codes);
@@ -110,24 +123,33 @@ void proj8_kernel(const float *src, int64_t n_frames, int hidden, const float *_
             float *drow = up.dst + n * hidden;
 #pragma unroll
             for (int t = 0; t < kT; ++t) {
-                const int col = lane + 64 * t;
-                if (col < cols) {
-                    const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * col);
+                const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * ccol[t]);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) r[t][e] = ok ? r[t][e] - p[e] : nan;
-                    *reinterpret_cast<f32x4 *>(drow + 4 * col) = r[t];
-                }
+                for (int e = 0; e < 4; ++e) r[t][e] = ok ? r[t][e] - p[e] : nan;
+                if (lane + 64 * t < cols) *reinterpret_cast<f32x4 *>(drow + 4 * ccol[t]) = r[t];
             }
+        }
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            const bool in_row = lane + 64 * t < cols;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) r[t][e] = in_row ? r[t][e] : 0.0f;
         }
         float a[kCosDim];
 #pragma unroll
-        for (int o = 0; o < kCosDim; ++o) {
-            float s = 0.0f;
+        for (int o = 0; o < kCosDim; ++o) a[o] = 0.0f;
 #pragma unroll
-            for (int t = 0; t < kT; ++t)
+        for (int t = 0; t < kT; ++t) {
+            // one float4 column block at a time: 8 weight float4s live, not 8 kT
+            f32x4 wv[kCosDim];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) s = __builtin_fmaf(wr[t][o][e], r[t][e], s);
-            a[o] = s;
+            for (int o = 0; o < kCosDim; ++o)
+                wv[o] = *reinterpret_cast<const f32x4 *>(&s_w[o * kProjMaxHidden + 4 * (lane + 64 * t)]);
+#pragma unroll
+            for (int o = 0; o < kCosDim; ++o)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[o] = __builtin_fmaf(wv[o][e], r[t][e], a[o]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         // butterfly: after the xor-32, -16 and -8 steps lane l carries output out_id(l) only
         float b[4], c[2];
@@ -285,7 +307,7 @@ hipError_t launch_proj8_t(const float *src, int64_t n_frames, int hidden, const 
 {
     const int64_t waves = (n_frames + 7) / 8;   // about 8 frames per wavefront, capped below
     int64_t blocks = (waves + kProjWaves - 1) / kProjWaves;
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
     const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kProjWaves);
     if (update) {
