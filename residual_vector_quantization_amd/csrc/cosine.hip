@@ -301,6 +301,289 @@ void cosine_argmin_kernel(const float *__restrict__ lat, int64_t n_frames, const
     if (valid) codes[frame * codes_ld] = bk;
 }
 
+// ---- all stages in one kernel --------------------------------------------
+//
+// For codebooks of at most 1024 entries and hidden <= 1024 the whole loop
+// runs in one kernel: a workgroup of 8 wavefronts owns 32 frames, each
+// wavefront 4 of them with their hidden-width residual rows in VGPRs for all
+// stages, so the residual crosses HBM once in and once out instead of twice
+// per stage. Per stage the workgroup stages W_in[q] (fixed row stride, zero
+// padded) and the stage's unit codewords in fp32 with their half norms in
+// LDS; every LDS value is then used for the 4 frames of a wavefront. The
+// in-projection sums per lane and reduces over the wavefront; the 8
+// projections of a frame are wave-uniform; the scores of codewords
+// lane + 64 m are kept as per-lane best / second and reduced over the
+// wavefront as (best, index, second). The exactness rule and the float64
+// rescan are those of cosine_argmin_kernel; the residual update gathers the
+// table row of the pick (r <- fl32(r - P[q, k])).
+// The float held by lane `src` (a constant) on every lane; the readlane
+// builtin moves 32-bit integers, so the value travels as its bit pattern.
+__device__ __forceinline__ float lane_value(float v, int src)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
+}
+
+constexpr int kFusedWaves = 8;
+constexpr int kFusedFrames = 4;           // frames per wavefront
+constexpr int kFusedMaxCodes = 1024;
+
+template <int kT, bool kBias>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kFusedWaves, 64 * kFusedWaves)))
+void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidden,
+                         const float *__restrict__ w_in, const float *__restrict__ b_in,
+                         const double *__restrict__ units, const float *__restrict__ table,
+                         int n_stages, int n_codes, int32_t *__restrict__ codes, int codes_ld,
+                         float *__restrict__ latent, float *__restrict__ residual)
+{
+    __shared__ __align__(16) float s_w[kCosDim * kProjMaxHidden];
+    __shared__ __align__(16) float s_v[kFusedMaxCodes * kCosDim];
+    __shared__ __align__(16) float s_hn[kFusedMaxCodes];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t frame0 = (static_cast<int64_t>(blockIdx.x) * kFusedWaves + wave) * kFusedFrames;
+    const int cols = hidden >> 2;
+    int ccol[kT];
+    bool inrow[kT];
+#pragma unroll
+    for (int t = 0; t < kT; ++t) {
+        inrow[t] = lane + 64 * t < cols;
+        ccol[t] = min(lane + 64 * t, cols - 1);
+    }
+
+    f32x4 r[kFusedFrames][kT];
+#pragma unroll
+    for (int f = 0; f < kFusedFrames; ++f) {
+        const int64_t fr = frame0 + f;
+        const float *row = h + (fr < n_frames ? fr : 0) * hidden;
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + 4 * ccol[t]);
+            r[f][t] = inrow[t] ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    }
+    // lane of output j after the butterfly: bits 5, 4, 3 of the lane are bits 2, 1, 0 of j
+    const int out_id = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
+    const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8;
+
+    for (int q = 0; q < n_stages; ++q) {
+        __syncthreads();   // the previous stage's LDS contents are no longer read
+        {
+            const float *wq = w_in + static_cast<int64_t>(q) * kCosDim * hidden;
+            for (int i = threadIdx.x; i < kCosDim * 64 * kT; i += 64 * kFusedWaves) {
+                const int o = i / (64 * kT), c4 = i - o * (64 * kT);
+                *reinterpret_cast<f32x4 *>(&s_w[o * kProjMaxHidden + 4 * c4]) =
+                    c4 < cols ? reinterpret_cast<const f32x4 *>(wq)[o * cols + c4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+            const double *uq = units + static_cast<int64_t>(q) * n_codes * kCosDim;
+            for (int k = threadIdx.x; k < n_codes; k += 64 * kFusedWaves) {
+                float hn = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kCosDim; ++j) {
+                    const float vj = static_cast<float>(uq[static_cast<int64_t>(k) * kCosDim + j]);
+                    s_v[k * kCosDim + j] = vj;
+                    hn = __builtin_fmaf(vj, vj, hn);
+                }
+                s_hn[k] = 0.5f * hn;
+            }
+        }
+        __syncthreads();
+
+        // ---- in-projection of the wavefront's frames ----
+        float a[kFusedFrames][kCosDim];
+#pragma unroll
+        for (int f = 0; f < kFusedFrames; ++f)
+#pragma unroll
+            for (int o = 0; o < kCosDim; ++o) a[f][o] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kT; ++t) {
+            f32x4 wv[kCosDim];
+#pragma unroll
+            for (int o = 0; o < kCosDim; ++o)
+                wv[o] = *reinterpret_cast<const f32x4 *>(&s_w[o * kProjMaxHidden + 4 * (lane + 64 * t)]);
+#pragma unroll
+            for (int f = 0; f < kFusedFrames; ++f)
+#pragma unroll
+                for (int o = 0; o < kCosDim; ++o)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[f][o] = __builtin_fmaf(wv[o][e], r[f][t][e], a[f][o]);
+        }
+        float e_own[kFusedFrames];   // this lane's output out_id of each frame, bias added
+#pragma unroll
+        for (int f = 0; f < kFusedFrames; ++f) {
+            float b[4], c[2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float give = hi32 ? a[f][i] : a[f][i + 4];
+                b[i] = (hi32 ? a[f][i + 4] : a[f][i]) + __shfl_xor(give, 32);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const float give = hi16 ? b[i] : b[i + 2];
+                c[i] = (hi16 ? b[i + 2] : b[i]) + __shfl_xor(give, 16);
+            }
+            float d;
+            {
+                const float give = hi8 ? c[0] : c[1];
+                d = (hi8 ? c[1] : c[0]) + __shfl_xor(give, 8);
+            }
+            d += __shfl_xor(d, 4);
+            d += __shfl_xor(d, 2);
+            d += __shfl_xor(d, 1);
+            e_own[f] = kBias ? d + b_in[q * kCosDim + out_id] : d;
+        }
+
+        // ---- per frame: projection (uniform), normalization, scores ----
+        float nu[kFusedFrames][kCosDim];   // -u32, wave-uniform
+        bool norm_ok[kFusedFrames];
+#pragma unroll
+        for (int f = 0; f < kFusedFrames; ++f) {
+            float ev[kCosDim];
+#pragma unroll
+            for (int j = 0; j < kCosDim; ++j)
+                ev[j] = lane_value(e_own[f], 32 * ((j >> 2) & 1) + 16 * ((j >> 1) & 1) + 8 * (j & 1));
+            const int64_t fr = frame0 + f;
+            if (fr < n_frames && lane < kCosDim) {
+                float mine = ev[0];
+#pragma unroll
+                for (int j = 1; j < kCosDim; ++j) mine = lane == j ? ev[j] : mine;
+                latent[(static_cast<int64_t>(q) * n_frames + fr) * kCosDim + lane] = mine;
+            }
+            float ss = 0.0f;
+#pragma unroll
+            for (int j = 0; j < kCosDim; ++j) ss = __builtin_fmaf(ev[j], ev[j], ss);
+            norm_ok[f] = ss >= 1e-30f && ss <= 1e30f;
+            const float inv = 1.0f / fmaxf(__builtin_sqrtf(ss), 1e-12f);
+#pragma unroll
+            for (int j = 0; j < kCosDim; ++j) nu[f][j] = -(ev[j] * inv);
+        }
+        float best[kFusedFrames], second[kFusedFrames];
+        int bk[kFusedFrames];
+#pragma unroll
+        for (int f = 0; f < kFusedFrames; ++f) {
+            best[f] = INFINITY;
+            second[f] = INFINITY;
+            bk[f] = 0x7fffffff;
+        }
+        for (int k = lane; k < n_codes; k += 64) {   // ascending per lane: strict "<" keeps the lowest
+            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&s_v[k * kCosDim]);
+            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&s_v[k * kCosDim + 4]);
+            const float hn = s_hn[k];
+#pragma unroll
+            for (int f = 0; f < kFusedFrames; ++f) {
+                float s = hn;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s = __builtin_fmaf(nu[f][j], v0[j], s);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s = __builtin_fmaf(nu[f][j + 4], v1[j], s);
+                if (s < best[f]) {
+                    second[f] = best[f];
+                    best[f] = s;
+                    bk[f] = k;
+                } else if (s < second[f]) {
+                    second[f] = s;
+                }
+            }
+        }
+
+        // ---- per frame: wavefront argmin, exactness check, update ----
+#pragma unroll
+        for (int f = 0; f < kFusedFrames; ++f) {
+            float bv = best[f], sv = second[f];
+            int bi = bk[f];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ob = __shfl_xor(bv, off);
+                const float os = __shfl_xor(sv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (ob < bv || (ob == bv && oi < bi)) {
+                    sv = fminf(os, bv);
+                    bv = ob;
+                    bi = oi;
+                } else {
+                    sv = fminf(sv, ob);
+                }
+            }
+            int pick = bi;
+            const int64_t fr = frame0 + f;
+            const bool ambiguous = !norm_ok[f] || !(sv - bv > kAmbiguous);
+            if (ambiguous) {   // wave-uniform: the float64 rescan of the oracle's formula
+                double u[kCosDim];
+                double uss = 0.0;
+                // from the projection itself (the latent written above), not the fp32 unit vector
+#pragma unroll
+                for (int j = 0; j < kCosDim; ++j) {
+                    const double ej = static_cast<double>(
+                        lane_value(e_own[f], 32 * ((j >> 2) & 1) + 16 * ((j >> 1) & 1) + 8 * (j & 1)));
+                    u[j] = ej;
+                    uss = __dadd_rn(uss, __dmul_rn(ej, ej));
+                }
+                double norm = __builtin_sqrt(uss);
+                if (norm < 1e-12) norm = 1e-12;
+#pragma unroll
+                for (int j = 0; j < kCosDim; ++j) u[j] = u[j] / norm;
+                const double *uq = units + static_cast<int64_t>(q) * n_codes * kCosDim;
+                double bd = INFINITY;
+                int bkk = 0x7fffffff;
+                for (int k = lane; k < n_codes; k += 64) {
+                    const double dd = unit_distance(u, uq, k);
+                    if (dd < bd) {
+                        bd = dd;
+                        bkk = k;
+                    }
+                }
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) {
+                    const double od = __shfl_xor(bd, off);
+                    const int oi = __shfl_xor(bkk, off);
+                    if (od < bd || (od == bd && oi < bkk)) {
+                        bd = od;
+                        bkk = oi;
+                    }
+                }
+                pick = bkk;
+            }
+            pick = __builtin_amdgcn_readfirstlane(pick);
+            if (fr < n_frames && lane == 0) codes[fr * codes_ld + q] = pick;
+            const float *prow = table + (static_cast<int64_t>(q) * n_codes + pick) * hidden;
+#pragma unroll
+            for (int t = 0; t < kT; ++t) {
+                const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * ccol[t]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) r[f][t][e] = inrow[t] ? r[f][t][e] - p[e] : 0.0f;
+            }
+        }
+    }
+
+#pragma unroll
+    for (int f = 0; f < kFusedFrames; ++f) {
+        const int64_t fr = frame0 + f;
+        if (fr >= n_frames) continue;
+        float *row = residual + fr * hidden;
+#pragma unroll
+        for (int t = 0; t < kT; ++t)
+            if (inrow[t]) *reinterpret_cast<f32x4 *>(row + 4 * ccol[t]) = r[f][t];
+    }
+}
+
+template <int kT>
+hipError_t launch_fused_t(const float *h, int64_t n_frames, int hidden, const float *w_in, const float *b_in,
+                          const double *units, const float *table, int n_stages, int n_codes, int32_t *codes,
+                          int codes_ld, float *latent, float *residual, hipStream_t stream)
+{
+    const int64_t per_block = static_cast<int64_t>(kFusedWaves) * kFusedFrames;
+    const int64_t blocks = (n_frames + per_block - 1) / per_block;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kFusedWaves);
+    if (b_in)
+        hipLaunchKernelGGL((cosine_fused_kernel<kT, true>), grid, block, 0, stream, h, n_frames, hidden, w_in, b_in,
+                           units, table, n_stages, n_codes, codes, codes_ld, latent, residual);
+    else
+        hipLaunchKernelGGL((cosine_fused_kernel<kT, false>), grid, block, 0, stream, h, n_frames, hidden, w_in,
+                           b_in, units, table, n_stages, n_codes, codes, codes_ld, latent, residual);
+    return hipGetLastError();
+}
+
 template <int kT>
 hipError_t launch_proj8_t(const float *src, int64_t n_frames, int hidden, const float *w, const float *bias,
                           float *y, const Update8 &up, bool update, hipStream_t stream)
@@ -347,6 +630,22 @@ hipError_t launch_proj8(const float *src, const int32_t *prev_codes, int codes_l
     case 2: return launch_proj8_t<2>(src, n_frames, hidden, w, bias, y, up, update, stream);
     case 3: return launch_proj8_t<3>(src, n_frames, hidden, w, bias, y, up, update, stream);
     case 4: return launch_proj8_t<4>(src, n_frames, hidden, w, bias, y, up, update, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+bool cosine_fused_supported(int n_codes, int hidden) { return n_codes <= kFusedMaxCodes && hidden <= kProjMaxHidden; }
+
+hipError_t launch_cosine_fused(const float *h, int64_t n_frames, int hidden, const float *w_in, const float *b_in,
+                               const double *units, const float *table, int n_stages, int n_codes, int32_t *codes,
+                               int codes_ld, float *latent, float *residual, hipStream_t stream)
+{
+    if (!cosine_fused_supported(n_codes, hidden)) return hipErrorInvalidValue;
+    switch ((hidden + 255) / 256) {
+    case 1: return launch_fused_t<1>(h, n_frames, hidden, w_in, b_in, units, table, n_stages, n_codes, codes, codes_ld, latent, residual, stream);
+    case 2: return launch_fused_t<2>(h, n_frames, hidden, w_in, b_in, units, table, n_stages, n_codes, codes, codes_ld, latent, residual, stream);
+    case 3: return launch_fused_t<3>(h, n_frames, hidden, w_in, b_in, units, table, n_stages, n_codes, codes, codes_ld, latent, residual, stream);
+    case 4: return launch_fused_t<4>(h, n_frames, hidden, w_in, b_in, units, table, n_stages, n_codes, codes, codes_ld, latent, residual, stream);
     default: return hipErrorInvalidValue;
     }
 }

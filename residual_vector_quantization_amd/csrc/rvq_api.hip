@@ -278,6 +278,10 @@ RVQ_API rvq_status rvq_cosine_encode(const float *h, int64_t n_frames, int32_t h
         !aligned(codes, 4) || !aligned(latent, 16) || !aligned(residual, 16) || (b_in && !aligned(b_in, 16)))
         return RVQ_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (rvq::cosine_fused_supported(n_codes, hidden))
+        return from_hip(rvq::launch_cosine_fused(h, n_frames, hidden, w_in, b_in, units, table, n_stages, n_codes,
+                                                 codes, codes_ld, latent, residual, s));
+    // larger codebooks: one projection and one argmin launch per stage
     hipError_t e = hipSuccess;
     const int64_t table_stage = static_cast<int64_t>(n_codes) * hidden;
     for (int32_t q = 0; q < n_stages && e == hipSuccess; ++q) {

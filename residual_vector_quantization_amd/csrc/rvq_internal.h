@@ -89,6 +89,13 @@ hipError_t launch_proj8(const float *src, const int32_t *prev_codes, int codes_l
                         int n_codes, float *dst, int64_t n_frames, int hidden, const float *w, const float *bias,
                         float *y, hipStream_t stream);
 
+// All stages of the normalized quantizer in one kernel (residual rows kept
+// in registers); supported for n_codes <= 1024 and hidden <= 1024.
+bool cosine_fused_supported(int n_codes, int hidden);
+hipError_t launch_cosine_fused(const float *h, int64_t n_frames, int hidden, const float *w_in, const float *b_in,
+                               const double *units, const float *table, int n_stages, int n_codes, int32_t *codes,
+                               int codes_ld, float *latent, float *residual, hipStream_t stream);
+
 // codes[n * ld] = argmin_k |u_n - units[k]|^2 with u_n = lat[n] / max(|lat[n]|, 1e-12), exact.
 hipError_t launch_cosine_argmin(const float *lat, int64_t n_frames, const double *units, int n_codes,
                                 int32_t *codes, int codes_ld, hipStream_t stream);

@@ -97,9 +97,12 @@ def check_cosine(h, books, w_in, b_in, w_out, b_out, idx=None, n_stages=None, co
     return {"frames": int(sel.size), "latent_max_rel": float(rel.max()), "mismatch_frames": int(mism.sum())}
 
 
+# codebooks of at most 1024 entries run all stages in one kernel; larger ones
+# (1500, 2048 here) take one projection and one argmin launch per stage
 @pytest.mark.parametrize("n,hidden,q,k,bias", [(1, 64, 1, 16, True), (63, 320, 4, 1000, True),
                                                (300, 1024, 32, 1024, True), (2000, 1024, 3, 1024, False),
-                                               (129, 512, 8, 200, True), (700, 768, 5, 1024, True)])
+                                               (129, 512, 8, 200, True), (700, 768, 5, 1024, True),
+                                               (33, 256, 6, 1500, True), (500, 1024, 3, 2048, False)])
 def test_cosine_small(n, hidden, q, k, bias):
     rng = np.random.default_rng(n * 5 + hidden + q + k)
     h = rng.standard_normal((n, hidden)).astype(np.float32)
