@@ -71,6 +71,9 @@ def parse():
     p.add_argument("--gather-sweep", metavar="OUT_MD",
                    help="time rvq_decode at Q=32, N=720000 over codebook sizes 0.25..16 MiB, write a "
                         "summary of the row-gather rates to OUT_MD, then exit")
+    p.add_argument("--summarize-trace", metavar="DIR",
+                   help="turn a rocprofv3 --kernel-trace --stats CSV directory of --workload into "
+                        "profiles/<workload>_rocprof.md (per-kernel times and rates), then exit")
     p.add_argument("--summarize-profiles", metavar="DIR",
                    help="turn rocprofv3 CSV output under DIR (trace/, fetch/, write/, mfma/) into the "
                         "summaries under profiles/, then exit")
@@ -239,6 +242,73 @@ def summarize_profiles(w, src_dir):
                   f"- LDS bank-conflict cycles / LDS active cycles: "
                   f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1%}", ""]
     path = os.path.join(out_dir, f"encode_decode_{w.name}_rocprof.md")
+    open(path, "w").write("\n".join(lines) + "\n")
+    print("wrote", path)
+
+
+# ------------------------------------------- per-kernel summary (any workload)
+
+def _trace_work(w):
+    """Algorithmic work per launch of each kernel of a workload: name -> (amount, unit, what)."""
+    n, q, k, d, hid = w.n_frames, w.n_stages, w.n_codes, w.dim, w.hidden
+    qe = 1 if w.per_stage else q   # per-stage workloads launch the encode once per stage
+    work = {
+        "encode_bf16_kernel": (3 * 2.0 * qe * k * d * n, "flop",
+                               "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
+                               "bf16 matrix flop, 3 x 2QKD per frame"),
+        "encode_kernel": (2.0 * q * k * d * n, "flop", "fp32 matrix flop, 2QKD per frame"),
+        "decode_kernel": ((4.0 * q + 4.0 * d) * n, "B", "HBM, (4Q+4D) per frame"),
+        "decode_tiled_kernel": ((4.0 * q + 4.0 * d) * n, "B", "HBM, (4Q+4D) per frame"),
+    }
+    if w.hidden:
+        work.update({
+            "linear_in_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
+            "linear_out_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
+            "update_kernel": (8.0 * hid * n, "B", "HBM, residual read + write (8 hidden per frame)"),
+            "proj8_kernel": (8.0 * hid * n, "B", "HBM, residual read + write (8 hidden per frame)"),
+            "projected_decode_kernel": ((4.0 * q + 4.0 * hid) * n, "B", "HBM, (4Q + 4 hidden) per frame"),
+            "projected_decode_tiled_kernel": ((4.0 * q + 4.0 * hid) * n, "B", "HBM, (4Q + 4 hidden) per frame"),
+            "table_kernel": (2.0 * k * hid * d, "flop", "float64 flop, 2 K hidden D per stage"),
+            "cosine_argmin_kernel": (2.0 * k * d * n, "flop", "fp32 flop, 2KD per frame"),
+            "cosine_fused_kernel": ((2.0 * hid * d + 2.0 * k * d) * q * n, "flop",
+                                    "fp32 flop, Q (2 hidden D + 2KD) per frame; HBM 8 hidden B per frame"),
+        })
+    return work
+
+
+def summarize_trace(w, src_dir):
+    out_dir = os.path.join(_ROOT, "profiles")
+    os.makedirs(out_dir, exist_ok=True)
+    stats = _csv(src_dir, "kernel_stats.csv")
+    work = _trace_work(w)
+    cmd = ("cd /tmp && export TMPDIR=/tmp   # R = repository root\n"
+           f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/tr_{w.name} -o t -- "
+           f"python3 $R/bench.py --workload {w.name} --steps 5 --no-cpu-baseline\n"
+           f"python3 $R/bench.py --workload {w.name} --summarize-trace $R/gpurun_out/tr_{w.name}")
+    lines = [f"# rocprofv3: kernel trace, workload `{w.name}`", "", f"Workload: {w.description}.", "",
+             "Commands:", "", "```", cmd, "```", "",
+             "8 steps ran (3 warmup + 5 timed). Rates are algorithmic work per launch / average duration.", "",
+             "| kernel | calls | average (us) | share | work per launch | rate |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        name = r["Name"]
+        short = name.split("(")[0] if not name.startswith(("void ", "rvq::")) else name
+        base = next((key for key in sorted(work, key=len, reverse=True) if key + "<" in name or key + "(" in name),
+                    None)
+        a = float(r["AverageNs"]) / 1e3
+        if base:
+            i = name.index(base)
+            j = name.find("(", i)
+            label = name[i:j if j >= 0 else len(name)]
+        else:
+            label = short[:48]
+        if base:
+            amt, unit, what = work[base]
+            rate = f"{amt / a / 1e6:.1f} TFLOP/s" if unit == "flop" else f"{amt / a / 1e3:.0f} GB/s"
+            lines.append(f"| {label} | {r['Calls']} | {a:.1f} | {float(r['Percentage']):.1f}% | "
+                         f"{amt:.4g} {unit} ({what}) | {rate} |")
+        else:
+            lines.append(f"| {label} | {r['Calls']} | {a:.1f} | {float(r['Percentage']):.1f}% | | |")
+    path = os.path.join(out_dir, f"{w.name}_rocprof.md")
     open(path, "w").write("\n".join(lines) + "\n")
     print("wrote", path)
 
@@ -465,6 +535,9 @@ def main():
         return
     if args.gather_sweep:
         gather_sweep(args.gather_sweep)
+        return
+    if args.summarize_trace:
+        summarize_trace(W.WORKLOADS[args.workload], args.summarize_trace)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
