@@ -162,6 +162,92 @@ __host__ __device__ inline int64_t stage_bytes(int n_codes)
     return (kp * 260 + 4 + kStageAlign - 1) / kStageAlign * kStageAlign;
 }
 
+// The decision for one stage, from this lane's best / second / third keys
+// and the indices of the first two (codeword slots of one half of a frame;
+// lanes l and l^32 hold the two halves): every codeword within twice the
+// error bound of the frame's smallest key is a candidate; two to four
+// candidates are re-ranked in float64, a third candidate inside one lane
+// (or ambiguous bookkeeping) sends the frame to the full float64 rescan.
+// Then the pick is stored (code_out, when not null) and subtracted from the
+// negated residual n (and added to acc for kRecon). Every lane must call it.
+template <bool kRecon>
+__device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], float best, float second, float third,
+                                             int best_k, int second_k, const float *book, int n_codes, float c2,
+                                             bool valid, int half, int col, int lane, float *frame_row,
+                                             int32_t *code_out)
+{
+    const float best_o = __shfl_xor(best, 32);
+    const float second_o = __shfl_xor(second, 32);
+    const float third_o = __shfl_xor(third, 32);
+    const int best_k_o = __shfl_xor(best_k, 32);
+    const int second_k_o = __shfl_xor(second_k, 32);
+    float rn = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) rn = __builtin_fmaf(n[j], n[j], rn);
+    rn = rn + __shfl_xor(rn, 32);
+
+    const float bound = kBoundScale * (c2 + sqrtf(rn) * sqrtf(2.0f * c2)) + kAbsSlack;
+    const float lim = fminf(best, best_o) + 2.0f * bound;
+    const bool overflow = third <= lim || third_o <= lim ||
+                          (second <= lim && second_k == best_k) ||
+                          (second_o <= lim && second_k_o == best_k_o);
+    // candidate slots in frame order: half 0's best and second, then half 1's
+    const float sv[4] = {half ? best_o : best, half ? second_o : second,
+                         half ? best : best_o, half ? second : second_o};
+    const int sk[4] = {half ? best_k_o : best_k, half ? second_k_o : second_k,
+                       half ? best_k : best_k_o, half ? second_k : second_k_o};
+    bool cf[4];
+    int ncand = 0, pick = sk[0];
+#pragma unroll
+    for (int i = 3; i >= 0; --i) {
+        cf[i] = sv[i] <= lim;
+        ncand += cf[i];
+        if (cf[i]) pick = sk[i];
+    }
+
+    // Two to four candidates: float64 re-rank (slot 0 is always a valid index).
+    const bool rerank = valid && !overflow && ncand >= 2;
+    if (__any(rerank)) {
+        double bd = INFINITY;
+        int bk = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool use = rerank && cf[i];
+            if (__any(use)) {
+                const int k = use ? sk[i] : sk[0];
+                const double dist = pair_distance(n, book, k, half);
+                if (use && (dist < bd || (dist == bd && k < bk))) {
+                    bd = dist;
+                    bk = k;
+                }
+            }
+        }
+        if (rerank) pick = bk;
+    }
+
+    // A third candidate inside one lane (or ambiguous bookkeeping): full rescan.
+    uint64_t pending = __ballot(valid && overflow && half == 0);
+    while (pending) {
+        const int f = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+        pending &= pending - 1;
+        const int w = rescan_frame(n, frame_row, book, n_codes, f, lane);
+        if (col == f) pick = w;
+    }
+
+    pick = min(max(pick, 0), n_codes - 1);
+    if (code_out) *code_out = pick;
+    const f32x4 *cw = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(pick) * kDim + 32 * half);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const f32x4 v = cw[t];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            n[4 * t + e] = n[4 * t + e] + v[e];   // = -(r - c), exactly
+            if (kRecon) acc[4 * t + e] = acc[4 * t + e] + v[e];
+        }
+    }
+}
+
 template <bool kRecon, bool kResidual, bool kPrepared>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
 void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
@@ -310,16 +396,6 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
         if (c == n_chunks - 1) {
             // ---- stage q is scored for this wavefront's 32 frames: decide ----
             const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
-            const float best_o = __shfl_xor(best, 32);
-            const float second_o = __shfl_xor(second, 32);
-            const float third_o = __shfl_xor(third, 32);
-            const int best_k_o = __shfl_xor(best_k, 32);
-            const int second_k_o = __shfl_xor(second_k, 32);
-            float rn = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 32; ++j) rn = __builtin_fmaf(n[j], n[j], rn);
-            rn = rn + __shfl_xor(rn, 32);
-
             float c2;   // max_k 0.5||c_k||^2 over the stage
             if (kPrepared) {
                 c2 = *reinterpret_cast<const float *>(prepared + q * sbytes + kp * 260);
@@ -329,66 +405,8 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
                 for (int w = 0; w < kWaves; ++w) m = max(m, s_cmax[q & 1][w]);
                 c2 = __uint_as_float(m);
             }
-            const float bound = kBoundScale * (c2 + sqrtf(rn) * sqrtf(2.0f * c2)) + kAbsSlack;
-            const float lim = fminf(best, best_o) + 2.0f * bound;
-            const bool overflow = third <= lim || third_o <= lim ||
-                                  (second <= lim && second_k == best_k) ||
-                                  (second_o <= lim && second_k_o == best_k_o);
-            // candidate slots in frame order: half 0's best and second, then half 1's
-            const float sv[4] = {half ? best_o : best, half ? second_o : second,
-                                 half ? best : best_o, half ? second : second_o};
-            const int sk[4] = {half ? best_k_o : best_k, half ? second_k_o : second_k,
-                               half ? best_k : best_k_o, half ? second_k : second_k_o};
-            bool cf[4];
-            int ncand = 0, pick = sk[0];
-#pragma unroll
-            for (int i = 3; i >= 0; --i) {
-                cf[i] = sv[i] <= lim;
-                ncand += cf[i];
-                if (cf[i]) pick = sk[i];
-            }
-
-            // Two to four candidates: float64 re-rank (slot 0 is always a valid index).
-            const bool rerank = valid && !overflow && ncand >= 2;
-            if (__any(rerank)) {
-                double bd = INFINITY;
-                int bk = 0x7fffffff;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool use = rerank && cf[i];
-                    if (__any(use)) {
-                        const int k = use ? sk[i] : sk[0];
-                        const double dist = pair_distance(n, book, k, half);
-                        if (use && (dist < bd || (dist == bd && k < bk))) {
-                            bd = dist;
-                            bk = k;
-                        }
-                    }
-                }
-                if (rerank) pick = bk;
-            }
-
-            // A third candidate inside one lane (or ambiguous bookkeeping): full rescan.
-            uint64_t pending = __ballot(valid && overflow && half == 0);
-            while (pending) {
-                const int f = __ffsll(static_cast<unsigned long long>(pending)) - 1;
-                pending &= pending - 1;
-                const int w = rescan_frame(n, s_frame[wave], book, n_codes, f, lane);
-                if (col == f) pick = w;
-            }
-
-            pick = min(max(pick, 0), n_codes - 1);
-            if (valid && half == 0) codes[frame * codes_ld + q] = pick;
-            const f32x4 *cw = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(pick) * kDim + 32 * half);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const f32x4 v = cw[t];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    n[4 * t + e] = n[4 * t + e] + v[e];   // = -(r - c), exactly
-                    if (kRecon) acc[4 * t + e] = acc[4 * t + e] + v[e];
-                }
-            }
+            decide_stage<kRecon>(n, acc, best, second, third, best_k, second_k, book, n_codes, c2, valid, half, col,
+                                 lane, s_frame[wave], (valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
             best = kNoScore;
             second = kNoScore;
             third = kNoScore;
@@ -399,6 +417,192 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
     }
 
     if (valid) {
+        if (kResidual) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(residual + frame * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dst[t] = f32x4{-n[4 * t], -n[4 * t + 1], -n[4 * t + 2], -n[4 * t + 3]};
+        }
+        if (kRecon) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(recon + frame * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                dst[t] = f32x4{acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]};
+        }
+    }
+}
+
+// ---- small batches: the codebook split over the wavefronts ----------------
+//
+// With few frames the kernel above fills few workgroups, and each
+// wavefront walks all K codewords of every stage alone. Here the 8
+// wavefronts of a workgroup share one tile of 32 frames (each holds the
+// tile's residual) and split every stage's codebook: wavefront w scores
+// 64-codeword groups w, w + 8, ..., each staged into its own LDS buffer
+// (no workgroup barrier while scoring). The per-lane best / second / third
+// keys with the first two indices are then merged over the 8 wavefronts
+// through LDS in a fixed order, so every wavefront reaches the same merged
+// state and takes the same decision (decide_stage) on its copy of the
+// residual; wavefront 0 writes the outputs.
+constexpr int kSplitWaves = 8;
+constexpr int kSplitGroup = 64;
+// up to this many frames the split kernel runs (its tiles are 8x smaller)
+constexpr int64_t kSplitMaxFrames = 8192;
+
+// top-3 of keys from disjoint codeword sets; k < 0 marks an unknown index,
+// which orders after known ones on equal keys
+struct Top3 {
+    float b, s, t;
+    int bk, sk;
+};
+
+__device__ __forceinline__ bool key_before(float v1, int k1, float v2, int k2)
+{
+    return v1 < v2 || (v1 == v2 && static_cast<unsigned>(k1) < static_cast<unsigned>(k2));
+}
+
+__device__ __forceinline__ void top3_insert(Top3 &m, float v, int k)
+{
+    if (key_before(v, k, m.b, m.bk)) {
+        m.t = m.s;
+        m.s = m.b;
+        m.sk = m.bk;
+        m.b = v;
+        m.bk = k;
+    } else if (key_before(v, k, m.s, m.sk)) {
+        m.t = m.s;
+        m.s = v;
+        m.sk = k;
+    } else {
+        m.t = fminf(m.t, v);
+    }
+}
+
+template <bool kRecon, bool kResidual, bool kPrepared>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kSplitWaves, 64 * kSplitWaves), amdgpu_waves_per_eu(2)))
+void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
+                               const float *__restrict__ books, const uint8_t *__restrict__ prepared,
+                               int n_stages, int n_codes,
+                               int32_t *__restrict__ codes, int codes_ld,
+                               float *__restrict__ residual, float *__restrict__ recon)
+{
+    __shared__ __align__(16) __bf16 s_rows[kSplitWaves][kSplitGroup * kRowH];
+    __shared__ __align__(16) float s_gnorm[kSplitWaves][kSplitGroup];
+    __shared__ __align__(16) float s_part[kSplitWaves][5][64];   // best, second, third, best_k, second_k
+    __shared__ unsigned s_wmax[kSplitWaves];
+    __shared__ __align__(16) float s_frame[kSplitWaves][kDim];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kFramesPerWave + col;
+    const bool valid = frame < n_frames;
+
+    float n[32];
+    float acc[32];
+    if (valid) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(x + frame * kDim + 32 * half);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 v = src[t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) n[4 * t + e] = -v[e];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) n[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+    bf16x8 nh[4], nl[4];
+
+    const int n_groups = (n_codes + kSplitGroup - 1) / kSplitGroup;
+    const int64_t kp = padded_codes(n_codes);
+    const int64_t sbytes = stage_bytes(n_codes);
+    __bf16 *rows = s_rows[wave];
+    float *gnorm = s_gnorm[wave];
+
+    for (int q = 0; q < n_stages; ++q) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) split8(&n[8 * s], nh[s], nl[s]);
+        float best = kNoScore, second = kNoScore, third = kNoScore;
+        int best_k = 0, second_k = 0;
+        unsigned wmax = 0u;
+
+        for (int g = wave; g < n_groups; g += kSplitWaves) {
+            // lane l stages row 64 g + l of the stage (rows past n_codes: prepared
+            // padding, or the last row again with norm kNoScore)
+            const int k = g * kSplitGroup + lane;
+            __bf16 *dst = rows + lane * kRowH;
+            if (kPrepared) {
+                const uint8_t *blk = prepared + q * sbytes;
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(blk + static_cast<int64_t>(k) * 256);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) reinterpret_cast<f32x4 *>(dst)[i] = p[i];
+                gnorm[lane] = reinterpret_cast<const float *>(blk + kp * 256)[k];
+            } else {
+                const f32x4 *p = reinterpret_cast<const f32x4 *>(
+                    books + (static_cast<int64_t>(q) * n_codes + min(k, n_codes - 1)) * kDim);
+                float hn = 0.0f;
+#pragma unroll
+                for (int grp = 0; grp < 8; ++grp) {
+                    const f32x4 a = p[2 * grp], b = p[2 * grp + 1];
+                    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hn = __builtin_fmaf(v[e], v[e], hn);
+                    bf16x8 hi, lo;
+                    split8(v, hi, lo);
+                    *reinterpret_cast<bf16x8 *>(dst + 16 * grp) = hi;
+                    *reinterpret_cast<bf16x8 *>(dst + 16 * grp + 8) = lo;
+                }
+                hn = 0.5f * hn;
+                gnorm[lane] = k < n_codes ? hn : kNoScore;
+                if (k < n_codes) wmax = max(wmax, __float_as_uint(hn));
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            score_group(0, rows, gnorm, col, half, nh, nl, g * kSplitGroup, best, second, third, best_k, second_k);
+            // the buffer is read before the next group overwrites it
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+        }
+
+        s_part[wave][0][lane] = best;
+        s_part[wave][1][lane] = second;
+        s_part[wave][2][lane] = third;
+        s_part[wave][3][lane] = __int_as_float(best_k);
+        s_part[wave][4][lane] = __int_as_float(second_k);
+        if (!kPrepared) {
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1)
+                wmax = max(wmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(wmax), off)));
+            if (lane == 0) s_wmax[wave] = wmax;
+        }
+        __syncthreads();
+        Top3 m = {kNoScore, kNoScore, kNoScore, 0, 0};   // the scan's own initial state
+#pragma unroll
+        for (int w = 0; w < kSplitWaves; ++w) {
+            top3_insert(m, s_part[w][0][lane], __float_as_int(s_part[w][3][lane]));
+            top3_insert(m, s_part[w][1][lane], __float_as_int(s_part[w][4][lane]));
+            top3_insert(m, s_part[w][2][lane], -1);
+        }
+        float c2;
+        if (kPrepared) {
+            c2 = *reinterpret_cast<const float *>(prepared + q * sbytes + kp * 260);
+        } else {
+            unsigned mm = 0u;
+#pragma unroll
+            for (int w = 0; w < kSplitWaves; ++w) mm = max(mm, s_wmax[w]);
+            c2 = __uint_as_float(mm);
+        }
+        __syncthreads();   // s_part and s_wmax are read before the next stage writes them
+        const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
+        decide_stage<kRecon>(n, acc, m.b, m.s, m.t, m.bk, m.sk, book, n_codes, c2, valid, half, col, lane,
+                             s_frame[wave], (wave == 0 && valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
+    }
+
+    if (wave == 0 && valid) {
         if (kResidual) {
             f32x4 *dst = reinterpret_cast<f32x4 *>(residual + frame * kDim + 32 * half);
 #pragma unroll
@@ -473,6 +677,24 @@ hipError_t launch_variant(const float *x, int64_t n_frames, const float *books, 
 {
     const int64_t blocks = (n_frames + kBlockFrames - 1) / kBlockFrames;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (n_frames <= kSplitMaxFrames) {
+        // few frames: one 32-frame tile per workgroup, the codebook split over its wavefronts
+        const dim3 sgrid(static_cast<unsigned>((n_frames + kFramesPerWave - 1) / kFramesPerWave));
+        const dim3 sblock(64 * kSplitWaves);
+        if (recon && residual)
+            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<true, true, kPrepared>), sgrid, sblock, 0, stream,
+                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
+        else if (recon)
+            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<true, false, kPrepared>), sgrid, sblock, 0, stream,
+                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
+        else if (residual)
+            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<false, true, kPrepared>), sgrid, sblock, 0, stream,
+                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
+        else
+            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<false, false, kPrepared>), sgrid, sblock, 0, stream,
+                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
+        return hipGetLastError();
+    }
     const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
     if (recon && residual)
         hipLaunchKernelGGL((encode_bf16_kernel<true, true, kPrepared>), grid, block, 0, stream,

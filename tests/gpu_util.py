@@ -33,6 +33,21 @@ def announce(what, **shape):
 
 SCORINGS = ["default", "fp32", "prepared"]
 
+# Batches of up to 8192 frames take the split-codebook encode (one 32-frame
+# tile per workgroup); larger ones the wide one (256 frames per workgroup).
+# widen() embeds a small case into a batch that takes the wide kernel.
+WIDE_FRAMES = 8192 + 300
+
+
+def widen(x, seed=0):
+    """(x_wide, idx): x followed by N(0,1) filler frames up to WIDE_FRAMES; idx selects x's frames
+    and the batch's last 32 frames (its ragged tail) for the oracle comparison."""
+    n = x.shape[0]
+    fill = np.random.default_rng(seed + 7777).standard_normal((WIDE_FRAMES - n, x.shape[1])).astype(np.float32)
+    xw = np.concatenate([x, fill], axis=0)
+    idx = np.unique(np.concatenate([np.arange(n), np.arange(WIDE_FRAMES - 32, WIDE_FRAMES)]))
+    return xw, idx
+
 
 def check_encode(x, books, n_stages=None, idx=None, roundtrip=True, scoring="default"):
     """Runs the HIP encode (and roundtrip) and compares with the oracle.

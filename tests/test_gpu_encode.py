@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import rvq_workloads as W
-from gpu_util import SCORINGS, needs_gpu, check_encode, rvq, to_dev, host, announce
+from gpu_util import SCORINGS, needs_gpu, check_encode, widen, rvq, to_dev, host, announce
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -32,6 +32,15 @@ def test_clip_workload_full(scoring):
     check_encode(x, books, scoring=scoring)
 
 
+def _check(x, books, wide, scoring, **kw):
+    """check_encode on x itself (split-codebook kernel for small batches) or embedded in a batch
+    large enough for the wide kernel."""
+    if wide:
+        xw, idx = widen(x)
+        return check_encode(xw, books, idx=idx, scoring=scoring, **kw)
+    return check_encode(x, books, scoring=scoring, **kw)
+
+
 @pytest.mark.parametrize("n", [1, 31, 129, 677])
 @pytest.mark.parametrize("scoring", SCORINGS)
 def test_ragged_frame_counts(n, scoring):
@@ -41,24 +50,36 @@ def test_ragged_frame_counts(n, scoring):
     check_encode(x, books, scoring=scoring)
 
 
+@pytest.mark.parametrize("n", [8192, 8193, 8192 + 31])
+def test_split_threshold_frame_counts(n):
+    """Either side of the split / wide switch, ragged tails included."""
+    rng = np.random.default_rng(150 + n)
+    books = _books(rng, 4, 1024)
+    x = rng.standard_normal((n, 64)).astype(np.float32)
+    idx = W.sample_frames(n, 600, seed=n)
+    check_encode(x, books, idx=idx)
+
+
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("k", [1, 63, 64, 65, 100, 1000, 4096])
 @pytest.mark.parametrize("scoring", SCORINGS)
-def test_codebook_sizes(k, scoring):
+def test_codebook_sizes(k, scoring, wide):
     rng = np.random.default_rng(200 + k)
     q = 10 if k == 4096 else 3
     books = _books(rng, q, k)
     x = rng.standard_normal((300, 64)).astype(np.float32)
-    check_encode(x, books, scoring=scoring)
+    _check(x, books, wide, scoring)
 
 
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("q,decay", [(1, 1.0), (32, 0.85), (64, 0.9)])
 @pytest.mark.parametrize("scoring", SCORINGS)
-def test_stage_counts(q, decay, scoring):
+def test_stage_counts(q, decay, scoring, wide):
     rng = np.random.default_rng(300 + q)
     k = 256 if q == 64 else 1024
     books = _books(rng, q, k, decay=decay)
     x = rng.standard_normal((257, 64)).astype(np.float32)
-    check_encode(x, books, scoring=scoring)
+    _check(x, books, wide, scoring)
 
 
 def test_partial_depth_prefix():
@@ -73,40 +94,44 @@ def test_partial_depth_prefix():
     np.testing.assert_array_equal(host(part), host(full)[:, :3])
 
 
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("scoring", SCORINGS)
-def test_exact_ties_integer_data(scoring):
+def test_exact_ties_integer_data(scoring, wide):
     """Small integers: exact scores, many exact ties and duplicated rows (lowest index wins)."""
     rng = np.random.default_rng(8)
     books = rng.integers(-3, 4, size=(4, 128, 64)).astype(np.float32)
     books[:, 100:128] = books[:, 0:28]
     x = rng.integers(-6, 7, size=(500, 64)).astype(np.float32)
-    check_encode(x, books, scoring=scoring)
+    _check(x, books, wide, scoring)
 
 
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("scoring", SCORINGS)
-def test_all_rows_identical(scoring):
+def test_all_rows_identical(scoring, wide):
     rng = np.random.default_rng(9)
     books = np.repeat(rng.standard_normal((3, 1, 64)).astype(np.float32), 192, axis=1)
     x = rng.standard_normal((130, 64)).astype(np.float32)
-    check_encode(x, books, scoring=scoring)
+    _check(x, books, wide, scoring)
     codes, _ = rvq().rvq_encode(to_dev(x), to_dev(books))
     assert (host(codes) == 0).all()
 
 
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("scoring", SCORINGS)
-def test_zero_inputs_and_codebooks(scoring):
+def test_zero_inputs_and_codebooks(scoring, wide):
     x = np.zeros((70, 64), np.float32)
     books = np.zeros((2, 128, 64), np.float32)
-    check_encode(x, books, scoring=scoring)
+    _check(x, books, wide, scoring)
 
 
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("scale", [1e-6, 1e6])
 @pytest.mark.parametrize("scoring", SCORINGS)
-def test_scaled_data(scale, scoring):
+def test_scaled_data(scale, scoring, wide):
     rng = np.random.default_rng(10)
     books = (_books(rng, 4, 512) * scale).astype(np.float32)
     x = (rng.standard_normal((200, 64)) * scale).astype(np.float32)
-    check_encode(x, books, scoring=scoring)
+    _check(x, books, wide, scoring)
 
 
 def test_codes_leading_dimension():
