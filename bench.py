@@ -45,6 +45,7 @@ COPY_BYTES = 512 << 20             # size of the counter-calibration copy
 # reaches at best over codebook sizes from 0.25 to 16 MiB (--gather-sweep);
 # the decode's row gathers are bound by it, not by HBM.
 GATHER_CEILING_TBPS = 21.9
+SPLIT_MAX_FRAMES = 8192   # batches up to this size take the split-codebook encode
 
 CSRC = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc")
 # kernel kind -> sources whose text defines it (hashed to detect stale counters)
@@ -121,6 +122,8 @@ def _csv(dirname, suffix):
 
 
 def _kernel_of(name):
+    if "encode_bf16_ksplit_kernel" in name:
+        return "encode_bf16_split"
     if "encode_bf16_kernel" in name:
         # template arguments <recon, residual, prepared>: the timed step runs the prepared one
         prepared = name.split("encode_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")[-1].strip()
@@ -256,6 +259,9 @@ def _trace_work(w):
         "encode_bf16_kernel": (3 * 2.0 * qe * k * d * n, "flop",
                                "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
                                "bf16 matrix flop, 3 x 2QKD per frame"),
+        "encode_bf16_ksplit_kernel": (3 * 2.0 * qe * k * d * n, "flop",
+                                      "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
+                                      "bf16 matrix flop, 3 x 2QKD per frame"),
         "encode_kernel": (2.0 * q * k * d * n, "flop", "fp32 matrix flop, 2QKD per frame"),
         "decode_kernel": ((4.0 * q + 4.0 * d) * n, "B", "HBM, (4Q+4D) per frame"),
         "decode_tiled_kernel": ((4.0 * q + 4.0 * d) * n, "B", "HBM, (4Q+4D) per frame"),
@@ -654,7 +660,9 @@ def main():
         "encode_ms": enc_ms,
         "decode_ms": dec_ms,
         "roofline": {"bound": "mfma",
-                     "kernel": "encode_bf16_kernel, prepared codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)",
+                     "kernel": ("encode_bf16_ksplit_kernel (codebook split over a workgroup's wavefronts)"
+                                if n <= SPLIT_MAX_FRAMES else "encode_bf16_kernel") +
+                               ", prepared codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)",
                      "achieved": bf16_tflops, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": bf16_tflops / PEAK_BF16_MFMA_TFLOPS,
                      "traffic": recorded_traffic("encode_bf16", w.name),
