@@ -45,7 +45,7 @@ COPY_BYTES = 512 << 20             # size of the counter-calibration copy
 # reaches at best over codebook sizes from 0.25 to 16 MiB (--gather-sweep);
 # the decode's row gathers are bound by it, not by HBM.
 GATHER_CEILING_TBPS = 21.9
-SPLIT_MAX_FRAMES = 8192   # batches up to this size take the split-codebook encode
+SPLIT_MAX_FRAMES = 16384   # batches up to this size take the split-codebook encode
 
 CSRC = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc")
 # kernel kind -> sources whose text defines it (hashed to detect stale counters)
@@ -132,10 +132,8 @@ def _kernel_of(name):
         return "encode_fp32"
     if "decode_kernel" in name or "decode_tiled_kernel" in name:
         return "decode"
-    if "prepare_rows_kernel" in name:
-        return "prepare_rows"
-    if "prepare_max_kernel" in name:
-        return "prepare_max"
+    if "prepare_kernel" in name:
+        return "prepare"
     if "elementwise" in name and "MulFunctor" in name:
         return "copy"
     return None

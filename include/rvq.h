@@ -162,8 +162,8 @@ RVQ_API rvq_status rvq_encode_scored(const float *x, int64_t n_frames, int32_t d
  * rvq_prepare_codebooks writes it on `stream` into caller-allocated device
  * memory `prepared` (16-byte aligned, at least rvq_prepared_bytes bytes).
  * Per stage it holds: each codeword as bf16 hi = bf16(c) and lo = bf16(c -
- * hi) in 8-dim groups, 0.5*||c||^2 in fp32, and the stage's largest
- * 0.5*||c||^2. The buffer depends only on the codebook values.
+ * hi) in 8-dim groups, 0.5*||c||^2 in fp32, and the largest 0.5*||c||^2
+ * of every 256 codewords. The buffer depends only on the codebook values.
  *
  * rvq_encode_prepared is rvq_encode_scored with split-bf16 scoring, reading
  * the split rows from `prepared` (which must have been prepared from the same

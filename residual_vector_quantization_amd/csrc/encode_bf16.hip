@@ -59,6 +59,17 @@ static_assert(kWaves * 32 == kChunk, "staging maps each wavefront to 32 codeword
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wavefront-wide direct load from global memory into LDS: active lane i
+// copies 16 bytes from src into dst + 16 i (dst wave-uniform, in LDS).
+// Issued as inline assembly so that the compiler does not order every LDS
+// read behind it; the caller waits with the vector-memory counter.
+__device__ __forceinline__ void dma16(const void *src, void *dst)
+{
+    const unsigned m0 = static_cast<unsigned>(reinterpret_cast<size_t>((lds_void *)dst));
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
 
 // hi = bf16(v), lo = bf16(v - hi), both round to nearest even, converted in
 // pairs (one v_cvt_pk_bf16_f32 per two values); hi is widened back to fp32 by
@@ -81,18 +92,21 @@ __device__ __forceinline__ void split8(const float *v, bf16x8 &hi, bf16x8 &lo)
 // Key scan of a 64-codeword group (two blocks): running best, second and
 // third key of this lane. Local index of accumulator v of block b:
 // b*32 + 8*(v/4) + v%4, plus the lane's 4*half row offset.
-__device__ __forceinline__ void scan_group(const f32x16 (&d)[2], float &best, float &second, float &third)
+__device__ __forceinline__ void scan_block(const f32x16 &d, int b, float &best, float &second, float &third)
 {
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const float key = make_key(d[b][v], b * 32 + 8 * (v >> 2) + (v & 3));
-            third = __builtin_amdgcn_fmed3f(key, second, third);
-            second = __builtin_amdgcn_fmed3f(key, best, second);
-            best = __builtin_amdgcn_fmed3f(key, best, -FLT_MAX);
-        }
+    for (int v = 0; v < 16; ++v) {
+        const float key = make_key(d[v], b * 32 + 8 * (v >> 2) + (v & 3));
+        third = __builtin_amdgcn_fmed3f(key, second, third);
+        second = __builtin_amdgcn_fmed3f(key, best, second);
+        best = __builtin_amdgcn_fmed3f(key, best, -FLT_MAX);
     }
+}
+
+__device__ __forceinline__ void scan_group(const f32x16 (&d)[2], float &best, float &second, float &third)
+{
+    scan_block(d[0], 0, best, second, third);
+    scan_block(d[1], 1, best, second, third);
 }
 
 // Index bookkeeping after scanning the group that starts at codeword `base`.
@@ -149,17 +163,54 @@ __device__ __forceinline__ void score_group(int kG, const __bf16 *sb, const floa
     fold_group(best, second, bb, sb0, base, half, best_k, second_k);
 }
 
+// Scores the 32 codewords of one block in LDS (rows sb, half-norms sn;
+// one chain of 12 matrix-core steps) that start at codeword `base`.
+__device__ __forceinline__ void score_block(const __bf16 *sb, const float *sn, int col, int half,
+                                            const bf16x8 (&nh)[4], const bf16x8 (&nl)[4], int base,
+                                            float &best, float &second, float &third,
+                                            int &best_k, int &second_k)
+{
+    f32x16 d;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const f32x4 nv = *reinterpret_cast<const f32x4 *>(sn + 8 * m + 4 * half);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[4 * m + e] = nv[e];
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const __bf16 *row = sb + col * kRowH + 16 * (4 * half + s);
+        const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(row);
+        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(row + 8);
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, nl[s], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, nh[s], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, nh[s], d, 0, 0, 0);
+    }
+    const unsigned bb = __float_as_uint(best), sb0 = __float_as_uint(second);
+    scan_block(d, 0, best, second, third);
+    fold_group(best, second, bb, sb0, base, half, best_k, second_k);
+}
+
 // Prepared codebooks (rvq_prepare_codebooks): per stage one block of
-//   rows  [Kp][256 B]  16-byte segments (8 bf16 hi, 8 bf16 lo) per 8-dim group
-//   norms [Kp] fp32    0.5*||c||^2, kNoScore for rows k >= n_codes
-//   max   uint32       bits of the largest valid 0.5*||c||^2
+//   rows  [Kp][256 B]      16-byte segments (8 bf16 hi, 8 bf16 lo) per 8-dim group
+//   norms [Kp] fp32        0.5*||c||^2, kNoScore for rows k >= n_codes
+//   max   [Kp/kChunk] u32  bits of the largest valid 0.5*||c||^2 of each kChunk rows
 // with Kp = n_codes rounded up to kChunk, blocks kStageAlign-aligned.
 constexpr int64_t kStageAlign = 256;
 __host__ __device__ inline int64_t padded_codes(int n_codes) { return (n_codes + kChunk - 1) / kChunk * kChunk; }
 __host__ __device__ inline int64_t stage_bytes(int n_codes)
 {
     const int64_t kp = padded_codes(n_codes);
-    return (kp * 260 + 4 + kStageAlign - 1) / kStageAlign * kStageAlign;
+    return (kp * 260 + 4 * (kp / kChunk) + kStageAlign - 1) / kStageAlign * kStageAlign;
+}
+
+// max_k 0.5*||c_k||^2 of a prepared stage block (values >= 0: bits order like values)
+__device__ inline float prepared_max(const uint8_t *blk, int64_t kp, int n_chunks)
+{
+    const unsigned *m = reinterpret_cast<const unsigned *>(blk + kp * 260);
+    unsigned r = 0u;
+    for (int c = 0; c < n_chunks; ++c) r = max(r, m[c]);
+    return __uint_as_float(r);
 }
 
 // The decision for one stage, from this lane's best / second / third keys
@@ -398,7 +449,7 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
             const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
             float c2;   // max_k 0.5||c_k||^2 over the stage
             if (kPrepared) {
-                c2 = *reinterpret_cast<const float *>(prepared + q * sbytes + kp * 260);
+                c2 = prepared_max(prepared + q * sbytes, kp, n_chunks);
             } else {
                 unsigned m = 0u;
 #pragma unroll
@@ -440,13 +491,25 @@ void encode_bf16_kernel(const float *__restrict__ x, int64_t n_frames,
 // 64-codeword groups w, w + 8, ..., each staged into its own LDS buffer
 // (no workgroup barrier while scoring). The per-lane best / second / third
 // keys with the first two indices are then merged over the 8 wavefronts
-// through LDS in a fixed order, so every wavefront reaches the same merged
-// state and takes the same decision (decide_stage) on its copy of the
-// residual; wavefront 0 writes the outputs.
+// through LDS in a fixed order by wavefront 0, which takes the decision
+// (decide_stage) on the residual it holds, writes the codes and publishes
+// the bf16 split of the updated residual through LDS for the other
+// wavefronts (which hold only the split); it writes the outputs at the end.
 constexpr int kSplitWaves = 8;
 constexpr int kSplitGroup = 64;
-// up to this many frames the split kernel runs (its tiles are 8x smaller)
-constexpr int64_t kSplitMaxFrames = 8192;
+// up to this many frames the split kernel runs: two rounds of one-tile
+// workgroups on 256 CUs are still faster than the wide kernel's 256-frame tiles
+constexpr int64_t kSplitMaxFrames = 16384;
+// prepared codebooks: 32-codeword blocks, two per wavefront buffer
+constexpr int kRowSlots = kRowH * 2 / 16;                 // 16-byte LDS slots per row (16 data + 1 padding)
+constexpr int kBlockSlots = 32 * kRowH * 2 / 16;          // 16-byte LDS slots of a block (544)
+constexpr int kBlockLoads = (kBlockSlots + 63) / 64;      // wavefront-wide loads per block's rows (9)
+static_assert(kBlockLoads == 9, "the wait count below assumes 9 row loads + 1 norm load per block");
+
+// Waits until at most the 10 loads of the block issued last are in flight
+// (vector-memory operations complete in order).
+__device__ __forceinline__ void wait_all_but_block() { asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); }
+__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // top-3 of keys from disjoint codeword sets; k < 0 marks an unknown index,
 // which orders after known ones on equal keys
@@ -490,9 +553,10 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
     __shared__ __align__(16) float s_part[kSplitWaves][5][64];   // best, second, third, best_k, second_k
     __shared__ unsigned s_wmax[kSplitWaves];
     __shared__ __align__(16) float s_frame[kSplitWaves][kDim];
+    __shared__ __align__(16) bf16x8 s_split[64][8];   // the tile's next-stage operand split, per lane
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 31;
     const int half = lane >> 5;
     const int64_t frame = static_cast<int64_t>(blockIdx.x) * kFramesPerWave + col;
@@ -522,25 +586,73 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
     __bf16 *rows = s_rows[wave];
     float *gnorm = s_gnorm[wave];
 
-    for (int q = 0; q < n_stages; ++q) {
+    // Prepared codebooks: wavefront w owns the 32-codeword blocks w, w + 8,
+    // ... of every stage and streams them through the two halves of its
+    // buffer with direct global->LDS loads, one block ahead; the first
+    // block of the next stage is loaded while the current stage is merged
+    // and decided.
+    const int n_blocks = (n_codes + 31) / 32;
+    const int my_blocks = wave < n_blocks ? (n_blocks - wave + kSplitWaves - 1) / kSplitWaves : 0;
+    auto load_block = [&](int q, int ib, int buf) {
+        const uint8_t *blk = prepared + q * sbytes;
+        const int k0 = (wave + kSplitWaves * ib) * 32;
+        const uint8_t *src = blk + static_cast<int64_t>(k0) * 256;
+        __bf16 *dst = rows + buf * 32 * kRowH;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) split8(&n[8 * s], nh[s], nl[s]);
+        for (int i = 0; i < kBlockLoads; ++i) {
+            // slot t of the block is segment t % 17 of row t / 17; the 17th
+            // (padding) slot loads the row's first segment again
+            int t = i * 64 + lane;
+            asm volatile("" : "+v"(t));   // recomputed per block rather than held in registers
+            const int r = t / kRowSlots;
+            const int seg = t - r * kRowSlots;
+            if (t < kBlockSlots) dma16(src + r * 256 + (seg < kRowSlots - 1 ? seg * 16 : 0), dst + i * 512);
+        }
+        if (lane < 8) dma16(blk + kp * 256 + static_cast<int64_t>(k0 + 4 * lane) * 4, gnorm + buf * 32);
+    };
+    int item = 0;   // blocks this wavefront has scored (their buffer alternates)
+    if constexpr (kPrepared) {
+        if (my_blocks > 0) load_block(0, 0, 0);
+    }
+
+#pragma unroll
+    for (int s = 0; s < 4; ++s) split8(&n[8 * s], nh[s], nl[s]);
+
+    for (int q = 0; q < n_stages; ++q) {
+        if (q > 0 && wave != 0) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                nh[s] = s_split[lane][s];
+                nl[s] = s_split[lane][4 + s];
+            }
+        }
         float best = kNoScore, second = kNoScore, third = kNoScore;
         int best_k = 0, second_k = 0;
         unsigned wmax = 0u;
+        float c2 = 0.0f;   // max_k 0.5||c_k||^2 over the stage
 
-        for (int g = wave; g < n_groups; g += kSplitWaves) {
-            // lane l stages row 64 g + l of the stage (rows past n_codes: prepared
-            // padding, or the last row again with norm kNoScore)
-            const int k = g * kSplitGroup + lane;
-            __bf16 *dst = rows + lane * kRowH;
-            if (kPrepared) {
-                const uint8_t *blk = prepared + q * sbytes;
-                const f32x4 *p = reinterpret_cast<const f32x4 *>(blk + static_cast<int64_t>(k) * 256);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) reinterpret_cast<f32x4 *>(dst)[i] = p[i];
-                gnorm[lane] = reinterpret_cast<const float *>(blk + kp * 256)[k];
-            } else {
+        if constexpr (kPrepared) {
+            c2 = prepared_max(prepared + q * sbytes, kp, static_cast<int>(kp / kChunk));
+            for (int ib = 0; ib < my_blocks; ++ib, ++item) {
+                if (ib + 1 < my_blocks) {
+                    load_block(q, ib + 1, (item + 1) & 1);
+                    wait_all_but_block();
+                } else if (q + 1 < n_stages) {
+                    load_block(q + 1, 0, (item + 1) & 1);
+                    wait_all_but_block();
+                } else {
+                    wait_all();
+                }
+                const int buf = item & 1;
+                score_block(rows + buf * 32 * kRowH, gnorm + buf * 32, col, half, nh, nl,
+                            (wave + kSplitWaves * ib) * 32, best, second, third, best_k, second_k);
+            }
+        } else {
+            for (int g = wave; g < n_groups; g += kSplitWaves) {
+                // lane l stages row 64 g + l of the stage (rows past n_codes:
+                // the last row again with norm kNoScore)
+                const int k = g * kSplitGroup + lane;
+                __bf16 *dst = rows + lane * kRowH;
                 const f32x4 *p = reinterpret_cast<const f32x4 *>(
                     books + (static_cast<int64_t>(q) * n_codes + min(k, n_codes - 1)) * kDim);
                 float hn = 0.0f;
@@ -558,14 +670,15 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
                 hn = 0.5f * hn;
                 gnorm[lane] = k < n_codes ? hn : kNoScore;
                 if (k < n_codes) wmax = max(wmax, __float_as_uint(hn));
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+                score_group(0, rows, gnorm, col, half, nh, nl, g * kSplitGroup, best, second, third, best_k,
+                            second_k);
+                // the buffer is read before the next group overwrites it
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __builtin_amdgcn_wave_barrier();
             }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-            score_group(0, rows, gnorm, col, half, nh, nl, g * kSplitGroup, best, second, third, best_k, second_k);
-            // the buffer is read before the next group overwrites it
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            __builtin_amdgcn_wave_barrier();
         }
 
         s_part[wave][0][lane] = best;
@@ -580,26 +693,35 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
             if (lane == 0) s_wmax[wave] = wmax;
         }
         __syncthreads();
-        Top3 m = {kNoScore, kNoScore, kNoScore, 0, 0};   // the scan's own initial state
+        if (wave == 0) {
+            // wavefront 0 merges the parts, decides, and publishes the split
+            // of the updated residual for the other wavefronts
+            Top3 m = {kNoScore, kNoScore, kNoScore, 0, 0};   // the scan's own initial state
 #pragma unroll
-        for (int w = 0; w < kSplitWaves; ++w) {
-            top3_insert(m, s_part[w][0][lane], __float_as_int(s_part[w][3][lane]));
-            top3_insert(m, s_part[w][1][lane], __float_as_int(s_part[w][4][lane]));
-            top3_insert(m, s_part[w][2][lane], -1);
-        }
-        float c2;
-        if (kPrepared) {
-            c2 = *reinterpret_cast<const float *>(prepared + q * sbytes + kp * 260);
-        } else {
-            unsigned mm = 0u;
+            for (int w = 0; w < kSplitWaves; ++w) {
+                top3_insert(m, s_part[w][0][lane], __float_as_int(s_part[w][3][lane]));
+                top3_insert(m, s_part[w][1][lane], __float_as_int(s_part[w][4][lane]));
+                top3_insert(m, s_part[w][2][lane], -1);
+            }
+            if constexpr (!kPrepared) {
+                unsigned mm = 0u;
 #pragma unroll
-            for (int w = 0; w < kSplitWaves; ++w) mm = max(mm, s_wmax[w]);
-            c2 = __uint_as_float(mm);
+                for (int w = 0; w < kSplitWaves; ++w) mm = max(mm, s_wmax[w]);
+                c2 = __uint_as_float(mm);
+            }
+            const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
+            decide_stage<kRecon>(n, acc, m.b, m.s, m.t, m.bk, m.sk, book, n_codes, c2, valid, half, col, lane,
+                                 s_frame[0], (valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
+            if (q + 1 < n_stages) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    split8(&n[8 * s], nh[s], nl[s]);
+                    s_split[lane][s] = nh[s];
+                    s_split[lane][4 + s] = nl[s];
+                }
+            }
         }
-        __syncthreads();   // s_part and s_wmax are read before the next stage writes them
-        const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
-        decide_stage<kRecon>(n, acc, m.b, m.s, m.t, m.bk, m.sk, book, n_codes, c2, valid, half, col, lane,
-                             s_frame[wave], (wave == 0 && valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
+        __syncthreads();   // the split is published; s_part and s_wmax are free again
     }
 
     if (wave == 0 && valid) {
@@ -617,57 +739,60 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
     }
 }
 
-// One thread per (stage, padded row): hi/lo split and half-norm of the row.
-__global__ __launch_bounds__(256)
-void prepare_rows_kernel(const float *__restrict__ books, int n_stages, int n_codes, uint8_t *__restrict__ prepared)
+// One workgroup per kChunk padded rows of a stage, 8 lanes per row (one
+// 8-dim group each, so a wavefront reads and writes 8 whole rows): hi/lo
+// split and half-norm of every row, and the largest valid half-norm of the
+// workgroup's rows.
+constexpr int kPrepThreads = 512;
+
+__global__ __launch_bounds__(kPrepThreads)
+void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__restrict__ prepared)
 {
+    __shared__ unsigned s_m[kPrepThreads / 64];
+    const int c = blockIdx.x;
+    const int q = blockIdx.y;
     const int64_t kp = padded_codes(n_codes);
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (i >= kp * n_stages) return;
-    const int q = static_cast<int>(i / kp);
-    const int k = static_cast<int>(i - q * kp);
     uint8_t *blk = prepared + q * stage_bytes(n_codes);
-    bf16x8 *row = reinterpret_cast<bf16x8 *>(blk + static_cast<int64_t>(k) * 256);
     float *norms = reinterpret_cast<float *>(blk + kp * 256);
-    if (k >= n_codes) {
-        const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-#pragma unroll
-        for (int j = 0; j < 16; ++j) row[j] = z;
-        norms[k] = kNoScore;
-        return;
-    }
-    const f32x4 *src = reinterpret_cast<const f32x4 *>(books + (static_cast<int64_t>(q) * n_codes + k) * kDim);
-    float s = 0.0f;
-#pragma unroll
-    for (int grp = 0; grp < 8; ++grp) {
-        const f32x4 a = src[2 * grp], b = src[2 * grp + 1];
+    const int grp = threadIdx.x & 7;
+    unsigned m = 0u;
+    for (int k = c * kChunk + (threadIdx.x >> 3); k < (c + 1) * kChunk; k += kPrepThreads / 8) {
+        bf16x8 *row = reinterpret_cast<bf16x8 *>(blk + static_cast<int64_t>(k) * 256);
+        if (k >= n_codes) {   // the 8 lanes of a row take the same branch
+            const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+            row[2 * grp] = z;
+            row[2 * grp + 1] = z;
+            if (grp == 0) norms[k] = kNoScore;
+            continue;
+        }
+        const f32x4 *src =
+            reinterpret_cast<const f32x4 *>(books + (static_cast<int64_t>(q) * n_codes + k) * kDim + 8 * grp);
+        const f32x4 a = src[0], b = src[1];
         const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        float s = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) s = __builtin_fmaf(v[e], v[e], s);
         bf16x8 hi, lo;
         split8(v, hi, lo);
         row[2 * grp] = hi;
         row[2 * grp + 1] = lo;
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        const float hn = 0.5f * s;
+        if (grp == 0) norms[k] = hn;
+        m = max(m, __float_as_uint(hn));   // hn >= 0: bits order like values
     }
-    norms[k] = 0.5f * s;
-}
-
-// One workgroup per stage: the largest valid half-norm (bits; values >= 0).
-__global__ __launch_bounds__(256)
-void prepare_max_kernel(int n_codes, uint8_t *__restrict__ prepared)
-{
-    __shared__ unsigned s_m[4];
-    const int64_t kp = padded_codes(n_codes);
-    uint8_t *blk = prepared + static_cast<int64_t>(blockIdx.x) * stage_bytes(n_codes);
-    const float *norms = reinterpret_cast<const float *>(blk + kp * 256);
-    unsigned m = 0u;
-    for (int k = threadIdx.x; k < n_codes; k += 256) m = max(m, __float_as_uint(norms[k]));
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
     if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0)
-        *reinterpret_cast<unsigned *>(blk + kp * 260) = max(max(s_m[0], s_m[1]), max(s_m[2], s_m[3]));
+    if (threadIdx.x == 0) {
+        unsigned mm = 0u;
+#pragma unroll
+        for (int w = 0; w < kPrepThreads / 64; ++w) mm = max(mm, s_m[w]);
+        reinterpret_cast<unsigned *>(blk + kp * 260)[c] = mm;
+    }
 }
 
 template <bool kPrepared>
@@ -717,15 +842,9 @@ int64_t prepared_bytes(int n_stages, int n_codes) { return stage_bytes(n_codes) 
 
 hipError_t launch_prepare(const float *books, int n_stages, int n_codes, void *prepared, hipStream_t stream)
 {
-    const int64_t rows = padded_codes(n_codes) * n_stages;
-    const int64_t blocks = (rows + 255) / 256;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    uint8_t *p = static_cast<uint8_t *>(prepared);
-    hipLaunchKernelGGL(prepare_rows_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                       books, n_stages, n_codes, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prepare_max_kernel, dim3(n_stages), dim3(256), 0, stream, n_codes, p);
+    const dim3 grid(static_cast<unsigned>(padded_codes(n_codes) / kChunk), static_cast<unsigned>(n_stages));
+    hipLaunchKernelGGL(prepare_kernel, grid, dim3(kPrepThreads), 0, stream, books, n_codes,
+                       static_cast<uint8_t *>(prepared));
     return hipGetLastError();
 }
 

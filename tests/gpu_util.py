@@ -33,10 +33,11 @@ def announce(what, **shape):
 
 SCORINGS = ["default", "fp32", "prepared"]
 
-# Batches of up to 8192 frames take the split-codebook encode (one 32-frame
+# Batches of up to 16384 frames take the split-codebook encode (one 32-frame
 # tile per workgroup); larger ones the wide one (256 frames per workgroup).
 # widen() embeds a small case into a batch that takes the wide kernel.
-WIDE_FRAMES = 8192 + 300
+SPLIT_MAX_FRAMES = 16384
+WIDE_FRAMES = SPLIT_MAX_FRAMES + 300
 
 
 def widen(x, seed=0):

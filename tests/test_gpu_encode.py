@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import rvq_workloads as W
-from gpu_util import SCORINGS, needs_gpu, check_encode, widen, rvq, to_dev, host, announce
+from gpu_util import SCORINGS, SPLIT_MAX_FRAMES, needs_gpu, check_encode, widen, rvq, to_dev, host, announce
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -50,7 +50,7 @@ def test_ragged_frame_counts(n, scoring):
     check_encode(x, books, scoring=scoring)
 
 
-@pytest.mark.parametrize("n", [8192, 8193, 8192 + 31])
+@pytest.mark.parametrize("n", [SPLIT_MAX_FRAMES, SPLIT_MAX_FRAMES + 1, SPLIT_MAX_FRAMES + 31])
 def test_split_threshold_frame_counts(n):
     """Either side of the split / wide switch, ragged tails included."""
     rng = np.random.default_rng(150 + n)
@@ -223,3 +223,43 @@ def test_unknown_scoring_rejected():
     import torch
     with pytest.raises(ValueError):
         m.rvq_encode_scored(torch.zeros((4, 64), device="cuda:0"), torch.zeros((1, 64, 64), device="cuda:0"), "fp8")
+
+
+def _bf16_rne(v):
+    """float32 -> bfloat16 (round to nearest even) as float32, for finite v."""
+    u = v.astype(np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("q,k", [(3, 1000), (2, 256), (1, 1)])
+def test_prepared_layout(q, k):
+    """rvq_prepare_codebooks: per stage Kp = roundup(K, 256) rows of 8-dim groups (8 hi, 8 lo bf16),
+    hi = bf16(v) and lo = bf16(v - hi) round to nearest even; Kp fp32 half-norms (FLT_MAX on padding
+    rows, which are zero); the bits of the largest valid half-norm of every 256 rows; stage blocks
+    256-byte aligned."""
+    m = rvq()
+    rng = np.random.default_rng(600 + k)
+    books = (rng.standard_normal((q, k, 64)) * 3.0).astype(np.float32)
+    books[0, 0] = 0.0
+    prep = host(m.rvq_prepare_codebooks(to_dev(books)))
+    kp = (k + 255) // 256 * 256
+    sbytes = (kp * 260 + 4 * (kp // 256) + 255) // 256 * 256
+    assert prep.size >= q * sbytes
+    for s in range(q):
+        blk = prep[s * sbytes:(s + 1) * sbytes]
+        rows = blk[:kp * 256].view(np.uint16).reshape(kp, 8, 2, 8)   # row, group, hi/lo, element
+        as_f32 = lambda h: (h.astype(np.uint32) << 16).view(np.float32)
+        hi, lo = as_f32(rows[:, :, 0, :]).reshape(kp, 64), as_f32(rows[:, :, 1, :]).reshape(kp, 64)
+        want_hi = _bf16_rne(books[s])
+        np.testing.assert_array_equal(hi[:k], want_hi)
+        np.testing.assert_array_equal(lo[:k], _bf16_rne(books[s] - want_hi))
+        assert not rows[k:].any()
+        norms = blk[kp * 256:kp * 260].view(np.float32)
+        exact = 0.5 * (books[s].astype(np.float64) ** 2).sum(axis=1)
+        np.testing.assert_allclose(norms[:k], exact, rtol=1e-6, atol=0)
+        assert (norms[k:] == np.finfo(np.float32).max).all()
+        maxima = blk[kp * 260:kp * 260 + 4 * (kp // 256)].view(np.uint32)
+        for c in range(kp // 256):
+            valid = norms[256 * c:min(256 * (c + 1), k)]
+            assert maxima[c] == (valid.view(np.uint32).max() if valid.size else 0)
