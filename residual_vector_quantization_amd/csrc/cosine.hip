@@ -22,6 +22,7 @@
 // the float64 winner (float64 distances are within 1e-14 of exact);
 // otherwise the frame is rescanned over all codewords in float64 by its
 // whole wavefront with the oracle's formula.
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -38,6 +39,11 @@ constexpr int kCosDim = 8;
 constexpr float kUnit = 5.9604644775390625e-08f;       // 2^-24
 constexpr float kScoreError = 96.0f * kUnit;
 constexpr float kAmbiguous = 2.0f * kScoreError + 1e-13f;
+// all-stage kernel: scores travel as keys with their 4 low mantissa bits
+// replaced by a per-lane codeword slot, at most 16 ulp (< 32u, as |s| < 2)
+// from the score: 24u + 32u in the worst case, 128u is used
+constexpr float kKeyScoreError = 128.0f * kUnit;
+constexpr float kKeyAmbiguous = 2.0f * kKeyScoreError + 1e-13f;
 constexpr int kArgChunk = 256;                          // unit codewords per LDS chunk
 constexpr int kProjWaves = 4;
 
@@ -365,6 +371,10 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
     // lane of output j after the butterfly: bits 5, 4, 3 of the lane are bits 2, 1, 0 of j
     const int out_id = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
     const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8;
+    // lane j < 8 stores projection output j, held by lane 32 j2 + 16 j1 + 8 j0
+    const int latent_src = 32 * ((lane >> 2) & 1) + 16 * ((lane >> 1) & 1) + 8 * (lane & 1);
+    const int n_slots = (n_codes + 63) / 64;   // codeword k = lane + 64 m, m < n_slots
+    const bool full = cols == 64 * kT;         // every column slot of a lane is in its row
 
     for (int q = 0; q < n_stages; ++q) {
         __syncthreads();   // the previous stage's LDS contents are no longer read
@@ -385,6 +395,12 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
                     hn = __builtin_fmaf(vj, vj, hn);
                 }
                 s_hn[k] = 0.5f * hn;
+            }
+            // slots up to the next multiple of 64 never win
+            for (int k = n_codes + threadIdx.x; k < 64 * n_slots; k += 64 * kFusedWaves) {
+#pragma unroll
+                for (int j = 0; j < kCosDim; ++j) s_v[k * kCosDim + j] = 0.0f;
+                s_hn[k] = FLT_MAX;
             }
         }
         __syncthreads();
@@ -443,29 +459,26 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
             for (int j = 0; j < kCosDim; ++j)
                 ev[j] = lane_value(e_own[f], 32 * ((j >> 2) & 1) + 16 * ((j >> 1) & 1) + 8 * (j & 1));
             const int64_t fr = frame0 + f;
-            if (fr < n_frames && lane < kCosDim) {
-                float mine = ev[0];
-#pragma unroll
-                for (int j = 1; j < kCosDim; ++j) mine = lane == j ? ev[j] : mine;
-                latent[(static_cast<int64_t>(q) * n_frames + fr) * kCosDim + lane] = mine;
-            }
+            const float mine = __shfl(e_own[f], latent_src);
+            if (fr < n_frames && lane < kCosDim) latent[(static_cast<int64_t>(q) * n_frames + fr) * kCosDim + lane] = mine;
             float ss = 0.0f;
 #pragma unroll
             for (int j = 0; j < kCosDim; ++j) ss = __builtin_fmaf(ev[j], ev[j], ss);
+            // outside [1e-30, 1e30] the float64 rescan decides; inside, 1/sqrt
+            // within 1 ulp keeps every element of u within 8u
             norm_ok[f] = ss >= 1e-30f && ss <= 1e30f;
-            const float inv = 1.0f / fmaxf(__builtin_sqrtf(ss), 1e-12f);
+            const float inv = __builtin_amdgcn_rsqf(norm_ok[f] ? ss : 1.0f);
 #pragma unroll
             for (int j = 0; j < kCosDim; ++j) nu[f][j] = -(ev[j] * inv);
         }
-        float best[kFusedFrames], second[kFusedFrames];
-        int bk[kFusedFrames];
+        float best[kFusedFrames], second[kFusedFrames];   // keys
 #pragma unroll
         for (int f = 0; f < kFusedFrames; ++f) {
             best[f] = INFINITY;
             second[f] = INFINITY;
-            bk[f] = 0x7fffffff;
         }
-        for (int k = lane; k < n_codes; k += 64) {   // ascending per lane: strict "<" keeps the lowest
+        for (int m = 0; m < n_slots; ++m) {
+            const int k = lane + 64 * m;
             const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&s_v[k * kCosDim]);
             const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&s_v[k * kCosDim + 4]);
             const float hn = s_hn[k];
@@ -476,13 +489,9 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
                 for (int j = 0; j < 4; ++j) s = __builtin_fmaf(nu[f][j], v0[j], s);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) s = __builtin_fmaf(nu[f][j + 4], v1[j], s);
-                if (s < best[f]) {
-                    second[f] = best[f];
-                    best[f] = s;
-                    bk[f] = k;
-                } else if (s < second[f]) {
-                    second[f] = s;
-                }
+                const float key = __uint_as_float((__float_as_uint(s) & ~15u) | static_cast<unsigned>(m));
+                second[f] = __builtin_amdgcn_fmed3f(key, best[f], second[f]);
+                best[f] = __builtin_amdgcn_fmed3f(key, best[f], -FLT_MAX);   // min (keys are finite)
             }
         }
 
@@ -490,23 +499,24 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
 #pragma unroll
         for (int f = 0; f < kFusedFrames; ++f) {
             float bv = best[f], sv = second[f];
-            int bi = bk[f];
+            const float own = bv;
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) {
                 const float ob = __shfl_xor(bv, off);
                 const float os = __shfl_xor(sv, off);
-                const int oi = __shfl_xor(bi, off);
-                if (ob < bv || (ob == bv && oi < bi)) {
-                    sv = fminf(os, bv);
-                    bv = ob;
-                    bi = oi;
-                } else {
-                    sv = fminf(sv, ob);
-                }
+                // second: the smaller of both seconds and the larger best (med3
+                // with -FLT_MAX / FLT_MAX is min / max here: bests are finite,
+                // seconds finite or +inf)
+                sv = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(sv, os, -FLT_MAX),
+                                             __builtin_amdgcn_fmed3f(bv, ob, FLT_MAX), -FLT_MAX);
+                bv = __builtin_amdgcn_fmed3f(bv, ob, -FLT_MAX);
             }
-            int pick = bi;
+            // the lowest lane holding the smallest key (equal keys: equal slot,
+            // so the lowest lane is the lowest codeword)
+            const int wl = __ffsll(static_cast<unsigned long long>(__ballot(own == bv))) - 1;
+            int pick = wl + 64 * static_cast<int>(__float_as_uint(bv) & 15u);
             const int64_t fr = frame0 + f;
-            const bool ambiguous = !norm_ok[f] || !(sv - bv > kAmbiguous);
+            const bool ambiguous = !norm_ok[f] || !(sv - bv > kKeyAmbiguous);
             if (ambiguous) {   // wave-uniform: the float64 rescan of the oracle's formula
                 double u[kCosDim];
                 double uss = 0.0;
@@ -546,11 +556,20 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
             pick = __builtin_amdgcn_readfirstlane(pick);
             if (fr < n_frames && lane == 0) codes[fr * codes_ld + q] = pick;
             const float *prow = table + (static_cast<int64_t>(q) * n_codes + pick) * hidden;
+            if (full) {
 #pragma unroll
-            for (int t = 0; t < kT; ++t) {
-                const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * ccol[t]);
+                for (int t = 0; t < kT; ++t) {
+                    const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * ccol[t]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) r[f][t][e] = inrow[t] ? r[f][t][e] - p[e] : 0.0f;
+                    for (int e = 0; e < 4; ++e) r[f][t][e] = r[f][t][e] - p[e];
+                }
+            } else {
+#pragma unroll
+                for (int t = 0; t < kT; ++t) {
+                    const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * ccol[t]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) r[f][t][e] = inrow[t] ? r[f][t][e] - p[e] : 0.0f;
+                }
             }
         }
     }
