@@ -124,10 +124,10 @@ def _csv(dirname, suffix):
 def _kernel_of(name):
     if "encode_bf16_ksplit_kernel" in name:
         return "encode_bf16_split"
+    if "encode_bf16_pipe_kernel" in name:
+        return "encode_bf16"
     if "encode_bf16_kernel" in name:
-        # template arguments <recon, residual, prepared>: the timed step runs the prepared one
-        prepared = name.split("encode_bf16_kernel<", 1)[1].split(">", 1)[0].split(",")[-1].strip()
-        return "encode_bf16" if prepared == "true" else "encode_bf16_onthefly"
+        return "encode_bf16_onthefly"   # codebooks split in every workgroup (no prepared layout)
     if "encode_kernel" in name:
         return "encode_fp32"
     if "decode_kernel" in name or "decode_tiled_kernel" in name:
@@ -200,8 +200,8 @@ def summarize_profiles(w, src_dir):
     w_scale = COPY_BYTES / (write["copy"] * 1024.0)
     enc_algo = (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d
     # the prepared encode reads the split-bf16 codebook rows (256 B), norms and stage maxima instead
-    kp = -(-k // 128) * 128
-    prep_bytes = q * (-(-(kp * 260 + 4) // 256) * 256)
+    kp = -(-k // 256) * 256
+    prep_bytes = q * (-(-(kp * 260 + 4 * (kp // 256)) // 256) * 256)
     algo = {"encode_bf16": enc_algo - 4.0 * q * k * d + prep_bytes, "encode_fp32": enc_algo,
             "decode": dec_bytes + 4.0 * q * k * d}
     lines += ["", "## HBM counters (per launch)", "",
@@ -257,6 +257,9 @@ def _trace_work(w):
         "encode_bf16_kernel": (3 * 2.0 * qe * k * d * n, "flop",
                                "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
                                "bf16 matrix flop, 3 x 2QKD per frame"),
+        "encode_bf16_pipe_kernel": (3 * 2.0 * qe * k * d * n, "flop",
+                                    "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
+                                    "bf16 matrix flop, 3 x 2QKD per frame"),
         "encode_bf16_ksplit_kernel": (3 * 2.0 * qe * k * d * n, "flop",
                                       "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
                                       "bf16 matrix flop, 3 x 2QKD per frame"),
@@ -659,7 +662,7 @@ def main():
         "decode_ms": dec_ms,
         "roofline": {"bound": "mfma",
                      "kernel": ("encode_bf16_ksplit_kernel (codebook split over a workgroup's wavefronts)"
-                                if n <= SPLIT_MAX_FRAMES else "encode_bf16_kernel") +
+                                if n <= SPLIT_MAX_FRAMES else "encode_bf16_pipe_kernel") +
                                ", prepared codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)",
                      "achieved": bf16_tflops, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": bf16_tflops / PEAK_BF16_MFMA_TFLOPS,

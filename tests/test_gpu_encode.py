@@ -51,13 +51,14 @@ def test_ragged_frame_counts(n, scoring):
 
 
 @pytest.mark.parametrize("n", [SPLIT_MAX_FRAMES, SPLIT_MAX_FRAMES + 1, SPLIT_MAX_FRAMES + 31])
-def test_split_threshold_frame_counts(n):
+@pytest.mark.parametrize("scoring", ["default", "prepared"])
+def test_split_threshold_frame_counts(n, scoring):
     """Either side of the split / wide switch, ragged tails included."""
     rng = np.random.default_rng(150 + n)
     books = _books(rng, 4, 1024)
     x = rng.standard_normal((n, 64)).astype(np.float32)
     idx = W.sample_frames(n, 600, seed=n)
-    check_encode(x, books, idx=idx)
+    check_encode(x, books, idx=idx, scoring=scoring)
 
 
 @pytest.mark.parametrize("wide", [False, True])
