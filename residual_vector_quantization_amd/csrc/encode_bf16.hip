@@ -206,13 +206,32 @@ __host__ __device__ inline int64_t stage_bytes(int n_codes)
     return (kp * 260 + 4 * (kp / kChunk) + kStageAlign - 1) / kStageAlign * kStageAlign;
 }
 
-// max_k 0.5*||c_k||^2 of a prepared stage block (values >= 0: bits order like values)
-__device__ inline float prepared_max(const uint8_t *blk, int64_t kp, int n_chunks)
+// The largest 0.5*||c_k||^2 of a prepared stage block is the maximum of its
+// Kp/kChunk words. stage_max_part loads lane's share of them (issued early,
+// so that the load is long done when the decision needs it); wave_max_bits
+// reduces the shares over the wavefront. Values are >= 0, so their bits
+// order like the values.
+__device__ __forceinline__ unsigned stage_max_part(const uint8_t *blk, int64_t kp, int lane)
 {
-    const unsigned *m = reinterpret_cast<const unsigned *>(blk + kp * 260);
-    unsigned r = 0u;
-    for (int c = 0; c < n_chunks; ++c) r = max(r, m[c]);
-    return __uint_as_float(r);
+    const unsigned *words = reinterpret_cast<const unsigned *>(blk + kp * 260);
+    const int n_words = static_cast<int>(kp / kChunk);
+    unsigned m = lane < n_words ? words[lane] : 0u;
+    for (int c = lane + 64; c < n_words; c += 64) m = max(m, words[c]);
+    return m;
+}
+
+__device__ __forceinline__ float wave_max_bits(unsigned m)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
+    return __uint_as_float(m);
+}
+
+// An upper bound of sqrt(x) for x >= 0: the hardware square root (within a
+// few ulp) of max(x, FLT_MIN), raised by 2^-20 of itself.
+__device__ __forceinline__ float sqrt_up(float x)
+{
+    return __builtin_amdgcn_sqrtf(fmaxf(x, FLT_MIN)) * (1.0f + 9.5367431640625e-07f);
 }
 
 // The decision for one stage, from this lane's best / second / third keys
@@ -239,7 +258,7 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], f
     for (int j = 0; j < 32; ++j) rn = __builtin_fmaf(n[j], n[j], rn);
     rn = rn + __shfl_xor(rn, 32);
 
-    const float bound = kBoundScale * (c2 + sqrtf(rn) * sqrtf(2.0f * c2)) + kAbsSlack;
+    const float bound = kBoundScale * (c2 + sqrt_up(rn) * sqrt_up(2.0f * c2)) + kAbsSlack;
     const float lim = fminf(best, best_o) + 2.0f * bound;
     const bool overflow = third <= lim || third_o <= lim ||
                           (second <= lim && second_k == best_k) ||
@@ -611,8 +630,9 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
         unsigned wmax = 0u;
         float c2 = 0.0f;   // max_k 0.5||c_k||^2 over the stage
 
+        unsigned cmax = 0u;   // prepared: wavefront 0's share of the stage maximum
         if constexpr (kPrepared) {
-            c2 = prepared_max(prepared + q * sbytes, kp, static_cast<int>(kp / kChunk));
+            if (wave == 0) cmax = stage_max_part(prepared + q * sbytes, kp, lane);
             for (int ib = 0; ib < my_blocks; ++ib, ++item) {
                 if (ib + 1 < my_blocks) {
                     load_block(q, ib + 1, (item + 1) & 1);
@@ -683,7 +703,9 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
                 top3_insert(m, s_part[w][1][lane], __float_as_int(s_part[w][4][lane]));
                 top3_insert(m, s_part[w][2][lane], -1);
             }
-            if constexpr (!kPrepared) {
+            if constexpr (kPrepared) {
+                c2 = wave_max_bits(cmax);
+            } else {
                 unsigned mm = 0u;
 #pragma unroll
                 for (int w = 0; w < kSplitWaves; ++w) mm = max(mm, s_wmax[w]);
@@ -935,7 +957,16 @@ void encode_bf16_pipe_kernel(const float *__restrict__ x, int64_t n_frames,
 
     // wavefront w copies rows 32w .. 32w+31 of chunk g and their half-norms
     // into buffer g % 2; slot t of its rows is segment t % 17 of row t / 17,
-    // the 17th (padding) slot of a row takes the row's first segment again
+    // the 17th (padding) slot of a row takes the row's first segment again.
+    // Source byte offsets of this lane's slots, fixed for the whole kernel:
+    unsigned slot_off[kWaveLoads];
+#pragma unroll
+    for (int i = 0; i < kWaveLoads; ++i) {
+        const int t = i * 64 + lane;
+        const int r = t / kRowSlots;
+        const int seg = t - r * kRowSlots;
+        slot_off[i] = static_cast<unsigned>(r * 256 + (seg < kRowSlots - 1 ? seg * 16 : 0));
+    }
     auto dma_chunk = [&](int g) {
         const int q = g / n_chunks;
         const int c = g - q * n_chunks;
@@ -944,13 +975,8 @@ void encode_bf16_pipe_kernel(const float *__restrict__ x, int64_t n_frames,
         const uint8_t *src = blk + static_cast<int64_t>(k0) * 256;
         __bf16 *dst = s_book[g & 1] + 32 * wave * kRowH;
 #pragma unroll
-        for (int i = 0; i < kWaveLoads; ++i) {
-            int t = i * 64 + lane;
-            asm volatile("" : "+v"(t));   // recomputed per chunk rather than held in registers
-            const int r = t / kRowSlots;
-            const int seg = t - r * kRowSlots;
-            if (t < kWaveSlots) dma16(src + r * 256 + (seg < kRowSlots - 1 ? seg * 16 : 0), dst + i * 512);
-        }
+        for (int i = 0; i < kWaveLoads; ++i)
+            if (i * 64 + lane < kWaveSlots) dma16(src + slot_off[i], dst + i * 512);
         if (lane < 8) dma16(blk + kp * 256 + static_cast<int64_t>(k0 + 4 * lane) * 4, s_norm[g & 1] + 32 * wave);
     };
 
@@ -959,6 +985,7 @@ void encode_bf16_pipe_kernel(const float *__restrict__ x, int64_t n_frames,
     __syncthreads();
 
     for (int q = 0; q < n_stages; ++q) {
+        const unsigned cmax = stage_max_part(prepared + q * sbytes, kp, lane);   // used at the decision
 #pragma unroll
         for (int s = 0; s < 4; ++s) split8(&n[8 * s], nh[s], nl[s]);
         float best = kNoScore, second = kNoScore, third = kNoScore;
@@ -993,7 +1020,7 @@ void encode_bf16_pipe_kernel(const float *__restrict__ x, int64_t n_frames,
 
         // ---- stage q is scored for this wavefront's 32 frames: decide ----
         const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
-        const float c2 = prepared_max(prepared + q * sbytes, kp, n_chunks);
+        const float c2 = wave_max_bits(cmax);
         decide_stage<kRecon>(n, acc, best, second, third, best_k, second_k, book, n_codes, c2, valid, half, col,
                              lane, s_frame[wave], (valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
         if (q + 1 < n_stages) {
