@@ -397,7 +397,7 @@ def cpu_baseline(w, x, books, codes_gpu, target_s):
 # --------------------------------------------------------------- benches
 
 def bench_projected(args, w):
-    """fc -> encode -> decode -> fc2 per step (rvq_project_roundtrip)."""
+    """Codebook preparation, then fc -> encode -> decode -> fc2, per step (rvq_project_roundtrip)."""
     import torch
     import residual_vector_quantization_amd as rvq
     books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
@@ -410,9 +410,12 @@ def bench_projected(args, w):
     n, q, k, d, hid = w.n_frames, w.n_stages, w.n_codes, w.dim, w.hidden
     out = (torch.empty((n, q), dtype=torch.int32, device=dev), torch.empty((n, d), device=dev),
            torch.empty((n, d), device=dev), torch.empty((n, hid), device=dev))
+    prep = torch.empty(rvq.rvq_prepared_bytes(q, k, d), dtype=torch.uint8, device=dev)
 
     def step():
-        rvq.rvq_project_roundtrip(t["h"], t["w_in"], t["b_in"], t["books"], t["w_out"], t["b_out"], out=out)
+        rvq.rvq_prepare_codebooks(t["books"], prep)
+        rvq.rvq_project_roundtrip(t["h"], t["w_in"], t["b_in"], t["books"], t["w_out"], t["b_out"], out=out,
+                                  prepared=prep)
 
     for _ in range(args.warmup):
         step()
@@ -440,7 +443,7 @@ def bench_projected(args, w):
 
 
 def bench_stage_projected(args, w):
-    """Per-stage projected RVQ: table prepare + encode + decode per step."""
+    """Per-stage projected RVQ: table (and codebook) preparation + encode + decode per step."""
     import torch
     import residual_vector_quantization_amd as rvq
     import oracle
@@ -457,6 +460,7 @@ def bench_stage_projected(args, w):
     out = (torch.empty((n, q), dtype=torch.int32, device=dev), torch.empty((q, n, d), device=dev),
            torch.empty((n, hid), device=dev))
     recon = torch.empty((n, hid), device=dev)
+    prep = None if w.normalized else torch.empty(rvq.rvq_prepared_bytes(q, k, d), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
         if ev is not None:
@@ -464,12 +468,14 @@ def bench_stage_projected(args, w):
         rvq.rvq_projected_prepare(t["books"], t["w_out"], t["b_out"], table)
         if w.normalized:
             rvq.rvq_cosine_prepare(t["books"], units)
+        else:
+            rvq.rvq_prepare_codebooks(t["books"], prep)
         if ev is not None:
             ev[1].record()
         if w.normalized:
             rvq.rvq_cosine_encode(t["h"], t["w_in"], t["b_in"], units, table, out=out)
         else:
-            rvq.rvq_projected_encode(t["h"], t["w_in"], t["b_in"], t["books"], table, out=out)
+            rvq.rvq_projected_encode(t["h"], t["w_in"], t["b_in"], t["books"], table, out=out, prepared=prep)
         if ev is not None:
             ev[2].record()
         rvq.rvq_projected_decode(out[0], table, out=recon)

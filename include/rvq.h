@@ -193,6 +193,10 @@ RVQ_API rvq_status rvq_encode_prepared(const float *x, int64_t n_frames, int32_t
  *   h            [n_frames, hidden] input (read only)
  *   w_in         [dim, hidden]  PyTorch (out, in) order; b_in [dim] or NULL
  *   codebooks    [n_stages, n_codes, dim]
+ *   prepared     NULL, or rvq_prepare_codebooks' output for these codebooks
+ *                (16-byte aligned, at least rvq_prepared_bytes(n_stages,
+ *                n_codes, dim) bytes); the encode then reads it as
+ *                rvq_encode_prepared does (same results, faster)
  *   w_out        [hidden, dim]  PyTorch (out, in) order; b_out [hidden] or NULL
  *   codes, latent, latent_recon, h_recon: caller-allocated outputs
  *
@@ -202,7 +206,8 @@ RVQ_API rvq_status rvq_encode_prepared(const float *x, int64_t n_frames, int32_t
  */
 RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32_t hidden,
                                          const float *w_in, const float *b_in,
-                                         const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                         const float *codebooks, const void *prepared,
+                                         int32_t n_stages, int32_t n_codes,
                                          int32_t dim, const float *w_out, const float *b_out,
                                          int32_t *codes, int32_t codes_ld, float *latent,
                                          float *latent_recon, float *h_recon, void *stream);
@@ -222,8 +227,9 @@ RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32
  *   w_in [n_stages, dim, hidden], b_in [n_stages, dim] or NULL,
  *   w_out [n_stages, hidden, dim], b_out [n_stages, hidden] or NULL.
  * dim must be 64 (8 for the table of the normalized quantizer below) and
- * hidden a positive multiple of 64 (RVQ_ERR_UNSUPPORTED otherwise). All pointers are caller-owned device memory, 16-byte aligned
- * (codes 4-byte); calls enqueue on `stream` and return.
+ * hidden a positive multiple of 64 (RVQ_ERR_UNSUPPORTED otherwise). All
+ * pointers are caller-owned device memory, 16-byte aligned (codes 4-byte);
+ * calls enqueue on `stream` and return.
  *
  * rvq_projected_prepare writes the table of projected codewords
  *   table [n_stages, n_codes, hidden] float32,
@@ -233,7 +239,10 @@ RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32
  *
  * rvq_projected_encode runs the loop above on n_frames hidden vectors h
  * [n_frames, hidden], reading the out-projections from `table` (prepared
- * from the same codebooks and weights; the library cannot check this):
+ * from the same codebooks and weights; the library cannot check this).
+ * `prepared` is NULL or rvq_prepare_codebooks' output for `codebooks`
+ * (at least rvq_prepared_bytes(n_stages, n_codes, dim) bytes): each
+ * stage's argmin then reads its stage block (same results, faster).
  *   codes    [n_frames, codes_ld] output, column q = k_q
  *   latent   [n_stages, n_frames, dim] output, latent[q] = e_q, computed as
  *            fp32 sums on the matrix cores (bias added last); the argmin of
@@ -253,7 +262,7 @@ RVQ_API rvq_status rvq_projected_prepare(const float *codebooks, int32_t n_stage
                                          int32_t hidden, float *table, void *stream);
 RVQ_API rvq_status rvq_projected_encode(const float *h, int64_t n_frames, int32_t hidden,
                                         const float *w_in, const float *b_in,
-                                        const float *codebooks, const float *table,
+                                        const float *codebooks, const void *prepared, const float *table,
                                         int32_t n_stages, int32_t n_codes, int32_t dim,
                                         int32_t *codes, int32_t codes_ld,
                                         float *latent, float *residual, void *stream);
@@ -279,8 +288,9 @@ RVQ_API rvq_status rvq_projected_decode(const int32_t *codes, int32_t codes_ld, 
  * aligned, caller-owned), the unit codewords v computed in float64
  * (squares summed in order, sqrt, one division per element).
  *
- * rvq_cosine_encode: arguments as rvq_projected_encode, with dim == 8,
- * hidden a multiple of 64 and at most 1024 (RVQ_ERR_UNSUPPORTED otherwise),
+ * rvq_cosine_encode: arguments as rvq_projected_encode, with `units` in
+ * place of `codebooks` and `prepared`, dim == 8, hidden a multiple of 64
+ * and at most 1024 (RVQ_ERR_UNSUPPORTED otherwise),
  * `units` from rvq_cosine_prepare and `table` from rvq_projected_prepare
  * (both from the same codebooks and weights), latent [n_stages, n_frames, 8]
  * the fp32 projections e_q (bias added last).

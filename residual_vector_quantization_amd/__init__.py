@@ -86,12 +86,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.rvq_encode_prepared.restype = ctypes.c_int
     lib.rvq_encode_prepared.argtypes = [vp, i64, i32, vp, vp, i32, i32, vp, i32, vp, vp, vp]
     lib.rvq_project_roundtrip.restype = ctypes.c_int
-    lib.rvq_project_roundtrip.argtypes = [vp, i64, i32, vp, vp, vp, i32, i32, i32, vp, vp,
+    lib.rvq_project_roundtrip.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, vp,
                                           vp, i32, vp, vp, vp, vp]
     lib.rvq_projected_prepare.restype = ctypes.c_int
     lib.rvq_projected_prepare.argtypes = [vp, i32, i32, i32, vp, vp, i32, vp, vp]
     lib.rvq_projected_encode.restype = ctypes.c_int
-    lib.rvq_projected_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
+    lib.rvq_projected_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     lib.rvq_projected_decode.restype = ctypes.c_int
     lib.rvq_projected_decode.argtypes = [vp, i32, i64, vp, i32, i32, i32, vp, vp]
     lib.rvq_cosine_prepare.restype = ctypes.c_int
@@ -266,6 +266,16 @@ def rvq_prepare_codebooks(codebooks: torch.Tensor, prepared: Optional[torch.Tens
     return prepared
 
 
+def _check_prepared(prepared: Optional[torch.Tensor], codebooks: torch.Tensor, q: int) -> None:
+    """A prepared-codebook buffer, if given, must be a uint8 tensor on the codebooks' device large enough
+    for their first ``q`` stages."""
+    if prepared is None:
+        return
+    _require(prepared, "prepared", torch.uint8, 1, codebooks.device)
+    if prepared.numel() < rvq_prepared_bytes(q, codebooks.shape[1], codebooks.shape[2]):
+        raise ValueError("prepared buffer is too small for these codebooks")
+
+
 def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torch.Tensor,
                         n_stages: Optional[int] = None, recon: bool = False, residual: bool = True,
                         out=None):
@@ -295,13 +305,14 @@ def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torc
 
 def rvq_project_roundtrip(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[torch.Tensor],
                           codebooks: torch.Tensor, w_out: torch.Tensor, b_out: Optional[torch.Tensor],
-                          n_stages: Optional[int] = None, out=None):
+                          n_stages: Optional[int] = None, out=None, prepared: Optional[torch.Tensor] = None):
     """fc -> encode -> decode -> fc2 on ``h`` [N, H].
 
     ``w_in`` [D, H], ``w_out`` [H, D] in PyTorch (out, in) order, biases
     [D] / [H] or None. Returns ``(codes [N, Q], latent [N, D],
     latent_recon [N, D], h_recon [N, H])``; ``out`` may pass those four
-    tensors preallocated.
+    tensors preallocated. ``prepared``: optional ``rvq_prepare_codebooks``
+    output for ``codebooks`` (same results, faster encode).
     """
     _require(h, "h", torch.float32, 2)
     dev = h.device
@@ -318,14 +329,15 @@ def rvq_project_roundtrip(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[to
             if b.shape[0] != size:
                 raise ValueError(f"{name} must have {size} entries")
     q = _stages(codebooks, n_stages)
+    _check_prepared(prepared, codebooks, q)
     if out is None:
         out = (torch.empty((n, q), dtype=torch.int32, device=dev),
                torch.empty((n, d), dtype=torch.float32, device=dev),
                torch.empty((n, d), dtype=torch.float32, device=dev),
                torch.empty((n, hid), dtype=torch.float32, device=dev))
     codes, latent, latent_recon, h_recon = out
-    st = load().rvq_project_roundtrip(_ptr(h), n, hid, _ptr(w_in), _ptr(b_in), _ptr(codebooks), q,
-                                      codebooks.shape[1], d, _ptr(w_out), _ptr(b_out), _ptr(codes),
+    st = load().rvq_project_roundtrip(_ptr(h), n, hid, _ptr(w_in), _ptr(b_in), _ptr(codebooks), _ptr(prepared),
+                                      q, codebooks.shape[1], d, _ptr(w_out), _ptr(b_out), _ptr(codes),
                                       codes.shape[1], _ptr(latent), _ptr(latent_recon), _ptr(h_recon),
                                       _stream(h))
     _check("rvq_project_roundtrip", st)
@@ -363,13 +375,15 @@ def rvq_projected_prepare(codebooks: torch.Tensor, w_out: torch.Tensor, b_out: O
 
 def rvq_projected_encode(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[torch.Tensor],
                          codebooks: torch.Tensor, table: torch.Tensor, n_stages: Optional[int] = None,
-                         out=None):
+                         out=None, prepared: Optional[torch.Tensor] = None):
     """Per-stage projected encode of ``h`` [N, H].
 
     ``w_in`` [Q, D, H], ``b_in`` [Q, D] or None, ``table`` from
     ``rvq_projected_prepare``. Returns ``(codes [N, Q], latent [Q, N, D],
     residual [N, H])``; ``out`` may pass those three tensors preallocated
-    (codes may be [N, L] with L >= Q).
+    (codes may be [N, L] with L >= Q). ``prepared``: optional
+    ``rvq_prepare_codebooks`` output for ``codebooks`` (same results,
+    faster argmin).
     """
     _require(h, "h", torch.float32, 2)
     dev = h.device
@@ -398,8 +412,10 @@ def rvq_projected_encode(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[tor
     if codes.shape[0] != n or codes.shape[1] < q or latent.shape[0] < q or tuple(latent.shape[1:]) != (n, d) \
             or residual.shape != h.shape:
         raise ValueError("output shapes do not match")
-    st = load().rvq_projected_encode(_ptr(h), n, hid, _ptr(w_in), _ptr(b_in), _ptr(codebooks), _ptr(table), q, k,
-                                     d, _ptr(codes), codes.shape[1], _ptr(latent), _ptr(residual), _stream(h))
+    _check_prepared(prepared, codebooks, q)
+    st = load().rvq_projected_encode(_ptr(h), n, hid, _ptr(w_in), _ptr(b_in), _ptr(codebooks), _ptr(prepared),
+                                     _ptr(table), q, k, d, _ptr(codes), codes.shape[1], _ptr(latent),
+                                     _ptr(residual), _stream(h))
     _check("rvq_projected_encode", st)
     return codes, latent, residual
 

@@ -150,7 +150,8 @@ RVQ_API rvq_status rvq_encode_prepared(const float *x, int64_t n_frames, int32_t
 
 RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32_t hidden,
                                          const float *w_in, const float *b_in,
-                                         const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                         const float *codebooks, const void *prepared,
+                                         int32_t n_stages, int32_t n_codes,
                                          int32_t dim, const float *w_out, const float *b_out,
                                          int32_t *codes, int32_t codes_ld, float *latent,
                                          float *latent_recon, float *h_recon, void *stream)
@@ -164,13 +165,15 @@ RVQ_API rvq_status rvq_project_roundtrip(const float *h, int64_t n_frames, int32
         return RVQ_ERR_INVALID_ARG;
     if (!aligned(h, 16) || !aligned(w_in, 16) || !aligned(codebooks, 16) || !aligned(w_out, 16) ||
         !aligned(codes, 4) || !aligned(latent, 16) || !aligned(latent_recon, 16) || !aligned(h_recon, 16) ||
-        (b_in && !aligned(b_in, 16)) || (b_out && !aligned(b_out, 16)))
+        (b_in && !aligned(b_in, 16)) || (b_out && !aligned(b_out, 16)) || (prepared && !aligned(prepared, 16)))
         return RVQ_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = rvq::launch_linear_in(h, n_frames, hidden, w_in, b_in, latent, s);
     if (e == hipSuccess)
-        e = launch_scored(RVQ_SCORING_DEFAULT, latent, n_frames, codebooks, n_stages, n_codes, codes,
-                          codes_ld, nullptr, latent_recon, s);
+        e = prepared ? rvq::launch_encode_prepared(latent, n_frames, codebooks, prepared, n_stages, n_codes, codes,
+                                                   codes_ld, nullptr, latent_recon, s)
+                     : launch_scored(RVQ_SCORING_DEFAULT, latent, n_frames, codebooks, n_stages, n_codes, codes,
+                                     codes_ld, nullptr, latent_recon, s);
     if (e == hipSuccess)
         e = rvq::launch_linear_out(latent_recon, n_frames, hidden, w_out, b_out, h_recon, s);
     return from_hip(e);
@@ -194,7 +197,7 @@ RVQ_API rvq_status rvq_projected_prepare(const float *codebooks, int32_t n_stage
 
 RVQ_API rvq_status rvq_projected_encode(const float *h, int64_t n_frames, int32_t hidden,
                                         const float *w_in, const float *b_in,
-                                        const float *codebooks, const float *table,
+                                        const float *codebooks, const void *prepared, const float *table,
                                         int32_t n_stages, int32_t n_codes, int32_t dim,
                                         int32_t *codes, int32_t codes_ld,
                                         float *latent, float *residual, void *stream)
@@ -206,11 +209,13 @@ RVQ_API rvq_status rvq_projected_encode(const float *h, int64_t n_frames, int32_
     if (n_frames == 0) return RVQ_OK;
     if (!h || !w_in || !codebooks || !table || !codes || !latent || !residual) return RVQ_ERR_INVALID_ARG;
     if (!aligned(h, 16) || !aligned(w_in, 16) || !aligned(codebooks, 16) || !aligned(table, 16) ||
-        !aligned(codes, 4) || !aligned(latent, 16) || !aligned(residual, 16) || (b_in && !aligned(b_in, 16)))
+        !aligned(codes, 4) || !aligned(latent, 16) || !aligned(residual, 16) || (b_in && !aligned(b_in, 16)) ||
+        (prepared && !aligned(prepared, 16)))
         return RVQ_ERR_INVALID_ARG;
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
     const int64_t table_stage = static_cast<int64_t>(n_codes) * hidden;
+    const int64_t prepared_stage = rvq::prepared_bytes(1, n_codes);   // stage blocks are consecutive
     for (int32_t q = 0; q < n_stages && e == hipSuccess; ++q) {
         float *lat = latent + static_cast<int64_t>(q) * n_frames * rvq::kDim;
         const float *book = codebooks + static_cast<int64_t>(q) * n_codes * rvq::kDim;
@@ -226,8 +231,11 @@ RVQ_API rvq_status rvq_projected_encode(const float *h, int64_t n_frames, int32_
                                              hidden, wq, bq, lat, s);
         }
         if (e == hipSuccess)
-            e = launch_scored(RVQ_SCORING_DEFAULT, lat, n_frames, book, 1, n_codes, codes + q, codes_ld,
-                              nullptr, nullptr, s);
+            e = prepared ? rvq::launch_encode_prepared(lat, n_frames, book,
+                                                       static_cast<const uint8_t *>(prepared) + q * prepared_stage,
+                                                       1, n_codes, codes + q, codes_ld, nullptr, nullptr, s)
+                         : launch_scored(RVQ_SCORING_DEFAULT, lat, n_frames, book, 1, n_codes, codes + q, codes_ld,
+                                         nullptr, nullptr, s);
     }
     if (e == hipSuccess)
         e = rvq::launch_projected_update(n_stages == 1 ? h : residual, codes + (n_stages - 1), codes_ld, n_frames,

@@ -39,13 +39,16 @@ int main(void)
     bad += expect("decode ld<q", rvq_decode(ic, 4, 10, fx, 8, 1024, 64, fx, NULL), RVQ_ERR_INVALID_ARG);
     bad += expect("decode misaligned out", rvq_decode(ic, 8, 10, fx, 8, 1024, 64, fx + 2, NULL), RVQ_ERR_INVALID_ARG);
     bad += expect("decode empty", rvq_decode(NULL, 8, 0, NULL, 8, 1024, 64, NULL, NULL), RVQ_OK);
-    bad += expect("project hidden 100", rvq_project_roundtrip(fx, 10, 100, fx, NULL, fx, 8, 1024, 64, fx, NULL,
+    bad += expect("project hidden 100", rvq_project_roundtrip(fx, 10, 100, fx, NULL, fx, NULL, 8, 1024, 64, fx, NULL,
                                                               ic, 8, fx, fx, fx, NULL), RVQ_ERR_UNSUPPORTED);
-    bad += expect("project null h_recon", rvq_project_roundtrip(fx, 10, 1024, fx, NULL, fx, 8, 1024, 64, fx, NULL,
+    bad += expect("project null h_recon", rvq_project_roundtrip(fx, 10, 1024, fx, NULL, fx, NULL, 8, 1024, 64, fx, NULL,
                                                                 ic, 8, fx, fx, NULL, NULL), RVQ_ERR_INVALID_ARG);
-    bad += expect("project misaligned bias", rvq_project_roundtrip(fx, 10, 1024, fx, fx + 1, fx, 8, 1024, 64, fx,
+    bad += expect("project misaligned bias", rvq_project_roundtrip(fx, 10, 1024, fx, fx + 1, fx, NULL, 8, 1024, 64, fx,
                                                                    NULL, ic, 8, fx, fx, fx, NULL), RVQ_ERR_INVALID_ARG);
-    bad += expect("project empty", rvq_project_roundtrip(NULL, 0, 1024, NULL, NULL, NULL, 8, 1024, 64, NULL, NULL,
+    bad += expect("project misaligned prepared", rvq_project_roundtrip(fx, 10, 1024, fx, NULL, fx, (const char *)fx + 4,
+                                                                       8, 1024, 64, fx, NULL, ic, 8, fx, fx, fx, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("project empty", rvq_project_roundtrip(NULL, 0, 1024, NULL, NULL, NULL, NULL, 8, 1024, 64, NULL, NULL,
                                                          NULL, 8, NULL, NULL, NULL, NULL), RVQ_OK);
     bad += expect("scored bad mode", rvq_encode_scored(fx, 10, 64, fx, 8, 1024, ic, 8, NULL, NULL, (rvq_scoring)7, NULL),
                   RVQ_ERR_INVALID_ARG);
@@ -65,13 +68,16 @@ int main(void)
                   RVQ_ERR_INVALID_ARG);
     bad += expect("projected prepare misaligned bias", rvq_projected_prepare(fx, 8, 1024, 64, fx, fx + 1, 1024, fx, NULL),
                   RVQ_ERR_INVALID_ARG);
-    bad += expect("projected encode null latent", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, fx, 8, 1024, 64,
+    bad += expect("projected encode null latent", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, NULL, fx, 8, 1024, 64,
                                                                        ic, 8, NULL, fx, NULL), RVQ_ERR_INVALID_ARG);
-    bad += expect("projected encode dim 32", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, fx, 8, 1024, 32,
+    bad += expect("projected encode dim 32", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, NULL, fx, 8, 1024, 32,
                                                                   ic, 8, fx, fx, NULL), RVQ_ERR_UNSUPPORTED);
-    bad += expect("projected encode ld<q", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, fx, 8, 1024, 64,
+    bad += expect("projected encode ld<q", rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, NULL, fx, 8, 1024, 64,
                                                                 ic, 7, fx, fx, NULL), RVQ_ERR_INVALID_ARG);
-    bad += expect("projected encode empty", rvq_projected_encode(NULL, 0, 1024, NULL, NULL, NULL, NULL, 8, 1024, 64,
+    bad += expect("projected encode misaligned prepared",
+                  rvq_projected_encode(fx, 10, 1024, fx, NULL, fx, (const char *)fx + 8, fx, 8, 1024, 64, ic, 8, fx, fx,
+                                       NULL), RVQ_ERR_INVALID_ARG);
+    bad += expect("projected encode empty", rvq_projected_encode(NULL, 0, 1024, NULL, NULL, NULL, NULL, NULL, 8, 1024, 64,
                                                                  NULL, 8, NULL, NULL, NULL), RVQ_OK);
     bad += expect("projected decode null out", rvq_projected_decode(ic, 8, 10, fx, 8, 1024, 1024, NULL, NULL),
                   RVQ_ERR_INVALID_ARG);

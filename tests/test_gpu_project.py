@@ -26,12 +26,15 @@ def _rel_rows(a, b):
     return num / np.maximum(den, 1e-30)
 
 
-def check_project(h, w_in, b_in, books, w_out, b_out, idx=None):
+def check_project(h, w_in, b_in, books, w_out, b_out, idx=None, prepared=False):
+    """``prepared``: pass rvq_prepare_codebooks' output (the encode then reads the prepared layout)."""
     m = rvq()
-    announce("project_roundtrip", n=h.shape[0], hidden=h.shape[1], q=books.shape[0])
+    announce("project_roundtrip", n=h.shape[0], hidden=h.shape[1], q=books.shape[0], prepared=prepared)
     dev = lambda a: None if a is None else to_dev(a)
+    bg = to_dev(books)
+    prep = m.rvq_prepare_codebooks(bg) if prepared else None
     codes, lat, lat_rec, h_rec = (host(t) for t in m.rvq_project_roundtrip(
-        to_dev(h), to_dev(w_in), dev(b_in), to_dev(books), to_dev(w_out), dev(b_out)))
+        to_dev(h), to_dev(w_in), dev(b_in), bg, to_dev(w_out), dev(b_out), prepared=prep))
     sel = np.arange(h.shape[0]) if idx is None else idx
     o = oracle.get()
     y = o.linear(h[sel], w_in, b_in)
@@ -46,9 +49,10 @@ def check_project(h, w_in, b_in, books, w_out, b_out, idx=None):
     return float(r1.max()), float(r3.max())
 
 
+@pytest.mark.parametrize("prepared", [False, True])
 @pytest.mark.parametrize("n,hidden,bias", [(677, 1024, True), (300, 1024, False), (129, 192, True),
-                                           (1, 64, True)])
-def test_project_small(n, hidden, bias):
+                                           (1, 64, True), (16500, 128, True)])
+def test_project_small(n, hidden, bias, prepared):
     rng = np.random.default_rng(n + hidden)
     h = rng.standard_normal((n, hidden)).astype(np.float32)
     w_in = (rng.standard_normal((64, hidden)) / np.sqrt(hidden)).astype(np.float32)
@@ -56,17 +60,18 @@ def test_project_small(n, hidden, bias):
     b_in = rng.standard_normal(64).astype(np.float32) if bias else None
     b_out = rng.standard_normal(hidden).astype(np.float32) if bias else None
     books = (rng.standard_normal((8, 1024, 64)) * 0.5 ** np.arange(8)[:, None, None]).astype(np.float32)
-    e1, e3 = check_project(h, w_in, b_in, books, w_out, b_out)
+    e1, e3 = check_project(h, w_in, b_in, books, w_out, b_out, prepared=prepared)
     announce("project errors", fc=e1, fc2=e3)
 
 
-def test_project_full_size_sampled():
+@pytest.mark.parametrize("prepared", [False, True])
+def test_project_full_size_sampled(prepared):
     w = W.WORKLOADS["projected"]
     books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
     w_in, b_in, w_out, b_out = W.projection_weights(w)
     h = W.hidden_states(w)
     idx = W.sample_frames(w.n_frames, 2048, seed=4)
-    e1, e3 = check_project(h, w_in, b_in, books, w_out, b_out, idx=idx)
+    e1, e3 = check_project(h, w_in, b_in, books, w_out, b_out, idx=idx, prepared=prepared)
     announce("project full-size errors", fc=e1, fc2=e3)
 
 

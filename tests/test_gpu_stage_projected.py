@@ -44,11 +44,12 @@ def _weights(rng, q, k, hidden, bias, decay=0.5):
 
 
 def check_stage_projected(h, books, w_in, b_in, w_out, b_out, idx=None, n_stages=None, codes_ld=None,
-                          in_place=False):
+                          in_place=False, prepared=False):
+    """``prepared``: pass rvq_prepare_codebooks' output, so that every stage's argmin reads its block."""
     m = rvq()
     q = books.shape[0] if n_stages is None else n_stages
     n, hidden = h.shape
-    announce("stage_projected", n=n, hidden=hidden, q=q, k=books.shape[1], in_place=in_place)
+    announce("stage_projected", n=n, hidden=hidden, q=q, k=books.shape[1], in_place=in_place, prepared=prepared)
     dev = lambda a: None if a is None else to_dev(a)
     bg, wo, bo = to_dev(books), to_dev(w_out), dev(b_out)
     table = m.rvq_projected_prepare(bg, wo, bo)
@@ -57,7 +58,9 @@ def check_stage_projected(h, books, w_in, b_in, w_out, b_out, idx=None, n_stages
     codes_buf = torch.full((n, ld), -7, dtype=torch.int32, device=hg.device)
     latent = torch.empty((q, n, 64), dtype=torch.float32, device=hg.device)
     residual = hg if in_place else torch.empty_like(hg)
-    m.rvq_projected_encode(hg, to_dev(w_in), dev(b_in), bg, table, n_stages=q, out=(codes_buf, latent, residual))
+    prep = m.rvq_prepare_codebooks(bg) if prepared else None
+    m.rvq_projected_encode(hg, to_dev(w_in), dev(b_in), bg, table, n_stages=q, out=(codes_buf, latent, residual),
+                           prepared=prep)
     recon = m.rvq_projected_decode(codes_buf, table, n_stages=q)
     torch.cuda.synchronize()
     codes_all, lat, res, rec, tab = host(codes_buf), host(latent), host(residual), host(recon), host(table)
@@ -90,14 +93,15 @@ def check_stage_projected(h, books, w_in, b_in, w_out, b_out, idx=None, n_stages
     return {"frames": int(sel.size), "latent_max_rel": float(rel.max()), "mismatch_frames": int(mism.sum())}
 
 
+@pytest.mark.parametrize("prepared", [False, True])
 @pytest.mark.parametrize("n,hidden,q,k,bias", [(1, 64, 1, 64, True), (31, 192, 3, 100, True),
                                                (129, 1024, 8, 1024, True), (677, 1024, 2, 1000, False),
                                                (1000, 320, 5, 257, True), (257, 64, 8, 1024, False)])
-def test_stage_projected_small(n, hidden, q, k, bias):
+def test_stage_projected_small(n, hidden, q, k, bias, prepared):
     rng = np.random.default_rng(n * 3 + hidden + q + k)
     h = rng.standard_normal((n, hidden)).astype(np.float32)
     books, w_in, b_in, w_out, b_out = _weights(rng, q, k, hidden, bias)
-    rep = check_stage_projected(h, books, w_in, b_in, w_out, b_out)
+    rep = check_stage_projected(h, books, w_in, b_in, w_out, b_out, prepared=prepared)
     announce("stage_projected report", **rep)
 
 
@@ -106,7 +110,9 @@ def test_stage_projected_partial_depth_ld_and_in_place():
     h = rng.standard_normal((300, 256)).astype(np.float32)
     books, w_in, b_in, w_out, b_out = _weights(rng, 6, 512, 256, True)
     check_stage_projected(h, books, w_in, b_in, w_out, b_out, n_stages=4, codes_ld=7)
+    check_stage_projected(h, books, w_in, b_in, w_out, b_out, n_stages=4, codes_ld=7, prepared=True)
     check_stage_projected(h, books, w_in, b_in, w_out, b_out, in_place=True)
+    check_stage_projected(h, books, w_in, b_in, w_out, b_out, in_place=True, prepared=True)
 
 
 def test_stage_projected_identity_is_plain_rvq():
@@ -161,12 +167,13 @@ def test_stage_projected_empty_and_errors():
     assert e.value.status == m.RVQ_ERR_UNSUPPORTED
 
 
-def test_stage_projected_full_size_sampled():
-    """The benchmark's workload and launch configuration; oracle on a seeded frame sample."""
+@pytest.mark.parametrize("prepared", [False, True])
+def test_stage_projected_full_size_sampled(prepared):
+    """The benchmark's workload (which passes prepared codebooks); oracle on a seeded frame sample."""
     w = W.WORKLOADS["stage_projected"]
     books = W.codebooks(w.n_stages, w.n_codes, w.dim, w.decay, w.seed)
     w_in, b_in, w_out, b_out = W.stage_projection_weights(w)
     h = W.hidden_states(w)
     idx = W.sample_frames(w.n_frames, 2048, seed=7)
-    rep = check_stage_projected(h, books, w_in, b_in, w_out, b_out, idx=idx)
+    rep = check_stage_projected(h, books, w_in, b_in, w_out, b_out, idx=idx, prepared=prepared)
     announce("stage_projected full-size report", **rep)
