@@ -1,4 +1,4 @@
-// fp32 matrix-core linear layers around the quantizer, gfx950 (CDNA4).
+// Linear layers around the quantizer on the matrix cores, gfx950 (CDNA4).
 //
 // The "Audio tokenizer pipeline" section of the "Architecture" page
 // (omnivoice.cpp) puts a linear layer before the RVQ encode (fc) and one
@@ -8,12 +8,25 @@
 //   linear_in : y[n, i]  = sum_k h[n, k] * W_in[i, k]  + b_in[i]   (i < 64)
 //   linear_out: o[n, i]  = sum_k x[n, k] * W_out[i, k] + b_out[i]  (k < 64)
 //
-// Both put weight rows on the M side and 32 frames per wavefront on the N
-// side of v_mfma_f32_32x32x2_f32, stream the weights through LDS (padded
-// rows, double buffered, shared by the 4 wavefronts of a workgroup) and
-// keep the frame operand in VGPRs. The contraction dimension is split the
-// same way as in the encode: lanes 0-31 supply one 32-wide half of each
-// 64-wide step, lanes 32-63 the other. Results are fp32 sums in the matrix
+// linear_in runs on the bf16 matrix cores with fp32 accuracy: every fp32
+// operand v is split into three bf16 parts, v = v_h + v_m + v_l exactly
+// (v_h = bf16(v), v_m = bf16(v - v_h), v_l = bf16(v - v_h - v_m), each
+// difference exact; for normal values v_l holds the last bits), and a
+// product v w is summed as v_h w_l + v_l w_h + v_m w_m + v_h w_m + v_m w_h
+// + v_h w_h (bf16 x bf16 products are exact in fp32). The dropped
+// v_m w_l + v_l w_m + v_l w_l are at most 2^-23 |v w|, the size of one fp32
+// rounding, so the result is as accurate as an fp32 contraction; six
+// v_mfma_f32_32x32x16_bf16 do the work of eight fp32 32x32x2 steps. fc2,
+// whose time goes to its 4 KiB output rows rather than to the contraction
+// (the split form measured 20% slower there), stays on
+// v_mfma_f32_32x32x2_f32.
+//
+// Both kernels put weight rows on the M side and 32 frames per wavefront on
+// the N side, stream the weights through LDS (padded rows, double buffered,
+// shared by the wavefronts of a workgroup; split into 8-column groups of 8
+// high, 8 middle and 8 low parts for linear_in) and keep the frame operand
+// in VGPRs. Lanes 0-31 supply one 32-wide half of each 64-wide chunk of the
+// contraction, lanes 32-63 the other. Results are fp32 sums in the matrix
 // core's order, the bias added last.
 #include <stdint.h>
 
@@ -26,13 +39,73 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 constexpr int kFramesPerWave = 32;
-constexpr int kRow = 64 + 4;   // padded LDS row: 8 lanes of a b128 read hit 32 banks
+constexpr int kInWaves = 8;                          // linear_in: 256 frames per workgroup
+constexpr int kInFrames = kInWaves * kFramesPerWave;
+constexpr int kOutWaves = 4;                         // linear_out: 128 frames per workgroup
+constexpr int kOutFrames = kOutWaves * kFramesPerWave;
+constexpr int kRow = 64 + 4;        // padded fp32 LDS row: 8 lanes of a b128 read hit 32 banks
+constexpr int kSRow = 3 * 64 + 8;   // bf16 per split weight row: 8 groups of (8 h, 8 m, 8 l) + 16 B pad
 
-static_assert(kWaves * kFramesPerWave == kLinearFramesPerBlock, "frames per block");
+// The three bf16 parts of 8 consecutive fp32 values.
+struct Split3 {
+    bf16x8 h, m, l;
+};
+
+// v = h + m + l exactly: each part is the round-to-nearest bf16 of what the
+// previous ones leave, and each difference is exact in fp32. Converted two
+// values at a time; a part is widened back by placing its 16 bits at the
+// top of a word.
+__device__ __forceinline__ Split3 split3(const float *v)
+{
+    u32x4 hp, mp, lp;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const unsigned h = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{v[2 * p], v[2 * p + 1]}, bf16x2));
+        const float r0 = v[2 * p] - __uint_as_float(h << 16);
+        const float r1 = v[2 * p + 1] - __uint_as_float(h & 0xFFFF0000u);
+        const unsigned m = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+        const float s0 = r0 - __uint_as_float(m << 16);
+        const float s1 = r1 - __uint_as_float(m & 0xFFFF0000u);
+        hp[p] = h;
+        mp[p] = m;
+        lp[p] = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{s0, s1}, bf16x2));
+    }
+    return {__builtin_bit_cast(bf16x8, hp), __builtin_bit_cast(bf16x8, mp), __builtin_bit_cast(bf16x8, lp)};
+}
+
+// acc += a . b over one 16-wide step of the contraction, in six products.
+__device__ __forceinline__ void mfma6(f32x16 &acc, const Split3 &a, const Split3 &b)
+{
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, b.l, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.l, b.h, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.m, b.m, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, b.m, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.m, b.h, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, b.h, acc, 0, 0, 0);
+}
+
+// Split weight row r of an LDS chunk: group g (columns 8g .. 8g+7) at
+// row * kSRow + 24 g as (h, m, l).
+__device__ __forceinline__ Split3 lds_split(const __bf16 *chunk, int row, int g)
+{
+    const __bf16 *p = chunk + row * kSRow + 24 * g;
+    return {*reinterpret_cast<const bf16x8 *>(p), *reinterpret_cast<const bf16x8 *>(p + 8),
+            *reinterpret_cast<const bf16x8 *>(p + 16)};
+}
+
+__device__ __forceinline__ void lds_store_split(__bf16 *chunk, int row, int g, const Split3 &s)
+{
+    __bf16 *p = chunk + row * kSRow + 24 * g;
+    *reinterpret_cast<bf16x8 *>(p) = s.h;
+    *reinterpret_cast<bf16x8 *>(p + 8) = s.m;
+    *reinterpret_cast<bf16x8 *>(p + 16) = s.l;
+}
 
 // ---- linear_in: [N, hidden] x [64, hidden]^T -> [N, 64] -------------------
 
@@ -55,22 +128,22 @@ struct Update {
 };
 
 template <bool kBias, bool kUpdate>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(64 * kInWaves)
 void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
                       const float *__restrict__ w, const float *__restrict__ bias,
                       float *__restrict__ y, Update up)
 {
-    // one chunk = 64 weight rows (all outputs) x 64 columns of the hidden dim
-    __shared__ __align__(16) float s_w[2][kDim * kRow];
+    // one chunk = 64 weight rows (all outputs) x 64 columns of the hidden dim, split
+    __shared__ __align__(16) __bf16 s_w[2][kDim * kSRow];
     // per wavefront: its 32 frames x 64 columns of the current chunk
-    __shared__ __align__(16) float s_h[kWaves][kFramesPerWave * kRow];
+    __shared__ __align__(16) float s_h[kInWaves][kFramesPerWave * kRow];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int64_t frame0 = static_cast<int64_t>(blockIdx.x) * kLinearFramesPerBlock + wave * kFramesPerWave;
+    const int64_t frame0 = static_cast<int64_t>(blockIdx.x) * kInFrames + wave * kFramesPerWave;
     const int64_t frame = frame0 + col;
     const bool valid = frame < n_frames;
 
@@ -95,22 +168,21 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
         }
     }
 
-    // staging: wavefront w stages weight rows 16w..16w+15; lane -> (row, 16-column quarter)
-    const int srow = wave * 16 + (lane & 15);
-    const int scol = (lane >> 4) * 16;
+    // staging: wavefront w stages weight rows 8w..8w+7; lane -> (row, 8-column group)
+    const int srow = wave * 8 + (lane & 7);
+    const int sgrp = lane >> 3;
     const int n_chunks = hidden / 64;
 
-    f32x4 ws[4];
+    f32x4 ws[2];
     f32x4 hv[8], pv[8];
     auto fetch_w = [&](int c) {
-        const f32x4 *p = reinterpret_cast<const f32x4 *>(w + static_cast<int64_t>(srow) * hidden + 64 * c + scol);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ws[i] = p[i];
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(w + static_cast<int64_t>(srow) * hidden + 64 * c + 8 * sgrp);
+        ws[0] = p[0];
+        ws[1] = p[1];
     };
     auto commit_w = [&](int buf) {
-        float *dst = &s_w[buf][srow * kRow + scol];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<f32x4 *>(dst + 4 * i) = ws[i];
+        const float v[8] = {ws[0][0], ws[0][1], ws[0][2], ws[0][3], ws[1][0], ws[1][1], ws[1][2], ws[1][3]};
+        lds_store_split(s_w[buf], srow, sgrp, split3(v));
     };
     auto fetch_h = [&](int c) {
 #pragma unroll
@@ -150,25 +222,26 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        f32x4 cur[8];
+        // this lane's operand: frame col, columns 32 half + 8 s .. + 7 in step s
+        Split3 fs[4];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) cur[t] = *reinterpret_cast<const f32x4 *>(&tile[col * kRow + 32 * half + 4 * t]);
+        for (int st = 0; st < 4; ++st) {
+            const f32x4 u = *reinterpret_cast<const f32x4 *>(&tile[col * kRow + 32 * half + 8 * st]);
+            const f32x4 v = *reinterpret_cast<const f32x4 *>(&tile[col * kRow + 32 * half + 8 * st + 4]);
+            const float e[8] = {u[0], u[1], u[2], u[3], v[0], v[1], v[2], v[3]};
+            fs[st] = split3(e);
+        }
         if (c + 1 < n_chunks) {
             fetch_w(c + 1);
             fetch_h(c + 1);
         }
-        const float *sb = s_w[buf];
+        const __bf16 *sb = s_w[buf];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            f32x4 a[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-                a[b] = *reinterpret_cast<const f32x4 *>(sb + (b * 32 + col) * kRow + 32 * half + 4 * t);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int b = 0; b < 2; ++b)
-                    acc[b] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[b][e], cur[t][e], acc[b], 0, 0, 0);
+        for (int st = 0; st < 4; ++st) {
+            const Split3 a0 = lds_split(sb, col, 4 * half + st);
+            const Split3 a1 = lds_split(sb, 32 + col, 4 * half + st);
+            mfma6(acc[0], a0, fs[st]);
+            mfma6(acc[1], a1, fs[st]);
         }
         if (c + 1 < n_chunks) commit_w(buf ^ 1);
         // every lane has read the tile (and the weight buffer) before they are overwritten
@@ -198,7 +271,7 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
 constexpr int kOutChunk = 128;   // weight rows (outputs) per LDS chunk
 
 template <bool kBias>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(64 * kOutWaves)
 void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden,
                        const float *__restrict__ w, const float *__restrict__ bias,
                        float *__restrict__ out)
@@ -210,7 +283,7 @@ void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden
     const int wave = tid >> 6;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kLinearFramesPerBlock +
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kOutFrames +
                           wave * kFramesPerWave + col;
     const bool valid = frame < n_frames;
 
@@ -301,9 +374,9 @@ void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden
 hipError_t launch_linear_in(const float *h, int64_t n_frames, int hidden, const float *w,
                             const float *bias, float *y, hipStream_t stream)
 {
-    const int64_t blocks = (n_frames + kLinearFramesPerBlock - 1) / kLinearFramesPerBlock;
+    const int64_t blocks = (n_frames + kInFrames - 1) / kInFrames;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kInWaves);
     const Update none = {nullptr, 0, nullptr, 0, nullptr};
     if (bias)
         hipLaunchKernelGGL((linear_in_kernel<true, false>), grid, block, 0, stream, h, n_frames, hidden, w, bias,
@@ -318,9 +391,9 @@ hipError_t launch_linear_in_update(const float *src, const int32_t *codes, int c
                                    int n_codes, float *dst, int64_t n_frames, int hidden, const float *w,
                                    const float *bias, float *y, hipStream_t stream)
 {
-    const int64_t blocks = (n_frames + kLinearFramesPerBlock - 1) / kLinearFramesPerBlock;
+    const int64_t blocks = (n_frames + kInFrames - 1) / kInFrames;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kInWaves);
     const Update up = {codes, codes_ld, table, n_codes, dst};
     if (bias)
         hipLaunchKernelGGL((linear_in_kernel<true, true>), grid, block, 0, stream, src, n_frames, hidden, w, bias,
@@ -334,9 +407,9 @@ hipError_t launch_linear_in_update(const float *src, const int32_t *codes, int c
 hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const float *w,
                              const float *bias, float *out, hipStream_t stream)
 {
-    const int64_t blocks = (n_frames + kLinearFramesPerBlock - 1) / kLinearFramesPerBlock;
+    const int64_t blocks = (n_frames + kOutFrames - 1) / kOutFrames;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kOutWaves);
     if (bias)
         hipLaunchKernelGGL((linear_out_kernel<true>), grid, block, 0, stream, x, n_frames, hidden, w, bias, out);
     else

@@ -20,9 +20,6 @@ constexpr int kDecodeThreads = 256;
 // Codebooks from this size on (one XCD's L2) take the stage-ordered decode.
 constexpr int64_t kDecodeTiledMinBookBytes = int64_t(4) << 20;
 
-// Linear layers: frames per workgroup (4 wavefronts x 32 frames).
-constexpr int kLinearFramesPerBlock = 128;
-
 // Launches the fused multi-stage encode. `residual` and `recon` may be null.
 hipError_t launch_encode(const float *x, int64_t n_frames, const float *books,
                          int n_stages, int n_codes, int32_t *codes, int codes_ld,
