@@ -147,19 +147,25 @@ void projected_decode_kernel(const int32_t *__restrict__ codes, int codes_ld, in
 // 1024) and adds stage q's rows for all of them before stage q+1, so the
 // resident wavefronts sweep the stages together and gather from one or two
 // stage tables at a time (4 MiB each at K = hidden = 1024) instead of the
-// whole table. Per element the sum is the same: +0, stage 0 first.
+// whole table. Per element the sum is the same: +0, stage 0 first. The
+// wavefront's codes are staged through LDS 32 stages at a time, so a row
+// address waits on an LDS read rather than on a global load per stage.
 constexpr int kTiledFrames = 4;
 constexpr int kTiledCols = 4;   // float4 columns per lane (hidden <= 1024)
+constexpr int kCodeStages = 32;                 // stages of codes staged in LDS at a time
+constexpr int kCodeRow = kCodeStages + 1;       // padded row per frame
 
 __global__ __launch_bounds__(64 * kRowFrames)
 void projected_decode_tiled_kernel(const int32_t *__restrict__ codes, int codes_ld, int64_t n_frames,
                                    const float *__restrict__ table, int n_stages, int n_codes, int hidden,
                                    float *__restrict__ out)
 {
+    __shared__ int s_codes[kRowFrames][kTiledFrames * kCodeRow];
     const int lane = threadIdx.x & 63;
     const int cols = hidden >> 2;
     const int64_t frame0 = (static_cast<int64_t>(blockIdx.x) * kRowFrames + (threadIdx.x >> 6)) * kTiledFrames;
     const int64_t stage_floats = static_cast<int64_t>(n_codes) * hidden;
+    int *sc = s_codes[threadIdx.x >> 6];
     f32x4 acc[kTiledFrames][kTiledCols];
 #pragma unroll
     for (int f = 0; f < kTiledFrames; ++f)
@@ -167,11 +173,24 @@ void projected_decode_tiled_kernel(const int32_t *__restrict__ codes, int codes_
         for (int t = 0; t < kTiledCols; ++t) acc[f][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     unsigned bad = 0u;   // bit f: frame f has a code outside [0, n_codes)
     for (int q = 0; q < n_stages; ++q) {
+        const int j = q % kCodeStages;
+        if (j == 0) {
+            // codes of stages q .. q+31 for the wavefront's frames (0 past the batch or the stages)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();   // the previous block of codes is read
+            for (int i = lane; i < kTiledFrames * kCodeStages; i += 64) {
+                const int f = i / kCodeStages, jj = i - f * kCodeStages;
+                const int64_t fr = frame0 + f;
+                sc[f * kCodeRow + jj] = (fr < n_frames && q + jj < n_stages) ? codes[fr * codes_ld + q + jj] : 0;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        }
         const float *tq = table + q * stage_floats;
 #pragma unroll
         for (int f = 0; f < kTiledFrames; ++f) {
-            const int64_t fr = frame0 + f;
-            int k = fr < n_frames ? codes[fr * codes_ld + q] : 0;
+            int k = sc[f * kCodeRow + j];   // 0 for frames past the batch
             const bool ok = static_cast<unsigned>(k) < static_cast<unsigned>(n_codes);
             bad |= ok ? 0u : (1u << f);
             k = ok ? k : 0;
