@@ -20,9 +20,17 @@ Functions (same names as the C entry points):
   ``rvq_prepare_codebooks(codebooks)`` -> uint8 device tensor;
   ``rvq_encode_prepared(x, codebooks, prepared, n_stages=None, recon=False, residual=True)``
   -> ``(codes, recon or None, residual or None)``
-* ``rvq_project_roundtrip(h, w_in, b_in, codebooks, w_out, b_out, n_stages=None)``
+* ``rvq_project_roundtrip(h, w_in, b_in, codebooks, w_out, b_out, n_stages=None, prepared=None)``
   -> ``(codes, latent, latent_recon, h_recon)``
+* ``rvq_projected_prepare(codebooks, w_out, b_out=None)`` -> table;
+  ``rvq_projected_encode(h, w_in, b_in, codebooks, table, n_stages=None, prepared=None)``
+  -> ``(codes, latent, residual)``; ``rvq_projected_decode(codes, table, n_stages=None)``
+* ``rvq_cosine_prepare(codebooks)`` -> unit codewords (float64);
+  ``rvq_cosine_encode(h, w_in, b_in, units, table, n_stages=None)`` -> ``(codes, latent, residual)``
 * ``rvq_version()``, ``rvq_status_string(status)``
+
+``prepared`` is ``rvq_prepare_codebooks``' output for the same codebooks; passing it selects
+the encode that reads the prepared layout (same results, faster).
 """
 
 from __future__ import annotations
