@@ -39,6 +39,7 @@
 // encode_bf16_pipe_kernel, which copies chunks straight into LDS and issues
 // each group's key scan between the next group's matrix-core steps.
 #include "encode_common.h"
+#include "prepared.h"
 
 namespace rvq {
 namespace {
@@ -193,18 +194,11 @@ __device__ __forceinline__ void score_block(const __bf16 *sb, const float *sn, i
     fold_group(best, second, bb, sb0, base, half, best_k, second_k);
 }
 
-// Prepared codebooks (rvq_prepare_codebooks): per stage one block of
-//   rows  [Kp][256 B]      16-byte segments (8 bf16 hi, 8 bf16 lo) per 8-dim group
-//   norms [Kp] fp32        0.5*||c||^2, kNoScore for rows k >= n_codes
-//   max   [Kp/kChunk] u32  bits of the largest valid 0.5*||c||^2 of each kChunk rows
-// with Kp = n_codes rounded up to kChunk, blocks kStageAlign-aligned.
-constexpr int64_t kStageAlign = 256;
-__host__ __device__ inline int64_t padded_codes(int n_codes) { return (n_codes + kChunk - 1) / kChunk * kChunk; }
-__host__ __device__ inline int64_t stage_bytes(int n_codes)
-{
-    const int64_t kp = padded_codes(n_codes);
-    return (kp * 260 + 4 * (kp / kChunk) + kStageAlign - 1) / kStageAlign * kStageAlign;
-}
+// Prepared codebooks: the layout is in prepared.h; these kernels read the
+// split-bf16 section (rows, half-norms and the per-chunk maxima).
+using prep::padded_codes;
+using prep::stage_bytes;
+static_assert(prep::kChunk == kChunk, "prepared rows come in whole chunks");
 
 // The largest 0.5*||c_k||^2 of a prepared stage block is the maximum of its
 // Kp/kChunk words. stage_max_part loads lane's share of them (issued early,
@@ -213,7 +207,7 @@ __host__ __device__ inline int64_t stage_bytes(int n_codes)
 // order like the values.
 __device__ __forceinline__ unsigned stage_max_part(const uint8_t *blk, int64_t kp, int lane)
 {
-    const unsigned *words = reinterpret_cast<const unsigned *>(blk + kp * 260);
+    const unsigned *words = reinterpret_cast<const unsigned *>(blk + prep::bf16_max(kp));
     const int n_words = static_cast<int>(kp / kChunk);
     unsigned m = lane < n_words ? words[lane] : 0u;
     for (int c = lane + 64; c < n_words; c += 64) m = max(m, words[c]);
@@ -607,7 +601,7 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
             const int seg = t - r * kRowSlots;
             if (t < kBlockSlots) dma16(src + r * 256 + (seg < kRowSlots - 1 ? seg * 16 : 0), dst + i * 512);
         }
-        if (lane < 8) dma16(blk + kp * 256 + static_cast<int64_t>(k0 + 4 * lane) * 4, gnorm + buf * 32);
+        if (lane < 8) dma16(blk + prep::bf16_norms(kp) + static_cast<int64_t>(k0 + 4 * lane) * 4, gnorm + buf * 32);
     };
     int item = 0;   // blocks this wavefront has scored (their buffer alternates)
     if constexpr (kPrepared) {
@@ -742,10 +736,28 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
 }
 
 // One workgroup per kChunk padded rows of a stage, 8 lanes per row (one
-// 8-dim group each, so a wavefront reads and writes 8 whole rows): hi/lo
-// split and half-norm of every row, and the largest valid half-norm of the
-// workgroup's rows.
+// 8-dim group each, so a wavefront reads and writes 8 whole rows). Every
+// workgroup first finds the stage's largest |c| itself, so all of a stage's
+// workgroups reach the same scale e. Then per row: the hi/lo split and the
+// half-norm (split-bf16 section), fp16 of c' = 2^e c and the fp16 parts of
+// 0.5*||c'||^2 (fp16 section); and the largest valid half-norms of the
+// workgroup's rows in both sections.
 constexpr int kPrepThreads = 512;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ unsigned block_max_bits(unsigned m, unsigned *s_m)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
+    __syncthreads();   // s_m is free (a previous call's readers are done)
+    if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+    __syncthreads();
+    unsigned mm = 0u;
+#pragma unroll
+    for (int w = 0; w < kPrepThreads / 64; ++w) mm = max(mm, s_m[w]);
+    return mm;
+}
 
 __global__ __launch_bounds__(kPrepThreads)
 void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__restrict__ prepared)
@@ -755,45 +767,92 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
     const int q = blockIdx.y;
     const int64_t kp = padded_codes(n_codes);
     uint8_t *blk = prepared + q * stage_bytes(n_codes);
-    float *norms = reinterpret_cast<float *>(blk + kp * 256);
+    float *norms = reinterpret_cast<float *>(blk + prep::bf16_norms(kp));
+    uint8_t *rows16 = blk + prep::f16_offset(kp);
+    unsigned *halfn = reinterpret_cast<unsigned *>(blk + prep::f16_halfn(kp));
+    const float *stage = books + static_cast<int64_t>(q) * n_codes * kDim;
+
+    // the stage's largest |c|: bits of non-negative floats order like the
+    // values, and a NaN's bits lie above those of +inf
+    unsigned a = 0u;
+    {
+        const f32x4 *sv = reinterpret_cast<const f32x4 *>(stage);
+        const int64_t n4 = static_cast<int64_t>(n_codes) * (kDim / 4);
+#pragma unroll 4
+        for (int64_t i = threadIdx.x; i < n4; i += kPrepThreads) {
+            const f32x4 v = sv[i];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) a = max(a, __float_as_uint(fabsf(v[t])));
+        }
+    }
+    const unsigned amax_bits = block_max_bits(a, s_m);
+    const float amax = __uint_as_float(amax_bits);
+    int e = 0;
+    if (amax_bits != 0u && amax_bits < 0x7F800000u) {
+        int x;
+        (void)frexpf(amax, &x);   // amax = f * 2^x, f in [1/2, 1)
+        e = min(max(-x, prep::kMinExp), prep::kMaxExp);
+    }
+    const bool in_range = amax_bits < 0x7F800000u && ldexpf(amax, e) <= prep::kMaxScaled;
+
     const int grp = threadIdx.x & 7;
-    unsigned m = 0u;
+    unsigned m = 0u, m16 = 0u;
     for (int k = c * kChunk + (threadIdx.x >> 3); k < (c + 1) * kChunk; k += kPrepThreads / 8) {
         bf16x8 *row = reinterpret_cast<bf16x8 *>(blk + static_cast<int64_t>(k) * 256);
+        u32x4 *row16 = reinterpret_cast<u32x4 *>(rows16 + static_cast<int64_t>(k) * 128);
         if (k >= n_codes) {   // the 8 lanes of a row take the same branch
             const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
             row[2 * grp] = z;
             row[2 * grp + 1] = z;
-            if (grp == 0) norms[k] = kNoScore;
+            row16[grp] = u32x4{0u, 0u, 0u, 0u};
+            if (grp == 0) {
+                norms[k] = kNoScore;
+                halfn[k] = 0u;
+            }
             continue;
         }
-        const f32x4 *src =
-            reinterpret_cast<const f32x4 *>(books + (static_cast<int64_t>(q) * n_codes + k) * kDim + 8 * grp);
-        const f32x4 a = src[0], b = src[1];
-        const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        float s = 0.0f;
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(stage + static_cast<int64_t>(k) * kDim + 8 * grp);
+        const f32x4 va = src[0], vb = src[1];
+        const float v[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+        float s = 0.0f, s16 = 0.0f;
+        f16x8 h16;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s = __builtin_fmaf(v[e], v[e], s);
+        for (int t = 0; t < 8; ++t) {
+            s = __builtin_fmaf(v[t], v[t], s);
+            const float w = ldexpf(v[t], e);   // exact unless it falls below the fp32 normal range
+            s16 = __builtin_fmaf(w, w, s16);
+            h16[t] = static_cast<_Float16>(w);   // round to nearest even
+        }
         bf16x8 hi, lo;
         split8(v, hi, lo);
         row[2 * grp] = hi;
         row[2 * grp + 1] = lo;
+        row16[grp] = __builtin_bit_cast(u32x4, h16);
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         s += __shfl_xor(s, 4);
+        s16 += __shfl_xor(s16, 1);
+        s16 += __shfl_xor(s16, 2);
+        s16 += __shfl_xor(s16, 4);
         const float hn = 0.5f * s;
-        if (grp == 0) norms[k] = hn;
+        const float hn16 = 0.5f * s16;
+        if (grp == 0) {
+            norms[k] = hn;
+            // two fp16 parts: hn16 - hi is exact in fp32
+            const _Float16 p_hi = static_cast<_Float16>(hn16);
+            const _Float16 p_lo = static_cast<_Float16>(hn16 - static_cast<float>(p_hi));
+            halfn[k] = static_cast<unsigned>(__builtin_bit_cast(unsigned short, p_hi)) |
+                       (static_cast<unsigned>(__builtin_bit_cast(unsigned short, p_lo)) << 16);
+        }
         m = max(m, __float_as_uint(hn));   // hn >= 0: bits order like values
+        m16 = max(m16, __float_as_uint(hn16));
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
-    if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
-    __syncthreads();
+    const unsigned mm = block_max_bits(m, s_m);
+    const unsigned mm16 = block_max_bits(m16, s_m);
     if (threadIdx.x == 0) {
-        unsigned mm = 0u;
-#pragma unroll
-        for (int w = 0; w < kPrepThreads / 64; ++w) mm = max(mm, s_m[w]);
-        reinterpret_cast<unsigned *>(blk + kp * 260)[c] = mm;
+        reinterpret_cast<unsigned *>(blk + prep::bf16_max(kp))[c] = mm;
+        reinterpret_cast<unsigned *>(blk + prep::f16_max(kp))[c] = in_range ? mm16 : 0x7F800000u;
+        if (c == 0) *reinterpret_cast<int *>(blk + prep::f16_exp(kp)) = e;
     }
 }
 
@@ -977,7 +1036,7 @@ void encode_bf16_pipe_kernel(const float *__restrict__ x, int64_t n_frames,
 #pragma unroll
         for (int i = 0; i < kWaveLoads; ++i)
             if (i * 64 + lane < kWaveSlots) dma16(src + slot_off[i], dst + i * 512);
-        if (lane < 8) dma16(blk + kp * 256 + static_cast<int64_t>(k0 + 4 * lane) * 4, s_norm[g & 1] + 32 * wave);
+        if (lane < 8) dma16(blk + prep::bf16_norms(kp) + static_cast<int64_t>(k0 + 4 * lane) * 4, s_norm[g & 1] + 32 * wave);
     };
 
     dma_chunk(0);
@@ -1124,6 +1183,9 @@ hipError_t launch_encode_prepared(const float *x, int64_t n_frames, const float 
                                   int n_stages, int n_codes, int32_t *codes, int codes_ld,
                                   float *residual, float *recon, hipStream_t stream)
 {
+    if (n_frames > kSplitMaxFrames)
+        return launch_encode_f16(x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon,
+                                 stream);
     return launch_variant<true>(x, n_frames, books, static_cast<const uint8_t *>(prepared), n_stages, n_codes,
                                 codes, codes_ld, residual, recon, stream);
 }

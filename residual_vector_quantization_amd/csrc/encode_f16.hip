@@ -1,0 +1,541 @@
+// Fused multi-stage residual vector quantization encode for gfx950 (CDNA4)
+// that scores with one fp16 product per dimension on the matrix cores and
+// decides every stage exactly.
+//
+// Computes the residual loop of the "RVQ codec" section of the
+// "Architecture" page (omnivoice.cpp): for q = 0..Q-1 pick
+// argmin_k ||r - C[q,k]||^2 (lowest k on ties), emit k, r <- r - C[q,k].
+// The picks, residuals and reconstructions are those of the other encode
+// kernels: a pick is made from fast scores only when no other codeword can
+// be within the scores' proven error of it, and otherwise by the float64
+// direct form that the oracle uses.
+//
+// Scores: with a per-stage power of two 2^e that brings the stage's
+// largest |c| into [1/2, 1), c' = 2^e c, n = -r and the key
+//     s'_k = 2^-e * 0.5*||c'_k||^2 + n . c'_k  =  2^e * (0.5*||c_k||^2 - r . c_k)
+// orders the codewords like the distance. One v_mfma_f32_32x32x16_f16 per
+// 16 dims multiplies fp16(n_j) by fp16(c'_j) (exact products in fp32), and
+// a fifth step adds the half-norm: its two fp16 parts times 2^-e. With
+// u = 2^-11 (fp16 rounding), the stage maxima T = 2^-e max 0.5*||c'||^2
+// and C = max ||c'||, every key is within
+//     E = (2u + u^2 + 2 gamma_{D+8} + 2^-17 + u^2 + gamma_64) (T + ||n|| C)
+//         + 2^-21 ||n|| + 2^-22 C + 2^-(e+25) + 2^-43                 (1)
+// of the exact scaled score: the products lose at most (2u + u^2)|n_j c'_j|
+// plus 2^-24 |n_j| + 2^-25 |c'_j| in the fp16 subnormal range (D = 64
+// dims, so the 1-norms are at most 8 times the 2-norms); the half-norm's
+// fp32 sum and its two fp16 parts lose gamma_64 + u^2 of it plus 2^-25;
+// the fp32 accumulation 2 gamma_{D+8} and the packed key 2^-17 of the sum.
+// Every codeword whose key is within 2E of the frame's smallest key is a
+// candidate for the true argmin. fp16 keeps its range only while every
+// |n_j| < 2^15: a frame whose residual leaves that range, or a stage whose
+// codebook does (marked by an infinite maximum when it was prepared), goes
+// to the full float64 rescan instead.
+//
+// The fp16 scores are about 20 times coarser than split-bf16 ones, so
+// candidate sets are wider: each lane keeps two sets of keys (even and odd
+// 64-codeword groups), best, second and third key and the first two
+// indices of each. A frame resolves from up to eight candidates (two per set
+// and lane) with the float64 re-rank; a third candidate inside one set sends
+// it to the full float64 rescan.
+//
+// Work split: 4 wavefronts x 32 frames per workgroup and two workgroups per
+// CU (76.8 KB of LDS each), residual in VGPRs, prepared fp16 rows copied
+// straight into LDS in 256-codeword chunks (144-byte rows, double
+// buffered), each chunk scored as four 64-codeword groups of two
+// interleaved matrix-core chains, with the key scan of one group issued
+// between the matrix-core steps of the next. Two independent workgroups per
+// CU let one workgroup's stage decision overlap the other's scoring.
+#include "encode_common.h"
+#include "prepared.h"
+
+namespace rvq {
+namespace {
+
+using namespace enc;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kFramesPerWave = 32;
+constexpr int kBlockFrames = kWaves * kFramesPerWave;
+constexpr int kChunk = prep::kChunk;                         // codewords per LDS chunk (4 groups of 64)
+constexpr int kGroups = kChunk / 64;
+constexpr int kRowSlots = 9;                                 // 16-byte LDS slots per row: 8 data + 1 padding
+constexpr int kRowHalfs = 8 * kRowSlots;                     // fp16 per LDS row
+constexpr int kWaveRows = kChunk / kWaves;                   // rows each wavefront copies per chunk
+constexpr int kWaveLoads = kWaveRows * kRowSlots / 64;       // wavefront-wide row copies per chunk
+static_assert(kWaveRows * kRowSlots % 64 == 0, "whole wavefront-wide copies");
+static_assert(kGroups == 4, "two group pairs per chunk");
+
+// Relative and absolute coefficients of (1), rounded up.
+constexpr float kRel = 1.0e-3f;        // 2u + u^2 + 2 gamma_72 + 2^-17 + u^2 + gamma_64 = 9.971e-4
+constexpr float kAbsN = 4.8e-7f;       // 2^-21 (1 + u) with the accumulation factor
+constexpr float kAbsC = 2.4e-7f;       // 2^-22 (1 + u) with the accumulation factor
+constexpr float kAbsNorm = 3.0e-8f;    // 2^-25, times 2^-e
+constexpr float kAbsConst = 1.2e-13f;  // 64 * 2^-49
+
+// One wavefront-wide direct load from global memory into LDS: active lane i
+// copies 16 bytes from src into dst + 16 i (dst wave-uniform, in LDS).
+// Issued as inline assembly so that the compiler does not order every LDS
+// read behind it; the caller waits with the vector-memory counter.
+__device__ __forceinline__ void dma16(const void *src, void *dst)
+{
+    const unsigned m0 = static_cast<unsigned>(reinterpret_cast<size_t>((lds_void *)dst));
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// fp16 (round to nearest even) of 8 consecutive floats, one v_cvt_pk_f16_f32 per pair.
+__device__ __forceinline__ f16x8 to_f16x8(const float *v)
+{
+    f16x8 h;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) h[t] = static_cast<_Float16>(v[t]);
+    return h;
+}
+
+// Running best / second / third key of one set and the indices of the first two.
+struct KeySet {
+    float best, second, third;
+    int best_k, second_k;
+};
+
+__device__ __forceinline__ void reset(KeySet &s)
+{
+    s.best = s.second = s.third = kNoScore;
+    s.best_k = s.second_k = 0;
+}
+
+__device__ __forceinline__ void scan_key(float v, int lk, KeySet &s)
+{
+    const float key = make_key(v, lk);
+    s.third = __builtin_amdgcn_fmed3f(key, s.second, s.third);
+    s.second = __builtin_amdgcn_fmed3f(key, s.best, s.second);
+    s.best = __builtin_amdgcn_fmed3f(key, s.best, -FLT_MAX);
+}
+
+// Score v (0..31) of a scored group: block v / 16, accumulator v % 16, local
+// index b*32 + 8*(a/4) + a%4 (the lane's 4*half row offset is added later).
+__device__ __forceinline__ void scan_score(const f32x16 (&d)[2], int v, KeySet &s)
+{
+    const int b = v >> 4, a = v & 15;
+    scan_key(d[b][a], b * 32 + 8 * (a >> 2) + (a & 3), s);
+}
+
+// Index bookkeeping after a group that starts at codeword `base` went into
+// set s (best / second bits before it: bb0, sb0). A changed second key is
+// either the previous best (demoted) or a key of this group; equal bit
+// patterns from different groups also leave a third key with the same
+// value, which the decision treats as an unresolved candidate.
+__device__ __forceinline__ void fold(KeySet &s, unsigned bb0, unsigned sb0, int base, int half)
+{
+    const unsigned bb = __float_as_uint(s.best), sbits = __float_as_uint(s.second);
+    const int k_of_best = base + 4 * half + static_cast<int>(bb & ~kKeyMask);
+    const int k_of_second = base + 4 * half + static_cast<int>(sbits & ~kKeyMask);
+    const bool best_moved = bb != bb0;
+    const int demoted = (best_moved && sbits == bb0) ? s.best_k : k_of_second;
+    s.second_k = sbits != sb0 ? demoted : s.second_k;
+    s.best_k = best_moved ? k_of_best : s.best_k;
+}
+
+// Scores [per step count] placed after each of a group's ten matrix-core
+// steps (norm block 0, norm block 1, then dims 0..63 for blocks 0 and 1).
+constexpr int kScanAfter[10] = {4, 4, 3, 3, 3, 3, 3, 3, 3, 3};
+
+// Matrix-core steps of group kG of the chunk in LDS (rows sb, half-norm
+// parts sh) into dn: two 32-codeword blocks, each a chain of the half-norm
+// step and four 16-dim steps. When kScan, the key scan of the previous
+// group dp (first codeword prev_base) into set `ks` is placed between them
+// in a fixed order, and the operands of the next step are read from LDS
+// before the current step's products are issued.
+template <bool kScan>
+__device__ __forceinline__ void step_group(f32x16 (&dn)[2], const f32x16 (&dp)[2], int kG, const _Float16 *sb,
+                                           const unsigned *sh, int col, int half, const f16x8 (&nb)[4],
+                                           const f16x8 &nnorm, int prev_base, KeySet &ks)
+{
+    const unsigned bb0 = __float_as_uint(ks.best), sb0 = __float_as_uint(ks.second);
+    f16x8 a[2][2];   // [step parity][block]
+    auto load_ops = [&](int s) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+            a[s & 1][b] = *reinterpret_cast<const f16x8 *>(sb + (kG * 64 + b * 32 + col) * kRowHalfs +
+                                                          8 * (4 * half + s));
+    };
+    f16x8 an[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+        an[b] = __builtin_bit_cast(f16x8, u32x4{sh[kG * 64 + b * 32 + col], 0u, 0u, 0u});
+    load_ops(0);
+    int v = 0;   // next score of dp
+    auto scan_some = [&](int count) {
+        if (kScan) {
+#pragma unroll
+            for (int i = 0; i < count; ++i) scan_score(dp, v + i, ks);
+        }
+        v += count;
+    };
+    const f32x16 zero = {};
+    dn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(an[0], nnorm, zero, 0, 0, 0);
+    scan_some(kScanAfter[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    dn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(an[1], nnorm, zero, 0, 0, 0);
+    scan_some(kScanAfter[1]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        if (s < 3) load_ops(s + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s & 1][0], nb[s], dn[0], 0, 0, 0);
+        scan_some(kScanAfter[2 + 2 * s]);
+        __builtin_amdgcn_sched_barrier(0);
+        dn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s & 1][1], nb[s], dn[1], 0, 0, 0);
+        scan_some(kScanAfter[3 + 2 * s]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (kScan) fold(ks, bb0, sb0, prev_base, half);
+}
+
+// The key scan of the last group of a stage, alone.
+__device__ __forceinline__ void scan_last(const f32x16 (&d)[2], int base, int half, KeySet &ks)
+{
+    const unsigned bb0 = __float_as_uint(ks.best), sb0 = __float_as_uint(ks.second);
+#pragma unroll
+    for (int v = 0; v < 32; ++v) scan_score(d, v, ks);
+    fold(ks, bb0, sb0, base, half);
+}
+
+// The group at `base` that holds codeword n_codes - 1 when n_codes is not a
+// multiple of 64: its rows at or past n_codes (zero rows of the prepared
+// block) get kNoScore before the scan, so they are never candidates.
+__device__ __forceinline__ void mask_tail(f32x16 (&d)[2], int base, int half, int n_codes)
+{
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int a = 0; a < 16; ++a)
+            if (base + b * 32 + 8 * (a >> 2) + 4 * half + (a & 3) >= n_codes) d[b][a] = kNoScore;
+}
+
+// The largest 0.5*||c'||^2 of a prepared stage: the maximum of its Kp/kChunk
+// fp16-section words (loaded early by stage_max_part, reduced over the
+// wavefront by wave_max_bits at the decision). Values are >= 0 (or +inf), so
+// their bits order like the values.
+__device__ __forceinline__ unsigned stage_max_part(const uint8_t *blk, int64_t kp, int lane)
+{
+    const unsigned *words = reinterpret_cast<const unsigned *>(blk + prep::f16_max(kp));
+    const int n_words = static_cast<int>(kp / kChunk);
+    unsigned m = lane < n_words ? words[lane] : 0u;
+    for (int c = lane + 64; c < n_words; c += 64) m = max(m, words[c]);
+    return m;
+}
+
+__device__ __forceinline__ float wave_max_bits(unsigned m)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
+    return __uint_as_float(m);
+}
+
+// An upper bound of sqrt(x) for x >= 0: the hardware square root (within a
+// few ulp) of max(x, FLT_MIN), raised by 2^-20 of itself.
+__device__ __forceinline__ float sqrt_up(float x)
+{
+    return __builtin_amdgcn_sqrtf(fmaxf(x, FLT_MIN)) * (1.0f + 9.5367431640625e-07f);
+}
+
+// Entry i (0..3) of a four-entry list, selected without indexing registers.
+__device__ __forceinline__ int pick4(const int (&l)[4], int i)
+{
+    return i == 0 ? l[0] : i == 1 ? l[1] : i == 2 ? l[2] : l[3];
+}
+
+// The decision for one stage from this lane's two key sets (codeword slots
+// of one half of a frame; lanes l and l^32 hold the two halves): every
+// codeword within 2E (1) of the frame's smallest key is a candidate; two to
+// eight candidates are re-ranked in float64, a third candidate inside one
+// set (or ambiguous bookkeeping, or fp16 out of range) sends the frame to the
+// full float64 rescan. Then the pick is stored (code_out, when not null) and
+// subtracted from the negated residual n (and added to acc for kRecon).
+// Every lane must call it.
+template <bool kRecon>
+__device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], const KeySet (&ks)[2],
+                                             const float *book, int n_codes, float m16, int e, bool valid,
+                                             int half, int col, int lane, float *frame_row, int32_t *code_out)
+{
+    float rn = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) rn = __builtin_fmaf(n[j], n[j], rn);
+    rn = rn + __shfl_xor(rn, 32);
+    // |n_j| < 2^15 keeps every fp16(n_j) finite; a stage out of the fp16
+    // range has an infinite maximum
+    const bool bad = !(rn < 1073741824.0f) || !(m16 <= FLT_MAX);
+
+    const float r_up = sqrt_up(rn * (1.0f + 1.52587890625e-05f));
+    const float m_up = m16 * (1.0f + 1.52587890625e-05f);
+    const float c_up = sqrt_up(2.0f * m_up);
+    const float t_up = ldexpf(m_up, -e);
+    const float bound = (kRel * (t_up + r_up * c_up) + kAbsN * r_up + kAbsC * c_up + ldexpf(kAbsNorm, -e) +
+                         kAbsConst) * (1.0f + 2.44140625e-04f);
+    const float lane_min = fminf(ks[0].best, ks[1].best);
+    const float frame_min = fminf(lane_min, __shfl_xor(lane_min, 32));
+    const float lim = frame_min + 2.0f * bound + fabsf(frame_min) * 2.4e-7f;
+
+    bool ov = false;
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        ov = ov || ks[s].third <= lim || (ks[s].second <= lim && ks[s].second_k == ks[s].best_k);
+    // the shuffle must run on every lane: a short-circuit would leave the
+    // partner lane inactive and the two halves of a frame could disagree
+    const int ov_o = __shfl_xor(static_cast<int>(ov), 32);
+    const bool overflow = bad || ov || ov_o != 0;
+
+    // this lane's candidates, compacted: set 0 best, second, set 1 best, second
+    const float sv[4] = {ks[0].best, ks[0].second, ks[1].best, ks[1].second};
+    const int sk[4] = {ks[0].best_k, ks[0].second_k, ks[1].best_k, ks[1].second_k};
+    int list[4] = {0, 0, 0, 0};
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool c = sv[i] <= lim;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (c && cnt == j) list[j] = sk[i];
+        cnt += c;
+    }
+    int list_o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) list_o[j] = __shfl_xor(list[j], 32);
+    const int cnt_o = __shfl_xor(cnt, 32);
+    const int ncand = cnt + cnt_o;
+    // frame candidate j: half 0's list, then half 1's
+    const int cnt0 = half ? cnt_o : cnt;
+    int l0[4], l1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        l0[j] = half ? list_o[j] : list[j];
+        l1[j] = half ? list[j] : list_o[j];
+    }
+    int pick = cnt0 > 0 ? l0[0] : l1[0];   // the one candidate when ncand == 1
+
+    // Two to eight candidates: float64 re-rank.
+    const bool rerank = valid && !overflow && ncand >= 2;
+    if (__any(rerank)) {
+        double bd = INFINITY;
+        int bk = 0x7fffffff;
+        for (int j = 0; __any(rerank && j < ncand); ++j) {
+            const bool use = rerank && j < ncand;
+            const int k = use ? (j < cnt0 ? pick4(l0, j) : pick4(l1, j - cnt0)) : pick;
+            const double dist = pair_distance(n, book, k, half);
+            if (use && (dist < bd || (dist == bd && k < bk))) {
+                bd = dist;
+                bk = k;
+            }
+        }
+        if (rerank) pick = bk;
+    }
+
+    // A third candidate inside one set (or a frame or stage out of range): full rescan.
+    uint64_t pending = __ballot(valid && overflow && half == 0);
+    while (pending) {
+        const int f = __ffsll(static_cast<unsigned long long>(pending)) - 1;
+        pending &= pending - 1;
+        const int w = rescan_frame(n, frame_row, book, n_codes, f, lane);
+        if (col == f) pick = w;
+    }
+
+    pick = min(max(pick, 0), n_codes - 1);
+    if (code_out) *code_out = pick;
+    const f32x4 *cw = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(pick) * kDim + 32 * half);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const f32x4 v = cw[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            n[4 * t + i] = n[4 * t + i] + v[i];   // = -(r - c), exactly
+            if (kRecon) acc[4 * t + i] = acc[4 * t + i] + v[i];
+        }
+    }
+}
+
+template <bool kRecon, bool kResidual>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
+void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
+                       const float *__restrict__ books, const uint8_t *__restrict__ prepared,
+                       int n_stages, int n_codes,
+                       int32_t *__restrict__ codes, int codes_ld,
+                       float *__restrict__ residual, float *__restrict__ recon)
+{
+    __shared__ __align__(16) unsigned s_half[2][kChunk];
+    __shared__ __align__(16) _Float16 s_rows[2][kChunk * kRowHalfs];
+    __shared__ __align__(16) float s_frame[kWaves][kDim];   // rescan: one frame's residual
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kBlockFrames + wave * kFramesPerWave + col;
+    const bool valid = frame < n_frames;
+
+    float n[32];     // negated residual, dims 32*half .. 32*half+31
+    float acc[32];   // reconstruction (kRecon)
+    if (valid) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(x + frame * kDim + 32 * half);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 v = src[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) n[4 * t + i] = -v[i];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) n[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+
+    const int64_t kp = prep::padded_codes(n_codes);
+    const int64_t sbytes = prep::stage_bytes(n_codes);
+    const int n_chunks = static_cast<int>(kp / kChunk);
+    const int n_groups = (n_codes + 63) / 64;   // groups past it hold only padding rows and are not scanned
+    const int total = n_stages * n_chunks;
+
+    // wavefront w copies rows kWaveRows*w .. +kWaveRows-1 of chunk g and their
+    // half-norm parts into buffer g % 2; slot t of its rows is segment t % 9
+    // of row t / 9, the 9th (padding) slot of a row takes the row's first
+    // segment again. Source byte offsets of this lane's slots:
+    unsigned slot_off[kWaveLoads];
+#pragma unroll
+    for (int i = 0; i < kWaveLoads; ++i) {
+        const int t = i * 64 + lane;
+        const int r = t / kRowSlots;
+        const int seg = t - r * kRowSlots;
+        slot_off[i] = static_cast<unsigned>(r * 128 + (seg < kRowSlots - 1 ? seg * 16 : 0));
+    }
+    auto dma_chunk = [&](int g) {
+        const int q = g / n_chunks;
+        const int c = g - q * n_chunks;
+        const uint8_t *blk = prepared + q * sbytes;
+        const int k0 = c * kChunk + kWaveRows * wave;
+        const uint8_t *src = blk + prep::f16_offset(kp) + static_cast<int64_t>(k0) * 128;
+        _Float16 *dst = s_rows[g & 1] + kWaveRows * wave * kRowHalfs;
+#pragma unroll
+        for (int i = 0; i < kWaveLoads; ++i) dma16(src + slot_off[i], dst + i * 512);
+        if (lane < kWaveRows / 4)
+            dma16(blk + prep::f16_halfn(kp) + static_cast<int64_t>(k0 + 4 * lane) * 4, s_half[g & 1] + kWaveRows * wave);
+    };
+
+    dma_chunk(0);
+    wait_all();
+    __syncthreads();
+
+    for (int q = 0; q < n_stages; ++q) {
+        const uint8_t *blk = prepared + q * sbytes;
+        const unsigned cmax = stage_max_part(blk, kp, lane);   // used at the decision
+        const int e = *reinterpret_cast<const int *>(blk + prep::f16_exp(kp));
+        f16x8 nb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) nb[s] = to_f16x8(&n[8 * s]);
+        // half-norm step: this frame's operand is (2^-e, 2^-e, 0, ...) on half 0, zero on half 1
+        const f16x2 sc = {static_cast<_Float16>(ldexpf(1.0f, -e)), static_cast<_Float16>(ldexpf(1.0f, -e))};
+        const f16x8 nnorm = __builtin_bit_cast(f16x8, u32x4{half ? 0u : __builtin_bit_cast(unsigned, sc), 0u, 0u, 0u});
+
+        KeySet ks[2];
+        reset(ks[0]);
+        reset(ks[1]);
+        f32x16 da[2], db[2];
+        int prev_base = 0;   // first codeword of the group held in db
+
+        for (int c = 0; c < n_chunks; ++c) {
+            const int g = q * n_chunks + c;
+            if (c > 0) {
+                wait_all();        // this wavefront's copies into chunk g's buffer have landed
+                __syncthreads();   // everyone's have; chunk g-1's buffer is no longer read
+            }
+            if (g + 1 < total) dma_chunk(g + 1);
+            const _Float16 *sb = s_rows[g & 1];
+            const unsigned *sh = s_half[g & 1];
+#pragma unroll 1
+            for (int p = 0; p < kGroups / 2; ++p) {
+                const int ka = 2 * p, kb = 2 * p + 1;
+                // step A scores group 4c+ka and scans the odd group before it (set 1);
+                // step B scores group 4c+kb and scans group 4c+ka (set 0)
+                const bool scan_a = !(c == 0 && p == 0) && (prev_base >> 6) < n_groups;
+                if (scan_a) {
+                    if (prev_base + 64 > n_codes) mask_tail(db, prev_base, half, n_codes);
+                    step_group<true>(da, db, ka, sb, sh, col, half, nb, nnorm, prev_base, ks[1]);
+                } else {
+                    step_group<false>(da, db, ka, sb, sh, col, half, nb, nnorm, prev_base, ks[1]);
+                }
+                const int base_a = c * kChunk + 64 * ka;
+                if ((base_a >> 6) < n_groups) {
+                    if (base_a + 64 > n_codes) mask_tail(da, base_a, half, n_codes);
+                    step_group<true>(db, da, kb, sb, sh, col, half, nb, nnorm, base_a, ks[0]);
+                } else {
+                    step_group<false>(db, da, kb, sb, sh, col, half, nb, nnorm, base_a, ks[0]);
+                }
+                prev_base = c * kChunk + 64 * kb;
+            }
+        }
+        if ((prev_base >> 6) < n_groups) {
+            if (prev_base + 64 > n_codes) mask_tail(db, prev_base, half, n_codes);
+            scan_last(db, prev_base, half, ks[1]);
+        }
+
+        // ---- stage q is scored for this wavefront's 32 frames: decide ----
+        const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
+        const float m16 = wave_max_bits(cmax);
+        decide_stage<kRecon>(n, acc, ks, book, n_codes, m16, e, valid, half, col, lane, s_frame[wave],
+                             (valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
+        if (q + 1 < n_stages) {
+            wait_all();
+            __syncthreads();   // the next stage's first chunk is in LDS; the last one's buffer is free
+        }
+    }
+
+    if (valid) {
+        if (kResidual) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(residual + frame * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dst[t] = f32x4{-n[4 * t], -n[4 * t + 1], -n[4 * t + 2], -n[4 * t + 3]};
+        }
+        if (kRecon) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(recon + frame * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                dst[t] = f32x4{acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_encode_f16(const float *x, int64_t n_frames, const float *books, const void *prepared,
+                             int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
+                             float *recon, hipStream_t stream)
+{
+    const int64_t blocks = (n_frames + kBlockFrames - 1) / kBlockFrames;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    const uint8_t *p = static_cast<const uint8_t *>(prepared);
+    if (recon && residual)
+        hipLaunchKernelGGL((encode_f16_kernel<true, true>), grid, block, 0, stream,
+                           x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else if (recon)
+        hipLaunchKernelGGL((encode_f16_kernel<true, false>), grid, block, 0, stream,
+                           x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else if (residual)
+        hipLaunchKernelGGL((encode_f16_kernel<false, true>), grid, block, 0, stream,
+                           x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else
+        hipLaunchKernelGGL((encode_f16_kernel<false, false>), grid, block, 0, stream,
+                           x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
+    return hipGetLastError();
+}
+
+}  // namespace rvq

@@ -233,19 +233,33 @@ def _bf16_rne(v):
     return r.astype(np.uint32).view(np.float32)
 
 
+def _stage_layout(k):
+    """(Kp, offset of the fp16 section, stage block bytes) of the prepared layout."""
+    kp = (k + 255) // 256 * 256
+    f16 = (kp * 260 + 4 * (kp // 256) + 255) // 256 * 256
+    return kp, f16, (f16 + kp * 132 + 4 * (kp // 256) + 4 + 255) // 256 * 256
+
+
+def _stage_exp(book):
+    """Power-of-two scale e of a stage: max |c| * 2^e in [1/2, 1), clamped to [-15, 24]."""
+    amax = float(np.abs(book).max())
+    return 0 if amax == 0.0 else int(np.clip(-np.frexp(amax)[1], -15, 24))
+
+
 @pytest.mark.parametrize("q,k", [(3, 1000), (2, 256), (1, 1)])
 def test_prepared_layout(q, k):
-    """rvq_prepare_codebooks: per stage Kp = roundup(K, 256) rows of 8-dim groups (8 hi, 8 lo bf16),
-    hi = bf16(v) and lo = bf16(v - hi) round to nearest even; Kp fp32 half-norms (FLT_MAX on padding
-    rows, which are zero); the bits of the largest valid half-norm of every 256 rows; stage blocks
-    256-byte aligned."""
+    """rvq_prepare_codebooks. Split-bf16 section: per stage Kp = roundup(K, 256) rows of 8-dim groups
+    (8 hi, 8 lo bf16), hi = bf16(v) and lo = bf16(v - hi) round to nearest even; Kp fp32 half-norms
+    (FLT_MAX on padding rows, which are zero); the bits of the largest valid half-norm of every 256
+    rows. fp16 section: fp16 (round to nearest even) of c' = 2^e c with the stage's power of two e;
+    the two fp16 parts of 0.5*||c'||^2; the largest of those per 256 rows; e. Stage blocks 256-byte
+    aligned."""
     m = rvq()
     rng = np.random.default_rng(600 + k)
-    books = (rng.standard_normal((q, k, 64)) * 3.0).astype(np.float32)
+    books = (rng.standard_normal((q, k, 64)) * 3.0 * 4.0 ** -np.arange(q)[:, None, None]).astype(np.float32)
     books[0, 0] = 0.0
     prep = host(m.rvq_prepare_codebooks(to_dev(books)))
-    kp = (k + 255) // 256 * 256
-    sbytes = (kp * 260 + 4 * (kp // 256) + 255) // 256 * 256
+    kp, f16, sbytes = _stage_layout(k)
     assert prep.size >= q * sbytes
     for s in range(q):
         blk = prep[s * sbytes:(s + 1) * sbytes]
@@ -264,3 +278,64 @@ def test_prepared_layout(q, k):
         for c in range(kp // 256):
             valid = norms[256 * c:min(256 * (c + 1), k)]
             assert maxima[c] == (valid.view(np.uint32).max() if valid.size else 0)
+        # fp16 section
+        e = _stage_exp(books[s])
+        assert blk[f16 + kp * 132 + 4 * (kp // 256):][:4].view(np.int32)[0] == e
+        scaled = (books[s].astype(np.float64) * 2.0 ** e).astype(np.float32)   # exact: a power of two
+        rows16 = blk[f16:f16 + kp * 128].view(np.float16).reshape(kp, 64)
+        np.testing.assert_array_equal(rows16[:k].view(np.uint16), scaled.astype(np.float16).view(np.uint16))
+        assert not rows16[k:].view(np.uint16).any()
+        parts = blk[f16 + kp * 128:f16 + kp * 132].view(np.float16).reshape(kp, 2).astype(np.float64)
+        want = 0.5 * (scaled.astype(np.float64) ** 2).sum(axis=1)
+        got = parts[:k, 0] + parts[:k, 1]
+        assert (np.abs(got - want) <= 2e-6 * want + 2.0 ** -24).all()
+        # the high part is the fp16 rounding of the sum of both parts
+        np.testing.assert_array_equal(parts[:k, 0], got.astype(np.float16).astype(np.float64))
+        assert not parts[k:].any()
+        max16 = blk[f16 + kp * 132:f16 + kp * 132 + 4 * (kp // 256)].view(np.float32)
+        for c in range(kp // 256):
+            w = want[256 * c:min(256 * (c + 1), k)]
+            assert max16[c] == pytest.approx(w.max() if w.size else 0.0, rel=2e-6, abs=1e-30)
+
+
+def test_prepared_out_of_fp16_range():
+    """A stage with entries beyond 2^20 is marked by infinite fp16-section maxima; an all-zero stage
+    has e = 0."""
+    m = rvq()
+    rng = np.random.default_rng(610)
+    books = rng.standard_normal((3, 300, 64)).astype(np.float32)
+    books[1] *= 2.0 ** 22
+    books[2] = 0.0
+    prep = host(m.rvq_prepare_codebooks(to_dev(books)))
+    kp, f16, sbytes = _stage_layout(300)
+    for s, inf in ((0, False), (1, True), (2, False)):
+        blk = prep[s * sbytes:(s + 1) * sbytes]
+        max16 = blk[f16 + kp * 132:f16 + kp * 132 + 4 * (kp // 256)].view(np.float32)
+        assert bool(np.isinf(max16).all()) == inf and bool(np.isinf(max16).any()) == inf
+        assert blk[f16 + kp * 132 + 4 * (kp // 256):][:4].view(np.int32)[0] == _stage_exp(books[s])
+
+
+@pytest.mark.parametrize("case", ["huge_stage", "huge_residual", "tiny_residual", "near_duplicates",
+                                  "clustered"])
+def test_prepared_wide_fp16_edges(case):
+    """Wide batches through the prepared path: a stage out of the fp16 range, residuals out of it
+    (both resolved by the float64 rescan), residuals in the fp16 subnormal range, near-duplicate
+    rows (re-rank within one key set) and rows clustered so tightly that frames hold many
+    candidates."""
+    rng = np.random.default_rng(620)
+    books = _books(rng, 4, 1024)
+    x = rng.standard_normal((400, 64)).astype(np.float32)
+    if case == "huge_stage":
+        books[1] *= 2.0 ** 22
+    elif case == "huge_residual":
+        x *= 1e5
+    elif case == "tiny_residual":
+        books *= 1e-6
+        x *= 1e-6
+    elif case == "near_duplicates":
+        books[:, 1::2] = books[:, 0::2] * (1.0 + 1e-5 * rng.standard_normal((4, 512, 64))).astype(np.float32)
+    else:
+        centre = rng.standard_normal((4, 1, 64)).astype(np.float32)
+        books = (centre + 1e-3 * rng.standard_normal((4, 1024, 64))).astype(np.float32)
+        x = (centre[0] + 1e-3 * rng.standard_normal((400, 64))).astype(np.float32)
+    _check(x, books, True, "prepared")
