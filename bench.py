@@ -2,16 +2,18 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
 
-One step = ``rvq_prepare_codebooks`` (codebooks split into bf16 halves with
-their half-norms), ``rvq_encode_prepared`` (codes + final residual, split-bf16
-scoring) and ``rvq_decode`` (codes -> reconstruction) over the whole batch,
+One step = ``rvq_prepare_codebooks`` (codebooks scaled and rounded to fp16,
+and split into bf16 halves, with their half-norms), ``rvq_encode_prepared``
+(codes + final residual; fp16 scores with exact re-rank for wide batches,
+split-bf16 for batches of up to 16384 frames) and ``rvq_decode`` (codes ->
+reconstruction) over the whole batch,
 inputs and outputs resident in HBM. W untimed steps, then K timed
 steps between ``torch.cuda.synchronize()`` calls. Per-launch kernel times
 come from HIP events recorded on the stream the kernels run on (torch's
 current stream, which is the stream handed to the C ABI).
 
 Prints one JSON line with the throughput, the roofline of the dominant
-kernel (the split-bf16 encode on the bf16 matrix cores), the same encode
+kernel (the encode on the fp16 matrix cores), the same encode
 with fp32 scores against the fp32 matrix-core roofline, the decode's HBM
 roofline, sampled parity against the CPU oracle, and the oracle's own
 throughput on a bounded sample of the same workload (``cpu_baseline``).
@@ -37,7 +39,8 @@ import rvq_workloads as W  # noqa: E402
 
 METRIC = "RVQ encode + decode frames/sec (Q=8,K=1024,D=64 fp32); % MFMA / HBM roofline"
 PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix peak
-PEAK_BF16_MFMA_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+PEAK_BF16_MFMA_TFLOPS = 2500.0     # MI355X dense bf16 (and fp16) matrix peak
+PEAK_F16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 N_XCD, N_SIMD = 8, 1024            # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 COPY_BYTES = 512 << 20             # size of the counter-calibration copy
@@ -50,7 +53,9 @@ SPLIT_MAX_FRAMES = 16384   # batches up to this size take the split-codebook enc
 CSRC = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc")
 # kernel kind -> sources whose text defines it (hashed to detect stale counters)
 KERNEL_SOURCES = {
-    "encode_bf16": ["encode_bf16.hip", "encode_common.h"],
+    "encode_f16": ["encode_f16.hip", "encode_common.h", "prepared.h"],
+    "encode_bf16": ["encode_bf16.hip", "encode_common.h", "prepared.h"],
+    "encode_bf16_split": ["encode_bf16.hip", "encode_common.h", "prepared.h"],
     "encode_fp32": ["encode.hip", "encode_common.h"],
     "decode": ["decode.hip"],
 }
@@ -105,7 +110,7 @@ PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp   # R = repository root
 rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o bench -- python3 $R/bench.py --workload {wl} --steps 20 --no-cpu-baseline
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
-rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
 python3 $R/bench.py --workload {wl} --summarize-profiles $R/gpurun_out/prof"""
 
 
@@ -122,10 +127,10 @@ def _csv(dirname, suffix):
 
 
 def _kernel_of(name):
+    if "encode_f16_kernel" in name:
+        return "encode_f16"
     if "encode_bf16_ksplit_kernel" in name:
         return "encode_bf16_split"
-    if "encode_bf16_pipe_kernel" in name:
-        return "encode_bf16"
     if "encode_bf16_kernel" in name:
         return "encode_bf16_onthefly"   # codebooks split in every workgroup (no prepared layout)
     if "encode_kernel" in name:
@@ -175,6 +180,14 @@ def summarize_profiles(w, src_dir):
         lines.append(f"| {kind} | {r['Calls']} | {a:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     lines.append("")
+    if "encode_f16" in avg:
+        t = avg["encode_f16"]
+        lines.append(f"- encode_f16 (prepared codebooks): {enc_flop:.4g} flop per launch (2QKD per frame, "
+                     f"on the fp16 matrix cores) / {t:.1f} us = {enc_flop / t / 1e6:.1f} TFLOP/s "
+                     f"({enc_flop / t / 1e6 / PEAK_F16_MFMA_TFLOPS:.1%} of {PEAK_F16_MFMA_TFLOPS:.0f} fp16; "
+                     f"{enc_flop / t / 1e6 / PEAK_FP32_MFMA_TFLOPS:.2f}x the {PEAK_FP32_MFMA_TFLOPS} fp32 matrix "
+                     f"peak); matrix steps issued {enc_flop * (d + 16) / d:.4g} flop (2QK(D+16) per frame, "
+                     f"the half-norm step included).")
     if "encode_bf16" in avg:
         t = avg["encode_bf16"]
         lines.append(f"- encode_bf16 (prepared codebooks): {3 * enc_flop:.4g} bf16 matrix flop per launch "
@@ -199,11 +212,14 @@ def summarize_profiles(w, src_dir):
     f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
     w_scale = COPY_BYTES / (write["copy"] * 1024.0)
     enc_algo = (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d
-    # the prepared encode reads the split-bf16 codebook rows (256 B), norms and stage maxima instead
+    # the prepared encodes read their section of the prepared codebooks: fp16 rows (128 B), half-norm
+    # parts, stage maxima and exponent (encode_f16; plus the fp32 rows of the picks), or split-bf16
+    # rows (256 B), norms and stage maxima (encode_bf16) in place of the fp32 codebook
     kp = -(-k // 256) * 256
-    prep_bytes = q * (-(-(kp * 260 + 4 * (kp // 256)) // 256) * 256)
-    algo = {"encode_bf16": enc_algo - 4.0 * q * k * d + prep_bytes, "encode_fp32": enc_algo,
-            "decode": dec_bytes + 4.0 * q * k * d}
+    prep16_bytes = q * (kp * 132 + 4 * (kp // 256) + 4)
+    prep_bytes = q * (kp * 260 + 4 * (kp // 256))
+    algo = {"encode_f16": enc_algo + prep16_bytes, "encode_bf16": enc_algo - 4.0 * q * k * d + prep_bytes,
+            "encode_fp32": enc_algo, "decode": dec_bytes + 4.0 * q * k * d}
     lines += ["", "## HBM counters (per launch)", "",
               f"A 512 MiB elementwise copy reads FETCH_SIZE = {fetch['copy']:.0f} KiB and WRITE_SIZE = "
               f"{write['copy']:.0f} KiB, so readings are scaled by {f_scale:.3f} (fetch) and "
@@ -225,11 +241,11 @@ def summarize_profiles(w, src_dir):
                   open(os.path.join(out_dir, f"{kind}_{w.name}_hbm_counters.json"), "w"), indent=1)
 
     mf = _csv(os.path.join(src_dir, "mfma"), "counter_collection.csv")
-    names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+    names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F32", "SQ_INSTS_VALU_MFMA_MOPS_F16",
              "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
     means = {name: _counter_means(mf, name) for name in names}
     lines += ["", "## Matrix-core counters (per launch)", ""]
-    for kind in ("encode_bf16", "encode_fp32"):
+    for kind in ("encode_f16", "encode_bf16", "encode_fp32"):
         c = {name: means[name].get(kind) for name in names}
         if c["GRBM_GUI_ACTIVE"] is None:
             continue
@@ -238,7 +254,7 @@ def summarize_profiles(w, src_dir):
                   f"- MFMA busy: {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (active * N_SIMD):.1%} of SIMD cycles "
                   f"(SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x {N_SIMD} SIMDs))",
                   f"- MFMA flop counted: fp32 {c['SQ_INSTS_VALU_MFMA_MOPS_F32'] * 512:.4g}, "
-                  f"bf16 {c['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512:.4g} (algorithmic 2QKD = {enc_flop:.4g})",
+                  f"fp16 {c['SQ_INSTS_VALU_MFMA_MOPS_F16'] * 512:.4g} (algorithmic 2QKD = {enc_flop:.4g})",
                   f"- instructions: VALU {c['SQ_INSTS_VALU']:.4g} of which MFMA {c['SQ_INSTS_MFMA']:.4g}",
                   f"- LDS bank-conflict cycles / LDS active cycles: "
                   f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1%}", ""]
@@ -254,12 +270,12 @@ def _trace_work(w):
     n, q, k, d, hid = w.n_frames, w.n_stages, w.n_codes, w.dim, w.hidden
     qe = 1 if w.per_stage else q   # per-stage workloads launch the encode once per stage
     work = {
+        "encode_f16_kernel": (2.0 * qe * k * d * n, "flop",
+                              "fp16 matrix flop, 2KD per frame" if w.per_stage else
+                              "fp16 matrix flop, 2QKD per frame"),
         "encode_bf16_kernel": (3 * 2.0 * qe * k * d * n, "flop",
                                "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
                                "bf16 matrix flop, 3 x 2QKD per frame"),
-        "encode_bf16_pipe_kernel": (3 * 2.0 * qe * k * d * n, "flop",
-                                    "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
-                                    "bf16 matrix flop, 3 x 2QKD per frame"),
         "encode_bf16_ksplit_kernel": (3 * 2.0 * qe * k * d * n, "flop",
                                       "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
                                       "bf16 matrix flop, 3 x 2QKD per frame"),
@@ -581,7 +597,7 @@ def main():
                            device=dev)
 
     def step(ev=None):
-        # codebook split into bf16 halves (every step), encode from it, decode the codes
+        # codebooks prepared (every step), encode from them, decode the codes
         if ev is not None:
             ev[0].record()
         rvq.rvq_prepare_codebooks(bg, prepared)
@@ -625,7 +641,7 @@ def main():
         torch.cuda.synchronize()
         fp32_ms = ev[0].elapsed_time(ev[1]) / args.fp32_steps
         if not torch.equal(c32, codes):
-            raise SystemExit("fp32 and split-bf16 scorings disagree")
+            raise SystemExit("fp32 scoring and the prepared encode disagree")
         rvq.rvq_encode(xg, bg, codes=c32, residual_out=r32)
         torch.cuda.synchronize()
         if not torch.equal(c32, codes):
@@ -642,7 +658,16 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = n * args.steps / wall
     enc_flop = 2.0 * q * k * d * n
-    bf16_tflops = 3 * enc_flop / (enc_ms * 1e-3) / 1e12
+    wide = n > SPLIT_MAX_FRAMES
+    if wide:   # one fp16 product per dimension; the method's 2QKD flop on the fp16 peak
+        mm_work, mm_what = enc_flop, f"2*Q*K*D*N = {enc_flop:.4g} flop on fp16 matrix cores"
+        mm_kernel = ("encode_f16_kernel, prepared codebooks (v_mfma_f32_32x32x16_f16, one product per "
+                     "dimension + a half-norm step; exact float64 re-rank of candidates)")
+    else:      # three split-bf16 products per dimension
+        mm_work, mm_what = 3 * enc_flop, f"3*2*Q*K*D*N = {3 * enc_flop:.4g} bf16 flop"
+        mm_kernel = ("encode_bf16_ksplit_kernel (codebook split over a workgroup's wavefronts), prepared "
+                     "codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)")
+    mm_tflops = mm_work / (enc_ms * 1e-3) / 1e12
     dec_bytes = (4.0 * q + 4.0 * d) * n
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
     gather_tbps = 4.0 * d * q * n / (dec_ms * 1e-3) / 1e12
@@ -660,20 +685,18 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "frames": n, "Q": q, "K": k, "D": d, "scoring": "split-bf16",
+        "config": {"workload": w.name, "frames": n, "Q": q, "K": k, "D": d,
+                   "scoring": "fp16 + exact re-rank" if wide else "split-bf16 + exact re-rank",
                    "recipe": w.description},
         "audio_seconds_per_s": value / w.frame_rate_hz,
         "prepare_ms": prep_ms,
         "encode_ms": enc_ms,
         "decode_ms": dec_ms,
-        "roofline": {"bound": "mfma",
-                     "kernel": ("encode_bf16_ksplit_kernel (codebook split over a workgroup's wavefronts)"
-                                if n <= SPLIT_MAX_FRAMES else "encode_bf16_pipe_kernel") +
-                               ", prepared codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)",
-                     "achieved": bf16_tflops, "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                     "frac": bf16_tflops / PEAK_BF16_MFMA_TFLOPS,
-                     "traffic": recorded_traffic("encode_bf16", w.name),
-                     "work_per_launch": f"3*2*Q*K*D*N = {3 * enc_flop:.4g} bf16 flop"},
+        "roofline": {"bound": "mfma", "kernel": mm_kernel,
+                     "achieved": mm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": mm_tflops / PEAK_F16_MFMA_TFLOPS,
+                     "traffic": recorded_traffic("encode_f16" if wide else "encode_bf16_split", w.name),
+                     "work_per_launch": mm_what},
         "encode_fp32_equivalent": {"achieved": enc_flop / (enc_ms * 1e-3) / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
                                    "unit": "TFLOP/s", "work_per_launch": f"2*Q*K*D*N = {enc_flop:.4g} flop"},
         "decode_roofline": {"bound": "hbm", "kernel": dec_kernel, "achieved": dec_gbps,

@@ -21,10 +21,11 @@
  *   - the pick of every stage equals the argmin of the float64 direct-form
  *     distance sum_j (r_j - c_j)^2 (j ascending, one rounding per
  *     operation) over all K codewords. Scores are computed on the matrix
- *     cores (split-bf16 by default, or fp32, see rvq_encode_scored); every
- *     codeword whose score lies within a proven error bound of the best is
- *     re-ranked with that float64 sum, so score rounding never decides a
- *     pick and both scorings give identical results;
+ *     cores (split-bf16 by default, or fp32, see rvq_encode_scored; fp16
+ *     for rvq_encode_prepared on wide batches); every codeword whose score
+ *     lies within a proven error bound of the best is re-ranked with that
+ *     float64 sum, so score rounding never decides a pick and all scorings
+ *     give identical results;
  *   - residuals are float32, r <- fl32(r - c) per element;
  *   - decode (and the reconstruction of rvq_roundtrip) is a float32 sum
  *     that starts at +0 and adds stage 0 first.
@@ -154,21 +155,31 @@ RVQ_API rvq_status rvq_encode_scored(const float *x, int64_t n_frames, int32_t d
                                      float *recon, float *residual, rvq_scoring scoring, void *stream);
 
 /*
- * Prepared codebooks: the split-bf16 layout of a codebook tensor, computed
- * once (codebooks are model constants) so that each encode only copies rows.
+ * Prepared codebooks: the codebook tensor in the layouts the matrix-core
+ * encodes read, computed once (codebooks are model constants) so that each
+ * encode only copies rows.
  *
  * rvq_prepared_bytes returns the size of the buffer for the given shape
  * (a negative rvq_status for invalid or unsupported shapes).
  * rvq_prepare_codebooks writes it on `stream` into caller-allocated device
  * memory `prepared` (16-byte aligned, at least rvq_prepared_bytes bytes).
- * Per stage it holds: each codeword as bf16 hi = bf16(c) and lo = bf16(c -
- * hi) in 8-dim groups, 0.5*||c||^2 in fp32, and the largest 0.5*||c||^2
- * of every 256 codewords. The buffer depends only on the codebook values.
+ * Per stage it holds a split-bf16 section (each codeword as bf16 hi =
+ * bf16(c) and lo = bf16(c - hi) in 8-dim groups, 0.5*||c||^2 in fp32, the
+ * largest 0.5*||c||^2 of every 256 codewords) and an fp16 section (one
+ * power of two 2^e per stage that brings max |c| into [1/2, 1); each
+ * codeword as fp16(2^e c); 0.5*||2^e c||^2 as two fp16 parts; the largest
+ * of those per 256 codewords; e). The buffer depends only on the codebook
+ * values.
  *
- * rvq_encode_prepared is rvq_encode_scored with split-bf16 scoring, reading
- * the split rows from `prepared` (which must have been prepared from the same
- * `codebooks` with at least `n_stages` stages and the same n_codes and dim;
- * the library cannot check this). Results are identical to rvq_encode.
+ * rvq_encode_prepared reads `prepared` (which must have been prepared from
+ * the same `codebooks` with at least `n_stages` stages and the same n_codes
+ * and dim; the library cannot check this): up to 16384 frames with
+ * split-bf16 scores, more with one fp16 product per dimension. Either way
+ * every codeword within the scores' proven error of the best is re-ranked
+ * in float64, so results are identical to rvq_encode. Codebook entries
+ * beyond 2^20 or residual entries beyond 2^15 leave fp16's range; such
+ * stages and frames are decided by the full float64 rescan (same results,
+ * slower).
  */
 RVQ_API int64_t rvq_prepared_bytes(int32_t n_stages, int32_t n_codes, int32_t dim);
 RVQ_API rvq_status rvq_prepare_codebooks(const float *codebooks, int32_t n_stages, int32_t n_codes,

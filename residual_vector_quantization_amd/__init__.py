@@ -261,7 +261,8 @@ def rvq_prepared_bytes(n_stages: int, n_codes: int, dim: int) -> int:
 
 
 def rvq_prepare_codebooks(codebooks: torch.Tensor, prepared: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Split-bf16 layout of ``codebooks`` [Q, K, D] (a uint8 tensor on the same device)."""
+    """Prepared layouts (split-bf16 and fp16 sections) of ``codebooks`` [Q, K, D], as a uint8 tensor on the
+    same device."""
     _require(codebooks, "codebooks", torch.float32, 3)
     q, k, d = codebooks.shape
     size = rvq_prepared_bytes(q, k, d)
@@ -287,7 +288,8 @@ def _check_prepared(prepared: Optional[torch.Tensor], codebooks: torch.Tensor, q
 def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torch.Tensor,
                         n_stages: Optional[int] = None, recon: bool = False, residual: bool = True,
                         out=None):
-    """Split-bf16 encode from prepared codebooks: ``(codes, recon or None, residual or None)``."""
+    """Encode from prepared codebooks (split-bf16 scores up to 16384 frames, fp16 above; exact either way):
+    ``(codes, recon or None, residual or None)``."""
     _require(x, "x", torch.float32, 2)
     _require(codebooks, "codebooks", torch.float32, 3, x.device)
     _require(prepared, "prepared", torch.uint8, 1, x.device)

@@ -35,9 +35,9 @@
 // its best, second and third keys and the indices of the first two: a
 // frame resolves from up to four candidates (two per half) with the float64
 // re-rank, and only a third candidate inside one lane sends it to the full
-// float64 rescan. With prepared codebooks the same work runs in
-// encode_bf16_pipe_kernel, which copies chunks straight into LDS and issues
-// each group's key scan between the next group's matrix-core steps.
+// float64 rescan. Small batches (the split-codebook kernel below) read the
+// split-bf16 section of prepared codebooks when they are given; wide batches
+// with prepared codebooks take the fp16 kernel (encode_f16.hip).
 #include "encode_common.h"
 #include "prepared.h"
 
@@ -856,253 +856,6 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
     }
 }
 
-// ---- prepared codebooks, many frames: matrix work and key scan overlapped --
-//
-// Same tiles, chunks, keys and decision as encode_bf16_kernel; two things
-// differ. The chunk rows and half-norms are copied from the prepared
-// codebooks straight into LDS (global_load_lds, no staging registers), and
-// the key scan of one 64-codeword group is issued between the matrix-core
-// steps of the next group (two accumulator pairs), so the vector ALU work
-// fills the matrix cores' latency instead of following it.
-constexpr int kGroups = kChunk / 64;                          // 64-codeword groups per chunk
-constexpr int kWaveSlots = 32 * kRowSlots;                    // 16-byte LDS slots of a wavefront's 32 rows (544)
-constexpr int kWaveLoads = (kWaveSlots + 63) / 64;            // wavefront-wide row loads per chunk (9)
-static_assert(kGroups == 4, "two group pairs per chunk");
-
-// One key into this lane's best / second / third.
-__device__ __forceinline__ void scan_key(float s, int lk, float &best, float &second, float &third)
-{
-    const float key = make_key(s, lk);
-    third = __builtin_amdgcn_fmed3f(key, second, third);
-    second = __builtin_amdgcn_fmed3f(key, best, second);
-    best = __builtin_amdgcn_fmed3f(key, best, -FLT_MAX);
-}
-
-// Score v (0..31) of a scored group: block v / 16, accumulator v % 16, local
-// index b*32 + 8*(a/4) + a%4 (the lane's 4*half row offset is added later).
-__device__ __forceinline__ void scan_score(const f32x16 (&d)[2], int v, float &best, float &second, float &third)
-{
-    const int b = v >> 4, a = v & 15;
-    scan_key(d[b][a], b * 32 + 8 * (a >> 2) + (a & 3), best, second, third);
-}
-
-// Matrix-core steps of group kG of the chunk at sb / sn into dn (two
-// 32-codeword blocks; accumulators start at the rows' 0.5*||c||^2), and,
-// when kScan, the key scan of the previous group dp (first codeword
-// prev_base) placed between them in a fixed order: each 16-dim step's six
-// products carry eight of dp's 32 scores, and the operands of the next step
-// are read from LDS before the current step's products are issued.
-template <bool kScan>
-__device__ __forceinline__ void step_group(f32x16 (&dn)[2], const f32x16 (&dp)[2], int kG, const __bf16 *sb,
-                                           const float *sn, int col, int half, const bf16x8 (&nh)[4],
-                                           const bf16x8 (&nl)[4], int prev_base, float &best, float &second,
-                                           float &third, int &best_k, int &second_k)
-{
-    const unsigned bb0 = __float_as_uint(best), sb0 = __float_as_uint(second);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const f32x4 nv = *reinterpret_cast<const f32x4 *>(sn + kG * 64 + b * 32 + 8 * m + 4 * half);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dn[b][4 * m + e] = nv[e];
-        }
-    }
-    bf16x8 ah[2][2], al[2][2];   // [step parity][block]
-    auto load_ops = [&](int s) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const __bf16 *row = sb + (kG * 64 + b * 32 + col) * kRowH + 16 * (4 * half + s);
-            ah[s & 1][b] = *reinterpret_cast<const bf16x8 *>(row);
-            al[s & 1][b] = *reinterpret_cast<const bf16x8 *>(row + 8);
-        }
-    };
-    load_ops(0);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        if (s < 3) load_ops(s + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        const int p = s & 1;
-        const int v0 = 8 * s;   // this step's first score of dp
-        dn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[p][0], nl[s], dn[0], 0, 0, 0);
-        if (kScan) scan_score(dp, v0 + 0, best, second, third);
-        __builtin_amdgcn_sched_barrier(0);
-        dn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[p][1], nl[s], dn[1], 0, 0, 0);
-        if (kScan) scan_score(dp, v0 + 1, best, second, third);
-        __builtin_amdgcn_sched_barrier(0);
-        dn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[p][0], nh[s], dn[0], 0, 0, 0);
-        if (kScan) {
-            scan_score(dp, v0 + 2, best, second, third);
-            scan_score(dp, v0 + 3, best, second, third);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        dn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[p][1], nh[s], dn[1], 0, 0, 0);
-        if (kScan) scan_score(dp, v0 + 4, best, second, third);
-        __builtin_amdgcn_sched_barrier(0);
-        dn[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[p][0], nh[s], dn[0], 0, 0, 0);
-        if (kScan) scan_score(dp, v0 + 5, best, second, third);
-        __builtin_amdgcn_sched_barrier(0);
-        dn[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[p][1], nh[s], dn[1], 0, 0, 0);
-        if (kScan) {
-            scan_score(dp, v0 + 6, best, second, third);
-            scan_score(dp, v0 + 7, best, second, third);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    if (kScan) {
-        // fold_group's bookkeeping, written with selects
-        const unsigned bb = __float_as_uint(best), sbits = __float_as_uint(second);
-        const int k_of_best = prev_base + 4 * half + static_cast<int>(bb & ~kKeyMask);
-        const int k_of_second = prev_base + 4 * half + static_cast<int>(sbits & ~kKeyMask);
-        const bool best_moved = bb != bb0;
-        const int demoted = (best_moved && sbits == bb0) ? best_k : k_of_second;
-        second_k = sbits != sb0 ? demoted : second_k;
-        best_k = best_moved ? k_of_best : best_k;
-    }
-}
-
-// The key scan of the last group of a stage, alone.
-__device__ __forceinline__ void scan_last(const f32x16 (&d)[2], int base, int half, float &best, float &second,
-                                          float &third, int &best_k, int &second_k)
-{
-    const unsigned bb0 = __float_as_uint(best), sb0 = __float_as_uint(second);
-    scan_group(d, best, second, third);
-    fold_group(best, second, bb0, sb0, base, half, best_k, second_k);
-}
-
-template <bool kRecon, bool kResidual>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2)))
-void encode_bf16_pipe_kernel(const float *__restrict__ x, int64_t n_frames,
-                             const float *__restrict__ books, const uint8_t *__restrict__ prepared,
-                             int n_stages, int n_codes,
-                             int32_t *__restrict__ codes, int codes_ld,
-                             float *__restrict__ residual, float *__restrict__ recon)
-{
-    __shared__ __align__(16) float s_norm[2][kChunk];
-    __shared__ __align__(16) __bf16 s_book[2][kChunk * kRowH];
-    __shared__ __align__(16) float s_frame[kWaves][kDim];  // rescan: one frame's residual
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int col = lane & 31;
-    const int half = lane >> 5;
-    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kBlockFrames +
-                          wave * kFramesPerWave + col;
-    const bool valid = frame < n_frames;
-
-    float n[32];     // negated residual, dims 32*half .. 32*half+31
-    float acc[32];   // reconstruction (kRecon)
-    if (valid) {
-        const f32x4 *src = reinterpret_cast<const f32x4 *>(x + frame * kDim + 32 * half);
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const f32x4 v = src[t];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) n[4 * t + e] = -v[e];
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) n[j] = 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
-    bf16x8 nh[4], nl[4];
-
-    const int64_t kp = padded_codes(n_codes);
-    const int64_t sbytes = stage_bytes(n_codes);
-    const int n_chunks = static_cast<int>(kp / kChunk);
-    const int total = n_stages * n_chunks;
-
-    // wavefront w copies rows 32w .. 32w+31 of chunk g and their half-norms
-    // into buffer g % 2; slot t of its rows is segment t % 17 of row t / 17,
-    // the 17th (padding) slot of a row takes the row's first segment again.
-    // Source byte offsets of this lane's slots, fixed for the whole kernel:
-    unsigned slot_off[kWaveLoads];
-#pragma unroll
-    for (int i = 0; i < kWaveLoads; ++i) {
-        const int t = i * 64 + lane;
-        const int r = t / kRowSlots;
-        const int seg = t - r * kRowSlots;
-        slot_off[i] = static_cast<unsigned>(r * 256 + (seg < kRowSlots - 1 ? seg * 16 : 0));
-    }
-    auto dma_chunk = [&](int g) {
-        const int q = g / n_chunks;
-        const int c = g - q * n_chunks;
-        const uint8_t *blk = prepared + q * sbytes;
-        const int k0 = c * kChunk + 32 * wave;
-        const uint8_t *src = blk + static_cast<int64_t>(k0) * 256;
-        __bf16 *dst = s_book[g & 1] + 32 * wave * kRowH;
-#pragma unroll
-        for (int i = 0; i < kWaveLoads; ++i)
-            if (i * 64 + lane < kWaveSlots) dma16(src + slot_off[i], dst + i * 512);
-        if (lane < 8) dma16(blk + prep::bf16_norms(kp) + static_cast<int64_t>(k0 + 4 * lane) * 4, s_norm[g & 1] + 32 * wave);
-    };
-
-    dma_chunk(0);
-    wait_all();
-    __syncthreads();
-
-    for (int q = 0; q < n_stages; ++q) {
-        const unsigned cmax = stage_max_part(prepared + q * sbytes, kp, lane);   // used at the decision
-#pragma unroll
-        for (int s = 0; s < 4; ++s) split8(&n[8 * s], nh[s], nl[s]);
-        float best = kNoScore, second = kNoScore, third = kNoScore;
-        int best_k = 0, second_k = 0;
-        f32x16 da[2], db[2];
-        int prev_base = 0;   // first codeword of the group held in db
-
-        for (int c = 0; c < n_chunks; ++c) {
-            const int g = q * n_chunks + c;
-            if (c > 0) {
-                wait_all();        // this wavefront's copies into chunk g's buffer have landed
-                __syncthreads();   // everyone's have; chunk g-1's buffer is no longer read
-            }
-            if (g + 1 < total) dma_chunk(g + 1);
-            const __bf16 *sb = s_book[g & 1];
-            const float *sn = s_norm[g & 1];
-#pragma unroll 1
-            for (int p = 0; p < kGroups / 2; ++p) {
-                const int ka = 2 * p, kb = 2 * p + 1;
-                if (c == 0 && p == 0)
-                    step_group<false>(da, db, ka, sb, sn, col, half, nh, nl, prev_base, best, second, third, best_k,
-                                      second_k);
-                else
-                    step_group<true>(da, db, ka, sb, sn, col, half, nh, nl, prev_base, best, second, third, best_k,
-                                     second_k);
-                step_group<true>(db, da, kb, sb, sn, col, half, nh, nl, c * kChunk + 64 * ka, best, second, third,
-                                 best_k, second_k);
-                prev_base = c * kChunk + 64 * kb;
-            }
-        }
-        scan_last(db, prev_base, half, best, second, third, best_k, second_k);
-
-        // ---- stage q is scored for this wavefront's 32 frames: decide ----
-        const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
-        const float c2 = wave_max_bits(cmax);
-        decide_stage<kRecon>(n, acc, best, second, third, best_k, second_k, book, n_codes, c2, valid, half, col,
-                             lane, s_frame[wave], (valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
-        if (q + 1 < n_stages) {
-            wait_all();
-            __syncthreads();   // the next stage's first chunk is in LDS; the last one's buffer is free
-        }
-    }
-
-    if (valid) {
-        if (kResidual) {
-            f32x4 *dst = reinterpret_cast<f32x4 *>(residual + frame * kDim + 32 * half);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) dst[t] = f32x4{-n[4 * t], -n[4 * t + 1], -n[4 * t + 2], -n[4 * t + 3]};
-        }
-        if (kRecon) {
-            f32x4 *dst = reinterpret_cast<f32x4 *>(recon + frame * kDim + 32 * half);
-#pragma unroll
-            for (int t = 0; t < 8; ++t)
-                dst[t] = f32x4{acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]};
-        }
-    }
-}
-
 template <bool kPrepared>
 hipError_t launch_variant(const float *x, int64_t n_frames, const float *books, const uint8_t *prepared,
                           int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
@@ -1128,21 +881,10 @@ hipError_t launch_variant(const float *x, int64_t n_frames, const float *books, 
                                x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
         return hipGetLastError();
     }
-    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
     if constexpr (kPrepared) {
-        if (recon && residual)
-            hipLaunchKernelGGL((encode_bf16_pipe_kernel<true, true>), grid, block, 0, stream,
-                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else if (recon)
-            hipLaunchKernelGGL((encode_bf16_pipe_kernel<true, false>), grid, block, 0, stream,
-                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else if (residual)
-            hipLaunchKernelGGL((encode_bf16_pipe_kernel<false, true>), grid, block, 0, stream,
-                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else
-            hipLaunchKernelGGL((encode_bf16_pipe_kernel<false, false>), grid, block, 0, stream,
-                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
+        return hipErrorInvalidValue;   // wide batches with prepared codebooks take the fp16 kernel
     } else {
+        const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
         if (recon && residual)
             hipLaunchKernelGGL((encode_bf16_kernel<true, true>), grid, block, 0, stream,
                                x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
