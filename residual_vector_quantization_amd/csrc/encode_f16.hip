@@ -248,6 +248,26 @@ __device__ __forceinline__ float sqrt_up(float x)
     return __builtin_amdgcn_sqrtf(fmaxf(x, FLT_MIN)) * (1.0f + 9.5367431640625e-07f);
 }
 
+// Float32 direct-form distance sum_j fl(n_j + c_j)^2 of codeword k to the
+// frame held by lanes (l, l^32), fused multiply-adds in four chains per
+// lane; the same value on both lanes. Every lane must call it.
+__device__ __forceinline__ float pair_distance_f32(const float (&n)[32], const float *book, int k, int half)
+{
+    const f32x4 *c = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(k) * kDim + 32 * half);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const f32x4 v = c[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float d = n[4 * t + i] + v[i];
+            a[i] = __builtin_fmaf(d, d, a[i]);
+        }
+    }
+    const float s = (a[0] + a[1]) + (a[2] + a[3]);
+    return s + __shfl_xor(s, 32);
+}
+
 // Entry i (0..3) of a four-entry list, selected without indexing registers.
 __device__ __forceinline__ int pick4(const int (&l)[4], int i)
 {
@@ -322,21 +342,45 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     }
     int pick = cnt0 > 0 ? l0[0] : l1[0];   // the one candidate when ncand == 1
 
-    // Two to eight candidates: float64 re-rank.
+    // Two to eight candidates. A float32 pass first: the direct form
+    // sum_j fl(n_j + c_j)^2 with fused multiply-adds is within
+    // (2u + u^2 + gamma_64) d < 4e-6 d of the exact distance d (u = 2^-24,
+    // all terms >= 0) and the oracle's float64 sum within 1e-14 d of it, so a
+    // candidate whose float32 distance exceeds the smallest one's by more than
+    // 2^-16 of it cannot be the oracle's pick. Only frames whose two smallest
+    // float32 distances are that close take the float64 re-rank of all their
+    // candidates (equal distances included, so ties still go to the lowest
+    // index).
     const bool rerank = valid && !overflow && ncand >= 2;
     if (__any(rerank)) {
-        double bd = INFINITY;
-        int bk = 0x7fffffff;
+        float f1 = INFINITY, f2 = INFINITY;
+        int k1 = pick;
         for (int j = 0; __any(rerank && j < ncand); ++j) {
             const bool use = rerank && j < ncand;
             const int k = use ? (j < cnt0 ? pick4(l0, j) : pick4(l1, j - cnt0)) : pick;
-            const double dist = pair_distance(n, book, k, half);
-            if (use && (dist < bd || (dist == bd && k < bk))) {
-                bd = dist;
-                bk = k;
+            const float f = pair_distance_f32(n, book, k, half);
+            if (use) {
+                f2 = f < f1 ? f1 : fminf(f2, f);
+                k1 = f < f1 ? k : k1;
+                f1 = fminf(f1, f);
             }
         }
-        if (rerank) pick = bk;
+        const bool exact = rerank && f2 <= f1 * (1.0f + 1.52587890625e-05f) + 1e-30f;
+        if (rerank) pick = k1;
+        if (__any(exact)) {
+            double bd = INFINITY;
+            int bk = 0x7fffffff;
+            for (int j = 0; __any(exact && j < ncand); ++j) {
+                const bool use = exact && j < ncand;
+                const int k = use ? (j < cnt0 ? pick4(l0, j) : pick4(l1, j - cnt0)) : pick;
+                const double dist = pair_distance(n, book, k, half);
+                if (use && (dist < bd || (dist == bd && k < bk))) {
+                    bd = dist;
+                    bk = k;
+                }
+            }
+            if (exact) pick = bk;
+        }
     }
 
     // A third candidate inside one set (or a frame or stage out of range): full rescan.
