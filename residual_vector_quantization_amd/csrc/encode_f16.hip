@@ -274,6 +274,157 @@ __device__ __forceinline__ int pick4(const int (&l)[4], int i)
     return i == 0 ? l[0] : i == 1 ? l[1] : i == 2 ? l[2] : l[3];
 }
 
+// Codeword i of key set (h, s) in ascending order: lane half h holds rows
+// with bit 2 equal to h, set s the 64-codeword groups with bit 6 equal to s.
+__device__ __forceinline__ int subset_code(int i, int h, int s)
+{
+    return ((i >> 5) << 7) | (s << 6) | (((i >> 2) & 7) << 3) | (h << 2) | (i & 3);
+}
+
+// Float32 direct form sum_j fl(r_j + c_j)^2 over all 64 dims of codeword k
+// (frame row r in LDS), four fused multiply-add chains; within
+// (2u + u^2 + gamma_64) of the exact distance, as pair_distance_f32.
+__device__ __forceinline__ float row_distance_f32(const float *row, const float *book, int k)
+{
+    const f32x4 *r4 = reinterpret_cast<const f32x4 *>(row);
+    const f32x4 *c4 = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(k) * kDim);
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+        const f32x4 rv = r4[t], cv = c4[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float d = rv[i] + cv[i];
+            a[i] = __builtin_fmaf(d, d, a[i]);
+        }
+    }
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
+
+// Float64 direct form in the oracle's order (j = 0..63, one rounding per
+// operation) of codeword k against the frame row in LDS.
+__device__ __forceinline__ double row_distance_f64(const float *row, const float *book, int k)
+{
+    const f32x4 *r4 = reinterpret_cast<const f32x4 *>(row);
+    const f32x4 *c4 = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(k) * kDim);
+    double acc = 0.0;
+#pragma unroll 4
+    for (int t = 0; t < 16; ++t) {
+        const f32x4 rv = r4[t], cv = c4[t];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double d = __dadd_rn(static_cast<double>(rv[i]), static_cast<double>(cv[i]));
+            acc = __dadd_rn(acc, __dmul_rn(d, d));
+        }
+    }
+    return acc;
+}
+
+// A third candidate inside one or more key sets of frame f (lanes f, f+32):
+// the wavefront takes every codeword of each overflowed set (bit 2h+s of
+// `mask`) and the listed candidates of the other sets (l0 / l1 / cnt0 /
+// ncand as held by lane f); float32 distances first, and the float64 direct
+// form for every entry within 2^-16 of the smallest when the two smallest
+// are that close (ties go to the lowest index). Returns the winner on every
+// lane. Every lane must call it; `row` is a 64-float LDS row of this
+// wavefront.
+__device__ int resolve_sets(const float (&n)[32], float *row, const float *book, int n_codes, int f, int lane,
+                            unsigned mask, const int (&l0)[4], const int (&l1)[4], int cnt0, int ncand)
+{
+    const int col = lane & 31, half = lane >> 5;
+    if (col == f) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+            *reinterpret_cast<f32x4 *>(&row[32 * half + 4 * t]) =
+                f32x4{n[4 * t], n[4 * t + 1], n[4 * t + 2], n[4 * t + 3]};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // frame f's listed candidates, on every lane
+    const int c0 = __builtin_amdgcn_readlane(cnt0, f);
+    const int nc = __builtin_amdgcn_readlane(ncand, f);
+    const int a0 = __builtin_amdgcn_readlane(l0[0], f), a1 = __builtin_amdgcn_readlane(l0[1], f);
+    const int a2 = __builtin_amdgcn_readlane(l0[2], f), a3 = __builtin_amdgcn_readlane(l0[3], f);
+    const int b0 = __builtin_amdgcn_readlane(l1[0], f), b1 = __builtin_amdgcn_readlane(l1[1], f);
+    const int b2 = __builtin_amdgcn_readlane(l1[2], f), b3 = __builtin_amdgcn_readlane(l1[3], f);
+    const int span = (n_codes + 127) / 128 * 32;   // index range of one set
+    auto in_mask = [&](int k) { return ((mask >> (2 * ((k >> 2) & 1) + ((k >> 6) & 1))) & 1u) != 0; };
+    // lane e < ncand takes listed candidate e (half 0's list, then half 1's)
+    // unless its set is swept anyway
+    int extra = -1;
+    if (lane < nc) {
+        const bool first = lane < c0;
+        const int j = first ? lane : lane - c0;
+        const int q0 = first ? a0 : b0, q1 = first ? a1 : b1, q2 = first ? a2 : b2, q3 = first ? a3 : b3;
+        const int k = j == 0 ? q0 : j == 1 ? q1 : j == 2 ? q2 : q3;
+        if (!in_mask(k)) extra = k;
+    }
+    // float32 pass
+    float f1 = INFINITY, f2 = INFINITY;
+    int k1 = 0x7fffffff;
+    auto take = [&](int k) {
+        const float d = row_distance_f32(row, book, k);
+        f2 = d < f1 ? f1 : fminf(f2, d);
+        k1 = d < f1 ? k : k1;
+        f1 = fminf(f1, d);
+    };
+    for (int b = 0; b < 4; ++b) {
+        if (!((mask >> b) & 1u)) continue;
+        for (int i = lane; i < span; i += 64) {
+            const int k = subset_code(i, b >> 1, b & 1);
+            if (k < n_codes) take(k);
+        }
+    }
+    if (extra >= 0) take(extra);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float of1 = __shfl_xor(f1, off), of2 = __shfl_xor(f2, off);
+        const int ok1 = __shfl_xor(k1, off);
+        const float lo = fminf(f1, of1), hi = fmaxf(f1, of1);
+        k1 = f1 < of1 ? k1 : (of1 < f1 ? ok1 : min(k1, ok1));
+        f2 = fminf(fminf(f2, of2), hi);
+        f1 = lo;
+    }
+    const float thr = f1 * (1.0f + 1.52587890625e-05f) + 1e-30f;
+    int win = k1;
+    if (f2 <= thr) {   // wave-uniform: float64 for every entry within thr of the smallest
+        double bd = INFINITY;
+        int bk = 0x7fffffff;
+        auto exact = [&](int k) {
+            if (row_distance_f32(row, book, k) <= thr) {
+                const double d = row_distance_f64(row, book, k);
+                if (d < bd || (d == bd && k < bk)) {
+                    bd = d;
+                    bk = k;
+                }
+            }
+        };
+        for (int b = 0; b < 4; ++b) {
+            if (!((mask >> b) & 1u)) continue;
+            for (int i = lane; i < span; i += 64) {
+                const int k = subset_code(i, b >> 1, b & 1);
+                if (k < n_codes) exact(k);
+            }
+        }
+        if (extra >= 0) exact(extra);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const double od = __shfl_xor(bd, off);
+            const int ok = __shfl_xor(bk, off);
+            if (od < bd || (od == bd && ok < bk)) {
+                bd = od;
+                bk = ok;
+            }
+        }
+        win = bk;
+    }
+    // all reads of `row` are done before a later call overwrites it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    return win;
+}
+
 // The decision for one stage from this lane's two key sets (codeword slots
 // of one half of a frame; lanes l and l^32 hold the two halves): every
 // codeword within 2E (1) of the frame's smallest key is a candidate; two to
@@ -305,14 +456,17 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     const float frame_min = fminf(lane_min, __shfl_xor(lane_min, 32));
     const float lim = frame_min + 2.0f * bound + fabsf(frame_min) * 2.4e-7f;
 
-    bool ov = false;
+    // key sets holding a third candidate (or ambiguous bookkeeping): bit s
+    // for this lane, bit 2h+s for the frame
+    unsigned ovs = 0u;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        ov = ov || ks[s].third <= lim || (ks[s].second <= lim && ks[s].second_k == ks[s].best_k);
-    // the shuffle must run on every lane: a short-circuit would leave the
-    // partner lane inactive and the two halves of a frame could disagree
-    const int ov_o = __shfl_xor(static_cast<int>(ov), 32);
-    const bool overflow = bad || ov || ov_o != 0;
+        if (ks[s].third <= lim || (ks[s].second <= lim && ks[s].second_k == ks[s].best_k)) ovs |= 1u << s;
+    // the shuffle must run on every lane: under a divergent mask the partner
+    // lane could be inactive and the two halves of a frame could disagree
+    const unsigned ovs_o = static_cast<unsigned>(__shfl_xor(static_cast<int>(ovs), 32));
+    const unsigned ovmask = half ? (ovs_o | (ovs << 2)) : (ovs | (ovs_o << 2));
+    const bool overflow = bad || ovmask != 0u;
 
     // this lane's candidates, compacted: set 0 best, second, set 1 best, second
     const float sv[4] = {ks[0].best, ks[0].second, ks[1].best, ks[1].second};
@@ -383,12 +537,17 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
         }
     }
 
-    // A third candidate inside one set (or a frame or stage out of range): full rescan.
+    // A third candidate inside a key set: those sets swept, the other
+    // candidates added. A frame or stage out of fp16's range: full rescan.
     uint64_t pending = __ballot(valid && overflow && half == 0);
     while (pending) {
         const int f = __ffsll(static_cast<unsigned long long>(pending)) - 1;
         pending &= pending - 1;
-        const int w = rescan_frame(n, frame_row, book, n_codes, f, lane);
+        const int w = __builtin_amdgcn_readlane(static_cast<int>(bad), f)
+                          ? rescan_frame(n, frame_row, book, n_codes, f, lane)
+                          : resolve_sets(n, frame_row, book, n_codes, f, lane,
+                                         static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(ovmask), f)),
+                                         l0, l1, cnt0, ncand);
         if (col == f) pick = w;
     }
 
