@@ -248,22 +248,28 @@ __device__ __forceinline__ float sqrt_up(float x)
     return __builtin_amdgcn_sqrtf(fmaxf(x, FLT_MIN)) * (1.0f + 9.5367431640625e-07f);
 }
 
-// Float32 direct-form distance sum_j fl(n_j + c_j)^2 of codeword k to the
-// frame held by lanes (l, l^32), fused multiply-adds in four chains per
-// lane; the same value on both lanes. Every lane must call it.
-__device__ __forceinline__ float pair_distance_f32(const float (&n)[32], const float *book, int k, int half)
+// This lane's half (32 dims) of codeword k's fp32 row.
+__device__ __forceinline__ void load_row(f32x4 (&row)[8], const float *book, int k, int half)
 {
-    const f32x4 *c = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(k) * kDim + 32 * half);
+    const f32x4 *src = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(k) * kDim + 32 * half);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) row[t] = src[t];
+}
+
+// Float32 direct-form distance sum_j fl(n_j + c_j)^2 of a codeword (this
+// lane's half of its row in registers) to the frame held by lanes
+// (l, l^32), fused multiply-adds in four chains per lane; the same value on
+// both lanes. Every lane must call it.
+__device__ __forceinline__ float pair_distance_f32_row(const float (&n)[32], const f32x4 (&row)[8])
+{
     float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const f32x4 v = c[t];
+    for (int t = 0; t < 8; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float d = n[4 * t + i] + v[i];
+            const float d = n[4 * t + i] + row[t][i];
             a[i] = __builtin_fmaf(d, d, a[i]);
         }
-    }
     const float s = (a[0] + a[1]) + (a[2] + a[3]);
     return s + __shfl_xor(s, 32);
 }
@@ -283,7 +289,7 @@ __device__ __forceinline__ int subset_code(int i, int h, int s)
 
 // Float32 direct form sum_j fl(r_j + c_j)^2 over all 64 dims of codeword k
 // (frame row r in LDS), four fused multiply-add chains; within
-// (2u + u^2 + gamma_64) of the exact distance, as pair_distance_f32.
+// (2u + u^2 + gamma_64) of the exact distance, as pair_distance_f32_row.
 __device__ __forceinline__ float row_distance_f32(const float *row, const float *book, int k)
 {
     const f32x4 *r4 = reinterpret_cast<const f32x4 *>(row);
@@ -453,8 +459,19 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     const float bound = (kRel * (t_up + r_up * c_up) + kAbsN * r_up + kAbsC * c_up + ldexpf(kAbsNorm, -e) +
                          kAbsConst) * (1.0f + 2.44140625e-04f);
     const float lane_min = fminf(ks[0].best, ks[1].best);
-    const float frame_min = fminf(lane_min, __shfl_xor(lane_min, 32));
+    const int lane_k = ks[0].best <= ks[1].best ? ks[0].best_k : ks[1].best_k;
+    const float other_min = __shfl_xor(lane_min, 32);
+    const int other_k = __shfl_xor(lane_k, 32);
+    const float frame_min = fminf(lane_min, other_min);
     const float lim = frame_min + 2.0f * bound + fabsf(frame_min) * 2.4e-7f;
+    // The smallest key's codeword (half 0's on equal keys) is the pick of
+    // every frame with one candidate, and one candidate of every other frame:
+    // its row is fetched now, for the re-rank and the update, so that the
+    // decision waits for at most one more round of row loads.
+    const int pred = (lane_min < other_min || (lane_min == other_min && half == 0)) ? lane_k : other_k;
+    f32x4 prow[8];
+    load_row(prow, book, min(max(pred, 0), n_codes - 1), half);
+    int have = pred;   // the codeword whose row prow holds
 
     // key sets holding a third candidate (or ambiguous bookkeeping): bit s
     // for this lane, bit 2h+s for the frame
@@ -494,7 +511,7 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
         l0[j] = half ? list_o[j] : list[j];
         l1[j] = half ? list[j] : list_o[j];
     }
-    int pick = cnt0 > 0 ? l0[0] : l1[0];   // the one candidate when ncand == 1
+    int pick = pred;   // the one candidate when ncand == 1
 
     // Two to eight candidates. A float32 pass first: the direct form
     // sum_j fl(n_j + c_j)^2 with fused multiply-adds is within
@@ -504,29 +521,44 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     // 2^-16 of it cannot be the oracle's pick. Only frames whose two smallest
     // float32 distances are that close take the float64 re-rank of all their
     // candidates (equal distances included, so ties still go to the lowest
-    // index).
+    // index). pred's row is already here; the loop loads the others, the
+    // list without pred (which appears in it once).
     const bool rerank = valid && !overflow && ncand >= 2;
     if (__any(rerank)) {
-        float f1 = INFINITY, f2 = INFINITY;
-        int k1 = pick;
-        for (int j = 0; __any(rerank && j < ncand); ++j) {
-            const bool use = rerank && j < ncand;
-            const int k = use ? (j < cnt0 ? pick4(l0, j) : pick4(l1, j - cnt0)) : pick;
-            const float f = pair_distance_f32(n, book, k, half);
+        auto entry = [&](int e) { return e < cnt0 ? pick4(l0, e) : pick4(l1, e - cnt0); };
+        int pos = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (e < ncand && entry(e & 7) == pred) pos = e;
+        float f1 = pair_distance_f32_row(n, prow), f2 = INFINITY;
+        int k1 = pred;
+        for (int j = 0; __any(rerank && j < ncand - 1); ++j) {
+            const bool use = rerank && j < ncand - 1;
+            const int k = use ? entry(j + (j >= pos)) : pred;
+            f32x4 cur[8];
+            load_row(cur, book, k, half);
+            const float f = pair_distance_f32_row(n, cur);
             if (use) {
                 f2 = f < f1 ? f1 : fminf(f2, f);
-                k1 = f < f1 ? k : k1;
+                if (f < f1) {
+                    k1 = k;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) prow[t] = cur[t];
+                }
                 f1 = fminf(f1, f);
             }
         }
+        if (rerank) {
+            pick = k1;
+            have = k1;
+        }
         const bool exact = rerank && f2 <= f1 * (1.0f + 1.52587890625e-05f) + 1e-30f;
-        if (rerank) pick = k1;
         if (__any(exact)) {
             double bd = INFINITY;
             int bk = 0x7fffffff;
             for (int j = 0; __any(exact && j < ncand); ++j) {
                 const bool use = exact && j < ncand;
-                const int k = use ? (j < cnt0 ? pick4(l0, j) : pick4(l1, j - cnt0)) : pick;
+                const int k = use ? entry(j) : pick;
                 const double dist = pair_distance(n, book, k, half);
                 if (use && (dist < bd || (dist == bd && k < bk))) {
                     bd = dist;
@@ -553,14 +585,15 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
 
     pick = min(max(pick, 0), n_codes - 1);
     if (code_out) *code_out = pick;
-    const f32x4 *cw = reinterpret_cast<const f32x4 *>(book + static_cast<int64_t>(pick) * kDim + 32 * half);
+    if (__any(pick != have)) {   // an exact re-rank, sweep or rescan moved the pick
+        if (pick != have) load_row(prow, book, pick, half);
+    }
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-        const f32x4 v = cw[t];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            n[4 * t + i] = n[4 * t + i] + v[i];   // = -(r - c), exactly
-            if (kRecon) acc[4 * t + i] = acc[4 * t + i] + v[i];
+            n[4 * t + i] = n[4 * t + i] + prow[t][i];   // = -(r - c), exactly
+            if (kRecon) acc[4 * t + i] = acc[4 * t + i] + prow[t][i];
         }
     }
 }
