@@ -530,13 +530,19 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             if (e < ncand && entry(e & 7) == pred) pos = e;
+        // the first other candidate's row is requested before pred's
+        // distance waits for pred's row
+        int k = rerank ? entry(pos == 0 ? 1 : 0) : pred;
+        f32x4 cur[8];
+        load_row(cur, book, k, half);
         float f1 = pair_distance_f32_row(n, prow), f2 = INFINITY;
         int k1 = pred;
         for (int j = 0; __any(rerank && j < ncand - 1); ++j) {
             const bool use = rerank && j < ncand - 1;
-            const int k = use ? entry(j + (j >= pos)) : pred;
-            f32x4 cur[8];
-            load_row(cur, book, k, half);
+            if (j > 0) {
+                k = use ? entry(j + (j >= pos)) : pred;
+                load_row(cur, book, k, half);
+            }
             const float f = pair_distance_f32_row(n, cur);
             if (use) {
                 f2 = f < f1 ? f1 : fminf(f2, f);
