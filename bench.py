@@ -111,6 +111,7 @@ rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
+rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/valu -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
 python3 $R/bench.py --workload {wl} --summarize-profiles $R/gpurun_out/prof"""
 
 
@@ -212,11 +213,11 @@ def summarize_profiles(w, src_dir):
     f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
     w_scale = COPY_BYTES / (write["copy"] * 1024.0)
     enc_algo = (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d
-    # the prepared encodes read their section of the prepared codebooks: fp16 rows (128 B), half-norm
-    # parts, stage maxima and exponent (encode_f16; plus the fp32 rows of the picks), or split-bf16
+    # the prepared encodes read their section of the prepared codebooks: fp16 rows with their half-norm
+    # parts (144 B), stage maxima and exponent (encode_f16; plus the fp32 rows of the picks), or split-bf16
     # rows (256 B), norms and stage maxima (encode_bf16) in place of the fp32 codebook
     kp = -(-k // 256) * 256
-    prep16_bytes = q * (kp * 132 + 4 * (kp // 256) + 4)
+    prep16_bytes = q * (kp * 144 + 4 * (kp // 256) + 4)
     prep_bytes = q * (kp * 260 + 4 * (kp // 256))
     algo = {"encode_f16": enc_algo + prep16_bytes, "encode_bf16": enc_algo - 4.0 * q * k * d + prep_bytes,
             "encode_fp32": enc_algo, "decode": dec_bytes + 4.0 * q * k * d}
@@ -258,6 +259,27 @@ def summarize_profiles(w, src_dir):
                   f"- instructions: VALU {c['SQ_INSTS_VALU']:.4g} of which MFMA {c['SQ_INSTS_MFMA']:.4g}",
                   f"- LDS bank-conflict cycles / LDS active cycles: "
                   f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_LDS_IDX_ACTIVE'], 1):.1%}", ""]
+    vdir = os.path.join(src_dir, "valu")
+    if os.path.isdir(vdir):
+        vf = _csv(vdir, "counter_collection.csv")
+        vnames = ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_MFMA", "SQ_WAIT_INST_ANY",
+                  "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+        vm = {name: _counter_means(vf, name) for name in vnames}
+        lines += ["## Instruction-issue counters (per launch)", ""]
+        for kind in ("encode_f16", "encode_fp32"):
+            c = {name: vm[name].get(kind) for name in vnames}
+            if c["GRBM_GUI_ACTIVE"] is None:
+                continue
+            active = c["GRBM_GUI_ACTIVE"] / N_XCD
+            lines += [f"{kind}:",
+                      f"- instructions: VALU {c['SQ_INSTS_VALU']:.4g} (MFMA {c['SQ_INSTS_MFMA']:.4g}), "
+                      f"SALU {c['SQ_INSTS_SALU']:.4g}, LDS {c['SQ_INSTS_LDS']:.4g}",
+                      f"- VALU issue: {c['SQ_INSTS_VALU'] * 4 / (active * N_SIMD):.1%} of SIMD cycles "
+                      f"(4 cycles per wavefront instruction on a 16-lane SIMD; SQ_INSTS_VALU x 4 / "
+                      f"(GRBM_GUI_ACTIVE per XCD x {N_SIMD} SIMDs))",
+                      f"- waves waiting on a dependency or counter: "
+                      f"{c['SQ_WAIT_INST_ANY'] / max(c['SQ_WAVE_CYCLES'], 1):.1%} of wave cycles "
+                      f"(SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)", ""]
     path = os.path.join(out_dir, f"encode_decode_{w.name}_rocprof.md")
     open(path, "w").write("\n".join(lines) + "\n")
     print("wrote", path)

@@ -769,7 +769,6 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
     uint8_t *blk = prepared + q * stage_bytes(n_codes);
     float *norms = reinterpret_cast<float *>(blk + prep::bf16_norms(kp));
     uint8_t *rows16 = blk + prep::f16_offset(kp);
-    unsigned *halfn = reinterpret_cast<unsigned *>(blk + prep::f16_halfn(kp));
     const float *stage = books + static_cast<int64_t>(q) * n_codes * kDim;
 
     // the stage's largest |c|: bits of non-negative floats order like the
@@ -799,7 +798,7 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
     unsigned m = 0u, m16 = 0u;
     for (int k = c * kChunk + (threadIdx.x >> 3); k < (c + 1) * kChunk; k += kPrepThreads / 8) {
         bf16x8 *row = reinterpret_cast<bf16x8 *>(blk + static_cast<int64_t>(k) * 256);
-        u32x4 *row16 = reinterpret_cast<u32x4 *>(rows16 + static_cast<int64_t>(k) * 128);
+        u32x4 *row16 = reinterpret_cast<u32x4 *>(rows16 + static_cast<int64_t>(k) * prep::kF16Row);
         if (k >= n_codes) {   // the 8 lanes of a row take the same branch
             const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
             row[2 * grp] = z;
@@ -807,7 +806,7 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
             row16[grp] = u32x4{0u, 0u, 0u, 0u};
             if (grp == 0) {
                 norms[k] = kNoScore;
-                halfn[k] = 0u;
+                row16[8] = u32x4{0u, 0u, 0u, 0u};
             }
             continue;
         }
@@ -841,8 +840,9 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
             // two fp16 parts: hn16 - hi is exact in fp32
             const _Float16 p_hi = static_cast<_Float16>(hn16);
             const _Float16 p_lo = static_cast<_Float16>(hn16 - static_cast<float>(p_hi));
-            halfn[k] = static_cast<unsigned>(__builtin_bit_cast(unsigned short, p_hi)) |
-                       (static_cast<unsigned>(__builtin_bit_cast(unsigned short, p_lo)) << 16);
+            row16[8] = u32x4{static_cast<unsigned>(__builtin_bit_cast(unsigned short, p_hi)) |
+                                 (static_cast<unsigned>(__builtin_bit_cast(unsigned short, p_lo)) << 16),
+                             0u, 0u, 0u};
         }
         m = max(m, __float_as_uint(hn));   // hn >= 0: bits order like values
         m16 = max(m16, __float_as_uint(hn16));

@@ -39,12 +39,11 @@
 // it to the full float64 rescan.
 //
 // Work split: 4 wavefronts x 32 frames per workgroup and two workgroups per
-// CU (76.8 KB of LDS each), residual in VGPRs, prepared fp16 rows copied
-// straight into LDS in 256-codeword chunks (144-byte rows, double
-// buffered), each chunk scored as four 64-codeword groups of two
-// interleaved matrix-core chains, with the key scan of one group issued
-// between the matrix-core steps of the next. Two independent workgroups per
-// CU let one workgroup's stage decision overlap the other's scoring.
+// CU (74.8 KB of LDS each), residual in VGPRs, prepared fp16 rows (64 dims
+// and the half-norm parts, 144 bytes) copied straight into LDS in
+// 256-codeword chunks (double buffered), each chunk scored as four
+// 64-codeword groups of two interleaved matrix-core chains, with the key
+// scan of one group issued between the matrix-core steps of the next.
 #include "encode_common.h"
 #include "prepared.h"
 
@@ -65,12 +64,13 @@ constexpr int kFramesPerWave = 32;
 constexpr int kBlockFrames = kWaves * kFramesPerWave;
 constexpr int kChunk = prep::kChunk;                         // codewords per LDS chunk (4 groups of 64)
 constexpr int kGroups = kChunk / 64;
-constexpr int kRowSlots = 9;                                 // 16-byte LDS slots per row: 8 data + 1 padding
+constexpr int kRowSlots = 9;                                 // 16-byte slots per row: 8 of dims, 1 of half-norm
 constexpr int kRowHalfs = 8 * kRowSlots;                     // fp16 per LDS row
 constexpr int kWaveRows = kChunk / kWaves;                   // rows each wavefront copies per chunk
 constexpr int kWaveLoads = kWaveRows * kRowSlots / 64;       // wavefront-wide row copies per chunk
 static_assert(kWaveRows * kRowSlots % 64 == 0, "whole wavefront-wide copies");
 static_assert(kGroups == 4, "two group pairs per chunk");
+static_assert(prep::kF16Row == 16 * kRowSlots, "LDS rows mirror the prepared rows");
 
 // Relative and absolute coefficients of (1), rounded up.
 constexpr float kRel = 1.0e-3f;        // 2u + u^2 + 2 gamma_72 + 2^-17 + u^2 + gamma_64 = 9.971e-4
@@ -147,15 +147,14 @@ __device__ __forceinline__ void fold(KeySet &s, unsigned bb0, unsigned sb0, int 
 // steps (norm block 0, norm block 1, then dims 0..63 for blocks 0 and 1).
 constexpr int kScanAfter[10] = {4, 4, 3, 3, 3, 3, 3, 3, 3, 3};
 
-// Matrix-core steps of group kG of the chunk in LDS (rows sb, half-norm
-// parts sh) into dn: two 32-codeword blocks, each a chain of the half-norm
+// Matrix-core steps of group kG of the chunk in LDS (rows sb) into dn: two 32-codeword blocks, each a chain of the half-norm
 // step and four 16-dim steps. When kScan, the key scan of the previous
 // group dp (first codeword prev_base) into set `ks` is placed between them
 // in a fixed order, and the operands of the next step are read from LDS
 // before the current step's products are issued.
 template <bool kScan>
 __device__ __forceinline__ void step_group(f32x16 (&dn)[2], const f32x16 (&dp)[2], int kG, const _Float16 *sb,
-                                           const unsigned *sh, int col, int half, const f16x8 (&nb)[4],
+                                           int col, int half, const f16x8 (&nb)[4],
                                            const f16x8 &nnorm, int prev_base, KeySet &ks)
 {
     const unsigned bb0 = __float_as_uint(ks.best), sb0 = __float_as_uint(ks.second);
@@ -166,10 +165,12 @@ __device__ __forceinline__ void step_group(f32x16 (&dn)[2], const f32x16 (&dp)[2
             a[s & 1][b] = *reinterpret_cast<const f16x8 *>(sb + (kG * 64 + b * 32 + col) * kRowHalfs +
                                                           8 * (4 * half + s));
     };
+    // the half-norm step's operand: the row's last slot (its two fp16 parts
+    // first, then zeros; only half 0's first two products are nonzero)
     f16x8 an[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b)
-        an[b] = __builtin_bit_cast(f16x8, u32x4{sh[kG * 64 + b * 32 + col], 0u, 0u, 0u});
+        an[b] = *reinterpret_cast<const f16x8 *>(sb + (kG * 64 + b * 32 + col) * kRowHalfs + 64);
     load_ops(0);
     int v = 0;   // next score of dp
     auto scan_some = [&](int count) {
@@ -612,7 +613,6 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
                        int32_t *__restrict__ codes, int codes_ld,
                        float *__restrict__ residual, float *__restrict__ recon)
 {
-    __shared__ __align__(16) unsigned s_half[2][kChunk];
     __shared__ __align__(16) _Float16 s_rows[2][kChunk * kRowHalfs];
     __shared__ __align__(16) float s_frame[kWaves][kDim];   // rescan: one frame's residual
 
@@ -647,29 +647,18 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
     const int n_groups = (n_codes + 63) / 64;   // groups past it hold only padding rows and are not scanned
     const int total = n_stages * n_chunks;
 
-    // wavefront w copies rows kWaveRows*w .. +kWaveRows-1 of chunk g and their
-    // half-norm parts into buffer g % 2; slot t of its rows is segment t % 9
-    // of row t / 9, the 9th (padding) slot of a row takes the row's first
-    // segment again. Source byte offsets of this lane's slots:
-    unsigned slot_off[kWaveLoads];
-#pragma unroll
-    for (int i = 0; i < kWaveLoads; ++i) {
-        const int t = i * 64 + lane;
-        const int r = t / kRowSlots;
-        const int seg = t - r * kRowSlots;
-        slot_off[i] = static_cast<unsigned>(r * 128 + (seg < kRowSlots - 1 ? seg * 16 : 0));
-    }
+    // wavefront w copies rows kWaveRows*w .. +kWaveRows-1 of chunk g (144
+    // bytes each, contiguous in the prepared block and in LDS) into buffer
+    // g % 2
     auto dma_chunk = [&](int g) {
         const int q = g / n_chunks;
         const int c = g - q * n_chunks;
         const uint8_t *blk = prepared + q * sbytes;
         const int k0 = c * kChunk + kWaveRows * wave;
-        const uint8_t *src = blk + prep::f16_offset(kp) + static_cast<int64_t>(k0) * 128;
+        const uint8_t *src = blk + prep::f16_offset(kp) + static_cast<int64_t>(k0) * prep::kF16Row + 16 * lane;
         _Float16 *dst = s_rows[g & 1] + kWaveRows * wave * kRowHalfs;
 #pragma unroll
-        for (int i = 0; i < kWaveLoads; ++i) dma16(src + slot_off[i], dst + i * 512);
-        if (lane < kWaveRows / 4)
-            dma16(blk + prep::f16_halfn(kp) + static_cast<int64_t>(k0 + 4 * lane) * 4, s_half[g & 1] + kWaveRows * wave);
+        for (int i = 0; i < kWaveLoads; ++i) dma16(src + 1024 * i, dst + i * 512);
     };
 
     dma_chunk(0);
@@ -701,7 +690,6 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
             }
             if (g + 1 < total) dma_chunk(g + 1);
             const _Float16 *sb = s_rows[g & 1];
-            const unsigned *sh = s_half[g & 1];
 #pragma unroll 1
             for (int p = 0; p < kGroups / 2; ++p) {
                 const int ka = 2 * p, kb = 2 * p + 1;
@@ -710,16 +698,16 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
                 const bool scan_a = !(c == 0 && p == 0) && (prev_base >> 6) < n_groups;
                 if (scan_a) {
                     if (prev_base + 64 > n_codes) mask_tail(db, prev_base, half, n_codes);
-                    step_group<true>(da, db, ka, sb, sh, col, half, nb, nnorm, prev_base, ks[1]);
+                    step_group<true>(da, db, ka, sb, col, half, nb, nnorm, prev_base, ks[1]);
                 } else {
-                    step_group<false>(da, db, ka, sb, sh, col, half, nb, nnorm, prev_base, ks[1]);
+                    step_group<false>(da, db, ka, sb, col, half, nb, nnorm, prev_base, ks[1]);
                 }
                 const int base_a = c * kChunk + 64 * ka;
                 if ((base_a >> 6) < n_groups) {
                     if (base_a + 64 > n_codes) mask_tail(da, base_a, half, n_codes);
-                    step_group<true>(db, da, kb, sb, sh, col, half, nb, nnorm, base_a, ks[0]);
+                    step_group<true>(db, da, kb, sb, col, half, nb, nnorm, base_a, ks[0]);
                 } else {
-                    step_group<false>(db, da, kb, sb, sh, col, half, nb, nnorm, base_a, ks[0]);
+                    step_group<false>(db, da, kb, sb, col, half, nb, nnorm, base_a, ks[0]);
                 }
                 prev_base = c * kChunk + 64 * kb;
             }

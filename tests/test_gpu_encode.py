@@ -237,7 +237,7 @@ def _stage_layout(k):
     """(Kp, offset of the fp16 section, stage block bytes) of the prepared layout."""
     kp = (k + 255) // 256 * 256
     f16 = (kp * 260 + 4 * (kp // 256) + 255) // 256 * 256
-    return kp, f16, (f16 + kp * 132 + 4 * (kp // 256) + 4 + 255) // 256 * 256
+    return kp, f16, (f16 + kp * 144 + 4 * (kp // 256) + 4 + 255) // 256 * 256
 
 
 def _stage_exp(book):
@@ -251,9 +251,9 @@ def test_prepared_layout(q, k):
     """rvq_prepare_codebooks. Split-bf16 section: per stage Kp = roundup(K, 256) rows of 8-dim groups
     (8 hi, 8 lo bf16), hi = bf16(v) and lo = bf16(v - hi) round to nearest even; Kp fp32 half-norms
     (FLT_MAX on padding rows, which are zero); the bits of the largest valid half-norm of every 256
-    rows. fp16 section: fp16 (round to nearest even) of c' = 2^e c with the stage's power of two e;
-    the two fp16 parts of 0.5*||c'||^2; the largest of those per 256 rows; e. Stage blocks 256-byte
-    aligned."""
+    rows. fp16 section: 144-byte rows of fp16 (round to nearest even) of c' = 2^e c with the stage's
+    power of two e, then the two fp16 parts of 0.5*||c'||^2 and zeros; the largest of those per 256
+    rows; e. Stage blocks 256-byte aligned."""
     m = rvq()
     rng = np.random.default_rng(600 + k)
     books = (rng.standard_normal((q, k, 64)) * 3.0 * 4.0 ** -np.arange(q)[:, None, None]).astype(np.float32)
@@ -280,19 +280,21 @@ def test_prepared_layout(q, k):
             assert maxima[c] == (valid.view(np.uint32).max() if valid.size else 0)
         # fp16 section
         e = _stage_exp(books[s])
-        assert blk[f16 + kp * 132 + 4 * (kp // 256):][:4].view(np.int32)[0] == e
+        assert blk[f16 + kp * 144 + 4 * (kp // 256):][:4].view(np.int32)[0] == e
         scaled = (books[s].astype(np.float64) * 2.0 ** e).astype(np.float32)   # exact: a power of two
-        rows16 = blk[f16:f16 + kp * 128].view(np.float16).reshape(kp, 64)
-        np.testing.assert_array_equal(rows16[:k].view(np.uint16), scaled.astype(np.float16).view(np.uint16))
-        assert not rows16[k:].view(np.uint16).any()
-        parts = blk[f16 + kp * 128:f16 + kp * 132].view(np.float16).reshape(kp, 2).astype(np.float64)
+        rows = blk[f16:f16 + kp * 144].view(np.uint16).reshape(kp, 72)
+        rows16 = rows[:, :64]
+        np.testing.assert_array_equal(rows16[:k], scaled.astype(np.float16).view(np.uint16))
+        assert not rows16[k:].any()
+        assert not rows[:, 66:].any()   # zeros after the half-norm parts
+        parts = rows[:, 64:66].copy().view(np.float16).astype(np.float64)
         want = 0.5 * (scaled.astype(np.float64) ** 2).sum(axis=1)
         got = parts[:k, 0] + parts[:k, 1]
         assert (np.abs(got - want) <= 2e-6 * want + 2.0 ** -24).all()
         # the high part is the fp16 rounding of the sum of both parts
         np.testing.assert_array_equal(parts[:k, 0], got.astype(np.float16).astype(np.float64))
         assert not parts[k:].any()
-        max16 = blk[f16 + kp * 132:f16 + kp * 132 + 4 * (kp // 256)].view(np.float32)
+        max16 = blk[f16 + kp * 144:f16 + kp * 144 + 4 * (kp // 256)].view(np.float32)
         for c in range(kp // 256):
             w = want[256 * c:min(256 * (c + 1), k)]
             assert max16[c] == pytest.approx(w.max() if w.size else 0.0, rel=2e-6, abs=1e-30)
@@ -310,9 +312,9 @@ def test_prepared_out_of_fp16_range():
     kp, f16, sbytes = _stage_layout(300)
     for s, inf in ((0, False), (1, True), (2, False)):
         blk = prep[s * sbytes:(s + 1) * sbytes]
-        max16 = blk[f16 + kp * 132:f16 + kp * 132 + 4 * (kp // 256)].view(np.float32)
+        max16 = blk[f16 + kp * 144:f16 + kp * 144 + 4 * (kp // 256)].view(np.float32)
         assert bool(np.isinf(max16).all()) == inf and bool(np.isinf(max16).any()) == inf
-        assert blk[f16 + kp * 132 + 4 * (kp // 256):][:4].view(np.int32)[0] == _stage_exp(books[s])
+        assert blk[f16 + kp * 144 + 4 * (kp // 256):][:4].view(np.int32)[0] == _stage_exp(books[s])
 
 
 @pytest.mark.parametrize("case", ["huge_stage", "huge_residual", "tiny_residual", "near_duplicates",
