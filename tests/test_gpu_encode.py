@@ -341,3 +341,21 @@ def test_prepared_wide_fp16_edges(case):
         books = (centre + 1e-3 * rng.standard_normal((4, 1024, 64))).astype(np.float32)
         x = (centre[0] + 1e-3 * rng.standard_normal((400, 64))).astype(np.float32)
     _check(x, books, True, "prepared")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_prepared_wide_random_shapes_and_scales(seed):
+    """fp16-scored path under random stage counts, codebook sizes (not multiples of 64), per-stage
+    codebook scales from 1e-3 to 1e3 (stage exponents across their range), residual scales, and
+    near-duplicate rows; codes, residuals and reconstructions against the oracle."""
+    rng = np.random.default_rng(700 + seed)
+    q = int(rng.integers(1, 6))
+    k = int(rng.integers(1, 1100))
+    scales = 10.0 ** rng.uniform(-3, 3, size=q)
+    books = (rng.standard_normal((q, k, 64)) * scales[:, None, None]).astype(np.float32)
+    if seed % 2 == 1 and k > 8:   # near-duplicate rows in every stage
+        j = rng.integers(0, k, size=k // 4)
+        books[:, j] = books[:, rng.integers(0, k, size=j.size)] * (
+            1.0 + 1e-6 * rng.standard_normal((q, j.size, 64))).astype(np.float32)
+    x = (rng.standard_normal((300, 64)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
+    _check(x, books, True, "prepared")
