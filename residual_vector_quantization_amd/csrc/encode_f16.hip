@@ -249,6 +249,23 @@ __device__ __forceinline__ float sqrt_up(float x)
     return __builtin_amdgcn_sqrtf(fmaxf(x, FLT_MIN)) * (1.0f + 9.5367431640625e-07f);
 }
 
+// The value held by lane l ^ 32, the other half of this lane's frame: one
+// v_permlane32_swap (a VALU op, no LDS round trip). Every lane must be
+// active.
+__device__ __forceinline__ unsigned other_half(unsigned x, int half)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return half ? r[0] : r[1];
+}
+__device__ __forceinline__ float other_half(float x, int half)
+{
+    return __uint_as_float(other_half(__float_as_uint(x), half));
+}
+__device__ __forceinline__ int other_half(int x, int half)
+{
+    return static_cast<int>(other_half(static_cast<unsigned>(x), half));
+}
+
 // This lane's half (32 dims) of codeword k's fp32 row.
 __device__ __forceinline__ void load_row(f32x4 (&row)[8], const float *book, int k, int half)
 {
@@ -261,7 +278,7 @@ __device__ __forceinline__ void load_row(f32x4 (&row)[8], const float *book, int
 // lane's half of its row in registers) to the frame held by lanes
 // (l, l^32), fused multiply-adds in four chains per lane; the same value on
 // both lanes. Every lane must call it.
-__device__ __forceinline__ float pair_distance_f32_row(const float (&n)[32], const f32x4 (&row)[8])
+__device__ __forceinline__ float pair_distance_f32_row(const float (&n)[32], const f32x4 (&row)[8], int half)
 {
     float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -272,7 +289,7 @@ __device__ __forceinline__ float pair_distance_f32_row(const float (&n)[32], con
             a[i] = __builtin_fmaf(d, d, a[i]);
         }
     const float s = (a[0] + a[1]) + (a[2] + a[3]);
-    return s + __shfl_xor(s, 32);
+    return s + other_half(s, half);
 }
 
 // Entry i (0..3) of a four-entry list, selected without indexing registers.
@@ -445,10 +462,11 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
                                              const float *book, int n_codes, float m16, int e, bool valid,
                                              int half, int col, int lane, float *frame_row, int32_t *code_out)
 {
-    float rn = 0.0f;
+    float r4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int j = 0; j < 32; ++j) rn = __builtin_fmaf(n[j], n[j], rn);
-    rn = rn + __shfl_xor(rn, 32);
+    for (int j = 0; j < 32; ++j) r4[j & 3] = __builtin_fmaf(n[j], n[j], r4[j & 3]);
+    float rn = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+    rn = rn + other_half(rn, half);
     // |n_j| < 2^15 keeps every fp16(n_j) finite; a stage out of the fp16
     // range has an infinite maximum
     const bool bad = !(rn < 1073741824.0f) || !(m16 <= FLT_MAX);
@@ -461,8 +479,8 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
                          kAbsConst) * (1.0f + 2.44140625e-04f);
     const float lane_min = fminf(ks[0].best, ks[1].best);
     const int lane_k = ks[0].best <= ks[1].best ? ks[0].best_k : ks[1].best_k;
-    const float other_min = __shfl_xor(lane_min, 32);
-    const int other_k = __shfl_xor(lane_k, 32);
+    const float other_min = other_half(lane_min, half);
+    const int other_k = other_half(lane_k, half);
     const float frame_min = fminf(lane_min, other_min);
     const float lim = frame_min + 2.0f * bound + fabsf(frame_min) * 2.4e-7f;
     // The smallest key's codeword (half 0's on equal keys) is the pick of
@@ -482,7 +500,7 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
         if (ks[s].third <= lim || (ks[s].second <= lim && ks[s].second_k == ks[s].best_k)) ovs |= 1u << s;
     // the shuffle must run on every lane: under a divergent mask the partner
     // lane could be inactive and the two halves of a frame could disagree
-    const unsigned ovs_o = static_cast<unsigned>(__shfl_xor(static_cast<int>(ovs), 32));
+    const unsigned ovs_o = other_half(ovs, half);
     const unsigned ovmask = half ? (ovs_o | (ovs << 2)) : (ovs | (ovs_o << 2));
     const bool overflow = bad || ovmask != 0u;
 
@@ -501,8 +519,8 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     }
     int list_o[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) list_o[j] = __shfl_xor(list[j], 32);
-    const int cnt_o = __shfl_xor(cnt, 32);
+    for (int j = 0; j < 4; ++j) list_o[j] = other_half(list[j], half);
+    const int cnt_o = other_half(cnt, half);
     const int ncand = cnt + cnt_o;
     // frame candidate j: half 0's list, then half 1's
     const int cnt0 = half ? cnt_o : cnt;
@@ -536,7 +554,7 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
         int k = rerank ? entry(pos == 0 ? 1 : 0) : pred;
         f32x4 cur[8];
         load_row(cur, book, k, half);
-        float f1 = pair_distance_f32_row(n, prow), f2 = INFINITY;
+        float f1 = pair_distance_f32_row(n, prow, half), f2 = INFINITY;
         int k1 = pred;
         for (int j = 0; __any(rerank && j < ncand - 1); ++j) {
             const bool use = rerank && j < ncand - 1;
@@ -544,7 +562,7 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
                 k = use ? entry(j + (j >= pos)) : pred;
                 load_row(cur, book, k, half);
             }
-            const float f = pair_distance_f32_row(n, cur);
+            const float f = pair_distance_f32_row(n, cur, half);
             if (use) {
                 f2 = f < f1 ? f1 : fminf(f2, f);
                 if (f < f1) {
