@@ -7,8 +7,9 @@ and split into bf16 halves, with their half-norms), ``rvq_encode_prepared``
 (codes + final residual; fp16 scores with exact re-rank for wide batches,
 split-bf16 for batches of up to 16384 frames) and ``rvq_decode`` (codes ->
 reconstruction) over the whole batch,
-inputs and outputs resident in HBM. W untimed steps, then K timed
-steps between ``torch.cuda.synchronize()`` calls. Per-launch kernel times
+inputs and outputs resident in HBM. W untimed steps (100 by default: the
+GPU's clocks settle after about 50 ms of load), then K timed steps (100)
+between ``torch.cuda.synchronize()`` calls. Per-launch kernel times
 come from HIP events recorded on the stream the kernels run on (torch's
 current stream, which is the stream handed to the C ABI).
 
@@ -64,8 +65,10 @@ KERNEL_SOURCES = {
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    # the GPU's clocks settle after roughly 50 ms of load: 3 warm-up + 20 timed
+    # steps measured the batched step 17% slower than 100 + 100 or 200 + 200
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="batched", choices=list(W.WORKLOADS))
     p.add_argument("--fp32-steps", type=int, default=5,
                    help="launches of the fp32-scored encode timed after the main steps")
