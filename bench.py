@@ -89,10 +89,20 @@ def parse():
     return p.parse_args()
 
 
-def source_hash(kind):
+def _code_only(text):
+    """Source text without comments and blank lines: edits to comments leave the hash alone."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines()]
+    return "\n".join(ln for ln in lines if ln.strip())
+
+
+def source_hash(kind, read=None):
+    """SHA-256 of the code (comments stripped) of the sources that define a kernel kind."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind]:
-        h.update(open(os.path.join(CSRC, name), "rb").read())
+        text = read(name) if read else open(os.path.join(CSRC, name)).read()
+        h.update(_code_only(text).encode())
     return h.hexdigest()
 
 

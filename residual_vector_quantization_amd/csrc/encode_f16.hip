@@ -34,9 +34,13 @@
 // The fp16 scores are about 20 times coarser than split-bf16 ones, so
 // candidate sets are wider: each lane keeps two sets of keys (even and odd
 // 64-codeword groups), best, second and third key and the first two
-// indices of each. A frame resolves from up to eight candidates (two per set
-// and lane) with the float64 re-rank; a third candidate inside one set sends
-// it to the full float64 rescan.
+// indices of each. The smallest key's codeword is fetched as the decision
+// starts (it is the pick of a frame with one candidate, and serves the
+// update); two to eight candidates (two per set and lane) are compared by
+// a float32 direct form, and only near ties by the float64 one; a third
+// candidate inside a set makes the wavefront sweep that set's K/4
+// codewords with the other sets' candidates, float32 first and float64 for
+// near ties.
 //
 // Work split: 4 wavefronts x 32 frames per workgroup and two workgroups per
 // CU (74.8 KB of LDS each), residual in VGPRs, prepared fp16 rows (64 dims
@@ -452,11 +456,12 @@ __device__ int resolve_sets(const float (&n)[32], float *row, const float *book,
 // The decision for one stage from this lane's two key sets (codeword slots
 // of one half of a frame; lanes l and l^32 hold the two halves): every
 // codeword within 2E (1) of the frame's smallest key is a candidate; two to
-// eight candidates are re-ranked in float64, a third candidate inside one
-// set (or ambiguous bookkeeping, or fp16 out of range) sends the frame to the
-// full float64 rescan. Then the pick is stored (code_out, when not null) and
-// subtracted from the negated residual n (and added to acc for kRecon).
-// Every lane must call it.
+// eight candidates are re-ranked (float32, float64 for near ties); a third
+// candidate inside a set (or ambiguous bookkeeping) sends the frame to the
+// sweep of its overflowed sets, fp16 out of range to the full float64
+// rescan. Then the pick is stored (code_out, when not null) and subtracted
+// from the negated residual n (and added to acc for kRecon). Every lane
+// must call it.
 template <bool kRecon>
 __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], const KeySet (&ks)[2],
                                              const float *book, int n_codes, float m16, int e, bool valid,
