@@ -317,11 +317,12 @@ def test_prepared_out_of_fp16_range():
         assert blk[f16 + kp * 144 + 4 * (kp // 256):][:4].view(np.int32)[0] == _stage_exp(books[s])
 
 
-@pytest.mark.parametrize("case", ["huge_stage", "huge_residual", "tiny_residual", "near_duplicates",
-                                  "clustered"])
+@pytest.mark.parametrize("case", ["huge_stage", "huge_residual", "some_huge_residuals", "tiny_residual",
+                                  "near_duplicates", "clustered"])
 def test_prepared_wide_fp16_edges(case):
     """Wide batches through the prepared path: a stage out of the fp16 range, residuals out of it
-    (both resolved by the float64 rescan), residuals in the fp16 subnormal range, near-duplicate
+    (both resolved by the float64 rescan; for some frames of each wavefront only, the others decided
+    as usual), residuals in the fp16 subnormal range, near-duplicate
     rows (re-rank within one key set) and rows clustered so tightly that frames hold many
     candidates."""
     rng = np.random.default_rng(620)
@@ -331,6 +332,8 @@ def test_prepared_wide_fp16_edges(case):
         books[1] *= 2.0 ** 22
     elif case == "huge_residual":
         x *= 1e5
+    elif case == "some_huge_residuals":   # every third frame out of fp16's range, the rest not
+        x[::3] *= 1e5
     elif case == "tiny_residual":
         books *= 1e-6
         x *= 1e-6
