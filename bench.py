@@ -5,7 +5,7 @@
 One step = ``rvq_prepare_codebooks`` (codebooks scaled and rounded to fp16,
 and split into bf16 halves, with their half-norms), ``rvq_encode_prepared``
 (codes + final residual; fp16 scores with exact re-rank for wide batches,
-split-bf16 for batches of up to 16384 frames) and ``rvq_decode`` (codes ->
+split-bf16 for batches of up to 8192 frames) and ``rvq_decode`` (codes ->
 reconstruction) over the whole batch,
 inputs and outputs resident in HBM. W untimed steps (100 by default: the
 GPU's clocks settle after about 50 ms of load), then K timed steps (100)
@@ -49,7 +49,7 @@ COPY_BYTES = 512 << 20             # size of the counter-calibration copy
 # reaches at best over codebook sizes from 0.25 to 16 MiB (--gather-sweep);
 # the decode's row gathers are bound by it, not by HBM.
 GATHER_CEILING_TBPS = 21.9
-SPLIT_MAX_FRAMES = 16384   # batches up to this size take the split-codebook encode
+SPLIT_MAX_FRAMES = 8192    # prepared encodes of up to this many frames take the split-codebook kernel
 
 CSRC = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc")
 # kernel kind -> sources whose text defines it (hashed to detect stale counters)

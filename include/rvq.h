@@ -173,7 +173,7 @@ RVQ_API rvq_status rvq_encode_scored(const float *x, int64_t n_frames, int32_t d
  *
  * rvq_encode_prepared reads `prepared` (which must have been prepared from
  * the same `codebooks` with at least `n_stages` stages and the same n_codes
- * and dim; the library cannot check this): up to 16384 frames with
+ * and dim; the library cannot check this): up to 8192 frames with
  * split-bf16 scores, more with one fp16 product per dimension. Either way
  * every codeword within the scores' proven error of the best is re-ranked
  * in float64, so results are identical to rvq_encode. Codebook entries

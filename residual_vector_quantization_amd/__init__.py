@@ -288,7 +288,7 @@ def _check_prepared(prepared: Optional[torch.Tensor], codebooks: torch.Tensor, q
 def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torch.Tensor,
                         n_stages: Optional[int] = None, recon: bool = False, residual: bool = True,
                         out=None):
-    """Encode from prepared codebooks (split-bf16 scores up to 16384 frames, fp16 above; exact either way):
+    """Encode from prepared codebooks (split-bf16 scores up to 8192 frames, fp16 above; exact either way):
     ``(codes, recon or None, residual or None)``."""
     _require(x, "x", torch.float32, 2)
     _require(codebooks, "codebooks", torch.float32, 3, x.device)

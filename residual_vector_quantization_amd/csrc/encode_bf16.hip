@@ -493,6 +493,11 @@ constexpr int kSplitGroup = 64;
 // up to this many frames the split kernel runs: two rounds of one-tile
 // workgroups on 256 CUs are still faster than the wide kernel's 256-frame tiles
 constexpr int64_t kSplitMaxFrames = 16384;
+// With prepared codebooks the fp16 kernel takes over as soon as the
+// split-codebook kernel needs a second round of one-tile workgroups on 256
+// CUs (measured, Q = 8: 8,192 frames 89 against 110 us, 12,288 frames 178
+// against 110 us).
+constexpr int64_t kPreparedSplitMaxFrames = 8192;
 // prepared codebooks: 32-codeword blocks, two per wavefront buffer
 constexpr int kRowSlots = kRowH * 2 / 16;                 // 16-byte LDS slots per row (16 data + 1 padding)
 constexpr int kBlockSlots = 32 * kRowH * 2 / 16;          // 16-byte LDS slots of a block (544)
@@ -925,7 +930,7 @@ hipError_t launch_encode_prepared(const float *x, int64_t n_frames, const float 
                                   int n_stages, int n_codes, int32_t *codes, int codes_ld,
                                   float *residual, float *recon, hipStream_t stream)
 {
-    if (n_frames > kSplitMaxFrames)
+    if (n_frames > kPreparedSplitMaxFrames)
         return launch_encode_f16(x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon,
                                  stream);
     return launch_variant<true>(x, n_frames, books, static_cast<const uint8_t *>(prepared), n_stages, n_codes,

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import rvq_workloads as W
-from gpu_util import SCORINGS, SPLIT_MAX_FRAMES, needs_gpu, check_encode, widen, rvq, to_dev, host, announce
+from gpu_util import SCORINGS, SPLIT_MAX_FRAMES, PREPARED_SPLIT_MAX_FRAMES, needs_gpu, check_encode, widen, rvq, to_dev, host, announce
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
@@ -50,10 +50,11 @@ def test_ragged_frame_counts(n, scoring):
     check_encode(x, books, scoring=scoring)
 
 
-@pytest.mark.parametrize("n", [SPLIT_MAX_FRAMES, SPLIT_MAX_FRAMES + 1, SPLIT_MAX_FRAMES + 31])
-@pytest.mark.parametrize("scoring", ["default", "prepared"])
+@pytest.mark.parametrize("n,scoring", [(m, sc) for sc, t in (("default", SPLIT_MAX_FRAMES),
+                                                              ("prepared", PREPARED_SPLIT_MAX_FRAMES))
+                                        for m in (t, t + 1, t + 31)] + [(SPLIT_MAX_FRAMES, "prepared")])
 def test_split_threshold_frame_counts(n, scoring):
-    """Either side of the split / wide switch, ragged tails included."""
+    """Either side of the split / wide switch of each path, ragged tails included."""
     rng = np.random.default_rng(150 + n)
     books = _books(rng, 4, 1024)
     x = rng.standard_normal((n, 64)).astype(np.float32)
