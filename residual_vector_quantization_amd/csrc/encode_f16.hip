@@ -58,7 +58,6 @@ using namespace enc;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -147,12 +146,14 @@ __device__ __forceinline__ void fold(KeySet &s, unsigned bb0, unsigned sb0, int 
     s.best_k = best_moved ? k_of_best : s.best_k;
 }
 
-// Scores [per step count] placed after each of a group's ten matrix-core
-// steps (norm block 0, norm block 1, then dims 0..63 for blocks 0 and 1).
+// How many of the previous group's 32 scores are scanned after each of a
+// group's ten matrix-core steps (half-norm of block 0 and of block 1, then
+// each 16-dim step of block 0 and block 1).
 constexpr int kScanAfter[10] = {4, 4, 3, 3, 3, 3, 3, 3, 3, 3};
 
-// Matrix-core steps of group kG of the chunk in LDS (rows sb) into dn: two 32-codeword blocks, each a chain of the half-norm
-// step and four 16-dim steps. When kScan, the key scan of the previous
+// Matrix-core steps of group kG of the chunk in LDS (rows sb) into dn: two
+// 32-codeword blocks, each a chain of the half-norm step and four 16-dim
+// steps. When kScan, the key scan of the previous
 // group dp (first codeword prev_base) into set `ks` is placed between them
 // in a fixed order, and the operands of the next step are read from LDS
 // before the current step's products are issued.
