@@ -120,7 +120,7 @@ def recorded_traffic(kind, workload):
 # ---------------------------------------------------------------- profiles
 
 PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp   # R = repository root
-rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o bench -- python3 $R/bench.py --workload {wl} --steps 20 --no-cpu-baseline
+rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o bench -- python3 $R/bench.py --workload {wl} --no-cpu-baseline
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
@@ -194,6 +194,19 @@ def summarize_profiles(w, src_dir):
         lines.append(f"| {kind} | {r['Calls']} | {a:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
                      f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     lines.append("")
+    # the bench times only its last `steps` launches (after the warm-up), so the
+    # same average over the trace's last launches is what its line reports
+    trace_rows = _csv(os.path.join(src_dir, "trace"), "kernel_trace.csv")
+    steps = 100
+    for kind in ("encode_f16", "decode", "prepare"):
+        durs = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                for r in trace_rows if _kernel_of(r["Kernel_Name"]) == kind]
+        durs.sort()
+        if len(durs) > steps:
+            tail = [d for _, d in durs[-steps:]]
+            lines.append(f"- {kind}: average over the last {steps} launches (the timed steps) "
+                         f"{sum(tail) / len(tail) / 1e3:.1f} us; over all {len(durs)} launches "
+                         f"{sum(d for _, d in durs) / len(durs) / 1e3:.1f} us")
     if "encode_f16" in avg:
         t = avg["encode_f16"]
         lines.append(f"- encode_f16 (prepared codebooks): {enc_flop:.4g} flop per launch (2QKD per frame, "
