@@ -363,3 +363,34 @@ def test_prepared_wide_random_shapes_and_scales(seed):
             1.0 + 1e-6 * rng.standard_normal((q, j.size, 64))).astype(np.float32)
     x = (rng.standard_normal((300, 64)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
     _check(x, books, True, "prepared")
+
+
+@pytest.mark.parametrize("case", ["mixed_dims", "subnormal_frames", "clamped_scale_stage", "zero_frames_and_rows",
+                                  "sparse_integer"])
+def test_prepared_wide_value_extremes(case):
+    """Wide batches through the fp16-scored path on value patterns the random cases do not reach:
+    per-dimension scales spread over eight decades (the bound's norm terms dominated by a few
+    dimensions), frames of float32 subnormals (flushed by the fp16 conversion, decided by the
+    bound's absolute terms), a stage whose scale exponent is clamped (entries near 1e-12, fp16
+    subnormal after scaling), all-zero frames against duplicated all-zero codewords (equal scores,
+    lowest index), and sparse integer data with exact ties at K not a multiple of 64."""
+    rng = np.random.default_rng(800)
+    k = 1000
+    books = _books(rng, 4, k)
+    x = rng.standard_normal((400, 64)).astype(np.float32)
+    if case == "mixed_dims":
+        dim_scale = (10.0 ** rng.uniform(-4, 4, size=64)).astype(np.float32)
+        books = (books * dim_scale).astype(np.float32)
+        x = (x * dim_scale).astype(np.float32)
+    elif case == "subnormal_frames":
+        x[::3] = (x[::3] * 1e-39).astype(np.float32)
+        assert np.all(np.abs(x[::3]) < np.finfo(np.float32).tiny)
+    elif case == "clamped_scale_stage":
+        books[2] = (books[2] * 1e-12).astype(np.float32)
+    elif case == "zero_frames_and_rows":
+        x[::4] = 0.0
+        books[:, [5, 77, 600, 601, 999]] = 0.0
+    else:
+        books = (rng.integers(-2, 3, size=(4, k, 64)) * (rng.random((4, k, 64)) < 0.1)).astype(np.float32)
+        x = (rng.integers(-3, 4, size=(400, 64)) * (rng.random((400, 64)) < 0.2)).astype(np.float32)
+    _check(x, books, True, "prepared")
