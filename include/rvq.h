@@ -73,12 +73,18 @@ extern "C" {
 #define RVQ_VERSION_MINOR 1
 #define RVQ_VERSION_PATCH 0
 
-/* Status codes: 0 on success, negative on failure (no output written). */
+/*
+ * Status codes: 0 on success, negative on failure (no output written). The
+ * convention -- 0 for success, small negative integers for each kind of
+ * failure, a static string per code -- is that of the ov_status enum in the
+ * "Public API" section of the "Architecture" page.
+ */
 typedef enum rvq_status {
     RVQ_OK = 0,
     RVQ_ERR_INVALID_ARG = -1,  /* null pointer, negative size, codes_ld < n_stages, misalignment */
     RVQ_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape (dim != 64, n_stages > 65536) */
-    RVQ_ERR_DEVICE = -3        /* the HIP runtime refused the launch or has no device */
+    RVQ_ERR_DEVICE = -3,       /* the HIP runtime refused the launch or has no device */
+    RVQ_ERR_OOM = -4           /* out of memory; reserved: no call allocates device memory today */
 } rvq_status;
 
 /* How encode scores codewords before the exact float64 decision. */
@@ -88,10 +94,17 @@ typedef enum rvq_scoring {
     RVQ_SCORING_FP32 = 2      /* fp32 matrix cores */
 } rvq_scoring;
 
-/* Static string "MAJOR.MINOR.PATCH (gfx950)". Never NULL. */
+/*
+ * Static string "MAJOR.MINOR.PATCH (gfx950)". Never NULL. The counterpart
+ * of ov_version in the "Public API" section of the "Architecture" page.
+ */
 RVQ_API const char *rvq_version(void);
 
-/* Static, human-readable name of a status code. Never NULL. */
+/*
+ * Static, human-readable name of a status code ("unknown status" for any
+ * other value). Never NULL. Like the status strings of the "Public API"
+ * section of the "Architecture" page.
+ */
 RVQ_API const char *rvq_status_string(rvq_status status);
 
 /*

@@ -48,6 +48,7 @@ RVQ_OK = 0
 RVQ_ERR_INVALID_ARG = -1
 RVQ_ERR_UNSUPPORTED = -2
 RVQ_ERR_DEVICE = -3
+RVQ_ERR_OOM = -4
 
 EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip",
             "rvq_encode_scored", "rvq_prepared_bytes", "rvq_prepare_codebooks", "rvq_encode_prepared",
@@ -153,6 +154,20 @@ def _stages(codebooks: torch.Tensor, n_stages: Optional[int]) -> int:
     return q
 
 
+def _check_dims(x: torch.Tensor, codebooks: torch.Tensor) -> None:
+    """The C ABI takes the latent width from ``x`` alone, so the codebooks' rows must have it too."""
+    if codebooks.shape[2] != x.shape[1]:
+        raise ValueError(f"codebooks {tuple(codebooks.shape)} do not match x {tuple(x.shape)} in the last dim")
+
+
+def _check_codes(codes: torch.Tensor, n: int, q: int) -> None:
+    """An output codes tensor needs one row per frame and at least ``q`` columns."""
+    if codes.shape[0] != n:
+        raise ValueError(f"codes must have one row per frame ({n}), got {tuple(codes.shape)}")
+    if codes.shape[1] < q:
+        raise ValueError(f"codes needs at least {q} columns, got {tuple(codes.shape)}")
+
+
 def rvq_encode(x: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[int] = None,
                residual: bool = True, codes: Optional[torch.Tensor] = None,
                residual_out: Optional[torch.Tensor] = None):
@@ -164,13 +179,13 @@ def rvq_encode(x: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[int]
     """
     _require(x, "x", torch.float32, 2)
     _require(codebooks, "codebooks", torch.float32, 3, x.device)
+    _check_dims(x, codebooks)
     n, d = x.shape
     q = _stages(codebooks, n_stages)
     if codes is None:
         codes = torch.empty((n, q), dtype=torch.int32, device=x.device)
     _require(codes, "codes", torch.int32, 2, x.device)
-    if codes.shape[0] != n:
-        raise ValueError("codes must have one row per frame")
+    _check_codes(codes, n, q)
     res = None
     if residual:
         res = residual_out if residual_out is not None else torch.empty_like(x)
@@ -212,6 +227,7 @@ def rvq_roundtrip(x: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[i
     """
     _require(x, "x", torch.float32, 2)
     _require(codebooks, "codebooks", torch.float32, 3, x.device)
+    _check_dims(x, codebooks)
     n, d = x.shape
     q = _stages(codebooks, n_stages)
     codes = torch.empty((n, q), dtype=torch.int32, device=x.device)
@@ -235,6 +251,7 @@ def rvq_encode_scored(x: torch.Tensor, codebooks: torch.Tensor, scoring: str = "
     _require(codebooks, "codebooks", torch.float32, 3, x.device)
     if scoring not in SCORING:
         raise ValueError(f"scoring must be one of {sorted(SCORING)}")
+    _check_dims(x, codebooks)
     n, d = x.shape
     q = _stages(codebooks, n_stages)
     if out is None:
@@ -242,6 +259,7 @@ def rvq_encode_scored(x: torch.Tensor, codebooks: torch.Tensor, scoring: str = "
                torch.empty_like(x) if recon else None, torch.empty_like(x) if residual else None)
     codes, rec, res = out
     _require(codes, "codes", torch.int32, 2, x.device)
+    _check_codes(codes, n, q)
     for t, name in ((rec, "recon"), (res, "residual")):
         if t is not None:
             _require(t, name, torch.float32, 2, x.device)
@@ -293,6 +311,7 @@ def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torc
     _require(x, "x", torch.float32, 2)
     _require(codebooks, "codebooks", torch.float32, 3, x.device)
     _require(prepared, "prepared", torch.uint8, 1, x.device)
+    _check_dims(x, codebooks)
     n, d = x.shape
     q = _stages(codebooks, n_stages)
     if prepared.numel() < rvq_prepared_bytes(q, codebooks.shape[1], d):
@@ -302,6 +321,7 @@ def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torc
                torch.empty_like(x) if recon else None, torch.empty_like(x) if residual else None)
     codes, rec, res = out
     _require(codes, "codes", torch.int32, 2, x.device)
+    _check_codes(codes, n, q)
     for t, name in ((rec, "recon"), (res, "residual")):
         if t is not None:
             _require(t, name, torch.float32, 2, x.device)
@@ -346,6 +366,12 @@ def rvq_project_roundtrip(h: torch.Tensor, w_in: torch.Tensor, b_in: Optional[to
                torch.empty((n, d), dtype=torch.float32, device=dev),
                torch.empty((n, hid), dtype=torch.float32, device=dev))
     codes, latent, latent_recon, h_recon = out
+    _require(codes, "codes", torch.int32, 2, dev)
+    _check_codes(codes, n, q)
+    for t, name, width in ((latent, "latent", d), (latent_recon, "latent_recon", d), (h_recon, "h_recon", hid)):
+        _require(t, name, torch.float32, 2, dev)
+        if tuple(t.shape) != (n, width):
+            raise ValueError(f"{name} must be [{n}, {width}], got {tuple(t.shape)}")
     st = load().rvq_project_roundtrip(_ptr(h), n, hid, _ptr(w_in), _ptr(b_in), _ptr(codebooks), _ptr(prepared),
                                       q, codebooks.shape[1], d, _ptr(w_out), _ptr(b_out), _ptr(codes),
                                       codes.shape[1], _ptr(latent), _ptr(latent_recon), _ptr(h_recon),

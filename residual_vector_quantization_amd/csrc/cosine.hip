@@ -304,7 +304,10 @@ void cosine_argmin_kernel(const float *__restrict__ lat, int64_t n_frames, const
         }
         if (lane == srcl) bk = bi;
     }
-    if (valid) codes[frame * codes_ld] = bk;
+    // a non-finite projection finds no smaller distance and keeps the
+    // sentinel: its (unspecified) code is clamped so that the next stage's
+    // update reads a real table row
+    if (valid) codes[frame * codes_ld] = min(max(bk, 0), n_codes - 1);
 }
 
 // ---- all stages in one kernel --------------------------------------------
@@ -553,7 +556,9 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
                 }
                 pick = bkk;
             }
-            pick = __builtin_amdgcn_readfirstlane(pick);
+            // a non-finite frame's pick is unspecified; clamped, so that the
+            // table row read below exists
+            pick = __builtin_amdgcn_readfirstlane(min(max(pick, 0), n_codes - 1));
             if (fr < n_frames && lane == 0) codes[fr * codes_ld + q] = pick;
             const float *prow = table + (static_cast<int64_t>(q) * n_codes + pick) * hidden;
             if (full) {

@@ -39,18 +39,12 @@
 //   codewords of that frame with the same float64 sum. The pick is
 //   therefore the argmin of that float64 distance (lowest index on ties),
 //   independent of the fp32 rounding order.
-#include <float.h>
-#include <stdint.h>
-
-#include <hip/hip_runtime.h>
-
-#include "rvq_internal.h"
+#include "encode_common.h"
 
 namespace rvq {
 namespace {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using namespace enc;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
@@ -62,44 +56,14 @@ static_assert(kThreads == kEncodeThreads, "thread count");
 static_assert(kWaves * kFramesPerWave == kEncodeFramesPerBlock, "frames per block");
 static_assert(kWaves * 32 == kChunk, "staging maps each wavefront to 32 codeword rows");
 
-// gamma_n = n*u / (1 - n*u), u = 2^-24. A score is a D+1 term sum (norm
-// plus D products, each product rounded) started from a norm that is itself
-// a D-term fp32 sum: n = 2D + 4 roundings cover both.
-constexpr float kUnit = 5.9604644775390625e-08f;
-constexpr float kGamma = (2 * kDim + 4) * kUnit / (1.0f - (2 * kDim + 4) * kUnit);
+// A score is a D+1 term sum (norm plus D products, each product rounded)
+// started from a norm that is itself a D-term fp32 sum: 2D + 4 roundings
+// cover both.
+constexpr float kGamma = gamma_n(2 * kDim + 4);
 // Margin for matrix-core rounding that is not round-to-nearest: an error
 // of up to 2u per operation (truncation) is still covered.
 constexpr float kSafety = 2.0f;
-// Replacing the 6 low mantissa bits moves a value by less than 2^-17 of it.
-constexpr float kKeyError = 7.62939453125e-06f;
 constexpr float kBoundScale = kSafety * kGamma + kKeyError;
-// Absolute slack for results that land in the fp32 subnormal range.
-constexpr float kAbsSlack = 1e-35f;
-constexpr unsigned kKeyMask = 0xFFFFFFC0u;
-// Stands in for +inf in keys: rows past n_codes score this and never win.
-constexpr float kNoScore = FLT_MAX;
-
-__device__ __forceinline__ float make_key(float s, int lk)
-{
-    return __uint_as_float((__float_as_uint(s) & kKeyMask) | static_cast<unsigned>(lk));
-}
-
-// Float64 sum_j (r_j - c_j)^2 over 32 dims with n = -r, continuing from
-// `acc`, one rounding per operation (no contraction into fma). Since
-// fl(n + c) = -fl(r - c) exactly, the squares match the direct form.
-__device__ inline double sq_dist_part(double acc, const float (&n)[32], const float *c)
-{
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(c + 4 * t);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const double d = __dadd_rn(static_cast<double>(n[4 * t + e]), static_cast<double>(v[e]));
-            acc = __dadd_rn(acc, __dmul_rn(d, d));
-        }
-    }
-    return acc;
-}
 
 // Key scan of accumulators v0, v0+1 of both blocks of a pair. The
 // pair-local codeword index of accumulator v of block b is
@@ -318,6 +282,10 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
                 for (int v = 0; v < 16; ++v) dB[b][v] = kNoScore;
 
             // ---- stage q is scored for this wavefront's 32 frames: decide ----
+            // A key decodes to a real codeword whenever the frame's scores are
+            // finite; a non-finite frame (its code is then unspecified) can
+            // decode a padding slot, so the index is clamped before any row load.
+            best_k = min(max(best_k, 0), n_codes - 1);
             const float best_o = __shfl_xor(best, 32);
             const float second_o = __shfl_xor(second, 32);
             const int best_k_o = __shfl_xor(best_k, 32);
@@ -369,62 +337,9 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
             while (pending) {
                 const int f = __ffsll(static_cast<unsigned long long>(pending)) - 1;
                 pending &= pending - 1;
-                // frame f's negated residual, broadcast through this wavefront's LDS row
-                if (col == f) {
-#pragma unroll
-                    for (int t = 0; t < 8; ++t)
-                        *reinterpret_cast<f32x4 *>(&s_frame[wave][32 * half + 4 * t]) =
-                            f32x4{n[4 * t], n[4 * t + 1], n[4 * t + 2], n[4 * t + 3]};
-                }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-                const float *rr = s_frame[wave];
-                double bd = INFINITY;
-                int bk = 0x7fffffff;
-                for (int k0 = lane; k0 < n_codes; k0 += 128) {
-                    const int k1 = k0 + 64;
-                    const bool has1 = k1 < n_codes;
-                    const float *c0 = books + (static_cast<int64_t>(q) * n_codes + k0) * kDim;
-                    const float *c1 = books + (static_cast<int64_t>(q) * n_codes + (has1 ? k1 : k0)) * kDim;
-                    double s0 = 0.0, s1 = 0.0;
-#pragma unroll 4
-                    for (int t = 0; t < 16; ++t) {
-                        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(c0 + 4 * t);
-                        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(c1 + 4 * t);
-                        const f32x4 rv = *reinterpret_cast<const f32x4 *>(rr + 4 * t);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const double rj = static_cast<double>(rv[e]);
-                            const double d0 = __dadd_rn(rj, static_cast<double>(v0[e]));
-                            const double d1 = __dadd_rn(rj, static_cast<double>(v1[e]));
-                            s0 = __dadd_rn(s0, __dmul_rn(d0, d0));
-                            s1 = __dadd_rn(s1, __dmul_rn(d1, d1));
-                        }
-                    }
-                    // k0 < k1 and both ascend, so strict "<" keeps the lowest index on ties
-                    if (s0 < bd) {
-                        bd = s0;
-                        bk = k0;
-                    }
-                    if (has1 && s1 < bd) {
-                        bd = s1;
-                        bk = k1;
-                    }
-                }
-#pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) {
-                    const double od = __shfl_xor(bd, off);
-                    const int ok = __shfl_xor(bk, off);
-                    if (od < bd || (od == bd && ok < bk)) {
-                        bd = od;
-                        bk = ok;
-                    }
-                }
-                if (col == f) pick = bk;
-                // all reads of s_frame[wave] are done before the next frame overwrites it
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                __builtin_amdgcn_wave_barrier();
+                const int w = rescan_frame(n, s_frame[wave], books + static_cast<int64_t>(q) * n_codes * kDim,
+                                           n_codes, f, lane);
+                if (col == f) pick = w;
             }
 
             pick = min(max(pick, 0), n_codes - 1);

@@ -242,6 +242,11 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], f
                                              bool valid, int half, int col, int lane, float *frame_row,
                                              int32_t *code_out)
 {
+    // Keys decode to real codewords whenever the frame's scores are finite;
+    // a non-finite frame (its code is then unspecified) can decode padding
+    // slots, so the indices are clamped before any row load.
+    best_k = min(max(best_k, 0), n_codes - 1);
+    second_k = min(max(second_k, 0), n_codes - 1);
     const float best_o = __shfl_xor(best, 32);
     const float second_o = __shfl_xor(second, 32);
     const float third_o = __shfl_xor(third, 32);

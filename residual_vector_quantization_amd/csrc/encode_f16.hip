@@ -484,8 +484,15 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     const float t_up = ldexpf(m_up, -e);
     const float bound = (kRel * (t_up + r_up * c_up) + kAbsN * r_up + kAbsC * c_up + ldexpf(kAbsNorm, -e) +
                          kAbsConst) * (1.0f + 2.44140625e-04f);
+    // Keys decode to real codewords whenever the frame's scores are finite;
+    // a non-finite frame (decided by the rescan, its code then unspecified)
+    // can decode padding slots past n_codes, so every index is clamped here,
+    // before any row load of the re-rank, the sweep or the update.
+    int kk[4] = {ks[0].best_k, ks[0].second_k, ks[1].best_k, ks[1].second_k};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kk[i] = min(max(kk[i], 0), n_codes - 1);
     const float lane_min = fminf(ks[0].best, ks[1].best);
-    const int lane_k = ks[0].best <= ks[1].best ? ks[0].best_k : ks[1].best_k;
+    const int lane_k = ks[0].best <= ks[1].best ? kk[0] : kk[2];
     const float other_min = other_half(lane_min, half);
     const int other_k = other_half(lane_k, half);
     const float frame_min = fminf(lane_min, other_min);
@@ -496,7 +503,7 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     // decision waits for at most one more round of row loads.
     const int pred = (lane_min < other_min || (lane_min == other_min && half == 0)) ? lane_k : other_k;
     f32x4 prow[8];
-    load_row(prow, book, min(max(pred, 0), n_codes - 1), half);
+    load_row(prow, book, pred, half);
     int have = pred;   // the codeword whose row prow holds
 
     // key sets holding a third candidate (or ambiguous bookkeeping): bit s
@@ -504,7 +511,7 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     unsigned ovs = 0u;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        if (ks[s].third <= lim || (ks[s].second <= lim && ks[s].second_k == ks[s].best_k)) ovs |= 1u << s;
+        if (ks[s].third <= lim || (ks[s].second <= lim && kk[2 * s + 1] == kk[2 * s])) ovs |= 1u << s;
     // the shuffle must run on every lane: under a divergent mask the partner
     // lane could be inactive and the two halves of a frame could disagree
     const unsigned ovs_o = other_half(ovs, half);
@@ -513,7 +520,7 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
 
     // this lane's candidates, compacted: set 0 best, second, set 1 best, second
     const float sv[4] = {ks[0].best, ks[0].second, ks[1].best, ks[1].second};
-    const int sk[4] = {ks[0].best_k, ks[0].second_k, ks[1].best_k, ks[1].second_k};
+    const int sk[4] = {kk[0], kk[1], kk[2], kk[3]};
     int list[4] = {0, 0, 0, 0};
     int cnt = 0;
 #pragma unroll

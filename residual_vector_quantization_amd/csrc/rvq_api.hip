@@ -70,6 +70,7 @@ RVQ_API const char *rvq_status_string(rvq_status status)
     case RVQ_ERR_INVALID_ARG: return "invalid argument";
     case RVQ_ERR_UNSUPPORTED: return "unsupported shape";
     case RVQ_ERR_DEVICE: return "device error";
+    case RVQ_ERR_OOM: return "out of memory";
     }
     return "unknown status";
 }

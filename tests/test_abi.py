@@ -67,6 +67,8 @@ def test_status_strings(libpath):
     import residual_vector_quantization_amd as rvq
     assert rvq.rvq_status_string(0) == "ok"
     assert rvq.rvq_status_string(-2) == "unsupported shape"
+    assert rvq.rvq_status_string(-4) == "out of memory"
+    assert rvq.rvq_status_string(-99) == "unknown status"
     assert "gfx950" in rvq.rvq_version()
 
 

@@ -394,3 +394,64 @@ def test_prepared_wide_value_extremes(case):
         books = (rng.integers(-2, 3, size=(4, k, 64)) * (rng.random((4, k, 64)) < 0.1)).astype(np.float32)
         x = (rng.integers(-3, 4, size=(400, 64)) * (rng.random((400, 64)) < 0.2)).astype(np.float32)
     _check(x, books, True, "prepared")
+
+
+@pytest.mark.parametrize("wide", [False, True])
+@pytest.mark.parametrize("k", [1, 65, 100, 1000, 1024])
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_out_of_range_and_nonfinite_frames(k, scoring, wide):
+    """Every third frame holds entries beyond fp16's 65504 (the fp16-scored path decides those by the
+    float64 rescan at every stage, the last included) and shares its wavefronts with ordinary frames
+    that need a re-rank (near-duplicate rows); one frame holds a NaN and one an infinity. Codes
+    decoded from such frames' keys may name padding slots past K; they must never be used as row
+    indices. Finite frames equal the oracle bit for bit; every code lies in [0, K)."""
+    rng = np.random.default_rng(900 + k)
+    books = _books(rng, 4, k)
+    if k > 1:
+        half = k // 2
+        books[:, half:2 * half] = books[:, :half] * (
+            1.0 + 1e-5 * rng.standard_normal((4, half, 64))).astype(np.float32)
+    x = rng.standard_normal((400, 64)).astype(np.float32)
+    x[::3] *= 1e5
+    x[5, 10] = np.nan
+    x[7, 3] = np.inf
+    nonfinite = np.nonzero(~np.isfinite(x).all(axis=1))[0]
+    xw, idx = widen(x) if wide else (x, np.arange(x.shape[0]))
+    sel = np.setdiff1d(idx, nonfinite)
+    check_encode(xw, books, idx=sel, scoring=scoring)
+    m = rvq()
+    xg, bg = to_dev(xw), to_dev(books)
+    if scoring == "default":
+        codes, _ = m.rvq_encode(xg, bg)
+    elif scoring == "prepared":
+        codes, _, _ = m.rvq_encode_prepared(xg, bg, m.rvq_prepare_codebooks(bg))
+    else:
+        codes, _, _ = m.rvq_encode_scored(xg, bg, scoring)
+    c = host(codes)
+    assert c.min() >= 0 and c.max() < k
+
+
+def test_shape_mismatches_rejected():
+    """The C ABI takes the latent width from x alone, and the code rows from n_frames: the binding
+    rejects codebooks of another width and output codes of the wrong shape before any launch."""
+    import torch
+    m = rvq()
+    dev = "cuda:0"
+    x = torch.zeros((10, 64), device=dev)
+    narrow = torch.zeros((2, 64, 8), device=dev)
+    books = torch.zeros((2, 64, 64), device=dev)
+    prep = m.rvq_prepare_codebooks(books)
+    for call in (lambda: m.rvq_encode(x, narrow), lambda: m.rvq_roundtrip(x, narrow),
+                 lambda: m.rvq_encode_scored(x, narrow, "fp32"),
+                 lambda: m.rvq_encode_prepared(x, narrow, prep)):
+        with pytest.raises(ValueError):
+            call()
+    short = torch.zeros((9, 2), dtype=torch.int32, device=dev)
+    thin = torch.zeros((10, 1), dtype=torch.int32, device=dev)
+    for codes in (short, thin):
+        with pytest.raises(ValueError):
+            m.rvq_encode(x, books, codes=codes)
+        with pytest.raises(ValueError):
+            m.rvq_encode_scored(x, books, "fp32", out=(codes, None, None))
+        with pytest.raises(ValueError):
+            m.rvq_encode_prepared(x, books, prep, out=(codes, None, None))
