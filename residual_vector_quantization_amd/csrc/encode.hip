@@ -302,13 +302,15 @@ void encode_kernel(const float *__restrict__ x, int64_t n_frames,
             const bool overflow = (second <= lim) || (second_o <= lim);
             const bool cand_me = best <= lim;
             const bool cand_o = best_o <= lim;
-            int pick = cand_me ? best_k : best_k_o;
+            const int k_lo = half ? best_k_o : best_k;   // half 0's best
+            const int k_hi = half ? best_k : best_k_o;   // half 1's best
+            // the same choice on both lanes of the frame, also when no key is a
+            // candidate (non-finite scores)
+            int pick = (half ? cand_o : cand_me) ? k_lo : k_hi;
 
             // Two candidates, one per half: float64 re-rank.
             const bool rerank = valid && !overflow && cand_me && cand_o;
             if (__any(rerank)) {
-                const int k_lo = half ? best_k_o : best_k;   // half 0's best
-                const int k_hi = half ? best_k : best_k_o;   // half 1's best
                 const float *ca = books + (static_cast<int64_t>(q) * n_codes + k_lo) * kDim + 32 * half;
                 const float *cb = books + (static_cast<int64_t>(q) * n_codes + k_hi) * kDim + 32 * half;
                 double sa = 0.0, sb2 = 0.0;

@@ -501,7 +501,10 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
     // every frame with one candidate, and one candidate of every other frame:
     // its row is fetched now, for the re-rank and the update, so that the
     // decision waits for at most one more round of row loads.
-    const int pred = (lane_min < other_min || (lane_min == other_min && half == 0)) ? lane_k : other_k;
+    // half 0's codeword unless half 1's key is smaller: the same choice on
+    // both lanes of the frame, also for non-finite keys
+    const int pred = (half ? lane_min < other_min : other_min < lane_min) ? (half ? lane_k : other_k)
+                                                                           : (half ? other_k : lane_k);
     f32x4 prow[8];
     load_row(prow, book, pred, half);
     int have = pred;   // the codeword whose row prow holds
