@@ -204,6 +204,30 @@ RVQ_API rvq_status rvq_encode_prepared(const float *x, int64_t n_frames, int32_t
                                        float *recon, float *residual, void *stream);
 
 /*
+ * rvq_encode_noalloc -- rvq_encode_prepared without a caller buffer, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, results and errors as rvq_encode_prepared (recon and residual
+ * may be NULL), with no `prepared` argument: every call prepares the
+ * codebooks on `stream` into a fixed array of RVQ_NOALLOC_SCRATCH_BYTES
+ * bytes that the library holds on each GPU it runs on (from first use until
+ * the process ends), then encodes from it. The call allocates and frees
+ * nothing. Shapes whose prepared layout exceeds the array
+ * (rvq_prepared_bytes(n_stages, n_codes, dim) > RVQ_NOALLOC_SCRATCH_BYTES,
+ * e.g. 40 stages of 1024 codewords or 10 of 4096 fit, 64 of 4096 do not)
+ * return RVQ_ERR_UNSUPPORTED before anything is enqueued. The array is
+ * shared by all calls on one GPU and keeps the last call's contents: calls
+ * that overlap on one GPU (other streams or threads) race and must be
+ * serialised by the caller. The stream's device is the GPU used.
+ */
+#define RVQ_NOALLOC_SCRATCH_BYTES (16LL * 1024 * 1024)
+RVQ_API rvq_status rvq_encode_noalloc(const float *x, int64_t n_frames, int32_t dim,
+                                      const float *codebooks, int32_t n_stages, int32_t n_codes,
+                                      int32_t *codes, int32_t codes_ld,
+                                      float *recon, float *residual, void *stream);
+
+/*
  * rvq_project_roundtrip -- linear in, encode, decode, linear out.
  *
  * The "Audio tokenizer pipeline" section of the "Architecture" page puts a

@@ -20,6 +20,9 @@ Functions (same names as the C entry points):
   ``rvq_prepare_codebooks(codebooks)`` -> uint8 device tensor;
   ``rvq_encode_prepared(x, codebooks, prepared, n_stages=None, recon=False, residual=True)``
   -> ``(codes, recon or None, residual or None)``
+* ``rvq_encode_noalloc(x, codebooks, n_stages=None, recon=False, residual=True)``
+  -> ``(codes, recon or None, residual or None)``: the prepared encode with the library's own fixed
+  per-GPU buffer, allocating nothing in the C call
 * ``rvq_project_roundtrip(h, w_in, b_in, codebooks, w_out, b_out, n_stages=None, prepared=None)``
   -> ``(codes, latent, latent_recon, h_recon)``
 * ``rvq_projected_prepare(codebooks, w_out, b_out=None)`` -> table;
@@ -53,7 +56,10 @@ RVQ_ERR_OOM = -4
 EXPORTED = ("rvq_version", "rvq_status_string", "rvq_encode", "rvq_decode", "rvq_roundtrip",
             "rvq_encode_scored", "rvq_prepared_bytes", "rvq_prepare_codebooks", "rvq_encode_prepared",
             "rvq_project_roundtrip", "rvq_projected_prepare", "rvq_projected_encode", "rvq_projected_decode",
-            "rvq_cosine_prepare", "rvq_cosine_encode")
+            "rvq_cosine_prepare", "rvq_cosine_encode", "rvq_encode_noalloc")
+
+# Bytes of the library's per-GPU array behind rvq_encode_noalloc (RVQ_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 SCORING = {"default": 0, "bf16x3": 1, "fp32": 2}
 
@@ -105,6 +111,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.rvq_projected_decode.argtypes = [vp, i32, i64, vp, i32, i32, i32, vp, vp]
     lib.rvq_cosine_prepare.restype = ctypes.c_int
     lib.rvq_cosine_prepare.argtypes = [vp, i32, i32, i32, vp, vp]
+    lib.rvq_encode_noalloc.restype = ctypes.c_int
+    lib.rvq_encode_noalloc.argtypes = [vp, i64, i32, vp, i32, i32, vp, i32, vp, vp, vp]
     lib.rvq_cosine_encode.restype = ctypes.c_int
     lib.rvq_cosine_encode.argtypes = [vp, i64, i32, vp, vp, vp, vp, i32, i32, i32, vp, i32, vp, vp, vp]
     _lib = lib
@@ -330,6 +338,34 @@ def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torc
     st = load().rvq_encode_prepared(_ptr(x), n, d, _ptr(codebooks), _ptr(prepared), q, codebooks.shape[1],
                                     _ptr(codes), codes.shape[1], _ptr(rec), _ptr(res), _stream(x))
     _check("rvq_encode_prepared", st)
+    return codes, rec, res
+
+
+def rvq_encode_noalloc(x: torch.Tensor, codebooks: torch.Tensor, n_stages: Optional[int] = None,
+                       recon: bool = False, residual: bool = True, out=None):
+    """``rvq_encode_prepared`` with the prepared layout in the library's fixed per-GPU array
+    (``NOALLOC_SCRATCH_BYTES``) instead of a caller buffer; the C call allocates nothing. Pass ``out``
+    = ``(codes, recon or None, residual or None)`` preallocated to keep the whole call allocation-free.
+    Calls that overlap on one GPU race on the array. Returns ``(codes, recon or None, residual or None)``."""
+    _require(x, "x", torch.float32, 2)
+    _require(codebooks, "codebooks", torch.float32, 3, x.device)
+    _check_dims(x, codebooks)
+    n, d = x.shape
+    q = _stages(codebooks, n_stages)
+    if out is None:
+        out = (torch.empty((n, q), dtype=torch.int32, device=x.device),
+               torch.empty_like(x) if recon else None, torch.empty_like(x) if residual else None)
+    codes, rec, res = out
+    _require(codes, "codes", torch.int32, 2, x.device)
+    _check_codes(codes, n, q)
+    for t, name in ((rec, "recon"), (res, "residual")):
+        if t is not None:
+            _require(t, name, torch.float32, 2, x.device)
+            if t.shape != x.shape:
+                raise ValueError(f"{name} must match x")
+    st = load().rvq_encode_noalloc(_ptr(x), n, d, _ptr(codebooks), q, codebooks.shape[1], _ptr(codes),
+                                   codes.shape[1], _ptr(rec), _ptr(res), _stream(x))
+    _check("rvq_encode_noalloc", st)
     return codes, rec, res
 
 

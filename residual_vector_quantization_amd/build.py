@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "librvq.so")
 SOURCES = ["rvq_api.hip", "encode.hip", "encode_bf16.hip", "encode_f16.hip", "decode.hip", "linear.hip", "projected.hip",
-           "cosine.hip"]
+           "cosine.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -62,6 +62,13 @@ int main(void)
                   RVQ_ERR_INVALID_ARG);
     bad += expect("encode prepared empty", rvq_encode_prepared(NULL, 0, 64, NULL, NULL, 8, 1024, NULL, 8, NULL, NULL, NULL),
                   RVQ_OK);
+    bad += expect("noalloc beyond its array", rvq_encode_noalloc(fx, 10, 64, fx, 64, 4096, ic, 64, NULL, NULL, NULL),
+                  RVQ_ERR_UNSUPPORTED);
+    bad += expect("noalloc null x", rvq_encode_noalloc(NULL, 10, 64, fx, 8, 1024, ic, 8, NULL, NULL, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("noalloc ld<q", rvq_encode_noalloc(fx, 10, 64, fx, 8, 1024, ic, 7, NULL, NULL, NULL),
+                  RVQ_ERR_INVALID_ARG);
+    bad += expect("noalloc empty", rvq_encode_noalloc(NULL, 0, 64, NULL, 8, 1024, NULL, 8, NULL, NULL, NULL), RVQ_OK);
     bad += expect("projected prepare hidden 96", rvq_projected_prepare(fx, 8, 1024, 64, fx, NULL, 96, fx, NULL),
                   RVQ_ERR_UNSUPPORTED);
     bad += expect("projected prepare null table", rvq_projected_prepare(fx, 8, 1024, 64, fx, NULL, 1024, NULL, NULL),

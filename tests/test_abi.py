@@ -26,7 +26,8 @@ def declared():
 
 def test_header_declares_the_entry_points():
     assert declared() == sorted(["rvq_cosine_encode", "rvq_cosine_prepare",
-                                 "rvq_decode", "rvq_encode", "rvq_encode_prepared", "rvq_encode_scored",
+                                 "rvq_decode", "rvq_encode", "rvq_encode_noalloc", "rvq_encode_prepared",
+                                 "rvq_encode_scored",
                                  "rvq_prepare_codebooks", "rvq_prepared_bytes", "rvq_project_roundtrip",
                                  "rvq_projected_decode", "rvq_projected_encode", "rvq_projected_prepare",
                                  "rvq_roundtrip", "rvq_status_string", "rvq_version"])
