@@ -18,13 +18,13 @@
 // a fifth step adds the half-norm: its two fp16 parts times 2^-e. With
 // u = 2^-11 (fp16 rounding), the stage maxima T = 2^-e max 0.5*||c'||^2
 // and C = max ||c'||, every key is within
-//     E = (2u + u^2 + 2 gamma_{D+8} + 2^-17 + u^2 + gamma_64) (T + ||n|| C)
+//     E = (2u + u^2 + 2 gamma_{D+8} + 2^-15 + u^2 + gamma_64) (T + ||n|| C)
 //         + 2^-21 ||n|| + 2^-22 C + 2^-(e+25) + 2^-43                 (1)
 // of the exact scaled score: the products lose at most (2u + u^2)|n_j c'_j|
 // plus 2^-24 |n_j| + 2^-25 |c'_j| in the fp16 subnormal range (D = 64
 // dims, so the 1-norms are at most 8 times the 2-norms); the half-norm's
 // fp32 sum and its two fp16 parts lose gamma_64 + u^2 of it plus 2^-25;
-// the fp32 accumulation 2 gamma_{D+8} and the packed key 2^-17 of the sum.
+// the fp32 accumulation 2 gamma_{D+8} and the packed key 2^-15 of the sum.
 // Every codeword whose key is within 2E of the frame's smallest key is a
 // candidate for the true argmin. fp16 keeps its range only while every
 // |n_j| < 2^15: a frame whose residual leaves that range, or a stage whose
@@ -33,8 +33,11 @@
 //
 // The fp16 scores are about 20 times coarser than split-bf16 ones, so
 // candidate sets are wider: each lane keeps two sets of keys (even and odd
-// 64-codeword groups), best, second and third key and the first two
-// indices of each. The smallest key's codeword is fetched as the decision
+// 64-codeword groups), best and second key, a lower bound of the third, and
+// the indices of the first two, updated two scores at a time (five
+// instructions per pair besides the keys). A key carries the codeword's
+// index inside a span of 1024 codewords, so index bookkeeping runs once per
+// span and set instead of once per group. The smallest key's codeword is fetched as the decision
 // starts (it is the pick of a frame with one candidate, and serves the
 // update); two to eight candidates (two per set and lane) are compared by
 // a float32 direct form, and only near ties by the float64 one; a third
@@ -77,7 +80,7 @@ static_assert(kGroups == 4, "two group pairs per chunk");
 static_assert(prep::kF16Row == 16 * kRowSlots, "LDS rows mirror the prepared rows");
 
 // Relative and absolute coefficients of (1), rounded up.
-constexpr float kRel = 1.0e-3f;        // 2u + u^2 + 2 gamma_72 + 2^-17 + u^2 + gamma_64 = 9.971e-4
+constexpr float kRel = 1.021e-3f;      // 2u + u^2 + 2 gamma_72 + 2^-15 + u^2 + gamma_64 = 1.01996e-3
 constexpr float kAbsN = 4.8e-7f;       // 2^-21 (1 + u) with the accumulation factor
 constexpr float kAbsC = 2.4e-7f;       // 2^-22 (1 + u) with the accumulation factor
 constexpr float kAbsNorm = 3.0e-8f;    // 2^-25, times 2^-e
@@ -103,7 +106,37 @@ __device__ __forceinline__ f16x8 to_f16x8(const float *v)
     return h;
 }
 
-// Running best / second / third key of one set and the indices of the first two.
+// Keys of this kernel: a score with its 8 low mantissa bits replaced by the
+// codeword's index inside a span of 1024 codewords of one key set and lane
+// half (256 codewords), which moves the value by less than 2^-15 of it. The
+// index bits of the score v (0..31, block v >> 4, accumulator v & 15) of the
+// group that starts at codeword g (a multiple of 64) are
+//   ((g >> 8) & 3) << 6  |  ((g >> 7) & 1) << 5  |  v
+// (chunk within the span, group pair within the chunk, score), and the
+// codeword is
+//   span + 64 * set + 4 * half + ((bits & 0xE0) << 2) + ((bits & 0x1C) << 1) + (bits & 3).
+constexpr int kSpan = 1024;              // codewords whose keys share one index space
+constexpr unsigned kKeyMask8 = 0xFFFFFF00u;
+
+// Index bits of the group starting at codeword g, before the score's own 5.
+__device__ __forceinline__ int group_bits(int g) { return (g >> 2) & 0xE0; }
+
+// base | c as an opaque scalar register (c a small constant), so that the key
+// of each score is one v_and_or_b32 with the mask in a vector register.
+__device__ __forceinline__ int sgpr_or(int base, int c)
+{
+    int r;
+    asm("s_or_b32 %0, %1, %2" : "=s"(r) : "s"(base), "i"(c));
+    return r;
+}
+
+__device__ __forceinline__ float key8(float s, unsigned mask, int bits)
+{
+    return __uint_as_float((__float_as_uint(s) & mask) | static_cast<unsigned>(bits));
+}
+
+// Running best and second key of one set, the indices of both, and a lower
+// bound of the third smallest key (exact in all but rare orders).
 struct KeySet {
     float best, second, third;
     int best_k, second_k;
@@ -115,55 +148,60 @@ __device__ __forceinline__ void reset(KeySet &s)
     s.best_k = s.second_k = 0;
 }
 
-__device__ __forceinline__ void scan_key(float v, int lk, KeySet &s)
-{
-    const float key = make_key(v, lk);
-    s.third = __builtin_amdgcn_fmed3f(key, s.second, s.third);
-    s.second = __builtin_amdgcn_fmed3f(key, s.best, s.second);
-    s.best = __builtin_amdgcn_fmed3f(key, s.best, -FLT_MAX);
-}
-
-// Score v (0..31) of a scored group: block v / 16, accumulator v % 16, local
-// index b*32 + 8*(a/4) + a%4 (the lane's 4*half row offset is added later).
-__device__ __forceinline__ void scan_score(const f32x16 (&d)[2], int v, KeySet &s)
+// Keys a, b of scores v and v+1 (same block) into set s. With the old best
+// B <= second S, the two smallest keys of {B, S, a, b} are min(B, a, b) and
+// min(S, med3(B, a, b)); and med3(S, a, b), the second smallest of the same
+// keys without B, is at most their third smallest, so third <- min(third,
+// med3(S, a, b)) keeps a lower bound of the third smallest key seen (equal
+// to it unless both a and b fall below B; a lower bound is all the decision
+// needs to find a set that may hold a third candidate). Five instructions
+// per two scores besides the keys, with consecutive second and third
+// updates merged into v_min3 by the compiler.
+__device__ __forceinline__ void scan_pair(const f32x16 (&d)[2], int v, int gbits, unsigned mask, KeySet &s)
 {
     const int b = v >> 4, a = v & 15;
-    scan_key(d[b][a], b * 32 + 8 * (a >> 2) + (a & 3), s);
+    const float k0 = key8(d[b][a], mask, sgpr_or(gbits, v));
+    const float k1 = key8(d[b][a + 1], mask, sgpr_or(gbits, v + 1));
+    const float t = __builtin_amdgcn_fmed3f(s.best, k0, k1);
+    const float u = __builtin_amdgcn_fmed3f(s.second, k0, k1);
+    s.best = __builtin_fminf(__builtin_fminf(s.best, k0), k1);
+    s.second = __builtin_fminf(s.second, t);
+    s.third = __builtin_fminf(s.third, u);
 }
 
-// Index bookkeeping after a group that starts at codeword `base` went into
-// set s (best / second bits before it: bb0, sb0). A changed second key is
-// either the previous best (demoted) or a key of this group; equal bit
-// patterns from different groups also leave a third key with the same
-// value, which the decision treats as an unresolved candidate.
-__device__ __forceinline__ void fold(KeySet &s, unsigned bb0, unsigned sb0, int base, int half)
+// Index bookkeeping of set `set` after the span that starts at codeword
+// `span` (best / second bits before it: bb0, sb0). A changed second key is
+// either the previous best (demoted) or a key of this span; equal bit
+// patterns from different spans leave a second key equal to the best, which
+// the decision treats as an unresolved candidate.
+__device__ __forceinline__ void fold(KeySet &s, unsigned bb0, unsigned sb0, int span, int set, int half)
 {
     const unsigned bb = __float_as_uint(s.best), sbits = __float_as_uint(s.second);
-    const int k_of_best = base + 4 * half + static_cast<int>(bb & ~kKeyMask);
-    const int k_of_second = base + 4 * half + static_cast<int>(sbits & ~kKeyMask);
+    const int base = span + 64 * set + 4 * half;
+    const int k_of_best = base + static_cast<int>(((bb & 0xE0u) << 2) + ((bb & 0x1Cu) << 1) + (bb & 3u));
+    const int k_of_second = base + static_cast<int>(((sbits & 0xE0u) << 2) + ((sbits & 0x1Cu) << 1) + (sbits & 3u));
     const bool best_moved = bb != bb0;
     const int demoted = (best_moved && sbits == bb0) ? s.best_k : k_of_second;
     s.second_k = sbits != sb0 ? demoted : s.second_k;
     s.best_k = best_moved ? k_of_best : s.best_k;
 }
 
-// How many of the previous group's 32 scores are scanned after each of a
-// group's ten matrix-core steps (half-norm of block 0 and of block 1, then
+// How many pairs of the previous group's 32 scores are scanned after each of
+// a group's ten matrix-core steps (half-norm of block 0 and of block 1, then
 // each 16-dim step of block 0 and block 1).
-constexpr int kScanAfter[10] = {4, 4, 3, 3, 3, 3, 3, 3, 3, 3};
+constexpr int kPairsAfter[10] = {2, 2, 2, 2, 2, 2, 1, 1, 1, 1};
 
 // Matrix-core steps of group kG of the chunk in LDS (rows sb) into dn: two
 // 32-codeword blocks, each a chain of the half-norm step and four 16-dim
-// steps. When kScan, the key scan of the previous
-// group dp (first codeword prev_base) into set `ks` is placed between them
-// in a fixed order, and the operands of the next step are read from LDS
-// before the current step's products are issued.
+// steps. When kScan, the key scan of the previous group dp (index bits
+// gbits) into set `ks` is placed between them in a fixed order, and the
+// operands of the next step are read from LDS before the current step's
+// products are issued.
 template <bool kScan>
 __device__ __forceinline__ void step_group(f32x16 (&dn)[2], const f32x16 (&dp)[2], int kG, const _Float16 *sb,
                                            int col, int half, const f16x8 (&nb)[4],
-                                           const f16x8 &nnorm, int prev_base, KeySet &ks)
+                                           const f16x8 &nnorm, int gbits, unsigned mask, KeySet &ks)
 {
-    const unsigned bb0 = __float_as_uint(ks.best), sb0 = __float_as_uint(ks.second);
     f16x8 a[2][2];   // [step parity][block]
     auto load_ops = [&](int s) {
 #pragma unroll
@@ -179,41 +217,45 @@ __device__ __forceinline__ void step_group(f32x16 (&dn)[2], const f32x16 (&dp)[2
         an[b] = *reinterpret_cast<const f16x8 *>(sb + (kG * 64 + b * 32 + col) * kRowHalfs + 64);
     load_ops(0);
     int v = 0;   // next score of dp
-    auto scan_some = [&](int count) {
+    auto scan_some = [&](int pairs) {
         if (kScan) {
 #pragma unroll
-            for (int i = 0; i < count; ++i) scan_score(dp, v + i, ks);
+            for (int i = 0; i < pairs; ++i) {
+                scan_pair(dp, v + 2 * i, gbits, mask, ks);
+                // keep the updates here, between the matrix steps (the
+                // compiler would otherwise sink the second and third chains
+                // past the group), after every second pair so that their
+                // updates still merge into v_min3
+                if (((v >> 1) + i) & 1) asm volatile("" : "+v"(ks.best), "+v"(ks.second), "+v"(ks.third));
+            }
         }
-        v += count;
+        v += 2 * pairs;
     };
     const f32x16 zero = {};
     dn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(an[0], nnorm, zero, 0, 0, 0);
-    scan_some(kScanAfter[0]);
+    scan_some(kPairsAfter[0]);
     __builtin_amdgcn_sched_barrier(0);
     dn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(an[1], nnorm, zero, 0, 0, 0);
-    scan_some(kScanAfter[1]);
+    scan_some(kPairsAfter[1]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         if (s < 3) load_ops(s + 1);
         __builtin_amdgcn_sched_barrier(0);
         dn[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s & 1][0], nb[s], dn[0], 0, 0, 0);
-        scan_some(kScanAfter[2 + 2 * s]);
+        scan_some(kPairsAfter[2 + 2 * s]);
         __builtin_amdgcn_sched_barrier(0);
         dn[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[s & 1][1], nb[s], dn[1], 0, 0, 0);
-        scan_some(kScanAfter[3 + 2 * s]);
+        scan_some(kPairsAfter[3 + 2 * s]);
         __builtin_amdgcn_sched_barrier(0);
     }
-    if (kScan) fold(ks, bb0, sb0, prev_base, half);
 }
 
 // The key scan of the last group of a stage, alone.
-__device__ __forceinline__ void scan_last(const f32x16 (&d)[2], int base, int half, KeySet &ks)
+__device__ __forceinline__ void scan_last(const f32x16 (&d)[2], int gbits, unsigned mask, KeySet &ks)
 {
-    const unsigned bb0 = __float_as_uint(ks.best), sb0 = __float_as_uint(ks.second);
 #pragma unroll
-    for (int v = 0; v < 32; ++v) scan_score(d, v, ks);
-    fold(ks, bb0, sb0, base, half);
+    for (int v = 0; v < 32; v += 2) scan_pair(d, v, gbits, mask, ks);
 }
 
 // The group at `base` that holds codeword n_codes - 1 when n_codes is not a
@@ -297,6 +339,7 @@ __device__ __forceinline__ float pair_distance_f32_row(const float (&n)[32], con
     const float s = (a[0] + a[1]) + (a[2] + a[3]);
     return s + other_half(s, half);
 }
+
 
 // Entry i (0..3) of a four-entry list, selected without indexing registers.
 __device__ __forceinline__ int pick4(const int (&l)[4], int i)
@@ -659,6 +702,10 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
     const int64_t frame = static_cast<int64_t>(blockIdx.x) * kBlockFrames + wave * kFramesPerWave + col;
     const bool valid = frame < n_frames;
 
+    // the key mask in a vector register, so that each key is one
+    // v_and_or_b32 whose index bits come from a scalar register
+    unsigned kmask;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(kmask) : "i"(kKeyMask8));
     float n[32];     // negated residual, dims 32*half .. 32*half+31
     float acc[32];   // reconstruction (kRecon)
     if (valid) {
@@ -714,6 +761,14 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
         KeySet ks[2];
         reset(ks[0]);
         reset(ks[1]);
+        // best / second bits of each set at the start of its current span
+        unsigned snap_b[2] = {__float_as_uint(kNoScore), __float_as_uint(kNoScore)};
+        unsigned snap_s[2] = {__float_as_uint(kNoScore), __float_as_uint(kNoScore)};
+        auto fold_set = [&](int set, int span) {
+            fold(ks[set], snap_b[set], snap_s[set], span, set, half);
+            snap_b[set] = __float_as_uint(ks[set].best);
+            snap_s[set] = __float_as_uint(ks[set].second);
+        };
         f32x16 da[2], db[2];
         int prev_base = 0;   // first codeword of the group held in db
 
@@ -733,24 +788,32 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
                 const bool scan_a = !(c == 0 && p == 0) && (prev_base >> 6) < n_groups;
                 if (scan_a) {
                     if (prev_base + 64 > n_codes) mask_tail(db, prev_base, half, n_codes);
-                    step_group<true>(da, db, ka, sb, col, half, nb, nnorm, prev_base, ks[1]);
+                    step_group<true>(da, db, ka, sb, col, half, nb, nnorm, group_bits(prev_base), kmask, ks[1]);
+                    // the last odd group of a span: set 1's keys of that span are complete
+                    if (((prev_base + 64) & (kSpan - 1)) == 0) fold_set(1, prev_base & ~(kSpan - 1));
                 } else {
-                    step_group<false>(da, db, ka, sb, col, half, nb, nnorm, prev_base, ks[1]);
+                    step_group<false>(da, db, ka, sb, col, half, nb, nnorm, 0, kmask, ks[1]);
                 }
                 const int base_a = c * kChunk + 64 * ka;
                 if ((base_a >> 6) < n_groups) {
                     if (base_a + 64 > n_codes) mask_tail(da, base_a, half, n_codes);
-                    step_group<true>(db, da, kb, sb, col, half, nb, nnorm, base_a, ks[0]);
+                    step_group<true>(db, da, kb, sb, col, half, nb, nnorm, group_bits(base_a), kmask, ks[0]);
+                    // the last even group of a span
+                    if (((base_a + 128) & (kSpan - 1)) == 0) fold_set(0, base_a & ~(kSpan - 1));
                 } else {
-                    step_group<false>(db, da, kb, sb, col, half, nb, nnorm, base_a, ks[0]);
+                    step_group<false>(db, da, kb, sb, col, half, nb, nnorm, 0, kmask, ks[0]);
                 }
                 prev_base = c * kChunk + 64 * kb;
             }
         }
         if ((prev_base >> 6) < n_groups) {
             if (prev_base + 64 > n_codes) mask_tail(db, prev_base, half, n_codes);
-            scan_last(db, prev_base, half, ks[1]);
+            scan_last(db, group_bits(prev_base), kmask, ks[1]);
         }
+        // keys of the last span (partial, or not yet folded) of both sets
+        const int last_span = ((n_groups - 1) * 64) & ~(kSpan - 1);
+        fold_set(0, last_span);
+        fold_set(1, last_span);
 
         // ---- stage q is scored for this wavefront's 32 frames: decide ----
         const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
