@@ -45,10 +45,7 @@ PEAK_F16_MFMA_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0             # MI355X HBM3E
 N_XCD, N_SIMD = 8, 1024            # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
 COPY_BYTES = 512 << 20             # size of the counter-calibration copy
-# Rate of random 256 B codebook-row gathers out of L2 / MALL that the decode
-# reaches at best over codebook sizes from 0.25 to 16 MiB (--gather-sweep);
-# the decode's row gathers are bound by it, not by HBM.
-GATHER_CEILING_TBPS = 21.9
+FLUSH_BYTES = 1 << 30             # written between cold decode launches to evict L2 / MALL
 SPLIT_MAX_FRAMES = 8192    # prepared encodes of up to this many frames take the split-codebook kernel
 
 CSRC = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc")
@@ -59,6 +56,8 @@ KERNEL_SOURCES = {
     "encode_bf16_split": ["encode_bf16.hip", "encode_common.h", "prepared.h"],
     "encode_fp32": ["encode.hip", "encode_common.h"],
     "decode": ["decode.hip"],
+    "linear_in": ["linear.hip"],
+    "linear_out": ["linear.hip"],
 }
 
 
@@ -77,6 +76,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain elementwise copy of 512 MiB (for HBM counter scaling)")
+    p.add_argument("--gather-probe", metavar="OUT_MD",
+                   help="run the ceiling probes (row gathers over 0.25..16 MiB tables, matrix cores, HBM copy), "
+                        "write a summary to OUT_MD, then exit")
+    p.add_argument("--no-probes", action="store_true",
+                   help="skip the live ceiling probes and the cold / warm decode timing")
     p.add_argument("--gather-sweep", metavar="OUT_MD",
                    help="time rvq_decode at Q=32, N=720000 over codebook sizes 0.25..16 MiB, write a "
                         "summary of the row-gather rates to OUT_MD, then exit")
@@ -120,12 +124,12 @@ def recorded_traffic(kind, workload):
 # ---------------------------------------------------------------- profiles
 
 PROFILE_COMMANDS = """cd /tmp && export TMPDIR=/tmp   # R = repository root
-rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o bench -- python3 $R/bench.py --workload {wl} --no-cpu-baseline
-rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
-rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --calibrate-copy
-rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
-rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof/valu -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline
-python3 $R/bench.py --workload {wl} --summarize-profiles $R/gpurun_out/prof"""
+rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_{wl}/trace -o bench -- python3 $R/bench.py --workload {wl} --no-cpu-baseline --no-probes
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_{wl}/fetch -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-probes --calibrate-copy
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_{wl}/write -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-probes --calibrate-copy
+rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof_{wl}/mfma -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-probes
+rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_MFMA SQ_WAIT_INST_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv -d $R/gpurun_out/prof_{wl}/valu -o bench -- python3 $R/bench.py --workload {wl} --steps 3 --warmup 1 --no-cpu-baseline --no-probes
+python3 $R/bench.py --workload {wl} --summarize-profiles $R/gpurun_out/prof_{wl}"""
 
 
 def _csv(dirname, suffix):
@@ -141,6 +145,10 @@ def _csv(dirname, suffix):
 
 
 def _kernel_of(name):
+    if "linear_in_kernel" in name:
+        return "linear_in"
+    if "linear_out_kernel" in name:
+        return "linear_out"
     if "encode_f16_kernel" in name:
         return "encode_f16"
     if "encode_bf16_ksplit_kernel" in name:
@@ -155,6 +163,8 @@ def _kernel_of(name):
         return "prepare"
     if "elementwise" in name and "MulFunctor" in name:
         return "copy"
+    if "gather_probe_kernel" in name:
+        return "calib_gather"
     return None
 
 
@@ -233,11 +243,24 @@ def summarize_profiles(w, src_dir):
         lines.append(f"- decode: {dec_bytes:.4g} bytes per launch ((4Q+4D) per frame) / {t:.1f} us = "
                      f"{dec_bytes / t / 1e3:.0f} GB/s ({dec_bytes / t / 1e3 / PEAK_HBM_GBPS:.1%} of "
                      f"{PEAK_HBM_GBPS:.0f} GB/s HBM).")
+    if w.hidden:
+        lin_bytes = (4.0 * w.hidden + 4.0 * d) * n
+        lin_flop = 2.0 * w.hidden * d * n
+        for kind, what in (("linear_in", "fc, hidden -> 64: h rows in, latent rows out"),
+                           ("linear_out", "fc2, 64 -> hidden: latent rows in, h rows out")):
+            if kind in avg:
+                t = avg[kind]
+                lines.append(f"- {kind} ({what}): {lin_bytes:.4g} bytes per launch ((4 hidden + 4D) per frame) / "
+                             f"{t:.1f} us = {lin_bytes / t / 1e3:.0f} GB/s ({lin_bytes / t / 1e3 / PEAK_HBM_GBPS:.1%} "
+                             f"of {PEAK_HBM_GBPS:.0f} GB/s HBM); {lin_flop / t / 1e6:.1f} TFLOP/s of fp32 work "
+                             f"(2 hidden D per frame).")
 
     fetch = _counter_means(_csv(os.path.join(src_dir, "fetch"), "counter_collection.csv"), "FETCH_SIZE")
     write = _counter_means(_csv(os.path.join(src_dir, "write"), "counter_collection.csv"), "WRITE_SIZE")
     f_scale = COPY_BYTES / (fetch["copy"] * 1024.0)
     w_scale = COPY_BYTES / (write["copy"] * 1024.0)
+    # the same fetch scale checked on a gather pattern: every 256 B row of a 1 GiB table read once
+    g_scale = (1 << 30) / (fetch["calib_gather"] * 1024.0) if "calib_gather" in fetch else None
     enc_algo = (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d
     # the prepared encodes read their section of the prepared codebooks: fp16 rows with their half-norm
     # parts (144 B), stage maxima and exponent (encode_f16; plus the fp32 rows of the picks), or split-bf16
@@ -245,12 +268,19 @@ def summarize_profiles(w, src_dir):
     kp = -(-k // 256) * 256
     prep16_bytes = q * (kp * 144 + 4 * (kp // 256) + 4)
     prep_bytes = q * (kp * 260 + 4 * (kp // 256))
+    hid = w.hidden or 0
     algo = {"encode_f16": enc_algo + prep16_bytes, "encode_bf16": enc_algo - 4.0 * q * k * d + prep_bytes,
-            "encode_fp32": enc_algo, "decode": dec_bytes + 4.0 * q * k * d}
+            "encode_fp32": enc_algo, "decode": dec_bytes + 4.0 * q * k * d,
+            # fc: h rows in, latent rows out (weights 256 KiB, read once); fc2 the reverse
+            "linear_in": (4.0 * hid + 4.0 * d) * n + 4.0 * hid * d,
+            "linear_out": (4.0 * hid + 4.0 * d) * n + 4.0 * hid * d}
     lines += ["", "## HBM counters (per launch)", "",
               f"A 512 MiB elementwise copy reads FETCH_SIZE = {fetch['copy']:.0f} KiB and WRITE_SIZE = "
               f"{write['copy']:.0f} KiB, so readings are scaled by {f_scale:.3f} (fetch) and "
-              f"{w_scale:.3f} (write).", "",
+              f"{w_scale:.3f} (write)." + (
+                  f" Check on a gather pattern (every 256 B row of a 1 GiB table read once, in a scattered "
+                  f"order): FETCH_SIZE = {fetch['calib_gather']:.0f} KiB for 1048576 KiB read, a scale of "
+                  f"{g_scale:.3f}." if g_scale else ""), "",
               "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB | algorithmic MB |",
               "|---|---|---|---|---|---|"]
     for kind in KERNEL_SOURCES:
@@ -272,7 +302,7 @@ def summarize_profiles(w, src_dir):
              "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
     means = {name: _counter_means(mf, name) for name in names}
     lines += ["", "## Matrix-core counters (per launch)", ""]
-    for kind in ("encode_f16", "encode_bf16", "encode_fp32"):
+    for kind in ("encode_f16", "encode_bf16", "encode_fp32", "linear_in", "linear_out"):
         c = {name: means[name].get(kind) for name in names}
         if c["GRBM_GUI_ACTIVE"] is None:
             continue
@@ -292,7 +322,7 @@ def summarize_profiles(w, src_dir):
                   "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
         vm = {name: _counter_means(vf, name) for name in vnames}
         lines += ["## Instruction-issue counters (per launch)", ""]
-        for kind in ("encode_f16", "encode_fp32"):
+        for kind in ("encode_f16", "encode_fp32", "linear_in", "linear_out"):
             c = {name: vm[name].get(kind) for name in vnames}
             if c["GRBM_GUI_ACTIVE"] is None:
                 continue
@@ -354,7 +384,7 @@ def summarize_trace(w, src_dir):
     work = _trace_work(w)
     cmd = ("cd /tmp && export TMPDIR=/tmp   # R = repository root\n"
            f"rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/tr_{w.name} -o t -- "
-           f"python3 $R/bench.py --workload {w.name} --steps 5 --no-cpu-baseline\n"
+           f"python3 $R/bench.py --workload {w.name} --steps 5 --no-cpu-baseline --no-probes\n"
            f"python3 $R/bench.py --workload {w.name} --summarize-trace $R/gpurun_out/tr_{w.name}")
     lines = [f"# rocprofv3: kernel trace, workload `{w.name}`", "", f"Workload: {w.description}.", "",
              "Commands:", "", "```", cmd, "```", "",
@@ -429,6 +459,179 @@ def gather_sweep(out_md):
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+# ------------------------------------------------------------ ceilings
+
+class Probes:
+    """The ceiling probes of librvq_probe.so (row gathers, matrix cores), timed with HIP events on torch's
+    current stream, plus a plain device copy for the HBM rate."""
+
+    def __init__(self):
+        import ctypes
+        import torch
+        path = os.path.join(_ROOT, "residual_vector_quantization_amd", "librvq_probe.so")
+        if not os.path.exists(path):
+            raise SystemExit(f"{path} is missing; build with `python -m residual_vector_quantization_amd.build`")
+        self.lib = ctypes.CDLL(path)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        self.lib.rvqprobe_gather_rows.argtypes = [vp, i64, i64, i32, i32, vp, vp]
+        self.lib.rvqprobe_mfma.argtypes = [i32, i32, i32, vp, vp]
+        self.torch = torch
+        self.dev = torch.device("cuda:0")
+
+    def _time(self, fn, reps):
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            ev[0].record()
+            fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+        return float(np.median(ts)), float(np.min(ts))
+
+    def gather(self, table_bytes, n_rows, reps=20):
+        """Random 256 B row gathers out of a table of table_bytes (rounded up to a power of two of rows):
+        (TB/s at the median launch, TB/s at the fastest)."""
+        torch = self.torch
+        rows = 1 << max(0, (int(table_bytes) // 256 - 1).bit_length())
+        table = torch.rand(rows * 64, device=self.dev)
+        n_groups = 1 << 18
+        per_group = max(8, -(-int(n_rows) // n_groups + 7) // 8 * 8)
+        sink = torch.empty(n_groups * 64, device=self.dev)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def run():
+            if self.lib.rvqprobe_gather_rows(table.data_ptr(), rows, n_groups, per_group, 0, sink.data_ptr(),
+                                             stream):
+                raise SystemExit("rvqprobe_gather_rows failed")
+        med, mn = self._time(run, reps)
+        moved = 256.0 * n_groups * per_group
+        return moved / med / 1e12, moved / mn / 1e12
+
+    def permuted_gather_once(self, table_bytes):
+        """Every 256 B row of a table_bytes table read once in a scattered order (counter calibration)."""
+        torch = self.torch
+        rows = int(table_bytes) // 256
+        table = torch.ones(rows * 64, device=self.dev)
+        n_groups = 1 << 18
+        sink = torch.empty(n_groups * 64, device=self.dev)
+        torch.cuda.synchronize()
+        if self.lib.rvqprobe_gather_rows(table.data_ptr(), rows, n_groups, rows // n_groups, 1, sink.data_ptr(),
+                                         torch.cuda.current_stream().cuda_stream):
+            raise SystemExit("rvqprobe_gather_rows failed")
+        torch.cuda.synchronize()
+
+    def mfma(self, fp16, reps=5):
+        """Back-to-back matrix-core products on every SIMD: TFLOP/s (median launch, fastest)."""
+        torch = self.torch
+        blocks, iters = 1024, (2000 if fp16 else 1000)
+        sink = torch.empty(blocks * 256, device=self.dev)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def run():
+            if self.lib.rvqprobe_mfma(1 if fp16 else 0, blocks, iters, sink.data_ptr(), stream):
+                raise SystemExit("rvqprobe_mfma failed")
+        med, mn = self._time(run, reps)
+        flop = blocks * 4 * 4 * iters * (32768.0 if fp16 else 4096.0)
+        return flop / med / 1e12, flop / mn / 1e12
+
+    def copy(self, reps=10):
+        """A 1 GiB device-to-device copy: GB/s of HBM traffic (read + write)."""
+        torch = self.torch
+        a = torch.ones(FLUSH_BYTES // 4, device=self.dev)
+        b = torch.empty_like(a)
+        med, mn = self._time(lambda: b.copy_(a), reps)
+        del a, b
+        return 2.0 * FLUSH_BYTES / med / 1e9, 2.0 * FLUSH_BYTES / mn / 1e9
+
+    def fill(self, reps=10):
+        """A 1 GiB device fill: GB/s written."""
+        torch = self.torch
+        a = torch.empty(FLUSH_BYTES // 4, device=self.dev)
+        med, mn = self._time(lambda: a.fill_(1.0), reps)
+        del a
+        return FLUSH_BYTES / med / 1e9, FLUSH_BYTES / mn / 1e9
+
+
+def time_decode(rvq, codes, books, out, reps=20):
+    """rvq_decode timed alone with HIP events: warm (right after a launch on the same data) and cold (after
+    writing a 1 GiB buffer, which evicts L2 and MALL); median and min in ms of each."""
+    import torch
+    flush = torch.empty(FLUSH_BYTES // 4, device=codes.device)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    res = {}
+    for mode in ("warm", "cold"):
+        ts = []
+        for _ in range(reps):
+            if mode == "cold":
+                flush.fill_(1.0)
+            else:
+                rvq.rvq_decode(codes, books, out=out)
+            ev[0].record()
+            rvq.rvq_decode(codes, books, out=out)
+            ev[1].record()
+            torch.cuda.synchronize()
+            ts.append(ev[0].elapsed_time(ev[1]))
+        res[mode] = {"median_ms": float(np.median(ts)), "min_ms": float(np.min(ts))}
+    del flush
+    return res
+
+
+def gather_probe(out_md):
+    """The row-gather ceiling over table sizes 0.25..16 MiB (5.9 GB of rows each) and the matrix-core and
+    copy ceilings; writes a summary to out_md."""
+    pr = Probes()
+    rows = []
+    for mib in (0.25, 1, 2, 4, 8, 16):
+        med, best = pr.gather(mib * 2 ** 20, 720000 * 32)
+        rec = {"table_MiB": mib, "gather_TBps_median": med, "gather_TBps_best": best}
+        print(json.dumps(rec), flush=True)
+        rows.append(rec)
+    f16 = pr.mfma(True)
+    f32 = pr.mfma(False)
+    cp = pr.copy()
+    fl = pr.fill()
+    print(json.dumps({"mfma_f16_TFLOPs": f16, "mfma_f32_TFLOPs": f32, "copy_GBps": cp, "fill_GBps": fl}),
+          flush=True)
+    lines = ["# Ceiling probes (row gathers, matrix cores, HBM copy)", "",
+             "`librvq_probe.so` (`csrc/probes.hip`), HIP events on the launch stream; median and best of the "
+             "timed launches.", "",
+             "Command: `python3 bench.py --gather-probe gpurun_out/ceilings.md`", "",
+             "## Random 256 B row gathers",
+             "",
+             "16 lanes x 16 B per row (the decode's access pattern), row index from an in-kernel hash (no "
+             "dependent load), 8 row loads in flight per lane, no store per row; 2^18 groups of 16 lanes, "
+             "5.9 GB of rows per launch (720,000 frames x 32 stages).", "",
+             "| table MiB | TB/s (median) | TB/s (best) |", "|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['table_MiB']} | {r['gather_TBps_median']:.1f} | {r['gather_TBps_best']:.1f} |")
+    lines += ["", "## Matrix cores and HBM", "",
+              "| probe | median | best | published |", "|---|---|---|---|",
+              f"| v_mfma_f32_32x32x16_f16, 4 chains per wavefront, 16 wavefronts per CU | {f16[0]:.0f} TFLOP/s | "
+              f"{f16[1]:.0f} TFLOP/s | {PEAK_F16_MFMA_TFLOPS:.0f} TFLOP/s |",
+              f"| v_mfma_f32_32x32x2_f32, same | {f32[0]:.1f} TFLOP/s | {f32[1]:.1f} TFLOP/s | "
+              f"{PEAK_FP32_MFMA_TFLOPS} TFLOP/s |",
+              f"| 1 GiB device copy (read + write) | {cp[0]:.0f} GB/s | {cp[1]:.0f} GB/s | {PEAK_HBM_GBPS:.0f} GB/s |",
+              f"| 1 GiB device fill (write only) | {fl[0]:.0f} GB/s | {fl[1]:.0f} GB/s | {PEAK_HBM_GBPS:.0f} GB/s |"]
+    os.makedirs(os.path.dirname(os.path.abspath(out_md)), exist_ok=True)
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def calibrate_counters(dev):
+    """Kernels of a known size for the HBM counters: an elementwise copy (streaming read + write) and a
+    scattered read of every 256 B row of a 1 GiB table once (gather pattern, read only)."""
+    import torch
+    a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    del a, b
+    Probes().permuted_gather_once(1 << 30)
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(w, x, books, codes_gpu, target_s):
@@ -493,6 +696,8 @@ def bench_projected(args, w):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = ev[0].elapsed_time(ev[1]) / args.steps
+    if args.calibrate_copy:
+        calibrate_counters(dev)
     lin_flop = 2 * 2.0 * hid * d * n
     enc_flop = 2.0 * q * k * d * n
     rec = {"metric": "RVQ projected round trip frames/sec (fc 1024->64, Q=8 K=1024 D=64 RVQ, fc2 64->1024; fp32)",
@@ -613,6 +818,9 @@ def main():
     if args.gather_sweep:
         gather_sweep(args.gather_sweep)
         return
+    if args.gather_probe:
+        gather_probe(args.gather_probe)
+        return
     if args.summarize_trace:
         summarize_trace(W.WORKLOADS[args.workload], args.summarize_trace)
         return
@@ -696,11 +904,7 @@ def main():
             raise SystemExit("rvq_encode and rvq_encode_prepared disagree")
 
     if args.calibrate_copy:
-        a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        torch.mul(a, 1.0, out=b)
-        torch.cuda.synchronize()
-        del a, b
+        calibrate_counters(dev)
 
     n, q, k, d = w.n_frames, w.n_stages, w.n_codes, w.dim
     ms_per_step = wall * 1e3 / args.steps
@@ -716,6 +920,17 @@ def main():
         mm_kernel = ("encode_bf16_ksplit_kernel (codebook split over a workgroup's wavefronts), prepared "
                      "codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)")
     mm_tflops = mm_work / (enc_ms * 1e-3) / 1e12
+    # measured ceilings (live, same box) and the decode timed alone, warm and after a 1 GiB flush
+    ceil = dec_alone = None
+    if not args.no_probes:
+        pr = Probes()
+        # the frame-parallel decode gathers from the whole codebook, the stage-ordered one (codebooks of
+        # 4 MiB and more) from the few stages in flight: probe tables of those sizes, long enough launches
+        table = 4.0 * q * k * d if 4 * q * k * d < 4 << 20 else 2 << 20
+        probe_rows = max(n * q, 1 << 24)
+        ceil = {"gather_TBps": pr.gather(table, probe_rows), "mfma_f16_TFLOPs": pr.mfma(True),
+                "mfma_f32_TFLOPs": pr.mfma(False), "copy_GBps": pr.copy()}
+        dec_alone = time_decode(rvq, codes, bg, out)
     dec_bytes = (4.0 * q + 4.0 * d) * n
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
     gather_tbps = 4.0 * d * q * n / (dec_ms * 1e-3) / 1e12
@@ -744,18 +959,46 @@ def main():
                      "achieved": mm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": mm_tflops / PEAK_F16_MFMA_TFLOPS,
                      "traffic": recorded_traffic("encode_f16" if wide else "encode_bf16_split", w.name),
-                     "work_per_launch": mm_what},
+                     "work_per_launch": mm_what,
+                     "contraction_dtype": "fp16" if wide else "bf16 (3-way split)",
+                     "decision": "float64 re-rank of every candidate within the proven fp16 error bound; "
+                                 "codes equal the oracle's float64 argmin",
+                     "results_dtype": "f32 residual and reconstruction, i32 codes"},
         "encode_fp32_equivalent": {"achieved": enc_flop / (enc_ms * 1e-3) / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
                                    "unit": "TFLOP/s", "work_per_launch": f"2*Q*K*D*N = {enc_flop:.4g} flop"},
         "decode_roofline": {"bound": "hbm", "kernel": dec_kernel, "achieved": dec_gbps,
                             "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": dec_gbps / PEAK_HBM_GBPS,
                             "traffic": recorded_traffic("decode", w.name),
                             "work_per_launch": f"(4Q+4D)*N = {dec_bytes:.4g} B",
-                            "row_gathers": {"achieved": gather_tbps, "ceiling": GATHER_CEILING_TBPS,
-                                            "unit": "TB/s", "frac": gather_tbps / GATHER_CEILING_TBPS,
+                            "row_gathers": {"achieved": gather_tbps, "unit": "TB/s",
                                             "work_per_launch": f"4*D*Q*N = {4.0 * d * q * n:.4g} B "
                                                                "of codebook rows from L2 / MALL"}},
     }
+    if ceil is not None:
+        g_med = ceil["gather_TBps"][0]
+        rg = rec["decode_roofline"]["row_gathers"]
+        rg.update({"ceiling": g_med, "frac": gather_tbps / g_med,
+                   "ceiling_source": f"rvqprobe_gather_rows (librvq_probe.so) on this box: random 256 B rows from "
+                                     f"a {table / 2 ** 20:g} MiB table (the decode's working set), no dependent "
+                                     f"loads, about {256 * probe_rows / 1e9:.1f} GB per launch, median launch"})
+        f16_med, f32_med = ceil["mfma_f16_TFLOPs"][0], ceil["mfma_f32_TFLOPs"][0]
+        # bf16 and fp16 share the dense matrix-core rate, so the fp16 probe serves both
+        rec["roofline"].update({"peak_measured": f16_med, "frac_measured": mm_tflops / f16_med,
+                                "peak_measured_source": "rvqprobe_mfma: back-to-back v_mfma_f32_32x32x16_f16 "
+                                                        "on every SIMD, this box"})
+        rec["encode_fp32_equivalent"].update({"peak_measured": f32_med})
+        cp_med = ceil["copy_GBps"][0]
+        rec["decode_roofline"].update({"peak_measured": cp_med, "frac_measured": dec_gbps / cp_med,
+                                       "peak_measured_source": "1 GiB device copy (read + write), this box"})
+        for mode, t in dec_alone.items():
+            rec["decode_roofline"][mode] = {
+                "median_ms": t["median_ms"], "min_ms": t["min_ms"],
+                "hbm_GBps_median": dec_bytes / (t["median_ms"] * 1e-3) / 1e9,
+                "row_gathers_TBps_median": 4.0 * d * q * n / (t["median_ms"] * 1e-3) / 1e12,
+                "timing": "rvq_decode alone, 20 launches, HIP events" +
+                          (", each after writing 1 GiB (L2 and MALL evicted)" if mode == "cold" else
+                           ", each right after a launch on the same data")}
+        rec["ceilings_measured"] = {k_: {"median": v[0], "best": v[1]} for k_, v in ceil.items()}
     if fp32_ms is not None:
         t32 = enc_flop / (fp32_ms * 1e-3) / 1e12
         rec["encode_fp32_scoring"] = {"kernel": "encode_kernel (v_mfma_f32_32x32x2_f32)", "ms": fp32_ms,
@@ -763,6 +1006,9 @@ def main():
                                       "unit": "TFLOP/s", "frac": t32 / PEAK_FP32_MFMA_TFLOPS,
                                       "traffic": recorded_traffic("encode_fp32", w.name),
                                       "codes_equal_to_default": True}
+        if ceil is not None:
+            rec["encode_fp32_scoring"].update({"peak_measured": ceil["mfma_f32_TFLOPs"][0],
+                                               "frac_measured": t32 / ceil["mfma_f32_TFLOPs"][0]})
     if not args.no_cpu_baseline:
         base, parity = cpu_baseline(w, x, books, codes_h, args.cpu_seconds)
         rec["cpu_baseline"] = base

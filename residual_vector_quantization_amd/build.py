@@ -16,6 +16,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIBRARY = os.path.join(PKG, "librvq.so")
+# measurement tooling beside the library: the ceilings (row gathers, matrix cores) the kernels are compared with
+PROBE_LIBRARY = os.path.join(PKG, "librvq_probe.so")
+PROBE_SOURCES = ["probes.hip"]
 SOURCES = ["rvq_api.hip", "encode.hip", "encode_bf16.hip", "encode_f16.hip", "decode.hip", "linear.hip", "projected.hip",
            "cosine.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -38,15 +41,20 @@ def _compile(src):
     return obj
 
 
+def _link(objs, target):
+    tmp = target + ".tmp%d" % os.getpid()
+    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
+    os.replace(tmp, target)
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIBRARY + ".tmp%d" % os.getpid()
-    subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], check=True)
-    os.replace(tmp, LIBRARY)
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    _link(objs[:len(SOURCES)], LIBRARY)
+    _link(objs[len(SOURCES):], PROBE_LIBRARY)
     if verbose:
-        print("built", LIBRARY)
+        print("built", LIBRARY, PROBE_LIBRARY)
     return LIBRARY
 
 
