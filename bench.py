@@ -7,17 +7,24 @@ and split into bf16 halves, with their half-norms), ``rvq_encode_prepared``
 (codes + final residual; fp16 scores with exact re-rank for wide batches,
 split-bf16 for batches of up to 8192 frames) and ``rvq_decode`` (codes ->
 reconstruction) over the whole batch,
-inputs and outputs resident in HBM. W untimed steps (100 by default: the
-GPU's clocks settle after about 50 ms of load), then K timed steps (100)
-between ``torch.cuda.synchronize()`` calls. Per-launch kernel times
-come from HIP events recorded on the stream the kernels run on (torch's
-current stream, which is the stream handed to the C ABI).
+inputs and outputs resident in HBM. Before the steps, the side
+measurements run (about a second of GPU load, so the clocks have settled
+when the steps start): the ceilings of this machine from ``librvq_probe.so``
+(random 256 B row gathers from a table of the decode's working set, fp16
+and fp32 matrix cores, a 1 GiB copy and fill), the decode alone warm and
+after a 1 GiB flush (median and min of 20), and the fp32-scored encode.
+Then W untimed steps (100 by default), then K timed steps (100) between
+``torch.cuda.synchronize()`` calls. Per-launch kernel times come from HIP
+events recorded on the stream the kernels run on (torch's current
+stream, which is the stream handed to the C ABI).
 
 Prints one JSON line with the throughput, the roofline of the dominant
-kernel (the encode on the fp16 matrix cores), the same encode
-with fp32 scores against the fp32 matrix-core roofline, the decode's HBM
-roofline, sampled parity against the CPU oracle, and the oracle's own
-throughput on a bounded sample of the same workload (``cpu_baseline``).
+kernel (the encode on the fp16 matrix cores: spec and measured peaks,
+contraction dtype, the float64 decision), the same encode with fp32 scores
+against the fp32 matrix-core roofline, the decode's HBM roofline with its
+row-gather ceiling and warm / cold times, sampled parity against the CPU
+oracle, and the oracle's own throughput on a bounded sample of the same
+workload (``cpu_baseline``).
 
 ``--summarize-profiles DIR`` turns the rocprofv3 runs listed in
 PROFILE_COMMANDS into the summaries under ``profiles/``.
@@ -69,7 +76,7 @@ def parse():
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="batched", choices=list(W.WORKLOADS))
-    p.add_argument("--fp32-steps", type=int, default=5,
+    p.add_argument("--fp32-steps", type=int, default=20,
                    help="launches of the fp32-scored encode timed after the main steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU-oracle baseline sample")
@@ -866,22 +873,21 @@ def main():
         if ev is not None:
             ev[3].record()
 
-    for _ in range(args.warmup):
-        step()
+    n, q, k, d = w.n_frames, w.n_stages, w.n_codes, w.dim
+    # Side measurements first (they also bring the GPU to its sustained clocks before the timed steps):
+    # the ceilings of this machine, the decode alone warm and cold, the fp32-scored encode.
+    step()
     torch.cuda.synchronize()
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    enc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
-    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
-    codes_h = codes.cpu().numpy()
-
+    ceil = dec_alone = None
+    if not args.no_probes:
+        pr = Probes()
+        # the frame-parallel decode gathers from the whole codebook, the stage-ordered one (codebooks of
+        # 4 MiB and more) from the few stages in flight: probe tables of those sizes, long enough launches
+        table = 4.0 * q * k * d if 4 * q * k * d < 4 << 20 else 2 << 20
+        probe_rows = max(n * q, 1 << 24)
+        ceil = {"gather_TBps": pr.gather(table, probe_rows), "mfma_f16_TFLOPs": pr.mfma(True),
+                "mfma_f32_TFLOPs": pr.mfma(False), "copy_GBps": pr.copy(), "fill_GBps": pr.fill()}
+        dec_alone = time_decode(rvq, codes, bg, out)
     # the same encode with fp32 matrix-core scores (identical results), timed separately
     fp32_ms = None
     if args.fp32_steps > 0:
@@ -903,10 +909,25 @@ def main():
         if not torch.equal(c32, codes):
             raise SystemExit("rvq_encode and rvq_encode_prepared disagree")
 
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    enc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+    codes_h = codes.cpu().numpy()
+
     if args.calibrate_copy:
         calibrate_counters(dev)
 
-    n, q, k, d = w.n_frames, w.n_stages, w.n_codes, w.dim
     ms_per_step = wall * 1e3 / args.steps
     value = n * args.steps / wall
     enc_flop = 2.0 * q * k * d * n
@@ -920,17 +941,6 @@ def main():
         mm_kernel = ("encode_bf16_ksplit_kernel (codebook split over a workgroup's wavefronts), prepared "
                      "codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)")
     mm_tflops = mm_work / (enc_ms * 1e-3) / 1e12
-    # measured ceilings (live, same box) and the decode timed alone, warm and after a 1 GiB flush
-    ceil = dec_alone = None
-    if not args.no_probes:
-        pr = Probes()
-        # the frame-parallel decode gathers from the whole codebook, the stage-ordered one (codebooks of
-        # 4 MiB and more) from the few stages in flight: probe tables of those sizes, long enough launches
-        table = 4.0 * q * k * d if 4 * q * k * d < 4 << 20 else 2 << 20
-        probe_rows = max(n * q, 1 << 24)
-        ceil = {"gather_TBps": pr.gather(table, probe_rows), "mfma_f16_TFLOPs": pr.mfma(True),
-                "mfma_f32_TFLOPs": pr.mfma(False), "copy_GBps": pr.copy()}
-        dec_alone = time_decode(rvq, codes, bg, out)
     dec_bytes = (4.0 * q + 4.0 * d) * n
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
     gather_tbps = 4.0 * d * q * n / (dec_ms * 1e-3) / 1e12
