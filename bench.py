@@ -77,7 +77,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="batched", choices=list(W.WORKLOADS))
     p.add_argument("--fp32-steps", type=int, default=20,
-                   help="launches of the fp32-scored encode timed after the main steps")
+                   help="launches of the fp32-scored encode timed before the main steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target wall time of the CPU-oracle baseline sample")
     p.add_argument("--no-cpu-baseline", action="store_true")

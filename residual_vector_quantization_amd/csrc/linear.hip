@@ -16,10 +16,10 @@
 // + v_h w_h (bf16 x bf16 products are exact in fp32). The dropped
 // v_m w_l + v_l w_m + v_l w_l are at most 2^-23 |v w|, the size of one fp32
 // rounding, so the result is as accurate as an fp32 contraction; six
-// v_mfma_f32_32x32x16_bf16 do the work of eight fp32 32x32x2 steps. fc2,
-// whose time goes to its 4 KiB output rows rather than to the contraction
-// (the split form measured 20% slower there), stays on
-// v_mfma_f32_32x32x2_f32.
+// v_mfma_f32_32x32x16_bf16 do the work of eight fp32 32x32x2 steps. fc2
+// uses the same split (linear_out_split_kernel) with its stores made
+// line-wide through LDS; linear_out_kernel, on v_mfma_f32_32x32x2_f32,
+// remains for hidden sizes that are not a multiple of 32.
 //
 // Both kernels put weight rows on the M side and 32 frames per wavefront on
 // the N side, stream the weights through LDS (padded rows, double buffered,
@@ -369,6 +369,105 @@ void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden
     }
 }
 
+// ---- linear_out on bf16 matrix cores at fp32 accuracy ----------------------
+//
+// The same contraction as linear_out_kernel, in the three-part bf16 split
+// of linear_in (six v_mfma_f32_32x32x16_bf16 per 16-wide step instead of
+// eight fp32 32x32x2 products: 2.7 times less matrix-core time, which bounds
+// fc2 on fp32 matrix cores). Every wavefront is independent -- no barrier:
+// it holds its 32 frames' split operand in VGPRs, and for each tile of 32
+// outputs loads the 32 weight rows' fp32 values of its lanes (128 B per
+// lane, from L2) and splits them in registers. The 32x32 result goes
+// through a wavefront-private LDS tile so that each store instruction
+// writes 8 frames x 128 contiguous bytes (whole cache lines) instead of
+// 32 frames x 32 bytes. The next tile's weights are requested before the
+// current tile's products, so their latency hides behind them, and no load
+// waits for an earlier tile's stores.
+constexpr int kOutSplitWaves = 4;
+constexpr int kTileRow = 36;   // floats per LDS tile row (32 outputs + pad)
+
+template <bool kBias>
+__global__ __launch_bounds__(64 * kOutSplitWaves)
+void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int hidden,
+                             const float *__restrict__ w, const float *__restrict__ bias,
+                             float *__restrict__ out)
+{
+    __shared__ __align__(16) float s_tile[kOutSplitWaves][kFramesPerWave * kTileRow];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t frame0 = (static_cast<int64_t>(blockIdx.x) * kOutSplitWaves + wave) * kFramesPerWave;
+    const int64_t frame = frame0 + col;
+    const bool valid = frame < n_frames;
+    float *tile = s_tile[wave];
+
+    // B operand: frame `col`, dims 16 s + 8 half .. +7 of step s, split once
+    Split3 xb[4];
+    {
+        const float *src = x + (valid ? frame : 0) * kDim + 8 * half;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float v[8];
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(src + 16 * s);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 16 * s + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[e] = valid ? a[e] : 0.0f;
+                v[4 + e] = valid ? b[e] : 0.0f;
+            }
+            xb[s] = split3(v);
+        }
+    }
+
+    // A operand of tile t: weight row 32 t + col, dims 16 s + 8 half .. +7
+    auto load_tile = [&](int t, f32x4 (&wv)[8]) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(w + static_cast<int64_t>(32 * t + col) * kDim + 8 * half);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            wv[2 * s] = p[4 * s];
+            wv[2 * s + 1] = p[4 * s + 1];
+        }
+    };
+    const int n_tiles = hidden / 32;
+    // store j of a tile: frame 8 j + lane / 8, outputs 4 (lane % 8) .. +3
+    const int sf = lane >> 3, sseg = lane & 7;
+    f32x4 cur[8], nxt[8];
+    load_tile(0, cur);
+    for (int t = 0; t < n_tiles; ++t) {
+        if (t + 1 < n_tiles) load_tile(t + 1, nxt);
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float v[8] = {cur[2 * s][0], cur[2 * s][1], cur[2 * s][2], cur[2 * s][3],
+                                cur[2 * s + 1][0], cur[2 * s + 1][1], cur[2 * s + 1][2], cur[2 * s + 1][3]};
+            mfma6(acc, split3(v), xb[s]);
+        }
+        // lane (col, half) holds outputs 8 m + 4 half .. +3 (m < 4) of frame col
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            *reinterpret_cast<f32x4 *>(&tile[col * kTileRow + 8 * m + 4 * half]) =
+                f32x4{acc[4 * m], acc[4 * m + 1], acc[4 * m + 2], acc[4 * m + 3]};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        f32x4 bb = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (kBias) bb = *reinterpret_cast<const f32x4 *>(bias + 32 * t + 4 * sseg);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int f = 8 * j + sf;
+            const f32x4 o = *reinterpret_cast<const f32x4 *>(&tile[f * kTileRow + 4 * sseg]) + bb;
+            if (frame0 + f < n_frames)
+                *reinterpret_cast<f32x4 *>(out + (frame0 + f) * static_cast<int64_t>(hidden) + 32 * t + 4 * sseg) = o;
+        }
+        // every lane has read the tile before the next tile overwrites it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+    }
+}
+
 }  // namespace
 
 hipError_t launch_linear_in(const float *h, int64_t n_frames, int hidden, const float *w,
@@ -407,6 +506,19 @@ hipError_t launch_linear_in_update(const float *src, const int32_t *codes, int c
 hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const float *w,
                              const float *bias, float *out, hipStream_t stream)
 {
+    if (hidden % 32 == 0) {
+        const int64_t per_block = kOutSplitWaves * kFramesPerWave;
+        const int64_t blocks = (n_frames + per_block - 1) / per_block;
+        if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+        const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kOutSplitWaves);
+        if (bias)
+            hipLaunchKernelGGL((linear_out_split_kernel<true>), grid, block, 0, stream, x, n_frames, hidden, w, bias,
+                               out);
+        else
+            hipLaunchKernelGGL((linear_out_split_kernel<false>), grid, block, 0, stream, x, n_frames, hidden, w, bias,
+                               out);
+        return hipGetLastError();
+    }
     const int64_t blocks = (n_frames + kOutFrames - 1) / kOutFrames;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kOutWaves);
