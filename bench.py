@@ -909,6 +909,20 @@ def main():
         if not torch.equal(c32, codes):
             raise SystemExit("rvq_encode and rvq_encode_prepared disagree")
 
+    # the encode's launch-to-launch settling: 40 back-to-back launches timed one by one (a fresh
+    # process's first launches run up to 1.3x slower while the clocks adjust to this kernel)
+    settle = None
+    if not args.no_probes:
+        sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(40)]
+        for e in sev:
+            e[0].record()
+            rvq.rvq_encode_prepared(xg, bg, prepared, out=(codes, None, residual))
+            e[1].record()
+        torch.cuda.synchronize()
+        st = [e[0].elapsed_time(e[1]) for e in sev]
+        settle = {"launches": 40, "first_ms": st[0], "median_2_10_ms": float(np.median(st[1:10])),
+                  "median_11_30_ms": float(np.median(st[10:30])), "median_31_40_ms": float(np.median(st[30:]))}
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -1009,6 +1023,8 @@ def main():
                           (", each after writing 1 GiB (L2 and MALL evicted)" if mode == "cold" else
                            ", each right after a launch on the same data")}
         rec["ceilings_measured"] = {k_: {"median": v[0], "best": v[1]} for k_, v in ceil.items()}
+    if settle is not None:
+        rec["encode_settling"] = settle
     if fp32_ms is not None:
         t32 = enc_flop / (fp32_ms * 1e-3) / 1e12
         rec["encode_fp32_scoring"] = {"kernel": "encode_kernel (v_mfma_f32_32x32x2_f32)", "ms": fp32_ms,
