@@ -154,7 +154,7 @@ def _csv(dirname, suffix):
 def _kernel_of(name):
     if "linear_in_kernel" in name:
         return "linear_in"
-    if "linear_out_kernel" in name:
+    if "linear_out_kernel" in name or "linear_out_split_kernel" in name:
         return "linear_out"
     if "encode_f16_kernel" in name:
         return "encode_f16"
@@ -372,6 +372,7 @@ def _trace_work(w):
         work.update({
             "linear_in_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
             "linear_out_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
+            "linear_out_split_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
             "update_kernel": (8.0 * hid * n, "B", "HBM, residual read + write (8 hidden per frame)"),
             "proj8_kernel": (8.0 * hid * n, "B", "HBM, residual read + write (8 hidden per frame)"),
             "projected_decode_kernel": ((4.0 * q + 4.0 * hid) * n, "B", "HBM, (4Q + 4 hidden) per frame"),

@@ -375,36 +375,49 @@ void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden
 // of linear_in (six v_mfma_f32_32x32x16_bf16 per 16-wide step instead of
 // eight fp32 32x32x2 products: 2.7 times less matrix-core time, which bounds
 // fc2 on fp32 matrix cores). Every wavefront is independent -- no barrier:
-// it holds its 32 frames' split operand in VGPRs, and for each tile of 32
-// outputs loads the 32 weight rows' fp32 values of its lanes (128 B per
-// lane, from L2) and splits them in registers. The 32x32 result goes
+// it holds the split operand of two groups of 32 frames in VGPRs, and for
+// each tile of 32 outputs loads the 32 weight rows' fp32 values of its
+// lanes (128 B per lane, from L2) and splits them once for both groups,
+// whose two product chains are interleaved (half the weight loads and
+// splits per output of one group per wavefront). Each 32x32 result goes
 // through a wavefront-private LDS tile so that each store instruction
 // writes 8 frames x 128 contiguous bytes (whole cache lines) instead of
-// 32 frames x 32 bytes. The next tile's weights are requested before the
-// current tile's products, so their latency hides behind them, and no load
-// waits for an earlier tile's stores.
+// 32 frames x 32 bytes.
+//
+// Loads and stores share one in-order completion counter, so a wait for a
+// load issued after a store also waits for the store. The next tile's bias
+// and weights are therefore requested before the current tile's products
+// and stores, every four rows of the transposed tile are read from LDS
+// before any of them is stored, tiles go in pairs with the weight registers
+// alternating, and the prefetches are unconditional (past the last tile
+// they reload it): a wait for a tile's weights then leaves the stores
+// issued after them in flight.
 constexpr int kOutSplitWaves = 4;
+constexpr int kOutGroups = 2;                              // groups of 32 frames per wavefront
+constexpr int kOutWaveFrames = kOutGroups * kFramesPerWave;
 constexpr int kTileRow = 36;   // floats per LDS tile row (32 outputs + pad)
 
 template <bool kBias>
-__global__ __launch_bounds__(64 * kOutSplitWaves)
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kOutSplitWaves, 64 * kOutSplitWaves),
+                          amdgpu_waves_per_eu(2)))   // at most 256 registers: no spills
 void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int hidden,
                              const float *__restrict__ w, const float *__restrict__ bias,
                              float *__restrict__ out)
 {
-    __shared__ __align__(16) float s_tile[kOutSplitWaves][kFramesPerWave * kTileRow];
+    __shared__ __align__(16) float s_tile[kOutSplitWaves][kOutWaveFrames * kTileRow];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int64_t frame0 = (static_cast<int64_t>(blockIdx.x) * kOutSplitWaves + wave) * kFramesPerWave;
-    const int64_t frame = frame0 + col;
-    const bool valid = frame < n_frames;
+    const int64_t frame0 = (static_cast<int64_t>(blockIdx.x) * kOutSplitWaves + wave) * kOutWaveFrames;
     float *tile = s_tile[wave];
 
-    // B operand: frame `col`, dims 16 s + 8 half .. +7 of step s, split once
-    Split3 xb[4];
-    {
+    // B operand of group g: frame 32 g + col, dims 16 s + 8 half .. +7 of step s, split once
+    Split3 xb[kOutGroups][4];
+#pragma unroll
+    for (int g = 0; g < kOutGroups; ++g) {
+        const int64_t frame = frame0 + 32 * g + col;
+        const bool valid = frame < n_frames;
         const float *src = x + (valid ? frame : 0) * kDim + 8 * half;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -416,7 +429,7 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
                 v[e] = valid ? a[e] : 0.0f;
                 v[4 + e] = valid ? b[e] : 0.0f;
             }
-            xb[s] = split3(v);
+            xb[g][s] = split3(v);
         }
     }
 
@@ -432,39 +445,76 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
     const int n_tiles = hidden / 32;
     // store j of a tile: frame 8 j + lane / 8, outputs 4 (lane % 8) .. +3
     const int sf = lane >> 3, sseg = lane & 7;
-    f32x4 cur[8], nxt[8];
-    load_tile(0, cur);
-    for (int t = 0; t < n_tiles; ++t) {
-        if (t + 1 < n_tiles) load_tile(t + 1, nxt);
-        f32x16 acc = {};
+    const bool all_in = frame0 + kOutWaveFrames <= n_frames;   // wave-uniform
+    // products and stores of tile t from its weights wv and bias bv
+    auto tile_out = [&](int t, const f32x4 (&wv)[8], const f32x4 &bv) {
+        f32x16 acc[kOutGroups] = {};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const float v[8] = {cur[2 * s][0], cur[2 * s][1], cur[2 * s][2], cur[2 * s][3],
-                                cur[2 * s + 1][0], cur[2 * s + 1][1], cur[2 * s + 1][2], cur[2 * s + 1][3]};
-            mfma6(acc, split3(v), xb[s]);
-        }
-        // lane (col, half) holds outputs 8 m + 4 half .. +3 (m < 4) of frame col
+            const float v[8] = {wv[2 * s][0], wv[2 * s][1], wv[2 * s][2], wv[2 * s][3],
+                                wv[2 * s + 1][0], wv[2 * s + 1][1], wv[2 * s + 1][2], wv[2 * s + 1][3]};
+            const Split3 a = split3(v);
+            // mfma6's six products in its order, the two groups' chains interleaved
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            *reinterpret_cast<f32x4 *>(&tile[col * kTileRow + 8 * m + 4 * half]) =
-                f32x4{acc[4 * m], acc[4 * m + 1], acc[4 * m + 2], acc[4 * m + 3]};
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, xb[g][s].l, acc[g], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.l, xb[g][s].h, acc[g], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.m, xb[g][s].m, acc[g], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, xb[g][s].m, acc[g], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.m, xb[g][s].h, acc[g], 0, 0, 0);
+#pragma unroll
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, xb[g][s].h, acc[g], 0, 0, 0);
+        }
+        // lane (col, half) holds outputs 8 m + 4 half .. +3 (m < 4) of frame 32 g + col
+#pragma unroll
+        for (int g = 0; g < kOutGroups; ++g)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                *reinterpret_cast<f32x4 *>(&tile[(32 * g + col) * kTileRow + 8 * m + 4 * half]) =
+                    f32x4{acc[g][4 * m], acc[g][4 * m + 1], acc[g][4 * m + 2], acc[g][4 * m + 3]};
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        f32x4 bb = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (kBias) bb = *reinterpret_cast<const f32x4 *>(bias + 32 * t + 4 * sseg);
+        // every row of the tile is read (into its own registers) before any is stored
+        f32x4 o[4 * kOutGroups];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int f = 8 * j + sf;
-            const f32x4 o = *reinterpret_cast<const f32x4 *>(&tile[f * kTileRow + 4 * sseg]) + bb;
-            if (frame0 + f < n_frames)
-                *reinterpret_cast<f32x4 *>(out + (frame0 + f) * static_cast<int64_t>(hidden) + 32 * t + 4 * sseg) = o;
+        for (int j = 0; j < 4 * kOutGroups; ++j) {
+            o[j] = *reinterpret_cast<const f32x4 *>(&tile[(8 * j + sf) * kTileRow + 4 * sseg]);
+            if (kBias) o[j] = o[j] + bv;
+        }
+        float *dst = out + (frame0 + sf) * static_cast<int64_t>(hidden) + 32 * t + 4 * sseg;
+        const int64_t jstride = 8 * static_cast<int64_t>(hidden);
+        if (all_in) {
+#pragma unroll
+            for (int j = 0; j < 4 * kOutGroups; ++j) *reinterpret_cast<f32x4 *>(dst + j * jstride) = o[j];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4 * kOutGroups; ++j)
+                if (frame0 + 8 * j + sf < n_frames) *reinterpret_cast<f32x4 *>(dst + j * jstride) = o[j];
         }
         // every lane has read the tile before the next tile overwrites it
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+    };
+    auto load_bias = [&](int t, f32x4 &bv) {
+        if (kBias) bv = *reinterpret_cast<const f32x4 *>(bias + 32 * t + 4 * sseg);
+    };
+    // tiles in pairs, the weight and bias registers alternating (no copies)
+    f32x4 wa[8], wb[8];
+    f32x4 ba = {0.0f, 0.0f, 0.0f, 0.0f}, bb = {0.0f, 0.0f, 0.0f, 0.0f};
+    load_bias(0, ba);
+    load_tile(0, wa);
+    for (int t = 0; t < n_tiles; t += 2) {
+        const int t1 = min(t + 1, n_tiles - 1), t2 = min(t + 2, n_tiles - 1);
+        load_bias(t1, bb);
+        load_tile(t1, wb);
+        tile_out(t, wa, ba);
+        load_bias(t2, ba);
+        load_tile(t2, wa);
+        if (t + 1 < n_tiles) tile_out(t + 1, wb, bb);
     }
 }
 
@@ -507,7 +557,7 @@ hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const
                              const float *bias, float *out, hipStream_t stream)
 {
     if (hidden % 32 == 0) {
-        const int64_t per_block = kOutSplitWaves * kFramesPerWave;
+        const int64_t per_block = kOutSplitWaves * kOutWaveFrames;
         const int64_t blocks = (n_frames + per_block - 1) / per_block;
         if (blocks > 0x7fffffff) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kOutSplitWaves);
