@@ -39,9 +39,10 @@ constexpr int kCosDim = 8;
 constexpr float kUnit = 5.9604644775390625e-08f;       // 2^-24
 constexpr float kScoreError = 96.0f * kUnit;
 constexpr float kAmbiguous = 2.0f * kScoreError + 1e-13f;
-// all-stage kernel: scores travel as keys with their 4 low mantissa bits
-// replaced by a per-lane codeword slot, at most 16 ulp (< 32u, as |s| < 2)
-// from the score: 24u + 32u in the worst case, 128u is used
+// all-stage kernel: scores (from the matrix cores, within 42u of exact)
+// travel as keys with their 4 low mantissa bits replaced by the codeword's
+// slot, at most 16 ulp (< 32u, as |s| < 2) from the score: 42u + 32u in the
+// worst case, 128u is used
 constexpr float kKeyScoreError = 128.0f * kUnit;
 constexpr float kKeyAmbiguous = 2.0f * kKeyScoreError + 1e-13f;
 constexpr int kArgChunk = 256;                          // unit codewords per LDS chunk
@@ -316,15 +317,21 @@ void cosine_argmin_kernel(const float *__restrict__ lat, int64_t n_frames, const
 // runs in one kernel: a workgroup of 8 wavefronts owns 32 frames, each
 // wavefront 4 of them with their hidden-width residual rows in VGPRs for all
 // stages, so the residual crosses HBM once in and once out instead of twice
-// per stage. Per stage the workgroup stages W_in[q] (fixed row stride, zero
-// padded) and the stage's unit codewords in fp32 with their half norms in
-// LDS; every LDS value is then used for the 4 frames of a wavefront. The
-// in-projection sums per lane and reduces over the wavefront; the 8
-// projections of a frame are wave-uniform; the scores of codewords
-// lane + 64 m are kept as per-lane best / second and reduced over the
-// wavefront as (best, index, second). The exactness rule and the float64
-// rescan are those of cosine_argmin_kernel; the residual update gathers the
-// table row of the pick (r <- fl32(r - P[q, k])).
+// per stage. Per stage the workgroup stages W_in[q] (padded row stride, zero
+// past `hidden`) and the stage's unit codewords in fp32 with their half
+// norms in LDS; every LDS value is then used for the 4 frames of a
+// wavefront. The in-projection and the scores run on the fp32 matrix cores
+// (v_mfma_f32_4x4x1f32, layout below); each lane keeps best / second keys
+// of its frame for each of its 4 codeword rows, merged over the frame's 16
+// lanes. The exactness rule and the float64 rescan are those of
+// cosine_argmin_kernel: a matrix-core step may round its product and its
+// sum separately (the 9-term sums measured within 3.4u of exact on 4 M
+// random operands), at most 2u per step more than the fused chain's 24u
+// worst case, so a score stays within 42u of its exact value. The
+// residual update gathers the table row of the pick (r <- fl32(r - P[q, k]));
+// the next stage's LDS contents are staged while the picks are decided and
+// those rows are in flight, and at most 128 registers keep four wavefronts
+// per SIMD, so other wavefronts' products hide the gathers' latency.
 // The float held by lane `src` (a constant) on every lane; the readlane
 // builtin moves 32-bit integers, so the value travels as its bit pattern.
 __device__ __forceinline__ float lane_value(float v, int src)
@@ -335,210 +342,227 @@ __device__ __forceinline__ float lane_value(float v, int src)
 constexpr int kFusedWaves = 8;
 constexpr int kFusedFrames = 4;           // frames per wavefront
 constexpr int kFusedMaxCodes = 1024;
+constexpr int kWRow = kProjMaxHidden + 16;   // LDS row stride of W_in: conflict-free operand reads
 
-template <int kT, bool kBias>
-__global__ __attribute__((amdgpu_flat_work_group_size(64 * kFusedWaves, 64 * kFusedWaves)))
+// Lane l = 4 b + j of a wavefront (block b = 0..15, j = 0..3) works on frame
+// j of the wavefront's 4. It holds that frame's residual columns
+// 64 t + 4 b .. 64 t + 4 b + 3 (t < hidden / 64), which are the columns block
+// b of a v_mfma_f32_4x4x1f32 takes: that instruction multiplies, in each of
+// its 16 blocks of 4 lanes, a 4-vector held one entry per lane (A: lane
+// 4 b + i holds row i) by another (B: lane 4 b + j holds column j) and adds
+// the outer product to a 4x4 accumulator of which lane 4 b + j holds column j
+// (register i = row i).
+//   in-projection: rows = outputs (0..3, then 4..7), columns = frames, one
+//     hidden column per block and instruction; the 16 blocks' partial sums
+//     are then added over the wavefront;
+//   scores: rows = codewords 64 s + 4 b + i, columns = frames, one codebook
+//     dimension per instruction, the accumulator starting at the half norms.
+template <int kT4, bool kBias>
+__global__ __attribute__((amdgpu_flat_work_group_size(64 * kFusedWaves, 64 * kFusedWaves),
+                          amdgpu_waves_per_eu(4)))   // <= 128 registers: two workgroups per CU
 void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidden,
                          const float *__restrict__ w_in, const float *__restrict__ b_in,
                          const double *__restrict__ units, const float *__restrict__ table,
                          int n_stages, int n_codes, int32_t *__restrict__ codes, int codes_ld,
                          float *__restrict__ latent, float *__restrict__ residual)
 {
-    __shared__ __align__(16) float s_w[kCosDim * kProjMaxHidden];
-    __shared__ __align__(16) float s_v[kFusedMaxCodes * kCosDim];
+    constexpr int kT = 4 * kT4;   // column groups of 64 (past hidden: zero rows of W, zero residual)
+    __shared__ __align__(16) float s_w[kCosDim * kWRow];
+    __shared__ __align__(16) float s_vlo[kFusedMaxCodes * 4];   // unit codewords, dims 0..3
+    __shared__ __align__(16) float s_vhi[kFusedMaxCodes * 4];   // dims 4..7
     __shared__ __align__(16) float s_hn[kFusedMaxCodes];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
+    const int j = lane & 3;    // frame of this lane; also row i of the A operand
+    const int b = lane >> 2;   // block
     const int64_t frame0 = (static_cast<int64_t>(blockIdx.x) * kFusedWaves + wave) * kFusedFrames;
-    const int cols = hidden >> 2;
-    int ccol[kT];
-    bool inrow[kT];
-#pragma unroll
-    for (int t = 0; t < kT; ++t) {
-        inrow[t] = lane + 64 * t < cols;
-        ccol[t] = min(lane + 64 * t, cols - 1);
-    }
+    const int64_t fr = frame0 + j;
+    const bool valid = fr < n_frames;
+    const int n_col = hidden >> 6;   // column groups in the rows (wave-uniform)
 
-    f32x4 r[kFusedFrames][kT];
+    // residual columns 64 t + 4 b .. +3 of frame j
+    f32x4 r[kT];
+    {
+        const float *row = h + (valid ? fr : 0) * hidden + 4 * b;
 #pragma unroll
-    for (int f = 0; f < kFusedFrames; ++f) {
-        const int64_t fr = frame0 + f;
-        const float *row = h + (fr < n_frames ? fr : 0) * hidden;
-#pragma unroll
-        for (int t = 0; t < kT; ++t) {
-            const f32x4 v = *reinterpret_cast<const f32x4 *>(row + 4 * ccol[t]);
-            r[f][t] = inrow[t] ? v : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        }
+        for (int t = 0; t < kT; ++t)
+            r[t] = (valid && t < n_col) ? *reinterpret_cast<const f32x4 *>(row + 64 * t) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    // lane of output j after the butterfly: bits 5, 4, 3 of the lane are bits 2, 1, 0 of j
+    // after the block reduction lane l holds output o(l) = 4 l5 + 2 l4 + l3 of frame l & 3
     const int out_id = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
     const bool hi32 = lane & 32, hi16 = lane & 16, hi8 = lane & 8;
-    // lane j < 8 stores projection output j, held by lane 32 j2 + 16 j1 + 8 j0
-    const int latent_src = 32 * ((lane >> 2) & 1) + 16 * ((lane >> 1) & 1) + 8 * (lane & 1);
-    const int n_slots = (n_codes + 63) / 64;   // codeword k = lane + 64 m, m < n_slots
-    const bool full = cols == 64 * kT;         // every column slot of a lane is in its row
+    const int n_slots = (n_codes + 63) / 64;   // codeword 64 s + 4 b + i, s < n_slots
 
-    for (int q = 0; q < n_stages; ++q) {
-        __syncthreads();   // the previous stage's LDS contents are no longer read
+    // stage q's W_in rows and unit codewords into LDS
+    auto stage_lds = [&](int q) {
         {
             const float *wq = w_in + static_cast<int64_t>(q) * kCosDim * hidden;
-            for (int i = threadIdx.x; i < kCosDim * 64 * kT; i += 64 * kFusedWaves) {
-                const int o = i / (64 * kT), c4 = i - o * (64 * kT);
-                *reinterpret_cast<f32x4 *>(&s_w[o * kProjMaxHidden + 4 * c4]) =
-                    c4 < cols ? reinterpret_cast<const f32x4 *>(wq)[o * cols + c4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int c4s = hidden >> 2;
+            for (int i = threadIdx.x; i < kCosDim * 16 * kT; i += 64 * kFusedWaves) {
+                const int o = i / (16 * kT), c4 = i - o * (16 * kT);
+                *reinterpret_cast<f32x4 *>(&s_w[o * kWRow + 4 * c4]) =
+                    c4 < c4s ? reinterpret_cast<const f32x4 *>(wq)[o * c4s + c4] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             }
             const double *uq = units + static_cast<int64_t>(q) * n_codes * kCosDim;
-            for (int k = threadIdx.x; k < n_codes; k += 64 * kFusedWaves) {
-                float hn = 0.0f;
+            for (int k = threadIdx.x; k < 64 * n_slots; k += 64 * kFusedWaves) {
+                float v[kCosDim];
+                float hn = FLT_MAX;   // slots past n_codes never win
 #pragma unroll
-                for (int j = 0; j < kCosDim; ++j) {
-                    const float vj = static_cast<float>(uq[static_cast<int64_t>(k) * kCosDim + j]);
-                    s_v[k * kCosDim + j] = vj;
-                    hn = __builtin_fmaf(vj, vj, hn);
+                for (int d = 0; d < kCosDim; ++d) v[d] = 0.0f;
+                if (k < n_codes) {
+                    hn = 0.0f;
+#pragma unroll
+                    for (int d = 0; d < kCosDim; ++d) {
+                        v[d] = static_cast<float>(uq[static_cast<int64_t>(k) * kCosDim + d]);
+                        hn = __builtin_fmaf(v[d], v[d], hn);
+                    }
+                    hn = 0.5f * hn;
                 }
-                s_hn[k] = 0.5f * hn;
-            }
-            // slots up to the next multiple of 64 never win
-            for (int k = n_codes + threadIdx.x; k < 64 * n_slots; k += 64 * kFusedWaves) {
-#pragma unroll
-                for (int j = 0; j < kCosDim; ++j) s_v[k * kCosDim + j] = 0.0f;
-                s_hn[k] = FLT_MAX;
+                *reinterpret_cast<f32x4 *>(&s_vlo[4 * k]) = f32x4{v[0], v[1], v[2], v[3]};
+                *reinterpret_cast<f32x4 *>(&s_vhi[4 * k]) = f32x4{v[4], v[5], v[6], v[7]};
+                s_hn[k] = hn;
             }
         }
-        __syncthreads();
+    };
+    stage_lds(0);
+    __syncthreads();
 
-        // ---- in-projection of the wavefront's frames ----
-        float a[kFusedFrames][kCosDim];
-#pragma unroll
-        for (int f = 0; f < kFusedFrames; ++f)
-#pragma unroll
-            for (int o = 0; o < kCosDim; ++o) a[f][o] = 0.0f;
+    for (int q = 0; q < n_stages; ++q) {
+        // ---- in-projection on the matrix cores ----
+        f32x4 p_lo = {0.0f, 0.0f, 0.0f, 0.0f}, p_hi = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int t = 0; t < kT; ++t) {
-            f32x4 wv[kCosDim];
+            const f32x4 wl = *reinterpret_cast<const f32x4 *>(&s_w[j * kWRow + 64 * t + 4 * b]);
+            const f32x4 wh = *reinterpret_cast<const f32x4 *>(&s_w[(j + 4) * kWRow + 64 * t + 4 * b]);
 #pragma unroll
-            for (int o = 0; o < kCosDim; ++o)
-                wv[o] = *reinterpret_cast<const f32x4 *>(&s_w[o * kProjMaxHidden + 4 * (lane + 64 * t)]);
-#pragma unroll
-            for (int f = 0; f < kFusedFrames; ++f)
-#pragma unroll
-                for (int o = 0; o < kCosDim; ++o)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) a[f][o] = __builtin_fmaf(wv[o][e], r[f][t][e], a[f][o]);
+            for (int e = 0; e < 4; ++e) {
+                p_lo = __builtin_amdgcn_mfma_f32_4x4x1f32(wl[e], r[t][e], p_lo, 0, 0, 0);
+                p_hi = __builtin_amdgcn_mfma_f32_4x4x1f32(wh[e], r[t][e], p_hi, 0, 0, 0);
+            }
+            // one column group's weights live at a time
+            __builtin_amdgcn_sched_barrier(0);
         }
-        float e_own[kFusedFrames];   // this lane's output out_id of each frame, bias added
+        // sum over the 16 blocks: a butterfly that halves the outputs each lane carries
+        float ev;
+        {
+            float c[4], d2[2];
+            const float a[8] = {p_lo[0], p_lo[1], p_lo[2], p_lo[3], p_hi[0], p_hi[1], p_hi[2], p_hi[3]};
 #pragma unroll
-        for (int f = 0; f < kFusedFrames; ++f) {
-            float b[4], c[2];
+            for (int m = 0; m < 4; ++m) {
+                const float give = hi32 ? a[m] : a[m + 4];
+                c[m] = (hi32 ? a[m + 4] : a[m]) + __shfl_xor(give, 32);
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const float give = hi16 ? c[m] : c[m + 2];
+                d2[m] = (hi16 ? c[m + 2] : c[m]) + __shfl_xor(give, 16);
+            }
+            const float give = hi8 ? d2[0] : d2[1];
+            ev = (hi8 ? d2[1] : d2[0]) + __shfl_xor(give, 8);
+            ev += __shfl_xor(ev, 4);
+            if (kBias) ev += b_in[q * kCosDim + out_id];
+        }
+        // this lane's frame's 8 projections: output o of frame j sits in lane
+        // 32 o2 + 16 o1 + 8 o0 + j
+        float e8[kCosDim];
+#pragma unroll
+        for (int o = 0; o < kCosDim; ++o) e8[o] = __shfl(ev, 32 * ((o >> 2) & 1) + 16 * ((o >> 1) & 1) + 8 * (o & 1) + j);
+        if (valid && (lane & 4) == 0)
+            latent[(static_cast<int64_t>(q) * n_frames + fr) * kCosDim + out_id] = ev;
+        float ss = 0.0f;
+#pragma unroll
+        for (int o = 0; o < kCosDim; ++o) ss = __builtin_fmaf(e8[o], e8[o], ss);
+        // outside [1e-30, 1e30] the float64 rescan decides; inside, 1/sqrt
+        // within 1 ulp keeps every element of u within 8u
+        const bool norm_ok = ss >= 1e-30f && ss <= 1e30f;
+        const float inv = __builtin_amdgcn_rsqf(norm_ok ? ss : 1.0f);
+        float nu[kCosDim];   // -u32 of frame j
+#pragma unroll
+        for (int o = 0; o < kCosDim; ++o) nu[o] = -(e8[o] * inv);
+
+        // ---- scores on the matrix cores: per lane, codewords 64 s + 4 b + i of frame j ----
+        // keys: the score with its 4 low mantissa bits replaced by s, kept per i
+        float best[4], second[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            best[i] = INFINITY;
+            second[i] = INFINITY;
+        }
+        for (int sl = 0; sl < n_slots; ++sl) {
+            const int k = 64 * sl + 4 * b + j;   // this lane's A row: codeword 64 s + 4 b + (lane & 3)
+            const f32x4 vl = *reinterpret_cast<const f32x4 *>(&s_vlo[4 * k]);
+            const f32x4 vh = *reinterpret_cast<const f32x4 *>(&s_vhi[4 * k]);
+            f32x4 sc = *reinterpret_cast<const f32x4 *>(&s_hn[64 * sl + 4 * b]);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) sc = __builtin_amdgcn_mfma_f32_4x4x1f32(vl[d], nu[d], sc, 0, 0, 0);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) sc = __builtin_amdgcn_mfma_f32_4x4x1f32(vh[d], nu[4 + d], sc, 0, 0, 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float give = hi32 ? a[f][i] : a[f][i + 4];
-                b[i] = (hi32 ? a[f][i + 4] : a[f][i]) + __shfl_xor(give, 32);
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const float give = hi16 ? b[i] : b[i + 2];
-                c[i] = (hi16 ? b[i + 2] : b[i]) + __shfl_xor(give, 16);
-            }
-            float d;
-            {
-                const float give = hi8 ? c[0] : c[1];
-                d = (hi8 ? c[1] : c[0]) + __shfl_xor(give, 8);
-            }
-            d += __shfl_xor(d, 4);
-            d += __shfl_xor(d, 2);
-            d += __shfl_xor(d, 1);
-            e_own[f] = kBias ? d + b_in[q * kCosDim + out_id] : d;
-        }
-
-        // ---- per frame: projection (uniform), normalization, scores ----
-        float nu[kFusedFrames][kCosDim];   // -u32, wave-uniform
-        bool norm_ok[kFusedFrames];
-#pragma unroll
-        for (int f = 0; f < kFusedFrames; ++f) {
-            float ev[kCosDim];
-#pragma unroll
-            for (int j = 0; j < kCosDim; ++j)
-                ev[j] = lane_value(e_own[f], 32 * ((j >> 2) & 1) + 16 * ((j >> 1) & 1) + 8 * (j & 1));
-            const int64_t fr = frame0 + f;
-            const float mine = __shfl(e_own[f], latent_src);
-            if (fr < n_frames && lane < kCosDim) latent[(static_cast<int64_t>(q) * n_frames + fr) * kCosDim + lane] = mine;
-            float ss = 0.0f;
-#pragma unroll
-            for (int j = 0; j < kCosDim; ++j) ss = __builtin_fmaf(ev[j], ev[j], ss);
-            // outside [1e-30, 1e30] the float64 rescan decides; inside, 1/sqrt
-            // within 1 ulp keeps every element of u within 8u
-            norm_ok[f] = ss >= 1e-30f && ss <= 1e30f;
-            const float inv = __builtin_amdgcn_rsqf(norm_ok[f] ? ss : 1.0f);
-#pragma unroll
-            for (int j = 0; j < kCosDim; ++j) nu[f][j] = -(ev[j] * inv);
-        }
-        float best[kFusedFrames], second[kFusedFrames];   // keys
-#pragma unroll
-        for (int f = 0; f < kFusedFrames; ++f) {
-            best[f] = INFINITY;
-            second[f] = INFINITY;
-        }
-        for (int m = 0; m < n_slots; ++m) {
-            const int k = lane + 64 * m;
-            const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&s_v[k * kCosDim]);
-            const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&s_v[k * kCosDim + 4]);
-            const float hn = s_hn[k];
-#pragma unroll
-            for (int f = 0; f < kFusedFrames; ++f) {
-                float s = hn;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s = __builtin_fmaf(nu[f][j], v0[j], s);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s = __builtin_fmaf(nu[f][j + 4], v1[j], s);
-                const float key = __uint_as_float((__float_as_uint(s) & ~15u) | static_cast<unsigned>(m));
-                second[f] = __builtin_amdgcn_fmed3f(key, best[f], second[f]);
-                best[f] = __builtin_amdgcn_fmed3f(key, best[f], -FLT_MAX);   // min (keys are finite)
+                const float key = __uint_as_float((__float_as_uint(sc[i]) & ~15u) | static_cast<unsigned>(sl));
+                second[i] = __builtin_amdgcn_fmed3f(key, best[i], second[i]);
+                best[i] = __builtin_amdgcn_fmed3f(key, best[i], -FLT_MAX);   // min (keys are finite)
             }
         }
 
-        // ---- per frame: wavefront argmin, exactness check, update ----
+        // the next stage's LDS contents are staged while this stage's picks are
+        // decided and their table rows fetched
+        __syncthreads();   // every wavefront has read this stage's LDS contents
+        if (q + 1 < n_stages) stage_lds(q + 1);
+
+        // ---- per frame: argmin over the wavefront's 16 lanes of the frame ----
+        float bv = fminf(fminf(best[0], best[1]), fminf(best[2], best[3]));
+        float sv;
+        {
+            // second smallest of the 8 (best, second) keys of this lane
+            const float m01 = fmaxf(best[0], best[1]), m23 = fmaxf(best[2], best[3]);
+            const float lo01 = fminf(best[0], best[1]), lo23 = fminf(best[2], best[3]);
+            sv = fminf(fminf(fminf(second[0], second[1]), fminf(second[2], second[3])),
+                       fminf(fminf(m01, m23), fmaxf(lo01, lo23)));
+        }
+        const float own = bv;
+#pragma unroll
+        for (int off = 4; off < 64; off <<= 1) {
+            const float ob = __shfl_xor(bv, off);
+            const float os = __shfl_xor(sv, off);
+            sv = fminf(fminf(sv, os), fmaxf(bv, ob));
+            bv = fminf(bv, ob);
+        }
+        // the codeword of the smallest key: the lowest block, then the lowest i,
+        // holding it (equal keys share the slot bits, so that is the lowest codeword)
+        int li = 4;
+#pragma unroll
+        for (int i = 3; i >= 0; --i) li = best[i] == bv ? i : li;
+        const bool ambiguous = valid && (!norm_ok || !(sv - bv > kKeyAmbiguous));
+        const uint64_t amb = __ballot(ambiguous);
+        const uint64_t has = __ballot(own == bv);
+        int pick_of[kFusedFrames];
 #pragma unroll
         for (int f = 0; f < kFusedFrames; ++f) {
-            float bv = best[f], sv = second[f];
-            const float own = bv;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ob = __shfl_xor(bv, off);
-                const float os = __shfl_xor(sv, off);
-                // second: the smaller of both seconds and the larger best (med3
-                // with -FLT_MAX / FLT_MAX is min / max here: bests are finite,
-                // seconds finite or +inf)
-                sv = __builtin_amdgcn_fmed3f(__builtin_amdgcn_fmed3f(sv, os, -FLT_MAX),
-                                             __builtin_amdgcn_fmed3f(bv, ob, FLT_MAX), -FLT_MAX);
-                bv = __builtin_amdgcn_fmed3f(bv, ob, -FLT_MAX);
-            }
-            // the lowest lane holding the smallest key (equal keys: equal slot,
-            // so the lowest lane is the lowest codeword)
-            const int wl = __ffsll(static_cast<unsigned long long>(__ballot(own == bv))) - 1;
-            int pick = wl + 64 * static_cast<int>(__float_as_uint(bv) & 15u);
-            const int64_t fr = frame0 + f;
-            const bool ambiguous = !norm_ok[f] || !(sv - bv > kKeyAmbiguous);
-            if (ambiguous) {   // wave-uniform: the float64 rescan of the oracle's formula
+            const uint64_t m = has & (0x1111111111111111ull << f);
+            const int wl = m ? __ffsll(static_cast<unsigned long long>(m)) - 1 : f;
+            const int slot = static_cast<int>(__float_as_uint(lane_value(bv, f)) & 15u);
+            pick_of[f] = 64 * slot + 4 * (wl >> 2) + __builtin_amdgcn_readlane(li, wl);
+            if ((amb >> f) & 1ull) {   // wave-uniform: the float64 rescan of the oracle's formula
                 double u[kCosDim];
                 double uss = 0.0;
-                // from the projection itself (the latent written above), not the fp32 unit vector
 #pragma unroll
-                for (int j = 0; j < kCosDim; ++j) {
-                    const double ej = static_cast<double>(
-                        lane_value(e_own[f], 32 * ((j >> 2) & 1) + 16 * ((j >> 1) & 1) + 8 * (j & 1)));
-                    u[j] = ej;
-                    uss = __dadd_rn(uss, __dmul_rn(ej, ej));
+                for (int o = 0; o < kCosDim; ++o) {
+                    // output o of frame f, where the block sum left it
+                    const double eo = static_cast<double>(
+                        lane_value(ev, 32 * ((o >> 2) & 1) + 16 * ((o >> 1) & 1) + 8 * (o & 1) + f));
+                    u[o] = eo;
+                    uss = __dadd_rn(uss, __dmul_rn(eo, eo));
                 }
                 double norm = __builtin_sqrt(uss);
                 if (norm < 1e-12) norm = 1e-12;
 #pragma unroll
-                for (int j = 0; j < kCosDim; ++j) u[j] = u[j] / norm;
+                for (int o = 0; o < kCosDim; ++o) u[o] = u[o] / norm;
                 const double *uq = units + static_cast<int64_t>(q) * n_codes * kCosDim;
                 double bd = INFINITY;
                 int bkk = 0x7fffffff;
-                for (int k = lane; k < n_codes; k += 64) {
+                for (int k = lane; k < n_codes; k += 64) {   // k ascends per lane: strict "<" keeps the lowest
                     const double dd = unit_distance(u, uq, k);
                     if (dd < bd) {
                         bd = dd;
@@ -554,43 +578,36 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
                         bkk = oi;
                     }
                 }
-                pick = bkk;
+                pick_of[f] = bkk;
             }
             // a non-finite frame's pick is unspecified; clamped, so that the
             // table row read below exists
-            pick = __builtin_amdgcn_readfirstlane(min(max(pick, 0), n_codes - 1));
-            if (fr < n_frames && lane == 0) codes[fr * codes_ld + q] = pick;
-            const float *prow = table + (static_cast<int64_t>(q) * n_codes + pick) * hidden;
-            if (full) {
+            pick_of[f] = __builtin_amdgcn_readfirstlane(min(max(pick_of[f], 0), n_codes - 1));
+        }
+        const int pick = j == 0 ? pick_of[0] : j == 1 ? pick_of[1] : j == 2 ? pick_of[2] : pick_of[3];
+        if (valid && b == 0) codes[fr * codes_ld + q] = pick;
+        // r <- fl32(r - P[q, pick]) over this lane's columns
+        const float *prow = table + (static_cast<int64_t>(q) * n_codes + pick) * hidden + 4 * b;
 #pragma unroll
-                for (int t = 0; t < kT; ++t) {
-                    const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * ccol[t]);
+        for (int t = 0; t < kT; ++t) {
+            if (t < n_col) {
+                const f32x4 pv = *reinterpret_cast<const f32x4 *>(prow + 64 * t);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) r[f][t][e] = r[f][t][e] - p[e];
-                }
-            } else {
-#pragma unroll
-                for (int t = 0; t < kT; ++t) {
-                    const f32x4 p = *reinterpret_cast<const f32x4 *>(prow + 4 * ccol[t]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) r[f][t][e] = inrow[t] ? r[f][t][e] - p[e] : 0.0f;
-                }
+                for (int e = 0; e < 4; ++e) r[t][e] = r[t][e] - pv[e];
             }
         }
+        __syncthreads();   // the next stage's LDS contents are in place
     }
 
-#pragma unroll
-    for (int f = 0; f < kFusedFrames; ++f) {
-        const int64_t fr = frame0 + f;
-        if (fr >= n_frames) continue;
-        float *row = residual + fr * hidden;
+    if (valid) {
+        float *row = residual + fr * hidden + 4 * b;
 #pragma unroll
         for (int t = 0; t < kT; ++t)
-            if (inrow[t]) *reinterpret_cast<f32x4 *>(row + 4 * ccol[t]) = r[f][t];
+            if (t < n_col) *reinterpret_cast<f32x4 *>(row + 64 * t) = r[t];
     }
 }
 
-template <int kT>
+template <int kT4>
 hipError_t launch_fused_t(const float *h, int64_t n_frames, int hidden, const float *w_in, const float *b_in,
                           const double *units, const float *table, int n_stages, int n_codes, int32_t *codes,
                           int codes_ld, float *latent, float *residual, hipStream_t stream)
@@ -600,10 +617,10 @@ hipError_t launch_fused_t(const float *h, int64_t n_frames, int hidden, const fl
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kFusedWaves);
     if (b_in)
-        hipLaunchKernelGGL((cosine_fused_kernel<kT, true>), grid, block, 0, stream, h, n_frames, hidden, w_in, b_in,
+        hipLaunchKernelGGL((cosine_fused_kernel<kT4, true>), grid, block, 0, stream, h, n_frames, hidden, w_in, b_in,
                            units, table, n_stages, n_codes, codes, codes_ld, latent, residual);
     else
-        hipLaunchKernelGGL((cosine_fused_kernel<kT, false>), grid, block, 0, stream, h, n_frames, hidden, w_in,
+        hipLaunchKernelGGL((cosine_fused_kernel<kT4, false>), grid, block, 0, stream, h, n_frames, hidden, w_in,
                            b_in, units, table, n_stages, n_codes, codes, codes_ld, latent, residual);
     return hipGetLastError();
 }
