@@ -224,9 +224,13 @@ __device__ __forceinline__ void step_group(f32x16 (&dn)[2], const f32x16 (&dp)[2
                 scan_pair(dp, v + 2 * i, gbits, mask, ks);
                 // keep the updates here, between the matrix steps (the
                 // compiler would otherwise sink the second and third chains
-                // past the group), after every second pair so that their
-                // updates still merge into v_min3
-                if (((v >> 1) + i) & 1) asm volatile("" : "+v"(ks.best), "+v"(ks.second), "+v"(ks.third));
+                // past the group), after every second pair so that the
+                // third's updates still merge into v_min3; the second key
+                // feeds the third's update, so it stays in place unpinned
+                // (a pinned value is opaque to the compiler, which then
+                // canonicalizes it before every minimum: one more
+                // instruction per pair)
+                if (((v >> 1) + i) & 1) asm volatile("" : "+v"(ks.best), "+v"(ks.third));
             }
         }
         v += 2 * pairs;
