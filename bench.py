@@ -16,7 +16,10 @@ after a 1 GiB flush (median and min of 20), and the fp32-scored encode.
 Then W untimed steps (100 by default), then K timed steps (100) between
 ``torch.cuda.synchronize()`` calls. Per-launch kernel times come from HIP
 events recorded on the stream the kernels run on (torch's current
-stream, which is the stream handed to the C ABI).
+stream, which is the stream handed to the C ABI): around every timed
+encode (the roofline's kernel), and around the preparation and the decode
+on 20 instrumented steps after the timed ones, since each recorded event
+adds a few microseconds between the kernels of a step.
 
 Prints one JSON line with the throughput, the roofline of the dominant
 kernel (the encode on the fp16 matrix cores: spec and measured peaks,
@@ -928,15 +931,27 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The timed steps record events around the encode only (each recorded event is one more packet on
+    # the stream, a few microseconds between the kernels); the codebook preparation and the decode
+    # are timed on separate instrumented steps right after.
+    enc_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(events[i])
+        rvq.rvq_prepare_codebooks(bg, prepared)
+        enc_events[i][0].record()
+        rvq.rvq_encode_prepared(xg, bg, prepared, out=(codes, None, residual))
+        enc_events[i][1].record()
+        rvq.rvq_decode(codes, bg, out=out)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in enc_events]))
+    n_inst = min(args.steps, 20)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_inst)]
+    for i in range(n_inst):
+        step(events[i])
+    torch.cuda.synchronize()
     prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    enc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     dec_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
     codes_h = codes.cpu().numpy()
 
@@ -980,6 +995,9 @@ def main():
         "prepare_ms": prep_ms,
         "encode_ms": enc_ms,
         "decode_ms": dec_ms,
+        "timing": "value and ms_per_step: wall clock over the timed steps (prepare + encode + decode, "
+                  "synchronized on both sides); encode_ms: HIP events around each timed encode; "
+                  "prepare_ms and decode_ms: HIP events on 20 instrumented steps after the timed ones",
         "roofline": {"bound": "mfma", "kernel": mm_kernel,
                      "achieved": mm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": mm_tflops / PEAK_F16_MFMA_TFLOPS,
