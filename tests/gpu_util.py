@@ -1,10 +1,13 @@
 """Shared helpers for the GPU parity tests (HIP path vs CPU oracle)."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
+import stage_dump
 
 HAS_GPU = torch.cuda.is_available()
 needs_gpu = pytest.mark.skipif(not HAS_GPU, reason="no GPU visible")
@@ -87,6 +90,9 @@ def check_encode(x, books, n_stages=None, idx=None, roundtrip=True, scoring="def
     gc = codes[sel]
     mism = (gc != oc).any(axis=1)
     ties = oracle.near_tie(best, second)
+    if os.environ.get("RVQ_DUMP"):   # per-stage dump before any assertion
+        test = os.environ.get("PYTEST_CURRENT_TEST", "encode").split(" ")[0]
+        stage_dump.write(os.environ["RVQ_DUMP"], f"{test}_{scoring}", sel, gc, oc, best, second, ties)
     report = {"frames": int(sel.size), "mismatch_frames": int(mism.sum()),
               "near_tie_frames": int(ties.any(axis=1).sum())}
     if mism.any():
