@@ -21,13 +21,16 @@
 // line-wide through LDS; linear_out_kernel, on v_mfma_f32_32x32x2_f32,
 // remains for hidden sizes that are not a multiple of 32.
 //
-// Both kernels put weight rows on the M side and 32 frames per wavefront on
-// the N side, stream the weights through LDS (padded rows, double buffered,
-// shared by the wavefronts of a workgroup; split into 8-column groups of 8
-// high, 8 middle and 8 low parts for linear_in) and keep the frame operand
-// in VGPRs. Lanes 0-31 supply one 32-wide half of each 64-wide chunk of the
-// contraction, lanes 32-63 the other. Results are fp32 sums in the matrix
-// core's order, the bias added last.
+// linear_in and the fp32 linear_out_kernel put weight rows on the M side and
+// 32 frames per wavefront on the N side, stream the weights through LDS
+// (padded rows, double buffered, shared by the wavefronts of a workgroup;
+// split into 8-column groups of 8 high, 8 middle and 8 low parts for
+// linear_in) and keep the frame operand in VGPRs; linear_out_split_kernel
+// (below) has every wavefront load and split its own weight tiles and
+// carries two 32-frame groups. Lanes 0-31 supply one 32-wide half of each
+// 64-wide chunk of the contraction, lanes 32-63 the other (one 8-wide half
+// of each 16-wide step in the split fc2). Results are fp32 sums in the
+// matrix core's order, the bias added last.
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
