@@ -1006,6 +1006,10 @@ def main():
                      "contraction_dtype": "fp16" if wide else "bf16 (3-way split)",
                      "decision": "float64 re-rank of every candidate within the proven fp16 error bound; "
                                  "codes equal the oracle's float64 argmin",
+                     "limiter": ("vector-ALU issue, not the matrix cores: every score's packed (score, index) "
+                                 "key is updated on the VALU (about 3 instructions per score, half the SIMD "
+                                 "cycles in the rocprofv3 issue counters against a quarter for the matrix "
+                                 "cores)" if wide else "matrix cores and the per-stage decision"),
                      "results_dtype": "f32 residual and reconstruction, i32 codes"},
         "encode_fp32_equivalent": {"achieved": enc_flop / (enc_ms * 1e-3) / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
                                    "unit": "TFLOP/s", "work_per_launch": f"2*Q*K*D*N = {enc_flop:.4g} flop"},
