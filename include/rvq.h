@@ -248,7 +248,9 @@ RVQ_API rvq_status rvq_encode_noalloc(const float *x, int64_t n_frames, int32_t 
  *   w_out        [hidden, dim]  PyTorch (out, in) order; b_out [hidden] or NULL
  *   codes, latent, latent_recon, h_recon: caller-allocated outputs
  *
- * The linear layers are fp32 sums on the matrix cores (bias added last);
+ * The linear layers are fp32 sums on the matrix cores (bias added last):
+ * fc as accurate as an fp32 contraction, fc2 within 3.01 * 2^-22 of
+ * sum_k |x_k w_k| per output beyond the fp32 accumulation's own error;
  * encode and decode keep the contract above, applied to `latent`.
  * hidden must be a positive multiple of 64 (RVQ_ERR_UNSUPPORTED otherwise).
  */

@@ -17,9 +17,13 @@
 // v_m w_l + v_l w_m + v_l w_l are at most 2^-23 |v w|, the size of one fp32
 // rounding, so the result is as accurate as an fp32 contraction; six
 // v_mfma_f32_32x32x16_bf16 do the work of eight fp32 32x32x2 steps. fc2
-// uses the same split (linear_out_split_kernel) with its stores made
-// line-wide through LDS; linear_out_kernel, on v_mfma_f32_32x32x2_f32,
-// remains for hidden sizes that are not a multiple of 32.
+// (linear_out_split_kernel), whose frame operand and weight tiles are
+// small enough to scale by a power of two before splitting, takes a
+// two-part fp16 split instead (three v_mfma_f32_32x32x16_f16 per step,
+// each product within 3.01 * 2^-22 of exact; bound below) and makes its
+// stores line-wide through LDS; linear_out_kernel, on
+// v_mfma_f32_32x32x2_f32, remains for hidden sizes that are not a multiple
+// of 32.
 //
 // linear_in and the fp32 linear_out_kernel put weight rows on the M side and
 // 32 frames per wavefront on the N side, stream the weights through LDS
@@ -30,7 +34,8 @@
 // carries two 32-frame groups. Lanes 0-31 supply one 32-wide half of each
 // 64-wide chunk of the contraction, lanes 32-63 the other (one 8-wide half
 // of each 16-wide step in the split fc2). Results are fp32 sums in the
-// matrix core's order, the bias added last.
+// matrix core's order, the bias added last (in fc2 with the scale undone in
+// the same rounding).
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -372,20 +377,35 @@ void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden
     }
 }
 
-// ---- linear_out on bf16 matrix cores at fp32 accuracy ----------------------
+// ---- linear_out on fp16 matrix cores in a scaled two-part split -----------
 //
-// The same contraction as linear_out_kernel, in the three-part bf16 split
-// of linear_in (six v_mfma_f32_32x32x16_bf16 per 16-wide step instead of
-// eight fp32 32x32x2 products: 2.7 times less matrix-core time, which bounds
-// fc2 on fp32 matrix cores). Every wavefront is independent -- no barrier:
-// it holds the split operand of two groups of 32 frames in VGPRs, and for
-// each tile of 32 outputs loads the 32 weight rows' fp32 values of its
-// lanes (128 B per lane, from L2) and splits them once for both groups,
-// whose two product chains are interleaved (half the weight loads and
-// splits per output of one group per wavefront). Each 32x32 result goes
-// through a wavefront-private LDS tile so that each store instruction
-// writes 8 frames x 128 contiguous bytes (whole cache lines) instead of
-// 32 frames x 32 bytes.
+// The same contraction as linear_out_kernel. Every operand value is scaled
+// by a power of two and split into two fp16 parts: with v' = 2^e v (exact),
+// v_h = fp16(v') and v_l = fp16(v' - v_h) (the difference is exact in fp32),
+// v' = v_h + v_l + d with |d| <= 2^-22 |v'| + 2^-25. A product x' w' is
+// summed as x_l w_h + x_h w_l + x_h w_h (fp16 x fp16 products are exact in
+// fp32); what is dropped, x_l w_l and the d terms, is at most
+// 3.01 * 2^-22 |x' w'| + 2^-25 (|x'| + |w'|). The exponents put the largest
+// magnitude of each frame's 64 values, and of each tile's 32 x 64 weights,
+// in [2^14, 2^15): no part overflows, and the 2^-25 terms stay below 2^-37
+// of the largest product of the frame and tile. So each output carries at
+// most 3.01 * 2^-22 of sum |x_k w_k| beyond the fp32 accumulation's own
+// error (a fifth of the worst-case bound of a 64-term fp32 sum), with three
+// v_mfma_f32_32x32x16_f16 per 16-wide step instead of eight fp32 32x32x2
+// products. The scale 2^-(e_frame + e_tile) is undone in the bias step:
+// one fused multiply-add by an exact power of two, so the result is the
+// accumulated sum scaled back and the bias added with one rounding.
+//
+// The four wavefronts of a workgroup share 64 frames (two groups of 32)
+// and take every fourth tile of 32 outputs, so that together they write
+// neighbouring 128 B pieces of the same rows; each is otherwise independent
+// (no barrier): it holds the split operand of both groups in VGPRs, and for
+// each of its tiles loads the 32 weight rows' fp32 values of its lanes
+// (128 B per lane, from L2) and splits them once for both groups, whose
+// product chains are interleaved. Each 32x32 result goes through a
+// wavefront-private LDS tile so that each store instruction writes 8 frames
+// x 128 contiguous bytes (whole cache lines) instead of 32 frames x 32
+// bytes.
 //
 // Loads and stores share one in-order completion counter, so a wait for a
 // load issued after a store also waits for the store. The next tile's bias
@@ -400,6 +420,49 @@ constexpr int kOutGroups = 2;                              // groups of 32 frame
 constexpr int kOutWaveFrames = kOutGroups * kFramesPerWave;
 constexpr int kTileRow = 36;   // floats per LDS tile row (32 outputs + pad)
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct Split2 {
+    f16x8 h, l;
+};
+
+// 2^e v of 8 values in two fp16 parts (v_h + v_l).
+__device__ __forceinline__ Split2 split2(const float *v, int e)
+{
+    f16x8 hp, lp;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float s = __builtin_amdgcn_ldexpf(v[t], e);
+        const _Float16 h = static_cast<_Float16>(s);
+        hp[t] = h;
+        lp[t] = static_cast<_Float16>(s - static_cast<float>(h));
+    }
+    return {hp, lp};
+}
+
+// The exponent e that puts m (>= 0) in [2^14, 2^15) as 2^e m; 15 for m = 0
+// or a non-finite m (whose values stay non-finite).
+__device__ __forceinline__ int scale_exponent(float m) { return 15 - __builtin_amdgcn_frexp_expf(m); }
+
+__device__ __forceinline__ float wave_max(float m)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+    return m;
+}
+__device__ __forceinline__ int wave_min_int(int m)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = min(m, __shfl_xor(m, off));
+    return m;
+}
+__device__ __forceinline__ int wave_max_int(int m)
+{
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = max(m, __shfl_xor(m, off));
+    return m;
+}
+
 template <bool kBias>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kOutSplitWaves, 64 * kOutSplitWaves),
                           amdgpu_waves_per_eu(2)))   // at most 256 registers: no spills
@@ -412,29 +475,43 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
     const int wave = threadIdx.x >> 6;
     const int col = lane & 31;
     const int half = lane >> 5;
-    const int64_t frame0 = (static_cast<int64_t>(blockIdx.x) * kOutSplitWaves + wave) * kOutWaveFrames;
+    const int64_t frame0 = static_cast<int64_t>(blockIdx.x) * kOutWaveFrames;   // shared by the workgroup
     float *tile = s_tile[wave];
 
-    // B operand of group g: frame 32 g + col, dims 16 s + 8 half .. +7 of step s, split once
-    Split3 xb[kOutGroups][4];
+    // B operand of group g: frame 32 g + col, dims 16 s + 8 half .. +7 of step s,
+    // scaled by the frame's 2^ef[g] and split once
+    Split2 xb[kOutGroups][4];
+    int ef[kOutGroups];
 #pragma unroll
     for (int g = 0; g < kOutGroups; ++g) {
         const int64_t frame = frame0 + 32 * g + col;
         const bool valid = frame < n_frames;
         const float *src = x + (valid ? frame : 0) * kDim + 8 * half;
+        float v[4][8];
+        float m = 0.0f;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            float v[8];
             const f32x4 a = *reinterpret_cast<const f32x4 *>(src + 16 * s);
             const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 16 * s + 4);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                v[e] = valid ? a[e] : 0.0f;
-                v[4 + e] = valid ? b[e] : 0.0f;
+                v[s][e] = valid ? a[e] : 0.0f;
+                v[s][4 + e] = valid ? b[e] : 0.0f;
             }
-            xb[g][s] = split3(v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[s][e]));
         }
+        m = fmaxf(m, __shfl_xor(m, 32));
+        ef[g] = scale_exponent(m);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xb[g][s] = split2(v[s], ef[g]);
     }
+    // store j of a tile: frame 8 j + lane / 8 (group j / 4), outputs 4 (lane % 8) .. +3
+    const int sf = lane >> 3, sseg = lane & 7;
+    int efs[4 * kOutGroups];   // exponent of the frame of store j
+#pragma unroll
+    for (int j = 0; j < 4 * kOutGroups; ++j) efs[j] = __shfl(ef[j >> 2], 8 * (j & 3) + sf);
+    const int ef_lo = wave_min_int(min(ef[0], ef[1])), ef_hi = wave_max_int(max(ef[0], ef[1]));
 
     // A operand of tile t: weight row 32 t + col, dims 16 s + 8 half .. +7
     auto load_tile = [&](int t, f32x4 (&wv)[8]) {
@@ -446,30 +523,28 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
         }
     };
     const int n_tiles = hidden / 32;
-    // store j of a tile: frame 8 j + lane / 8, outputs 4 (lane % 8) .. +3
-    const int sf = lane >> 3, sseg = lane & 7;
     const bool all_in = frame0 + kOutWaveFrames <= n_frames;   // wave-uniform
     // products and stores of tile t from its weights wv and bias bv
     auto tile_out = [&](int t, const f32x4 (&wv)[8], const f32x4 &bv) {
+        float m = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(wv[i][e]));
+        const int et = scale_exponent(wave_max(m));
         f32x16 acc[kOutGroups] = {};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             const float v[8] = {wv[2 * s][0], wv[2 * s][1], wv[2 * s][2], wv[2 * s][3],
                                 wv[2 * s + 1][0], wv[2 * s + 1][1], wv[2 * s + 1][2], wv[2 * s + 1][3]};
-            const Split3 a = split3(v);
-            // mfma6's six products in its order, the two groups' chains interleaved
+            const Split2 a = split2(v, et);
+            // small products first, the two groups' chains interleaved
 #pragma unroll
-            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, xb[g][s].l, acc[g], 0, 0, 0);
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.l, xb[g][s].h, acc[g], 0, 0, 0);
 #pragma unroll
-            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.l, xb[g][s].h, acc[g], 0, 0, 0);
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, xb[g][s].l, acc[g], 0, 0, 0);
 #pragma unroll
-            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.m, xb[g][s].m, acc[g], 0, 0, 0);
-#pragma unroll
-            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, xb[g][s].m, acc[g], 0, 0, 0);
-#pragma unroll
-            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.m, xb[g][s].h, acc[g], 0, 0, 0);
-#pragma unroll
-            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.h, xb[g][s].h, acc[g], 0, 0, 0);
+            for (int g = 0; g < kOutGroups; ++g) acc[g] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, xb[g][s].h, acc[g], 0, 0, 0);
         }
         // lane (col, half) holds outputs 8 m + 4 half .. +3 (m < 4) of frame 32 g + col
 #pragma unroll
@@ -481,12 +556,27 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-        // every row of the tile is read (into its own registers) before any is stored
+        // every row of the tile is read (into its own registers) before any is
+        // stored; scaled back by 2^-(ef + et) with the bias added: one fused
+        // multiply-add by an exact power of two while every such factor is a
+        // float (2^-149 .. 2^127), else the scaling and the bias apart
+        const bool one_step = et + ef_hi <= 149 && et + ef_lo >= -127;   // wave-uniform
         f32x4 o[4 * kOutGroups];
 #pragma unroll
         for (int j = 0; j < 4 * kOutGroups; ++j) {
             o[j] = *reinterpret_cast<const f32x4 *>(&tile[(8 * j + sf) * kTileRow + 4 * sseg]);
-            if (kBias) o[j] = o[j] + bv;
+            const int k = -(efs[j] + et);
+            if (one_step) {
+                const float f = __builtin_amdgcn_ldexpf(1.0f, k);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[j][e] = kBias ? __builtin_fmaf(o[j][e], f, bv[e]) : o[j][e] * f;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[j][e] = __builtin_amdgcn_ldexpf(o[j][e], k);
+                    if (kBias) o[j][e] += bv[e];
+                }
+            }
         }
         float *dst = out + (frame0 + sf) * static_cast<int64_t>(hidden) + 32 * t + 4 * sseg;
         const int64_t jstride = 8 * static_cast<int64_t>(hidden);
@@ -508,16 +598,20 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
     // tiles in pairs, the weight and bias registers alternating (no copies)
     f32x4 wa[8], wb[8];
     f32x4 ba = {0.0f, 0.0f, 0.0f, 0.0f}, bb = {0.0f, 0.0f, 0.0f, 0.0f};
-    load_bias(0, ba);
-    load_tile(0, wa);
-    for (int t = 0; t < n_tiles; t += 2) {
-        const int t1 = min(t + 1, n_tiles - 1), t2 = min(t + 2, n_tiles - 1);
+    // wavefront w takes tiles w, w + 4, ...: the four write neighbouring 128 B of the same rows
+    const int W = kOutSplitWaves;
+    if (wave >= n_tiles) return;   // no tile for this wavefront (no barrier follows)
+    const int last = wave + ((n_tiles - 1 - wave) / W) * W;   // this wavefront's last tile (wave < n_tiles)
+    load_bias(min(wave, last), ba);
+    load_tile(min(wave, last), wa);
+    for (int t = wave; t < n_tiles; t += 2 * W) {
+        const int t1 = min(t + W, last), t2 = min(t + 2 * W, last);
         load_bias(t1, bb);
         load_tile(t1, wb);
         tile_out(t, wa, ba);
         load_bias(t2, ba);
         load_tile(t2, wa);
-        if (t + 1 < n_tiles) tile_out(t + 1, wb, bb);
+        if (t + W < n_tiles) tile_out(t + W, wb, bb);
     }
 }
 
@@ -560,7 +654,7 @@ hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const
                              const float *bias, float *out, hipStream_t stream)
 {
     if (hidden % 32 == 0) {
-        const int64_t per_block = kOutSplitWaves * kOutWaveFrames;
+        const int64_t per_block = kOutWaveFrames;
         const int64_t blocks = (n_frames + per_block - 1) / per_block;
         if (blocks > 0x7fffffff) return hipErrorInvalidValue;
         const dim3 grid(static_cast<unsigned>(blocks)), block(64 * kOutSplitWaves);

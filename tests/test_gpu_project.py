@@ -83,3 +83,25 @@ def test_project_unsupported_hidden():
         m.rvq_project_roundtrip(torch.zeros((4, 100), device=d), torch.zeros((64, 100), device=d), None,
                                 torch.zeros((2, 64, 64), device=d), torch.zeros((100, 64), device=d), None)
     assert e.value.status == m.RVQ_ERR_UNSUPPORTED
+
+
+# fc2 scales each frame's 64 values and each 32-row weight tile by a power of
+# two before its fp16 split, and undoes both in the bias step (one fused
+# multiply-add while the combined factor is a float, two steps otherwise).
+# Codebooks and fc2 weights far from 1 move the frame and tile exponents over
+# their range; the first case takes the two-step path (a combined factor
+# below 2^-149), the others the fused one at large exponents of either sign.
+@pytest.mark.parametrize("book_scale,w_scale,bias", [(2.0 ** -60, 2.0 ** -64, False), (1.0, 2.0 ** -100, False),
+                                                     (2.0 ** 40, 2.0 ** -40, True), (2.0 ** 50, 2.0 ** 50, False),
+                                                     (2.0 ** -60, 2.0 ** -64, True)])
+def test_project_fc2_scales(book_scale, w_scale, bias):
+    rng = np.random.default_rng(17)
+    n, hidden = 300, 1024
+    h = rng.standard_normal((n, hidden)).astype(np.float32)
+    w_in = (rng.standard_normal((64, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    books = (rng.standard_normal((4, 256, 64)) * 0.5 ** np.arange(4)[:, None, None] * book_scale).astype(np.float32)
+    w_in = (w_in * np.float32(book_scale)).astype(np.float32)   # latents on the codebooks' scale
+    w_out = (rng.standard_normal((hidden, 64)) / 8.0 * w_scale).astype(np.float32)
+    b_out = (rng.standard_normal(hidden) * book_scale * w_scale).astype(np.float32) if bias else None
+    e1, e3 = check_project(h, w_in, None, books, w_out, b_out)
+    announce("project fc2-scale errors", fc=e1, fc2=e3)
