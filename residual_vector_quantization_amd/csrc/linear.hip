@@ -426,6 +426,11 @@ struct Split2 {
     f16x8 h, l;
 };
 
+template <bool kValue>
+struct Flag {
+    static constexpr bool value = kValue;
+};
+
 // 2^e v of 8 values in two fp16 parts (v_h + v_l).
 __device__ __forceinline__ Split2 split2(const float *v, int e)
 {
@@ -511,7 +516,9 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
     int efs[4 * kOutGroups];   // exponent of the frame of store j
 #pragma unroll
     for (int j = 0; j < 4 * kOutGroups; ++j) efs[j] = __shfl(ef[j >> 2], 8 * (j & 3) + sf);
-    const int ef_lo = wave_min_int(min(ef[0], ef[1])), ef_hi = wave_max_int(max(ef[0], ef[1]));
+    // (read from the first lane: known to the compiler to be the same on every lane)
+    const int ef_lo = __builtin_amdgcn_readfirstlane(wave_min_int(min(ef[0], ef[1])));
+    const int ef_hi = __builtin_amdgcn_readfirstlane(wave_max_int(max(ef[0], ef[1])));
 
     // A operand of tile t: weight row 32 t + col, dims 16 s + 8 half .. +7
     auto load_tile = [&](int t, f32x4 (&wv)[8]) {
@@ -523,15 +530,16 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
         }
     };
     const int n_tiles = hidden / 32;
-    const bool all_in = frame0 + kOutWaveFrames <= n_frames;   // wave-uniform
-    // products and stores of tile t from its weights wv and bias bv
-    auto tile_out = [&](int t, const f32x4 (&wv)[8], const f32x4 &bv) {
+    // products and stores of tile t from its weights wv and bias bv; kAll: all
+    // 64 frames exist, so that every path stores the same number of times
+    auto tile_out = [&](auto all_tag, int t, const f32x4 (&wv)[8], const f32x4 &bv) {
+        constexpr bool kAll = decltype(all_tag)::value;
         float m = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(wv[i][e]));
-        const int et = scale_exponent(wave_max(m));
+        const int et = __builtin_amdgcn_readfirstlane(scale_exponent(wave_max(m)));
         f32x16 acc[kOutGroups] = {};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -560,27 +568,29 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
         // stored; scaled back by 2^-(ef + et) with the bias added: one fused
         // multiply-add by an exact power of two while every such factor is a
         // float (2^-149 .. 2^127), else the scaling and the bias apart
-        const bool one_step = et + ef_hi <= 149 && et + ef_lo >= -127;   // wave-uniform
         f32x4 o[4 * kOutGroups];
 #pragma unroll
-        for (int j = 0; j < 4 * kOutGroups; ++j) {
+        for (int j = 0; j < 4 * kOutGroups; ++j)
             o[j] = *reinterpret_cast<const f32x4 *>(&tile[(8 * j + sf) * kTileRow + 4 * sseg]);
-            const int k = -(efs[j] + et);
-            if (one_step) {
-                const float f = __builtin_amdgcn_ldexpf(1.0f, k);
+        if (et + ef_hi <= 149 && et + ef_lo >= -127) {   // scalar: the same on every lane
+#pragma unroll
+            for (int j = 0; j < 4 * kOutGroups; ++j) {
+                const float f = __builtin_amdgcn_ldexpf(1.0f, -(efs[j] + et));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[j][e] = kBias ? __builtin_fmaf(o[j][e], f, bv[e]) : o[j][e] * f;
-            } else {
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4 * kOutGroups; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    o[j][e] = __builtin_amdgcn_ldexpf(o[j][e], k);
+                    o[j][e] = __builtin_amdgcn_ldexpf(o[j][e], -(efs[j] + et));
                     if (kBias) o[j][e] += bv[e];
                 }
-            }
         }
         float *dst = out + (frame0 + sf) * static_cast<int64_t>(hidden) + 32 * t + 4 * sseg;
         const int64_t jstride = 8 * static_cast<int64_t>(hidden);
-        if (all_in) {
+        if constexpr (kAll) {
 #pragma unroll
             for (int j = 0; j < 4 * kOutGroups; ++j) *reinterpret_cast<f32x4 *>(dst + j * jstride) = o[j];
         } else {
@@ -595,24 +605,41 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
     auto load_bias = [&](int t, f32x4 &bv) {
         if (kBias) bv = *reinterpret_cast<const f32x4 *>(bias + 32 * t + 4 * sseg);
     };
-    // tiles in pairs, the weight and bias registers alternating (no copies)
-    f32x4 wa[8], wb[8];
-    f32x4 ba = {0.0f, 0.0f, 0.0f, 0.0f}, bb = {0.0f, 0.0f, 0.0f, 0.0f};
-    // wavefront w takes tiles w, w + 4, ...: the four write neighbouring 128 B of the same rows
-    const int W = kOutSplitWaves;
+    // Wavefront w takes tiles w, w + 4, ... (the four write neighbouring 128 B
+    // of the same rows), in pairs, the weight and bias registers alternating
+    // (no copies). The loop has no path around either tile of a pair (an odd
+    // last tile follows it), and the workgroup with frames past n_frames runs
+    // its own copy of the loop, so that the compiler's count of the memory
+    // operations issued after a tile's loads is exact.
     if (wave >= n_tiles) return;   // no tile for this wavefront (no barrier follows)
-    const int last = wave + ((n_tiles - 1 - wave) / W) * W;   // this wavefront's last tile (wave < n_tiles)
-    load_bias(min(wave, last), ba);
-    load_tile(min(wave, last), wa);
-    for (int t = wave; t < n_tiles; t += 2 * W) {
-        const int t1 = min(t + W, last), t2 = min(t + 2 * W, last);
-        load_bias(t1, bb);
-        load_tile(t1, wb);
-        tile_out(t, wa, ba);
-        load_bias(t2, ba);
-        load_tile(t2, wa);
-        if (t + W < n_tiles) tile_out(t + W, wb, bb);
-    }
+    const int n_w = (n_tiles - 1 - wave) / kOutSplitWaves + 1;   // tiles of this wavefront
+    auto tile_of = [&](int i) { return wave + kOutSplitWaves * min(i, n_w - 1); };
+    auto run = [&](auto all_tag) {
+        f32x4 wa[8], wb[8];
+        f32x4 ba = {0.0f, 0.0f, 0.0f, 0.0f}, bb = {0.0f, 0.0f, 0.0f, 0.0f};
+        load_bias(tile_of(0), ba);
+        load_tile(tile_of(0), wa);
+        int i = 0;
+        // (scheduling barriers keep each request where it is written: ahead of
+        // the stores that precede its tile)
+        for (; i + 1 < n_w; i += 2) {
+            load_bias(tile_of(i + 1), bb);
+            load_tile(tile_of(i + 1), wb);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_out(all_tag, tile_of(i), wa, ba);
+            __builtin_amdgcn_sched_barrier(0);
+            load_bias(tile_of(i + 2), ba);
+            load_tile(tile_of(i + 2), wa);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_out(all_tag, tile_of(i + 1), wb, bb);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (i < n_w) tile_out(all_tag, tile_of(i), wa, ba);
+    };
+    if (frame0 + kOutWaveFrames <= n_frames)
+        run(Flag<true>{});
+    else
+        run(Flag<false>{});
 }
 
 }  // namespace
