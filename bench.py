@@ -68,6 +68,7 @@ KERNEL_SOURCES = {
     "decode": ["decode.hip"],
     "linear_in": ["linear.hip"],
     "linear_out": ["linear.hip"],
+    "linear_out_touch": ["linear.hip"],
 }
 
 
@@ -157,8 +158,10 @@ def _csv(dirname, suffix):
 def _kernel_of(name):
     if "linear_in_kernel" in name:
         return "linear_in"
-    if "linear_out_kernel" in name or "linear_out_split_kernel" in name:
+    if "linear_out_kernel" in name or "linear_out_split_kernel" in name or "linear_out_res_kernel" in name:
         return "linear_out"
+    if "touch_kernel" in name:
+        return "linear_out_touch"   # fc2's inputs read once ahead of it
     if "encode_f16_kernel" in name:
         return "encode_f16"
     if "encode_bf16_ksplit_kernel" in name:
@@ -264,6 +267,11 @@ def summarize_profiles(w, src_dir):
                              f"{t:.1f} us = {lin_bytes / t / 1e3:.0f} GB/s ({lin_bytes / t / 1e3 / PEAK_HBM_GBPS:.1%} "
                              f"of {PEAK_HBM_GBPS:.0f} GB/s HBM); {lin_flop / t / 1e6:.1f} TFLOP/s of fp32 work "
                              f"(2 hidden D per frame).")
+        if "linear_out" in avg and "linear_out_touch" in avg:
+            t = avg["linear_out"] + avg["linear_out_touch"]
+            lines.append(f"- fc2 with the read of its inputs ahead of it (linear_out_touch, {avg['linear_out_touch']:.1f}"
+                         f" us): {t:.1f} us = {lin_bytes / t / 1e3:.0f} GB/s "
+                         f"({lin_bytes / t / 1e3 / PEAK_HBM_GBPS:.1%} of {PEAK_HBM_GBPS:.0f} GB/s HBM).")
 
     fetch = _counter_means(_csv(os.path.join(src_dir, "fetch"), "counter_collection.csv"), "FETCH_SIZE")
     write = _counter_means(_csv(os.path.join(src_dir, "write"), "counter_collection.csv"), "WRITE_SIZE")
@@ -283,7 +291,8 @@ def summarize_profiles(w, src_dir):
             "encode_fp32": enc_algo, "decode": dec_bytes + 4.0 * q * k * d,
             # fc: h rows in, latent rows out (weights 256 KiB, read once); fc2 the reverse
             "linear_in": (4.0 * hid + 4.0 * d) * n + 4.0 * hid * d,
-            "linear_out": (4.0 * hid + 4.0 * d) * n + 4.0 * hid * d}
+            "linear_out": (4.0 * hid + 4.0 * d) * n + 4.0 * hid * d,
+            "linear_out_touch": 4.0 * d * n}
     lines += ["", "## HBM counters (per launch)", "",
               f"A 512 MiB elementwise copy reads FETCH_SIZE = {fetch['copy']:.0f} KiB and WRITE_SIZE = "
               f"{write['copy']:.0f} KiB, so readings are scaled by {f_scale:.3f} (fetch) and "
@@ -376,6 +385,8 @@ def _trace_work(w):
             "linear_in_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
             "linear_out_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
             "linear_out_split_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
+            "linear_out_res_kernel": (2.0 * hid * 64 * n, "flop", "fp32 matrix flop, 2 hidden 64 per frame"),
+            "touch_kernel": (4.0 * 64 * n, "B", "HBM, fc2's input rows read once ahead of it (4D per frame)"),
             "update_kernel": (8.0 * hid * n, "B", "HBM, residual read + write (8 hidden per frame)"),
             "proj8_kernel": (8.0 * hid * n, "B", "HBM, residual read + write (8 hidden per frame)"),
             "projected_decode_kernel": ((4.0 * q + 4.0 * hid) * n, "B", "HBM, (4Q + 4 hidden) per frame"),

@@ -16,14 +16,15 @@
 // + v_h w_h (bf16 x bf16 products are exact in fp32). The dropped
 // v_m w_l + v_l w_m + v_l w_l are at most 2^-23 |v w|, the size of one fp32
 // rounding, so the result is as accurate as an fp32 contraction; six
-// v_mfma_f32_32x32x16_bf16 do the work of eight fp32 32x32x2 steps. fc2
-// (linear_out_split_kernel), whose frame operand and weight tiles are
-// small enough to scale by a power of two before splitting, takes a
-// two-part fp16 split instead (three v_mfma_f32_32x32x16_f16 per step,
-// each product within 3.01 * 2^-22 of exact; bound below) and makes its
-// stores line-wide through LDS; linear_out_kernel, on
-// v_mfma_f32_32x32x2_f32, remains for hidden sizes that are not a multiple
-// of 32.
+// v_mfma_f32_32x32x16_bf16 do the work of eight fp32 32x32x2 steps. fc2,
+// whose frame operand and weight tiles are small enough to scale by a
+// power of two before splitting, takes a two-part fp16 split instead
+// (three v_mfma_f32_32x32x16_f16 per step, each product within
+// 3.01 * 2^-22 of exact; bound below) and makes its stores line-wide
+// through LDS: linear_out_res_kernel (weights resident in registers) for
+// hidden a multiple of 512, linear_out_split_kernel for other multiples of
+// 32; linear_out_kernel, on v_mfma_f32_32x32x2_f32, remains for hidden
+// sizes that are not a multiple of 32.
 //
 // linear_in and the fp32 linear_out_kernel put weight rows on the M side and
 // 32 frames per wavefront on the N side, stream the weights through LDS
@@ -37,6 +38,8 @@
 // matrix core's order, the bias added last (in fc2 with the scale undone in
 // the same rounding).
 #include <stdint.h>
+
+#include <algorithm>
 
 #include <hip/hip_runtime.h>
 
@@ -421,6 +424,7 @@ constexpr int kOutWaveFrames = kOutGroups * kFramesPerWave;
 constexpr int kTileRow = 36;   // floats per LDS tile row (32 outputs + pad)
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 struct Split2 {
     f16x8 h, l;
@@ -642,6 +646,220 @@ void linear_out_split_kernel(const float *__restrict__ x, int64_t n_frames, int 
         run(Flag<false>{});
 }
 
+// ---- fc2 with the weight split resident in registers ------------------------
+//
+// For hidden a multiple of 512: a workgroup of 16 wavefronts owns 512
+// outputs (wavefront w: tile 16 blockIdx.y + w of 32 outputs), scales and
+// splits its weights once into registers, and then runs through groups of
+// 32 frames (blockIdx.x, + gridDim.x, ...). The whole workgroup stages each
+// group's frame operand: thread i loads two values of frame i / 32, the
+// frame's 32 threads agree on its exponent, and the scaled fp16 parts go
+// to LDS in the matrix-core operand layout (double buffered, one barrier
+// per group). Each wavefront then runs its tile's twelve products, passes
+// the result through its LDS tile and stores 8 frames x 128 B per store
+// instruction; together the 16 write 2 KB of each frame's row. Same
+// arithmetic, bound and rounding as linear_out_split_kernel.
+//
+// The outputs (4 KiB per frame at hidden 1024) are written with
+// non-temporal stores, and the inputs (256 B per frame) are read once by
+// touch_kernel just before, in chunks of at most 2^20 frames (256 MiB, the
+// size of the memory-side cache): the
+// kernel's input reads then come from the memory-side cache instead of
+// reaching DRAM between the output writes, where they cost about a quarter
+// of the kernel's time.
+__global__ __launch_bounds__(256) void touch_kernel(const f32x4 *p, int64_t n4)
+{
+    f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n4;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        a += p[i];
+    asm volatile("" ::"v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]));   // the loads stay
+}
+
+constexpr int kResWaves = 16;
+constexpr int kResFrames = 32;
+
+template <bool kBias>
+__global__ __launch_bounds__(64 * kResWaves)
+void linear_out_res_kernel(const float *__restrict__ x, int64_t n_frames, int hidden,
+                           const float *__restrict__ w, const float *__restrict__ bias,
+                           float *__restrict__ out)
+{
+    // frame operand of a group: [step][part][lane], part 0 = v_h, 1 = v_l
+    __shared__ __align__(16) f16x8 s_b[2][4 * 2 * 64];
+    __shared__ int s_ef[2][kResFrames];   // the frames' exponents
+    __shared__ __align__(16) float s_tile[kResWaves][kResFrames * kTileRow];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int t = blockIdx.y * kResWaves + wave;   // this wavefront's tile (hidden % 512 == 0: all exist)
+    const int64_t n_groups = (n_frames + kResFrames - 1) / kResFrames;
+    const int64_t n_full = n_frames / kResFrames;
+    const int64_t g0 = blockIdx.x, gs = gridDim.x;
+    if (g0 >= n_groups) return;   // whole workgroup, before any barrier
+
+    // A operand: weight row 32 t + col, dims 16 s + 8 half .. +7, scaled by 2^et and split
+    Split2 wa[4];
+    int et;
+    {
+        float v[4][8];
+        float m = 0.0f;
+        const float *src = w + static_cast<int64_t>(32 * t + col) * kDim + 8 * half;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const f32x4 a = *reinterpret_cast<const f32x4 *>(src + 16 * s);
+            const f32x4 b = *reinterpret_cast<const f32x4 *>(src + 16 * s + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[s][e] = a[e];
+                v[s][4 + e] = b[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[s][e]));
+        }
+        et = __builtin_amdgcn_readfirstlane(scale_exponent(wave_max(m)));
+#pragma unroll
+        for (int s = 0; s < 4; ++s) wa[s] = split2(v[s], et);
+    }
+    // store j of a group: frame 8 j + lane / 8, outputs 32 t + 4 (lane % 8) .. +3
+    const int sf = lane >> 3, sseg = lane & 7;
+    f32x4 bv = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (kBias) bv = *reinterpret_cast<const f32x4 *>(bias + 32 * t + 4 * sseg);
+
+    // staging: thread tid takes dims pd, pd + 1 of frame pf (step ps, half ph, entry pe)
+    const int pf = tid >> 5, pd = 2 * (tid & 31);
+    const int pidx = ((pd >> 4) * 2) * 64 + ((pd >> 3) & 1) * 32 + pf, pe = pd & 7;
+    // (a frame past n_frames loads the last frame's values, and stages zeros)
+    auto load_x = [&](int64_t g) {
+        const int64_t fr = g * kResFrames + pf;
+        return *reinterpret_cast<const f32x2 *>(x + (fr < n_frames ? fr : n_frames - 1) * kDim + pd);
+    };
+    auto stage = [&](f32x2 v, int64_t g, int buf) {
+        if (g * kResFrames + pf >= n_frames) v = f32x2{0.0f, 0.0f};
+        float m = fmaxf(fabsf(v[0]), fabsf(v[1]));
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));   // the frame's 32 threads
+        const int e = scale_exponent(m);
+        const float s0 = __builtin_amdgcn_ldexpf(v[0], e), s1 = __builtin_amdgcn_ldexpf(v[1], e);
+        const _Float16 h0 = static_cast<_Float16>(s0), h1 = static_cast<_Float16>(s1);
+        const _Float16 l0 = static_cast<_Float16>(s0 - static_cast<float>(h0));
+        const _Float16 l1 = static_cast<_Float16>(s1 - static_cast<float>(h1));
+        _Float16 *ph = reinterpret_cast<_Float16 *>(&s_b[buf][pidx]) + pe;
+        _Float16 *pl = reinterpret_cast<_Float16 *>(&s_b[buf][pidx + 64]) + pe;
+        *reinterpret_cast<f16x2 *>(ph) = f16x2{h0, h1};
+        *reinterpret_cast<f16x2 *>(pl) = f16x2{l0, l1};
+        if ((tid & 31) == 0) s_ef[buf][pf] = e;
+    };
+
+    float *tile = s_tile[wave];
+    // products, transpose and stores of group g (operands in buffer buf)
+    auto group_out = [&](auto all_tag, int64_t g, int buf) {
+        constexpr bool kAll = decltype(all_tag)::value;
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const f16x8 bh = s_b[buf][(2 * s) * 64 + lane];
+            const f16x8 bl = s_b[buf][(2 * s + 1) * 64 + lane];
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa[s].l, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa[s].h, bl, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(wa[s].h, bh, acc, 0, 0, 0);
+        }
+        // lane (col, half) holds outputs 8 m + 4 half .. +3 (m < 4) of frame col
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            *reinterpret_cast<f32x4 *>(&tile[col * kTileRow + 8 * m + 4 * half]) =
+                f32x4{acc[4 * m], acc[4 * m + 1], acc[4 * m + 2], acc[4 * m + 3]};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        f32x4 o[4];
+        int k[4];
+        bool inside = true;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o[j] = *reinterpret_cast<const f32x4 *>(&tile[(8 * j + sf) * kTileRow + 4 * sseg]);
+            k[j] = -(s_ef[buf][8 * j + sf] + et);
+            inside = inside && k[j] >= -149 && k[j] <= 127;
+        }
+        // scaled back by 2^k with the bias added: one fused multiply-add by an
+        // exact power of two when every factor of the wavefront is a float
+        if (__builtin_amdgcn_ballot_w64(!inside) == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float f = __builtin_amdgcn_ldexpf(1.0f, k[j]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[j][e] = kBias ? __builtin_fmaf(o[j][e], f, bv[e]) : o[j][e] * f;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    o[j][e] = __builtin_amdgcn_ldexpf(o[j][e], k[j]);
+                    if (kBias) o[j][e] += bv[e];
+                }
+        }
+        const int64_t f0 = g * kResFrames;
+        float *dst = out + (f0 + sf) * static_cast<int64_t>(hidden) + 32 * t + 4 * sseg;
+        const int64_t jstride = 8 * static_cast<int64_t>(hidden);
+        if constexpr (kAll) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) __builtin_nontemporal_store(o[j], reinterpret_cast<f32x4 *>(dst + j * jstride));
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (f0 + 8 * j + sf < n_frames) *reinterpret_cast<f32x4 *>(dst + j * jstride) = o[j];
+        }
+        // every lane has read the tile before the next group overwrites it
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // The loop holds no conditional memory operation (requests are clamped to
+    // the last group), so that the compiler's count of what was issued after
+    // a request is exact; the partial last group follows it. The values of
+    // the next kAhead groups are requested ahead, each after the stores of
+    // its iteration, so that the wait for a group's values covers only
+    // stores issued kAhead iterations earlier; slot j of xs is loaded and
+    // consumed in the j-th iteration of each unrolled block, so no register
+    // copy waits for a load early.
+    constexpr int kAhead = 4;
+    const int64_t last = n_groups - 1;
+    const f32x2 x0 = load_x(g0);
+    __builtin_amdgcn_s_waitcnt(0xF70);   // vmcnt(0): weights, bias and the first values
+    stage(x0, g0, 0);
+    f32x2 xs[kAhead];   // xs[j]: the group of the iteration's successor, j iterations on
+#pragma unroll
+    for (int j = 0; j < kAhead; ++j) xs[j] = load_x(min(g0 + (j + 1) * gs, last));
+    __syncthreads();
+    int buf = 0;
+    int64_t g = g0;
+    auto full_group = [&](int j) {
+        group_out(Flag<true>{}, g, buf);
+        __builtin_amdgcn_sched_barrier(0);
+        stage(xs[j], min(g + gs, last), buf ^ 1);
+        xs[j] = load_x(min(g + (kAhead + 1) * gs, last));
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        buf ^= 1;
+        g += gs;
+    };
+    // whole blocks of kAhead full groups (no path leaves a block early), then the rest
+    const int64_t n_it = n_full > g0 ? (n_full - g0 + gs - 1) / gs : 0;
+    for (int64_t b = 0; b < n_it / kAhead; ++b) {
+#pragma unroll
+        for (int j = 0; j < kAhead; ++j) full_group(j);
+    }
+    const int rest = static_cast<int>(n_it % kAhead);
+#pragma unroll
+    for (int j = 0; j < kAhead - 1; ++j)
+        if (j < rest) full_group(j);
+    if (g < n_groups) group_out(Flag<false>{}, g, buf);
+}
+
 }  // namespace
 
 hipError_t launch_linear_in(const float *h, int64_t n_frames, int hidden, const float *w,
@@ -680,6 +898,28 @@ hipError_t launch_linear_in_update(const float *src, const int32_t *codes, int c
 hipError_t launch_linear_out(const float *x, int64_t n_frames, int hidden, const float *w,
                              const float *bias, float *out, hipStream_t stream)
 {
+    if (hidden % (32 * kResWaves) == 0) {
+        const int halves = hidden / (32 * kResWaves);
+        constexpr int64_t kChunk = int64_t(1) << 20;   // frames per touch + product pair
+        for (int64_t f = 0; f < n_frames; f += kChunk) {
+            const int64_t n = std::min(kChunk, n_frames - f);
+            hipLaunchKernelGGL(touch_kernel, dim3(1024), dim3(256), 0, stream,
+                               reinterpret_cast<const f32x4 *>(x + f * kDim), n * kDim / 4);
+            // one workgroup of 16 wavefronts per CU, 256 CUs
+            const int64_t n_groups = (n + kResFrames - 1) / kResFrames;
+            const int64_t slices = std::max<int64_t>(1, std::min<int64_t>(n_groups, 256 / std::min(halves, 256)));
+            const dim3 grid(static_cast<unsigned>(slices), static_cast<unsigned>(halves)), block(64 * kResWaves);
+            if (bias)
+                hipLaunchKernelGGL((linear_out_res_kernel<true>), grid, block, 0, stream, x + f * kDim, n, hidden, w,
+                                   bias, out + f * hidden);
+            else
+                hipLaunchKernelGGL((linear_out_res_kernel<false>), grid, block, 0, stream, x + f * kDim, n, hidden, w,
+                                   bias, out + f * hidden);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
     if (hidden % 32 == 0) {
         const int64_t per_block = kOutWaveFrames;
         const int64_t blocks = (n_frames + per_block - 1) / per_block;

@@ -51,7 +51,8 @@ def check_project(h, w_in, b_in, books, w_out, b_out, idx=None, prepared=False):
 
 @pytest.mark.parametrize("prepared", [False, True])
 @pytest.mark.parametrize("n,hidden,bias", [(677, 1024, True), (300, 1024, False), (129, 192, True),
-                                           (1, 64, True), (16500, 128, True)])
+                                           (1, 64, True), (16500, 128, True), (5, 1024, True), (40, 512, False),
+                                           (100, 2048, True), (9000, 512, True)])
 def test_project_small(n, hidden, bias, prepared):
     rng = np.random.default_rng(n + hidden)
     h = rng.standard_normal((n, hidden)).astype(np.float32)
