@@ -381,13 +381,15 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
     const bool valid = fr < n_frames;
     const int n_col = hidden >> 6;   // column groups in the rows (wave-uniform)
 
-    // residual columns 64 t + 4 b .. +3 of frame j
+    // residual columns 64 t + 4 b .. +3 of frame j (read and written once,
+    // non-temporally: the cache is left to the table rows gathered every stage)
     f32x4 r[kT];
     {
         const float *row = h + (valid ? fr : 0) * hidden + 4 * b;
 #pragma unroll
         for (int t = 0; t < kT; ++t)
-            r[t] = (valid && t < n_col) ? *reinterpret_cast<const f32x4 *>(row + 64 * t) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            r[t] = (valid && t < n_col) ? __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(row + 64 * t))
+                                        : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
     // after the block reduction lane l holds output o(l) = 4 l5 + 2 l4 + l3 of frame l & 3
     const int out_id = 4 * ((lane >> 5) & 1) + 2 * ((lane >> 4) & 1) + ((lane >> 3) & 1);
@@ -603,7 +605,7 @@ void cosine_fused_kernel(const float *__restrict__ h, int64_t n_frames, int hidd
         float *row = residual + fr * hidden + 4 * b;
 #pragma unroll
         for (int t = 0; t < kT; ++t)
-            if (t < n_col) *reinterpret_cast<f32x4 *>(row + 64 * t) = r[t];
+            if (t < n_col) __builtin_nontemporal_store(r[t], reinterpret_cast<f32x4 *>(row + 64 * t));
     }
 }
 

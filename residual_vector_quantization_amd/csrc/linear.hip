@@ -198,7 +198,11 @@ void linear_in_kernel(const float *h, int64_t n_frames, int hidden,
     auto fetch_h = [&](int c) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            hv[i] = *reinterpret_cast<const f32x4 *>(h + roff[i] + 64 * c);
+            // read once: non-temporal, so that the rows do not displace cached
+            // data (the per-stage quantizer's residual rows are read again by
+            // its update and are left to the cache)
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(h + roff[i] + 64 * c);
+            hv[i] = kUpdate ? *src : __builtin_nontemporal_load(src);
             if (kUpdate) pv[i] = *reinterpret_cast<const f32x4 *>(prow[i] + 64 * c);
         }
     };
