@@ -497,6 +497,7 @@ class Probes:
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         self.lib.rvqprobe_gather_rows.argtypes = [vp, i64, i64, i32, i32, vp, vp]
         self.lib.rvqprobe_mfma.argtypes = [i32, i32, i32, vp, vp]
+        self.lib.rvqprobe_read.argtypes = [vp, i64, i32, vp, vp]
         self.torch = torch
         self.dev = torch.device("cuda:0")
 
@@ -569,6 +570,20 @@ class Probes:
         del a, b
         return 2.0 * FLUSH_BYTES / med / 1e9, 2.0 * FLUSH_BYTES / mn / 1e9
 
+    def read(self, reps=10, blocks=2048):
+        """1 GiB read by a grid-stride sum (one store per thread): GB/s read."""
+        torch = self.torch
+        a = torch.ones(FLUSH_BYTES // 4, device=self.dev)
+        sink = torch.empty(blocks * 256, device=self.dev)
+        stream = torch.cuda.current_stream().cuda_stream
+
+        def run():
+            if self.lib.rvqprobe_read(a.data_ptr(), a.numel(), blocks, sink.data_ptr(), stream):
+                raise SystemExit("rvqprobe_read failed")
+        med, mn = self._time(run, reps)
+        del a, sink
+        return FLUSH_BYTES / med / 1e9, FLUSH_BYTES / mn / 1e9
+
     def fill(self, reps=10):
         """A 1 GiB device fill: GB/s written."""
         torch = self.torch
@@ -616,8 +631,9 @@ def gather_probe(out_md):
     f32 = pr.mfma(False)
     cp = pr.copy()
     fl = pr.fill()
-    print(json.dumps({"mfma_f16_TFLOPs": f16, "mfma_f32_TFLOPs": f32, "copy_GBps": cp, "fill_GBps": fl}),
-          flush=True)
+    rd = pr.read()
+    print(json.dumps({"mfma_f16_TFLOPs": f16, "mfma_f32_TFLOPs": f32, "copy_GBps": cp, "fill_GBps": fl,
+                      "read_GBps": rd}), flush=True)
     lines = ["# Ceiling probes (row gathers, matrix cores, HBM copy)", "",
              "`librvq_probe.so` (`csrc/probes.hip`), HIP events on the launch stream; median and best of the "
              "timed launches.", "",
@@ -637,7 +653,9 @@ def gather_probe(out_md):
               f"| v_mfma_f32_32x32x2_f32, same | {f32[0]:.1f} TFLOP/s | {f32[1]:.1f} TFLOP/s | "
               f"{PEAK_FP32_MFMA_TFLOPS} TFLOP/s |",
               f"| 1 GiB device copy (read + write) | {cp[0]:.0f} GB/s | {cp[1]:.0f} GB/s | {PEAK_HBM_GBPS:.0f} GB/s |",
-              f"| 1 GiB device fill (write only) | {fl[0]:.0f} GB/s | {fl[1]:.0f} GB/s | {PEAK_HBM_GBPS:.0f} GB/s |"]
+              f"| 1 GiB device fill (write only) | {fl[0]:.0f} GB/s | {fl[1]:.0f} GB/s | {PEAK_HBM_GBPS:.0f} GB/s |",
+              f"| 1 GiB read, grid-stride sum of 16 B loads (read only; 2048 workgroups of 256) | {rd[0]:.0f} GB/s | "
+              f"{rd[1]:.0f} GB/s | {PEAK_HBM_GBPS:.0f} GB/s |"]
     os.makedirs(os.path.dirname(os.path.abspath(out_md)), exist_ok=True)
     open(out_md, "w").write("\n".join(lines) + "\n")
 

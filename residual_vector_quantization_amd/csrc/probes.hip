@@ -8,7 +8,11 @@
 //     compared with;
 //   - matrix cores: back-to-back independent v_mfma_f32_32x32x16_f16 or
 //     v_mfma_f32_32x32x2_f32 chains on register operands with full-mantissa
-//     values, the measured peaks beside the published ones.
+//     values, the measured peaks beside the published ones;
+//   - HBM reads: a grid-stride sum of 16-byte loads over a buffer much larger
+//     than the caches, one store per thread, the read-only rate the
+//     in-projection (which reads 4 KiB and writes 256 B per frame) is
+//     compared with.
 #include <stdint.h>
 
 #include <hip/hip_runtime.h>
@@ -116,9 +120,33 @@ void mfma_f32_probe_kernel(int iters, float *__restrict__ sink)
     sink[lane] = s;
 }
 
+// Grid-stride sum of n4 float4 (one 16-byte load per lane per step), one
+// float per thread to sink.
+__global__ __launch_bounds__(kThreads)
+void read_probe_kernel(const f32x4 *__restrict__ src, int64_t n4, float *__restrict__ sink)
+{
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n4; i += stride) acc += src[i];
+    sink[static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 }  // namespace
 
 extern "C" {
+
+// Reads n_floats floats of `src` (device memory, 16-byte aligned, n_floats a
+// multiple of 4) with `blocks` workgroups of 256 threads; `sink` receives
+// blocks * 256 floats (device memory). Returns 0, -1 for invalid arguments,
+// -3 if the launch failed.
+__attribute__((visibility("default"))) int rvqprobe_read(const float *src, int64_t n_floats, int32_t blocks,
+                                                          float *sink, void *stream)
+{
+    if (!src || !sink || n_floats <= 0 || n_floats % 4 != 0 || blocks <= 0) return -1;
+    hipLaunchKernelGGL(read_probe_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0,
+                       static_cast<hipStream_t>(stream), reinterpret_cast<const f32x4 *>(src), n_floats / 4, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 // Runs `blocks` workgroups of 256 threads, each wavefront 4 chains of
 // `iters` matrix-core products: fp16 32x32x16 (32768 flop each) when
