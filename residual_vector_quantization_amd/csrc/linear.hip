@@ -401,7 +401,8 @@ void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden
 // v_mfma_f32_32x32x16_f16 per 16-wide step instead of eight fp32 32x32x2
 // products. The scale 2^-(e_frame + e_tile) is undone in the bias step:
 // one fused multiply-add by an exact power of two, so the result is the
-// accumulated sum scaled back and the bias added with one rounding.
+// accumulated sum scaled back and the bias added with one rounding (two
+// steps instead where that power of two is not a float).
 //
 // The four wavefronts of a workgroup share 64 frames (two groups of 32)
 // and take every fourth tile of 32 outputs, so that together they write
@@ -417,8 +418,8 @@ void linear_out_kernel(const float *__restrict__ x, int64_t n_frames, int hidden
 // Loads and stores share one in-order completion counter, so a wait for a
 // load issued after a store also waits for the store. The next tile's bias
 // and weights are therefore requested before the current tile's products
-// and stores, every four rows of the transposed tile are read from LDS
-// before any of them is stored, tiles go in pairs with the weight registers
+// and stores, all rows of the transposed tile are read from LDS before any
+// of them is stored, tiles go in pairs with the weight registers
 // alternating, and the prefetches are unconditional (past the last tile
 // they reload it): a wait for a tile's weights then leaves the stores
 // issued after them in flight.
