@@ -106,3 +106,19 @@ def test_project_fc2_scales(book_scale, w_scale, bias):
     b_out = (rng.standard_normal(hidden) * book_scale * w_scale).astype(np.float32) if bias else None
     e1, e3 = check_project(h, w_in, None, books, w_out, b_out)
     announce("project fc2-scale errors", fc=e1, fc2=e3)
+
+
+def test_project_fc2_chunks():
+    """More frames than one fc2 chunk (2^20 frames: read-ahead of the inputs, then the products), so the
+    second chunk's offsets are exercised; sampled frames on both sides of the boundary and at the end."""
+    rng = np.random.default_rng(23)
+    n, hidden = (1 << 20) + 37, 512
+    h = rng.standard_normal((n, hidden), dtype=np.float32)
+    w_in = (rng.standard_normal((64, hidden)) / np.sqrt(hidden)).astype(np.float32)
+    w_out = (rng.standard_normal((hidden, 64)) / 8.0).astype(np.float32)
+    b_out = rng.standard_normal(hidden).astype(np.float32)
+    books = (rng.standard_normal((4, 256, 64)) * 0.5 ** np.arange(4)[:, None, None]).astype(np.float32)
+    edge = np.arange((1 << 20) - 40, n)
+    idx = np.unique(np.concatenate([W.sample_frames(n, 512, seed=7), edge, [0, 1, 31, 32]]))
+    e1, e3 = check_project(h, w_in, None, books, w_out, b_out, idx=idx, prepared=True)
+    announce("project fc2-chunk errors", fc=e1, fc2=e3)
