@@ -15,7 +15,7 @@ DEV = torch.device("cuda:0") if HAS_GPU else None
 
 
 def rvq():
-    """The HIP binding; raises (fails the test) if librvq.so is missing on a GPU machine."""
+    """The HIP binding; raises (fails the test) if librvq.so is missing where a GPU is present."""
     import residual_vector_quantization_amd as m
     m.load()
     return m
