@@ -9,7 +9,7 @@ split-bf16 for batches of up to 8192 frames) and ``rvq_decode`` (codes ->
 reconstruction) over the whole batch,
 inputs and outputs resident in HBM. Before the steps, the side
 measurements run (about a second of GPU load, so the clocks have settled
-when the steps start): the ceilings of this machine from ``librvq_probe.so``
+when the steps start): the ceilings of this GPU from ``librvq_probe.so``
 (random 256 B row gathers from a table of the decode's working set, fp16
 and fp32 matrix cores, a 1 GiB copy and fill), the decode alone warm and
 after a 1 GiB flush (median and min of 20), and the fp32-scored encode.
@@ -908,7 +908,7 @@ def main():
 
     n, q, k, d = w.n_frames, w.n_stages, w.n_codes, w.dim
     # Side measurements first (they also bring the GPU to its sustained clocks before the timed steps):
-    # the ceilings of this machine, the decode alone warm and cold, the fp32-scored encode.
+    # the ceilings of this GPU, the decode alone warm and cold, the fp32-scored encode.
     step()
     torch.cuda.synchronize()
     ceil = dec_alone = None
@@ -1054,18 +1054,18 @@ def main():
         g_med = ceil["gather_TBps"][0]
         rg = rec["decode_roofline"]["row_gathers"]
         rg.update({"ceiling": g_med, "frac": gather_tbps / g_med,
-                   "ceiling_source": f"rvqprobe_gather_rows (librvq_probe.so) on this box: random 256 B rows from "
+                   "ceiling_source": f"rvqprobe_gather_rows (librvq_probe.so) on this GPU: random 256 B rows from "
                                      f"a {table / 2 ** 20:g} MiB table (the decode's working set), no dependent "
                                      f"loads, about {256 * probe_rows / 1e9:.1f} GB per launch, median launch"})
         f16_med, f32_med = ceil["mfma_f16_TFLOPs"][0], ceil["mfma_f32_TFLOPs"][0]
         # bf16 and fp16 share the dense matrix-core rate, so the fp16 probe serves both
         rec["roofline"].update({"peak_measured": f16_med, "frac_measured": mm_tflops / f16_med,
                                 "peak_measured_source": "rvqprobe_mfma: back-to-back v_mfma_f32_32x32x16_f16 "
-                                                        "on every SIMD, this box"})
+                                                        "on every SIMD, this GPU"})
         rec["encode_fp32_equivalent"].update({"peak_measured": f32_med})
         cp_med = ceil["copy_GBps"][0]
         rec["decode_roofline"].update({"peak_measured": cp_med, "frac_measured": dec_gbps / cp_med,
-                                       "peak_measured_source": "1 GiB device copy (read + write), this box"})
+                                       "peak_measured_source": "1 GiB device copy (read + write), this GPU"})
         for mode, t in dec_alone.items():
             rec["decode_roofline"][mode] = {
                 "median_ms": t["median_ms"], "min_ms": t["min_ms"],
