@@ -3,10 +3,10 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batched]
 
 One step = ``rvq_prepare_codebooks`` (codebooks scaled and rounded to fp16,
-and split into bf16 halves, with their half-norms), ``rvq_encode_prepared``
-(codes + final residual; fp16 scores with exact re-rank for wide batches,
-split-bf16 for batches of up to 8192 frames) and ``rvq_decode`` (codes ->
-reconstruction) over the whole batch,
+with their half-norms), ``rvq_encode_prepared`` (codes + final residual;
+fp16 scores with exact re-rank, batches of up to 8192 frames with every
+stage's codebook split over a workgroup's wavefronts) and ``rvq_decode``
+(codes -> reconstruction) over the whole batch,
 inputs and outputs resident in HBM. Before the steps, the side
 measurements run (about a second of GPU load, so the clocks have settled
 when the steps start): the ceilings of this GPU from ``librvq_probe.so``
@@ -62,8 +62,7 @@ CSRC = os.path.join(_ROOT, "residual_vector_quantization_amd", "csrc")
 # kernel kind -> sources whose text defines it (hashed to detect stale counters)
 KERNEL_SOURCES = {
     "encode_f16": ["encode_f16.hip", "encode_common.h", "prepared.h"],
-    "encode_bf16": ["encode_bf16.hip", "encode_common.h", "prepared.h"],
-    "encode_bf16_split": ["encode_bf16.hip", "encode_common.h", "prepared.h"],
+    "encode_f16_split": ["encode_f16.hip", "encode_common.h", "prepared.h"],
     "encode_fp32": ["encode.hip", "encode_common.h"],
     "decode": ["decode.hip"],
     "linear_in": ["linear.hip"],
@@ -164,9 +163,9 @@ def _kernel_of(name):
         return "linear_out_touch"   # fc2's inputs read once ahead of it
     if "encode_f16_kernel" in name:
         return "encode_f16"
-    if "encode_bf16_ksplit_kernel" in name:
-        return "encode_bf16_split"
-    if "encode_bf16_kernel" in name:
+    if "encode_f16_ksplit_kernel" in name:
+        return "encode_f16_split"
+    if "encode_bf16_ksplit_kernel" in name or "encode_bf16_kernel" in name:
         return "encode_bf16_onthefly"   # codebooks split in every workgroup (no prepared layout)
     if "encode_kernel" in name:
         return "encode_fp32"
@@ -238,14 +237,6 @@ def summarize_profiles(w, src_dir):
                      f"{enc_flop / t / 1e6 / PEAK_FP32_MFMA_TFLOPS:.2f}x the {PEAK_FP32_MFMA_TFLOPS} fp32 matrix "
                      f"peak); matrix steps issued {enc_flop * (d + 16) / d:.4g} flop (2QK(D+16) per frame, "
                      f"the half-norm step included).")
-    if "encode_bf16" in avg:
-        t = avg["encode_bf16"]
-        lines.append(f"- encode_bf16 (prepared codebooks): {3 * enc_flop:.4g} bf16 matrix flop per launch "
-                     f"(3 x 2QKD per frame) / "
-                     f"{t:.1f} us = {3 * enc_flop / t / 1e6:.1f} TFLOP/s "
-                     f"({3 * enc_flop / t / 1e6 / PEAK_BF16_MFMA_TFLOPS:.1%} of {PEAK_BF16_MFMA_TFLOPS:.0f} bf16); "
-                     f"fp32-equivalent {enc_flop / t / 1e6:.1f} TFLOP/s "
-                     f"({enc_flop / t / 1e6 / PEAK_FP32_MFMA_TFLOPS:.1%} of {PEAK_FP32_MFMA_TFLOPS} fp32).")
     if "encode_fp32" in avg:
         t = avg["encode_fp32"]
         lines.append(f"- encode_fp32: {enc_flop:.4g} flop per launch (2QKD per frame) / {t:.1f} us = "
@@ -280,14 +271,12 @@ def summarize_profiles(w, src_dir):
     # the same fetch scale checked on a gather pattern: every 256 B row of a 1 GiB table read once
     g_scale = (1 << 30) / (fetch["calib_gather"] * 1024.0) if "calib_gather" in fetch else None
     enc_algo = (4.0 * d + 4.0 * d + 4.0 * q) * n + 4.0 * q * k * d
-    # the prepared encodes read their section of the prepared codebooks: fp16 rows with their half-norm
-    # parts (144 B), stage maxima and exponent (encode_f16; plus the fp32 rows of the picks), or split-bf16
-    # rows (256 B), norms and stage maxima (encode_bf16) in place of the fp32 codebook
+    # the prepared encodes read the prepared codebooks: fp16 rows with their half-norm parts (144 B),
+    # stage maxima and exponent, besides the fp32 rows of the picks
     kp = -(-k // 256) * 256
     prep16_bytes = q * (kp * 144 + 4 * (kp // 256) + 4)
-    prep_bytes = q * (kp * 260 + 4 * (kp // 256))
     hid = w.hidden or 0
-    algo = {"encode_f16": enc_algo + prep16_bytes, "encode_bf16": enc_algo - 4.0 * q * k * d + prep_bytes,
+    algo = {"encode_f16": enc_algo + prep16_bytes, "encode_f16_split": enc_algo + prep16_bytes,
             "encode_fp32": enc_algo, "decode": dec_bytes + 4.0 * q * k * d,
             # fc: h rows in, latent rows out (weights 256 KiB, read once); fc2 the reverse
             "linear_in": (4.0 * hid + 4.0 * d) * n + 4.0 * hid * d,
@@ -321,7 +310,7 @@ def summarize_profiles(w, src_dir):
              "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
     means = {name: _counter_means(mf, name) for name in names}
     lines += ["", "## Matrix-core counters (per launch)", ""]
-    for kind in ("encode_f16", "encode_bf16", "encode_fp32", "linear_in", "linear_out"):
+    for kind in ("encode_f16", "encode_f16_split", "encode_fp32", "linear_in", "linear_out"):
         c = {name: means[name].get(kind) for name in names}
         if c["GRBM_GUI_ACTIVE"] is None:
             continue
@@ -376,6 +365,9 @@ def _trace_work(w):
         "encode_bf16_ksplit_kernel": (3 * 2.0 * qe * k * d * n, "flop",
                                       "bf16 matrix flop, 3 x 2KD per frame" if w.per_stage else
                                       "bf16 matrix flop, 3 x 2QKD per frame"),
+        "encode_f16_ksplit_kernel": (2.0 * qe * k * d * n, "flop",
+                                     "fp16 matrix flop, 2KD per frame" if w.per_stage else
+                                     "fp16 matrix flop, 2QKD per frame"),
         "encode_kernel": (2.0 * q * k * d * n, "flop", "fp32 matrix flop, 2QKD per frame"),
         "decode_kernel": ((4.0 * q + 4.0 * d) * n, "B", "HBM, (4Q+4D) per frame"),
         "decode_tiled_kernel": ((4.0 * q + 4.0 * d) * n, "B", "HBM, (4Q+4D) per frame"),
@@ -991,14 +983,12 @@ def main():
     value = n * args.steps / wall
     enc_flop = 2.0 * q * k * d * n
     wide = n > SPLIT_MAX_FRAMES
-    if wide:   # one fp16 product per dimension; the method's 2QKD flop on the fp16 peak
-        mm_work, mm_what = enc_flop, f"2*Q*K*D*N = {enc_flop:.4g} flop on fp16 matrix cores"
-        mm_kernel = ("encode_f16_kernel, prepared codebooks (v_mfma_f32_32x32x16_f16, one product per "
-                     "dimension + a half-norm step; exact float64 re-rank of candidates)")
-    else:      # three split-bf16 products per dimension
-        mm_work, mm_what = 3 * enc_flop, f"3*2*Q*K*D*N = {3 * enc_flop:.4g} bf16 flop"
-        mm_kernel = ("encode_bf16_ksplit_kernel (codebook split over a workgroup's wavefronts), prepared "
-                     "codebooks (v_mfma_f32_32x32x16_bf16, 3 split products)")
+    # one fp16 product per dimension; the method's 2QKD flop on the fp16 peak
+    mm_work, mm_what = enc_flop, f"2*Q*K*D*N = {enc_flop:.4g} flop on fp16 matrix cores"
+    mm_kernel = (("encode_f16_kernel" if wide else
+                  "encode_f16_ksplit_kernel (codebook split over a workgroup's wavefronts)") +
+                 ", prepared codebooks (v_mfma_f32_32x32x16_f16, one product per dimension + a half-norm "
+                 "step; exact float64 re-rank of candidates)")
     mm_tflops = mm_work / (enc_ms * 1e-3) / 1e12
     dec_bytes = (4.0 * q + 4.0 * d) * n
     dec_gbps = dec_bytes / (dec_ms * 1e-3) / 1e9
@@ -1018,7 +1008,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "frames": n, "Q": q, "K": k, "D": d,
-                   "scoring": "fp16 + exact re-rank" if wide else "split-bf16 + exact re-rank",
+                   "scoring": "fp16 + exact re-rank",
                    "recipe": w.description},
         "audio_seconds_per_s": value / w.frame_rate_hz,
         "prepare_ms": prep_ms,
@@ -1030,15 +1020,17 @@ def main():
         "roofline": {"bound": "mfma", "kernel": mm_kernel,
                      "achieved": mm_tflops, "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
                      "frac": mm_tflops / PEAK_F16_MFMA_TFLOPS,
-                     "traffic": recorded_traffic("encode_f16" if wide else "encode_bf16_split", w.name),
+                     "traffic": recorded_traffic("encode_f16" if wide else "encode_f16_split", w.name),
                      "work_per_launch": mm_what,
-                     "contraction_dtype": "fp16" if wide else "bf16 (3-way split)",
+                     "contraction_dtype": "fp16",
                      "decision": "float64 re-rank of every candidate within the proven fp16 error bound; "
                                  "codes equal the oracle's float64 argmin",
                      "limiter": ("vector-ALU issue, not the matrix cores: every score's packed (score, index) "
                                  "key is updated on the VALU (about 3 instructions per score, half the SIMD "
                                  "cycles in the rocprofv3 issue counters against a quarter for the matrix "
-                                 "cores)" if wide else "matrix cores and the per-stage decision"),
+                                 "cores)" if wide else "latency: one four-wavefront workgroup per CU and 32 frames "
+                                 "each, with the merge of the wavefronts' keys and the decision between "
+                                 "stages"),
                      "results_dtype": "f32 residual and reconstruction, i32 codes"},
         "encode_fp32_equivalent": {"achieved": enc_flop / (enc_ms * 1e-3) / 1e12, "peak": PEAK_FP32_MFMA_TFLOPS,
                                    "unit": "TFLOP/s", "work_per_launch": f"2*Q*K*D*N = {enc_flop:.4g} flop"},

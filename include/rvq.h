@@ -22,7 +22,7 @@
  *     distance sum_j (r_j - c_j)^2 (j ascending, one rounding per
  *     operation) over all K codewords. Scores are computed on the matrix
  *     cores (split-bf16 by default, or fp32, see rvq_encode_scored; fp16
- *     for rvq_encode_prepared on wide batches); every codeword whose score
+ *     for rvq_encode_prepared); every codeword whose score
  *     lies within a proven error bound of the best is re-ranked with that
  *     float64 sum, so score rounding never decides a pick and all scorings
  *     give identical results;
@@ -168,26 +168,24 @@ RVQ_API rvq_status rvq_encode_scored(const float *x, int64_t n_frames, int32_t d
                                      float *recon, float *residual, rvq_scoring scoring, void *stream);
 
 /*
- * Prepared codebooks: the codebook tensor in the layouts the matrix-core
- * encodes read, computed once (codebooks are model constants) so that each
- * encode only copies rows.
+ * Prepared codebooks: the codebook tensor in the layout the fp16
+ * matrix-core encodes read, computed once (codebooks are model constants)
+ * so that each encode only copies rows.
  *
  * rvq_prepared_bytes returns the size of the buffer for the given shape
  * (a negative rvq_status for invalid or unsupported shapes).
  * rvq_prepare_codebooks writes it on `stream` into caller-allocated device
  * memory `prepared` (16-byte aligned, at least rvq_prepared_bytes bytes).
- * Per stage it holds a split-bf16 section (each codeword as bf16 hi =
- * bf16(c) and lo = bf16(c - hi) in 8-dim groups, 0.5*||c||^2 in fp32, the
- * largest 0.5*||c||^2 of every 256 codewords) and an fp16 section (one
- * power of two 2^e per stage that brings max |c| into [1/2, 1); each
- * codeword as fp16(2^e c); 0.5*||2^e c||^2 as two fp16 parts; the largest
- * of those per 256 codewords; e). The buffer depends only on the codebook
- * values.
+ * Per stage it holds one power of two 2^e that brings max |c| into
+ * [1/2, 1), each codeword as fp16(2^e c), 0.5*||2^e c||^2 as two fp16
+ * parts, and the largest of those per 256 codewords (about 144 bytes per
+ * codeword). The buffer depends only on the codebook values.
  *
  * rvq_encode_prepared reads `prepared` (which must have been prepared from
  * the same `codebooks` with at least `n_stages` stages and the same n_codes
- * and dim; the library cannot check this): up to 8192 frames with
- * split-bf16 scores, more with one fp16 product per dimension. Either way
+ * and dim; the library cannot check this) and scores with one fp16
+ * product per dimension: up to 8192 frames split every stage's codebook
+ * over the wavefronts of a workgroup, more tile the frames. Either way
  * every codeword within the scores' proven error of the best is re-ranked
  * in float64, so results are identical to rvq_encode. Codebook entries
  * beyond 2^20 or residual entries beyond 2^15 leave fp16's range; such
@@ -215,7 +213,7 @@ RVQ_API rvq_status rvq_encode_prepared(const float *x, int64_t n_frames, int32_t
  * the process ends), then encodes from it. The call allocates and frees
  * nothing. Shapes whose prepared layout exceeds the array
  * (rvq_prepared_bytes(n_stages, n_codes, dim) > RVQ_NOALLOC_SCRATCH_BYTES,
- * e.g. 40 stages of 1024 codewords or 10 of 4096 fit, 64 of 4096 do not)
+ * e.g. 113 stages of 1024 codewords or 28 of 4096 fit, 29 of 4096 do not)
  * return RVQ_ERR_UNSUPPORTED before anything is enqueued. The array is
  * shared by all calls on one GPU and keeps the last call's contents: calls
  * that overlap on one GPU (other streams or threads) race and must be

@@ -287,8 +287,8 @@ def rvq_prepared_bytes(n_stages: int, n_codes: int, dim: int) -> int:
 
 
 def rvq_prepare_codebooks(codebooks: torch.Tensor, prepared: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Prepared layouts (split-bf16 and fp16 sections) of ``codebooks`` [Q, K, D], as a uint8 tensor on the
-    same device."""
+    """Prepared layout (per stage a power-of-two scale, fp16 rows and half-norm parts) of ``codebooks``
+    [Q, K, D], as a uint8 tensor on the same device."""
     _require(codebooks, "codebooks", torch.float32, 3)
     q, k, d = codebooks.shape
     size = rvq_prepared_bytes(q, k, d)
@@ -314,7 +314,7 @@ def _check_prepared(prepared: Optional[torch.Tensor], codebooks: torch.Tensor, q
 def rvq_encode_prepared(x: torch.Tensor, codebooks: torch.Tensor, prepared: torch.Tensor,
                         n_stages: Optional[int] = None, recon: bool = False, residual: bool = True,
                         out=None):
-    """Encode from prepared codebooks (split-bf16 scores up to 8192 frames, fp16 above; exact either way):
+    """Encode from prepared codebooks (fp16 scores, exact re-rank):
     ``(codes, recon or None, residual or None)``."""
     _require(x, "x", torch.float32, 2)
     _require(codebooks, "codebooks", torch.float32, 3, x.device)

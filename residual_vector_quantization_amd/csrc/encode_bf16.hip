@@ -35,9 +35,9 @@
 // its best, second and third keys and the indices of the first two: a
 // frame resolves from up to four candidates (two per half) with the float64
 // re-rank, and only a third candidate inside one lane sends it to the full
-// float64 rescan. Small batches (the split-codebook kernel below) read the
-// split-bf16 section of prepared codebooks when they are given; wide batches
-// with prepared codebooks take the fp16 kernel (encode_f16.hip).
+// float64 rescan. This file holds the encodes of codebooks given as fp32
+// (split in every workgroup) and the preparation of codebooks for the fp16
+// kernels (encode_f16.hip), which take every prepared encode.
 #include "encode_common.h"
 #include "prepared.h"
 
@@ -62,17 +62,6 @@ static_assert(kWaves * 32 == kChunk, "staging maps each wavefront to 32 codeword
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// One wavefront-wide direct load from global memory into LDS: active lane i
-// copies 16 bytes from src into dst + 16 i (dst wave-uniform, in LDS).
-// Issued as inline assembly so that the compiler does not order every LDS
-// read behind it; the caller waits with the vector-memory counter.
-__device__ __forceinline__ void dma16(const void *src, void *dst)
-{
-    const unsigned m0 = static_cast<unsigned>(reinterpret_cast<size_t>((lds_void *)dst));
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
-}
 
 // hi = bf16(v), lo = bf16(v - hi), both round to nearest even, converted in
 // pairs (one v_cvt_pk_bf16_f32 per two values); hi is widened back to fp32 by
@@ -166,60 +155,8 @@ __device__ __forceinline__ void score_group(int kG, const __bf16 *sb, const floa
     fold_group(best, second, bb, sb0, base, half, best_k, second_k);
 }
 
-// Scores the 32 codewords of one block in LDS (rows sb, half-norms sn;
-// one chain of 12 matrix-core steps) that start at codeword `base`.
-__device__ __forceinline__ void score_block(const __bf16 *sb, const float *sn, int col, int half,
-                                            const bf16x8 (&nh)[4], const bf16x8 (&nl)[4], int base,
-                                            float &best, float &second, float &third,
-                                            int &best_k, int &second_k)
-{
-    f32x16 d;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const f32x4 nv = *reinterpret_cast<const f32x4 *>(sn + 8 * m + 4 * half);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d[4 * m + e] = nv[e];
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const __bf16 *row = sb + col * kRowH + 16 * (4 * half + s);
-        const bf16x8 ah = *reinterpret_cast<const bf16x8 *>(row);
-        const bf16x8 al = *reinterpret_cast<const bf16x8 *>(row + 8);
-        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, nl[s], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, nh[s], d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, nh[s], d, 0, 0, 0);
-    }
-    const unsigned bb = __float_as_uint(best), sb0 = __float_as_uint(second);
-    scan_block(d, 0, best, second, third);
-    fold_group(best, second, bb, sb0, base, half, best_k, second_k);
-}
-
-// Prepared codebooks: the layout is in prepared.h; these kernels read the
-// split-bf16 section (rows, half-norms and the per-chunk maxima).
 using prep::padded_codes;
 using prep::stage_bytes;
-static_assert(prep::kChunk == kChunk, "prepared rows come in whole chunks");
-
-// The largest 0.5*||c_k||^2 of a prepared stage block is the maximum of its
-// Kp/kChunk words. stage_max_part loads lane's share of them (issued early,
-// so that the load is long done when the decision needs it); wave_max_bits
-// reduces the shares over the wavefront. Values are >= 0, so their bits
-// order like the values.
-__device__ __forceinline__ unsigned stage_max_part(const uint8_t *blk, int64_t kp, int lane)
-{
-    const unsigned *words = reinterpret_cast<const unsigned *>(blk + prep::bf16_max(kp));
-    const int n_words = static_cast<int>(kp / kChunk);
-    unsigned m = lane < n_words ? words[lane] : 0u;
-    for (int c = lane + 64; c < n_words; c += 64) m = max(m, words[c]);
-    return m;
-}
-
-__device__ __forceinline__ float wave_max_bits(unsigned m)
-{
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) m = max(m, static_cast<unsigned>(__shfl_xor(static_cast<int>(m), off)));
-    return __uint_as_float(m);
-}
 
 // An upper bound of sqrt(x) for x >= 0: the hardware square root (within a
 // few ulp) of max(x, FLT_MIN), raised by 2^-20 of itself.
@@ -498,21 +435,6 @@ constexpr int kSplitGroup = 64;
 // up to this many frames the split kernel runs: two rounds of one-tile
 // workgroups on 256 CUs are still faster than the wide kernel's 256-frame tiles
 constexpr int64_t kSplitMaxFrames = 16384;
-// With prepared codebooks the fp16 kernel takes over as soon as the
-// split-codebook kernel needs a second round of one-tile workgroups on 256
-// CUs (measured, Q = 8: 8,192 frames 89 against 110 us, 12,288 frames 178
-// against 110 us).
-constexpr int64_t kPreparedSplitMaxFrames = 8192;
-// prepared codebooks: 32-codeword blocks, two per wavefront buffer
-constexpr int kRowSlots = kRowH * 2 / 16;                 // 16-byte LDS slots per row (16 data + 1 padding)
-constexpr int kBlockSlots = 32 * kRowH * 2 / 16;          // 16-byte LDS slots of a block (544)
-constexpr int kBlockLoads = (kBlockSlots + 63) / 64;      // wavefront-wide loads per block's rows (9)
-static_assert(kBlockLoads == 9, "the wait count below assumes 9 row loads + 1 norm load per block");
-
-// Waits until at most the 10 loads of the block issued last are in flight
-// (vector-memory operations complete in order).
-__device__ __forceinline__ void wait_all_but_block() { asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); }
-__device__ __forceinline__ void wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // top-3 of keys from disjoint codeword sets; k < 0 marks an unknown index,
 // which orders after known ones on equal keys
@@ -543,11 +465,10 @@ __device__ __forceinline__ void top3_insert(Top3 &m, float v, int k)
     }
 }
 
-template <bool kRecon, bool kResidual, bool kPrepared>
+template <bool kRecon, bool kResidual>
 __global__ __attribute__((amdgpu_flat_work_group_size(64 * kSplitWaves, 64 * kSplitWaves), amdgpu_waves_per_eu(2)))
 void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
-                               const float *__restrict__ books, const uint8_t *__restrict__ prepared,
-                               int n_stages, int n_codes,
+                               const float *__restrict__ books, int n_stages, int n_codes,
                                int32_t *__restrict__ codes, int codes_ld,
                                float *__restrict__ residual, float *__restrict__ recon)
 {
@@ -584,39 +505,8 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
     bf16x8 nh[4], nl[4];
 
     const int n_groups = (n_codes + kSplitGroup - 1) / kSplitGroup;
-    const int64_t kp = padded_codes(n_codes);
-    const int64_t sbytes = stage_bytes(n_codes);
     __bf16 *rows = s_rows[wave];
     float *gnorm = s_gnorm[wave];
-
-    // Prepared codebooks: wavefront w owns the 32-codeword blocks w, w + 8,
-    // ... of every stage and streams them through the two halves of its
-    // buffer with direct global->LDS loads, one block ahead; the first
-    // block of the next stage is loaded while the current stage is merged
-    // and decided.
-    const int n_blocks = (n_codes + 31) / 32;
-    const int my_blocks = wave < n_blocks ? (n_blocks - wave + kSplitWaves - 1) / kSplitWaves : 0;
-    auto load_block = [&](int q, int ib, int buf) {
-        const uint8_t *blk = prepared + q * sbytes;
-        const int k0 = (wave + kSplitWaves * ib) * 32;
-        const uint8_t *src = blk + static_cast<int64_t>(k0) * 256;
-        __bf16 *dst = rows + buf * 32 * kRowH;
-#pragma unroll
-        for (int i = 0; i < kBlockLoads; ++i) {
-            // slot t of the block is segment t % 17 of row t / 17; the 17th
-            // (padding) slot loads the row's first segment again
-            int t = i * 64 + lane;
-            asm volatile("" : "+v"(t));   // recomputed per block rather than held in registers
-            const int r = t / kRowSlots;
-            const int seg = t - r * kRowSlots;
-            if (t < kBlockSlots) dma16(src + r * 256 + (seg < kRowSlots - 1 ? seg * 16 : 0), dst + i * 512);
-        }
-        if (lane < 8) dma16(blk + prep::bf16_norms(kp) + static_cast<int64_t>(k0 + 4 * lane) * 4, gnorm + buf * 32);
-    };
-    int item = 0;   // blocks this wavefront has scored (their buffer alternates)
-    if constexpr (kPrepared) {
-        if (my_blocks > 0) load_block(0, 0, 0);
-    }
 
 #pragma unroll
     for (int s = 0; s < 4; ++s) split8(&n[8 * s], nh[s], nl[s]);
@@ -632,57 +522,37 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
         float best = kNoScore, second = kNoScore, third = kNoScore;
         int best_k = 0, second_k = 0;
         unsigned wmax = 0u;
-        float c2 = 0.0f;   // max_k 0.5||c_k||^2 over the stage
 
-        unsigned cmax = 0u;   // prepared: wavefront 0's share of the stage maximum
-        if constexpr (kPrepared) {
-            if (wave == 0) cmax = stage_max_part(prepared + q * sbytes, kp, lane);
-            for (int ib = 0; ib < my_blocks; ++ib, ++item) {
-                if (ib + 1 < my_blocks) {
-                    load_block(q, ib + 1, (item + 1) & 1);
-                    wait_all_but_block();
-                } else if (q + 1 < n_stages) {
-                    load_block(q + 1, 0, (item + 1) & 1);
-                    wait_all_but_block();
-                } else {
-                    wait_all();
-                }
-                const int buf = item & 1;
-                score_block(rows + buf * 32 * kRowH, gnorm + buf * 32, col, half, nh, nl,
-                            (wave + kSplitWaves * ib) * 32, best, second, third, best_k, second_k);
-            }
-        } else {
-            for (int g = wave; g < n_groups; g += kSplitWaves) {
-                // lane l stages row 64 g + l of the stage (rows past n_codes:
-                // the last row again with norm kNoScore)
-                const int k = g * kSplitGroup + lane;
-                __bf16 *dst = rows + lane * kRowH;
-                const f32x4 *p = reinterpret_cast<const f32x4 *>(
-                    books + (static_cast<int64_t>(q) * n_codes + min(k, n_codes - 1)) * kDim);
-                float hn = 0.0f;
+        for (int g = wave; g < n_groups; g += kSplitWaves) {
+            // lane l stages row 64 g + l of the stage (rows past n_codes:
+            // the last row again with norm kNoScore)
+            const int k = g * kSplitGroup + lane;
+            __bf16 *dst = rows + lane * kRowH;
+            const f32x4 *p = reinterpret_cast<const f32x4 *>(
+                books + (static_cast<int64_t>(q) * n_codes + min(k, n_codes - 1)) * kDim);
+            float hn = 0.0f;
 #pragma unroll
-                for (int grp = 0; grp < 8; ++grp) {
-                    const f32x4 a = p[2 * grp], b = p[2 * grp + 1];
-                    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            for (int grp = 0; grp < 8; ++grp) {
+                const f32x4 a = p[2 * grp], b = p[2 * grp + 1];
+                const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) hn = __builtin_fmaf(v[e], v[e], hn);
-                    bf16x8 hi, lo;
-                    split8(v, hi, lo);
-                    *reinterpret_cast<bf16x8 *>(dst + 16 * grp) = hi;
-                    *reinterpret_cast<bf16x8 *>(dst + 16 * grp + 8) = lo;
-                }
-                hn = 0.5f * hn;
-                gnorm[lane] = k < n_codes ? hn : kNoScore;
-                if (k < n_codes) wmax = max(wmax, __float_as_uint(hn));
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-                score_group(0, rows, gnorm, col, half, nh, nl, g * kSplitGroup, best, second, third, best_k,
-                            second_k);
-                // the buffer is read before the next group overwrites it
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-                __builtin_amdgcn_wave_barrier();
+                for (int e = 0; e < 8; ++e) hn = __builtin_fmaf(v[e], v[e], hn);
+                bf16x8 hi, lo;
+                split8(v, hi, lo);
+                *reinterpret_cast<bf16x8 *>(dst + 16 * grp) = hi;
+                *reinterpret_cast<bf16x8 *>(dst + 16 * grp + 8) = lo;
             }
+            hn = 0.5f * hn;
+            gnorm[lane] = k < n_codes ? hn : kNoScore;
+            if (k < n_codes) wmax = max(wmax, __float_as_uint(hn));
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            score_group(0, rows, gnorm, col, half, nh, nl, g * kSplitGroup, best, second, third, best_k,
+                        second_k);
+            // the buffer is read before the next group overwrites it
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __builtin_amdgcn_wave_barrier();
         }
 
         s_part[wave][0][lane] = best;
@@ -690,12 +560,10 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
         s_part[wave][2][lane] = third;
         s_part[wave][3][lane] = __int_as_float(best_k);
         s_part[wave][4][lane] = __int_as_float(second_k);
-        if (!kPrepared) {
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1)
-                wmax = max(wmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(wmax), off)));
-            if (lane == 0) s_wmax[wave] = wmax;
-        }
+        for (int off = 1; off < 64; off <<= 1)
+            wmax = max(wmax, static_cast<unsigned>(__shfl_xor(static_cast<int>(wmax), off)));
+        if (lane == 0) s_wmax[wave] = wmax;
         __syncthreads();
         if (wave == 0) {
             // wavefront 0 merges the parts, decides, and publishes the split
@@ -707,14 +575,10 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
                 top3_insert(m, s_part[w][1][lane], __float_as_int(s_part[w][4][lane]));
                 top3_insert(m, s_part[w][2][lane], -1);
             }
-            if constexpr (kPrepared) {
-                c2 = wave_max_bits(cmax);
-            } else {
-                unsigned mm = 0u;
+            unsigned mm = 0u;
 #pragma unroll
-                for (int w = 0; w < kSplitWaves; ++w) mm = max(mm, s_wmax[w]);
-                c2 = __uint_as_float(mm);
-            }
+            for (int w = 0; w < kSplitWaves; ++w) mm = max(mm, s_wmax[w]);
+            const float c2 = __uint_as_float(mm);   // max_k 0.5||c_k||^2 over the stage
             const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
             decide_stage<kRecon>(n, acc, m.b, m.s, m.t, m.bk, m.sk, book, n_codes, c2, valid, half, col, lane,
                                  s_frame[0], (valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
@@ -748,10 +612,9 @@ void encode_bf16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
 // One workgroup per kChunk padded rows of a stage, 8 lanes per row (one
 // 8-dim group each, so a wavefront reads and writes 8 whole rows). Every
 // workgroup first finds the stage's largest |c| itself, so all of a stage's
-// workgroups reach the same scale e. Then per row: the hi/lo split and the
-// half-norm (split-bf16 section), fp16 of c' = 2^e c and the fp16 parts of
-// 0.5*||c'||^2 (fp16 section); and the largest valid half-norms of the
-// workgroup's rows in both sections.
+// workgroups reach the same scale e. Then per row: fp16 of c' = 2^e c and
+// the fp16 parts of 0.5*||c'||^2; and the largest valid half-norm of the
+// workgroup's rows.
 constexpr int kPrepThreads = 512;
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -777,8 +640,6 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
     const int q = blockIdx.y;
     const int64_t kp = padded_codes(n_codes);
     uint8_t *blk = prepared + q * stage_bytes(n_codes);
-    float *norms = reinterpret_cast<float *>(blk + prep::bf16_norms(kp));
-    uint8_t *rows16 = blk + prep::f16_offset(kp);
     const float *stage = books + static_cast<int64_t>(q) * n_codes * kDim;
 
     // the stage's largest |c|: bits of non-negative floats order like the
@@ -805,48 +666,31 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
     const bool in_range = amax_bits < 0x7F800000u && ldexpf(amax, e) <= prep::kMaxScaled;
 
     const int grp = threadIdx.x & 7;
-    unsigned m = 0u, m16 = 0u;
+    unsigned m16 = 0u;
     for (int k = c * kChunk + (threadIdx.x >> 3); k < (c + 1) * kChunk; k += kPrepThreads / 8) {
-        bf16x8 *row = reinterpret_cast<bf16x8 *>(blk + static_cast<int64_t>(k) * 256);
-        u32x4 *row16 = reinterpret_cast<u32x4 *>(rows16 + static_cast<int64_t>(k) * prep::kF16Row);
+        u32x4 *row16 = reinterpret_cast<u32x4 *>(blk + static_cast<int64_t>(k) * prep::kF16Row);
         if (k >= n_codes) {   // the 8 lanes of a row take the same branch
-            const bf16x8 z = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-            row[2 * grp] = z;
-            row[2 * grp + 1] = z;
             row16[grp] = u32x4{0u, 0u, 0u, 0u};
-            if (grp == 0) {
-                norms[k] = kNoScore;
-                row16[8] = u32x4{0u, 0u, 0u, 0u};
-            }
+            if (grp == 0) row16[8] = u32x4{0u, 0u, 0u, 0u};
             continue;
         }
         const f32x4 *src = reinterpret_cast<const f32x4 *>(stage + static_cast<int64_t>(k) * kDim + 8 * grp);
         const f32x4 va = src[0], vb = src[1];
         const float v[8] = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-        float s = 0.0f, s16 = 0.0f;
+        float s16 = 0.0f;
         f16x8 h16;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            s = __builtin_fmaf(v[t], v[t], s);
             const float w = ldexpf(v[t], e);   // exact unless it falls below the fp32 normal range
             s16 = __builtin_fmaf(w, w, s16);
             h16[t] = static_cast<_Float16>(w);   // round to nearest even
         }
-        bf16x8 hi, lo;
-        split8(v, hi, lo);
-        row[2 * grp] = hi;
-        row[2 * grp + 1] = lo;
         row16[grp] = __builtin_bit_cast(u32x4, h16);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
         s16 += __shfl_xor(s16, 1);
         s16 += __shfl_xor(s16, 2);
         s16 += __shfl_xor(s16, 4);
-        const float hn = 0.5f * s;
         const float hn16 = 0.5f * s16;
         if (grp == 0) {
-            norms[k] = hn;
             // two fp16 parts: hn16 - hi is exact in fp32
             const _Float16 p_hi = static_cast<_Float16>(hn16);
             const _Float16 p_lo = static_cast<_Float16>(hn16 - static_cast<float>(p_hi));
@@ -854,61 +698,13 @@ void prepare_kernel(const float *__restrict__ books, int n_codes, uint8_t *__res
                                  (static_cast<unsigned>(__builtin_bit_cast(unsigned short, p_lo)) << 16),
                              0u, 0u, 0u};
         }
-        m = max(m, __float_as_uint(hn));   // hn >= 0: bits order like values
-        m16 = max(m16, __float_as_uint(hn16));
+        m16 = max(m16, __float_as_uint(hn16));   // hn16 >= 0: bits order like values
     }
-    const unsigned mm = block_max_bits(m, s_m);
     const unsigned mm16 = block_max_bits(m16, s_m);
     if (threadIdx.x == 0) {
-        reinterpret_cast<unsigned *>(blk + prep::bf16_max(kp))[c] = mm;
         reinterpret_cast<unsigned *>(blk + prep::f16_max(kp))[c] = in_range ? mm16 : 0x7F800000u;
         if (c == 0) *reinterpret_cast<int *>(blk + prep::f16_exp(kp)) = e;
     }
-}
-
-template <bool kPrepared>
-hipError_t launch_variant(const float *x, int64_t n_frames, const float *books, const uint8_t *prepared,
-                          int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
-                          float *recon, hipStream_t stream)
-{
-    const int64_t blocks = (n_frames + kBlockFrames - 1) / kBlockFrames;
-    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-    if (n_frames <= kSplitMaxFrames) {
-        // few frames: one 32-frame tile per workgroup, the codebook split over its wavefronts
-        const dim3 sgrid(static_cast<unsigned>((n_frames + kFramesPerWave - 1) / kFramesPerWave));
-        const dim3 sblock(64 * kSplitWaves);
-        if (recon && residual)
-            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<true, true, kPrepared>), sgrid, sblock, 0, stream,
-                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else if (recon)
-            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<true, false, kPrepared>), sgrid, sblock, 0, stream,
-                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else if (residual)
-            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<false, true, kPrepared>), sgrid, sblock, 0, stream,
-                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else
-            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<false, false, kPrepared>), sgrid, sblock, 0, stream,
-                               x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon);
-        return hipGetLastError();
-    }
-    if constexpr (kPrepared) {
-        return hipErrorInvalidValue;   // wide batches with prepared codebooks take the fp16 kernel
-    } else {
-        const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-        if (recon && residual)
-            hipLaunchKernelGGL((encode_bf16_kernel<true, true>), grid, block, 0, stream,
-                               x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else if (recon)
-            hipLaunchKernelGGL((encode_bf16_kernel<true, false>), grid, block, 0, stream,
-                               x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else if (residual)
-            hipLaunchKernelGGL((encode_bf16_kernel<false, true>), grid, block, 0, stream,
-                               x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
-        else
-            hipLaunchKernelGGL((encode_bf16_kernel<false, false>), grid, block, 0, stream,
-                               x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
-    }
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -927,19 +723,40 @@ hipError_t launch_encode_bf16(const float *x, int64_t n_frames, const float *boo
                               int n_stages, int n_codes, int32_t *codes, int codes_ld,
                               float *residual, float *recon, hipStream_t stream)
 {
-    return launch_variant<false>(x, n_frames, books, nullptr, n_stages, n_codes, codes, codes_ld, residual,
-                                 recon, stream);
-}
-
-hipError_t launch_encode_prepared(const float *x, int64_t n_frames, const float *books, const void *prepared,
-                                  int n_stages, int n_codes, int32_t *codes, int codes_ld,
-                                  float *residual, float *recon, hipStream_t stream)
-{
-    if (n_frames > kPreparedSplitMaxFrames)
-        return launch_encode_f16(x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon,
-                                 stream);
-    return launch_variant<true>(x, n_frames, books, static_cast<const uint8_t *>(prepared), n_stages, n_codes,
-                                codes, codes_ld, residual, recon, stream);
+    const int64_t blocks = (n_frames + kBlockFrames - 1) / kBlockFrames;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    if (n_frames <= kSplitMaxFrames) {
+        // few frames: one 32-frame tile per workgroup, the codebook split over its wavefronts
+        const dim3 sgrid(static_cast<unsigned>((n_frames + kFramesPerWave - 1) / kFramesPerWave));
+        const dim3 sblock(64 * kSplitWaves);
+        if (recon && residual)
+            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<true, true>), sgrid, sblock, 0, stream,
+                               x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+        else if (recon)
+            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<true, false>), sgrid, sblock, 0, stream,
+                               x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+        else if (residual)
+            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<false, true>), sgrid, sblock, 0, stream,
+                               x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+        else
+            hipLaunchKernelGGL((encode_bf16_ksplit_kernel<false, false>), sgrid, sblock, 0, stream,
+                               x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+        return hipGetLastError();
+    }
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+    if (recon && residual)
+        hipLaunchKernelGGL((encode_bf16_kernel<true, true>), grid, block, 0, stream,
+                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else if (recon)
+        hipLaunchKernelGGL((encode_bf16_kernel<true, false>), grid, block, 0, stream,
+                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else if (residual)
+        hipLaunchKernelGGL((encode_bf16_kernel<false, true>), grid, block, 0, stream,
+                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else
+        hipLaunchKernelGGL((encode_bf16_kernel<false, false>), grid, block, 0, stream,
+                           x, n_frames, books, n_stages, n_codes, codes, codes_ld, residual, recon);
+    return hipGetLastError();
 }
 
 }  // namespace rvq

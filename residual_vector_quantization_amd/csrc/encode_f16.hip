@@ -51,6 +51,9 @@
 // 256-codeword chunks (double buffered), each chunk scored as four
 // 64-codeword groups of two interleaved matrix-core chains, with the key
 // scan of one group issued between the matrix-core steps of the next.
+// Batches too small to fill the CUs that way (up to 8,192 frames) take a
+// second kernel, at the end of this file, that splits every stage's
+// codebook over the wavefronts of a workgroup instead.
 #include "encode_common.h"
 #include "prepared.h"
 
@@ -741,7 +744,7 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
         const int c = g - q * n_chunks;
         const uint8_t *blk = prepared + q * sbytes;
         const int k0 = c * kChunk + kWaveRows * wave;
-        const uint8_t *src = blk + prep::f16_offset(kp) + static_cast<int64_t>(k0) * prep::kF16Row + 16 * lane;
+        const uint8_t *src = blk + static_cast<int64_t>(k0) * prep::kF16Row + 16 * lane;
         _Float16 *dst = s_rows[g & 1] + kWaveRows * wave * kRowHalfs;
 #pragma unroll
         for (int i = 0; i < kWaveLoads; ++i) dma16(src + 1024 * i, dst + i * 512);
@@ -845,11 +848,228 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
     }
 }
 
-}  // namespace
+// ---- small batches: the codebook split over a workgroup's wavefronts -------
+//
+// A workgroup of four wavefronts holds one 32-frame tile (every wavefront
+// the same frames, in the same lanes); wavefront w scores the 256-codeword
+// chunks w, w + 4, ... of every stage out of its own LDS buffer (copied
+// straight from the prepared block, the next chunk as soon as the current
+// one is scored, so the next stage's first chunk loads during the
+// decision). Within a 1024-codeword span each wavefront holds one chunk,
+// so its keys are folded into indices after every chunk. The wavefronts'
+// key sets are then merged through LDS in wavefront order -- the smallest
+// key and its codeword, the second smallest of the two sets' four keys,
+// and a lower bound of the third -- and every wavefront takes the same
+// decision from the same merged sets (the decision only reads the
+// codebook), so each keeps the residual without a broadcast; wavefront 0
+// stores codes, residual and reconstruction. The keys, bound and decision
+// are the wide kernel's, so the codes are too.
+constexpr int kKsWaves = 4;
+constexpr int kKsThreads = 64 * kKsWaves;
+constexpr int kKsChunkLoads = kChunk * kRowSlots / 64;   // wavefront-wide 16-byte copies per chunk
+constexpr int kKsKeyWords = 10;                          // per lane: 2 sets x (best, second, third, best_k, second_k)
 
-hipError_t launch_encode_f16(const float *x, int64_t n_frames, const float *books, const void *prepared,
-                             int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
-                             float *recon, hipStream_t stream)
+// The two smallest keys of the union of sets a and b (with their codewords;
+// equal keys: the lower codeword first) and a lower bound of the third
+// smallest: the third order statistic of two sorted lists is
+// min(a3, b3, max(a1, b2), max(a2, b1)), and a.third, b.third are at most a3, b3.
+__device__ __forceinline__ KeySet merge_sets(const KeySet &a, const KeySet &b)
+{
+    const bool a_first = a.best < b.best || (a.best == b.best && a.best_k <= b.best_k);
+    const float wb = a_first ? a.best : b.best, ws = a_first ? a.second : b.second;
+    const int wbk = a_first ? a.best_k : b.best_k, wsk = a_first ? a.second_k : b.second_k;
+    const float lb = a_first ? b.best : a.best;
+    const int lbk = a_first ? b.best_k : a.best_k;
+    const bool loser_second = lb < ws || (lb == ws && lbk <= wsk);
+    KeySet m;
+    m.best = wb;
+    m.best_k = wbk;
+    m.second = loser_second ? lb : ws;
+    m.second_k = loser_second ? lbk : wsk;
+    m.third = fminf(fminf(a.third, b.third), fminf(fmaxf(a.best, b.second), fmaxf(a.second, b.best)));
+    return m;
+}
+
+template <bool kRecon, bool kResidual>
+__global__ __attribute__((amdgpu_flat_work_group_size(kKsThreads, kKsThreads), amdgpu_waves_per_eu(1)))   // one workgroup per CU (LDS)
+void encode_f16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
+                              const float *__restrict__ books, const uint8_t *__restrict__ prepared,
+                              int n_stages, int n_codes,
+                              int32_t *__restrict__ codes, int codes_ld,
+                              float *__restrict__ residual, float *__restrict__ recon)
+{
+    __shared__ __align__(16) _Float16 s_rows[kKsWaves][kChunk * kRowHalfs];   // one chunk per wavefront
+    __shared__ __align__(16) float s_frame[kKsWaves][kDim];                    // rescan: one frame's residual
+    __shared__ unsigned s_keys[kKsWaves][kKsKeyWords][64];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31;
+    const int half = lane >> 5;
+    const int64_t frame = static_cast<int64_t>(blockIdx.x) * kFramesPerWave + col;
+    const bool valid = frame < n_frames;
+
+    unsigned kmask;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(kmask) : "i"(kKeyMask8));
+    float n[32];     // negated residual, dims 32*half .. 32*half+31
+    float acc[32];   // reconstruction (kRecon)
+    if (valid) {
+        const f32x4 *src = reinterpret_cast<const f32x4 *>(x + frame * kDim + 32 * half);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const f32x4 v = src[t];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) n[4 * t + i] = -v[i];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) n[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) acc[j] = 0.0f;
+
+    const int64_t kp = prep::padded_codes(n_codes);
+    const int64_t sbytes = prep::stage_bytes(n_codes);
+    const int n_chunks = static_cast<int>(kp / kChunk);
+    const int n_groups = (n_codes + 63) / 64;
+    _Float16 *sb = s_rows[wave];
+    // chunk c of stage q into this wavefront's buffer (after its earlier
+    // reads of the buffer have completed)
+    auto dma_chunk = [&](int q, int c) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const uint8_t *src = prepared + q * sbytes + static_cast<int64_t>(c) * kChunk * prep::kF16Row + 16 * lane;
+#pragma unroll 4
+        for (int i = 0; i < kKsChunkLoads; ++i) dma16(src + 1024 * i, sb + i * 512);
+    };
+    if (wave < n_chunks) dma_chunk(0, wave);
+
+    for (int q = 0; q < n_stages; ++q) {
+        const uint8_t *blk = prepared + q * sbytes;
+        const unsigned cmax = stage_max_part(blk, kp, lane);
+        const int e = *reinterpret_cast<const int *>(blk + prep::f16_exp(kp));
+        f16x8 nb[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) nb[s] = to_f16x8(&n[8 * s]);
+        const f16x2 sc = {static_cast<_Float16>(ldexpf(1.0f, -e)), static_cast<_Float16>(ldexpf(1.0f, -e))};
+        const f16x8 nnorm = __builtin_bit_cast(f16x8, u32x4{half ? 0u : __builtin_bit_cast(unsigned, sc), 0u, 0u, 0u});
+
+        KeySet ks[2];
+        reset(ks[0]);
+        reset(ks[1]);
+        for (int c = wave; c < n_chunks; c += kKsWaves) {
+            wait_all();   // this chunk has landed in the buffer
+            const unsigned bb0[2] = {__float_as_uint(ks[0].best), __float_as_uint(ks[1].best)};
+            const unsigned sb0[2] = {__float_as_uint(ks[0].second), __float_as_uint(ks[1].second)};
+            f32x16 da[2], db[2];
+            // groups 4c + 0..3: each step scores one group and scans the one before
+            // (even groups into set 0, odd into set 1), the last one alone
+#pragma unroll
+            for (int kg = 0; kg < kGroups; ++kg) {
+                f32x16 (&dn)[2] = (kg & 1) ? db : da;
+                f32x16 (&dp)[2] = (kg & 1) ? da : db;
+                const int pbase = c * kChunk + 64 * (kg - 1);   // the group scanned in this step
+                if (kg > 0 && (pbase >> 6) < n_groups) {
+                    if (pbase + 64 > n_codes) mask_tail(dp, pbase, half, n_codes);
+                    step_group<true>(dn, dp, kg, sb, col, half, nb, nnorm, group_bits(pbase), kmask, ks[(kg - 1) & 1]);
+                } else {
+                    step_group<false>(dn, dp, kg, sb, col, half, nb, nnorm, 0, kmask, ks[0]);
+                }
+            }
+            const int lbase = c * kChunk + 64 * (kGroups - 1);
+            if ((lbase >> 6) < n_groups) {
+                if (lbase + 64 > n_codes) mask_tail(db, lbase, half, n_codes);
+                scan_last(db, group_bits(lbase), kmask, ks[1]);
+            }
+            // this wavefront holds no other chunk of the span: fold both sets
+            const int span = (c * kChunk) & ~(kSpan - 1);
+            fold(ks[0], bb0[0], sb0[0], span, 0, half);
+            fold(ks[1], bb0[1], sb0[1], span, 1, half);
+            // the buffer is free: the next chunk of this stage, or the next stage's first
+            if (c + kKsWaves < n_chunks)
+                dma_chunk(q, c + kKsWaves);
+            else if (q + 1 < n_stages)
+                dma_chunk(q + 1, wave);
+        }
+
+        // ---- merge the wavefronts' key sets (the same result on every wavefront) ----
+        __syncthreads();   // the previous stage's merge has read s_keys
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            s_keys[wave][5 * s + 0][lane] = __float_as_uint(ks[s].best);
+            s_keys[wave][5 * s + 1][lane] = __float_as_uint(ks[s].second);
+            s_keys[wave][5 * s + 2][lane] = __float_as_uint(ks[s].third);
+            s_keys[wave][5 * s + 3][lane] = static_cast<unsigned>(ks[s].best_k);
+            s_keys[wave][5 * s + 4][lane] = static_cast<unsigned>(ks[s].second_k);
+        }
+        __syncthreads();
+        KeySet mk[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            for (int w = 0; w < kKsWaves; ++w) {
+                KeySet o;
+                o.best = __uint_as_float(s_keys[w][5 * s + 0][lane]);
+                o.second = __uint_as_float(s_keys[w][5 * s + 1][lane]);
+                o.third = __uint_as_float(s_keys[w][5 * s + 2][lane]);
+                o.best_k = static_cast<int>(s_keys[w][5 * s + 3][lane]);
+                o.second_k = static_cast<int>(s_keys[w][5 * s + 4][lane]);
+                mk[s] = w == 0 ? o : merge_sets(mk[s], o);
+            }
+        }
+
+        const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
+        const float m16 = wave_max_bits(cmax);
+        decide_stage<kRecon>(n, acc, mk, book, n_codes, m16, e, valid, half, col, lane, s_frame[wave],
+                             (wave == 0 && valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
+    }
+
+    if (wave == 0 && valid) {
+        if (kResidual) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(residual + frame * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) dst[t] = f32x4{-n[4 * t], -n[4 * t + 1], -n[4 * t + 2], -n[4 * t + 3]};
+        }
+        if (kRecon) {
+            f32x4 *dst = reinterpret_cast<f32x4 *>(recon + frame * kDim + 32 * half);
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                dst[t] = f32x4{acc[4 * t], acc[4 * t + 1], acc[4 * t + 2], acc[4 * t + 3]};
+        }
+    }
+}
+
+// Up to this many frames the split-codebook kernel runs: at 32 frames per
+// workgroup, one workgroup per CU, the batch still fits one round on 256 CUs
+// (measured, 8 stages of 1024: 8,192 frames 72 us against 97 us for the
+// wide kernel's 256-frame tiles).
+constexpr int64_t kSplitMaxFrames = 8192;
+
+hipError_t launch_ksplit(const float *x, int64_t n_frames, const float *books, const void *prepared,
+                         int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
+                         float *recon, hipStream_t stream)
+{
+    const int64_t blocks = (n_frames + kFramesPerWave - 1) / kFramesPerWave;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<unsigned>(blocks)), block(kKsThreads);
+    const uint8_t *p = static_cast<const uint8_t *>(prepared);
+    if (recon && residual)
+        hipLaunchKernelGGL((encode_f16_ksplit_kernel<true, true>), grid, block, 0, stream,
+                           x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else if (recon)
+        hipLaunchKernelGGL((encode_f16_ksplit_kernel<true, false>), grid, block, 0, stream,
+                           x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else if (residual)
+        hipLaunchKernelGGL((encode_f16_ksplit_kernel<false, true>), grid, block, 0, stream,
+                           x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
+    else
+        hipLaunchKernelGGL((encode_f16_ksplit_kernel<false, false>), grid, block, 0, stream,
+                           x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
+    return hipGetLastError();
+}
+
+hipError_t launch_wide(const float *x, int64_t n_frames, const float *books, const void *prepared,
+                       int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
+                       float *recon, hipStream_t stream)
 {
     const int64_t blocks = (n_frames + kBlockFrames - 1) / kBlockFrames;
     if (blocks > 0x7fffffff) return hipErrorInvalidValue;
@@ -868,6 +1088,18 @@ hipError_t launch_encode_f16(const float *x, int64_t n_frames, const float *book
         hipLaunchKernelGGL((encode_f16_kernel<false, false>), grid, block, 0, stream,
                            x, n_frames, books, p, n_stages, n_codes, codes, codes_ld, residual, recon);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_encode_prepared(const float *x, int64_t n_frames, const float *books, const void *prepared,
+                                  int n_stages, int n_codes, int32_t *codes, int codes_ld,
+                                  float *residual, float *recon, hipStream_t stream)
+{
+    if (n_frames <= kSplitMaxFrames)
+        return launch_ksplit(x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon,
+                             stream);
+    return launch_wide(x, n_frames, books, prepared, n_stages, n_codes, codes, codes_ld, residual, recon, stream);
 }
 
 }  // namespace rvq

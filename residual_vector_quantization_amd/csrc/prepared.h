@@ -4,18 +4,13 @@
 //
 // Per stage one block, kStageAlign-aligned, with Kp = n_codes rounded up to
 // kChunk rows:
-//   split-bf16 section (at 0)
-//     rows   [Kp][256 B]        16-byte segments (8 bf16 hi, 8 bf16 lo) per 8-dim group
-//     norms  [Kp] f32           0.5*||c||^2, FLT_MAX for rows k >= n_codes
-//     max    [Kp/kChunk] u32    bits of the largest valid 0.5*||c||^2 of each kChunk rows
-//   fp16 section (at f16_offset(Kp))
-//     rows   [Kp][144 B]        128 B: fp16 of c' = 2^e c (round to nearest even), dims in
-//                               order; then 16 B: 0.5*||c'||^2 (fp32 sum) as two fp16 parts
-//                               hi | lo << 16 in the first word, zeros after it
-//     max    [Kp/kChunk] u32    bits of the largest valid 0.5*||c'||^2 of each kChunk rows,
-//                               or of +inf when the stage is out of the fp16 range
-//     e      i32                the stage's power-of-two scale
-// Rows k >= n_codes are zero in both sections.
+//   rows   [Kp][144 B]        128 B: fp16 of c' = 2^e c (round to nearest even), dims in
+//                             order; then 16 B: 0.5*||c'||^2 (fp32 sum) as two fp16 parts
+//                             hi | lo << 16 in the first word, zeros after it
+//   max    [Kp/kChunk] u32    bits of the largest valid 0.5*||c'||^2 of each kChunk rows,
+//                             or of +inf when the stage is out of the fp16 range
+//   e      i32                the stage's power-of-two scale
+// Rows k >= n_codes are zero.
 #pragma once
 
 #include <stdint.h>
@@ -29,14 +24,8 @@ constexpr int64_t kStageAlign = 256;
 __host__ __device__ inline int64_t padded_codes(int n_codes) { return (n_codes + kChunk - 1) / kChunk * kChunk; }
 __host__ __device__ inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
-// split-bf16 section
-__host__ __device__ inline int64_t bf16_norms(int64_t kp) { return kp * 256; }
-__host__ __device__ inline int64_t bf16_max(int64_t kp) { return kp * 260; }
-
-// fp16 section
-__host__ __device__ inline int64_t f16_offset(int64_t kp) { return round_up(kp * 260 + 4 * (kp / kChunk), kStageAlign); }
-constexpr int64_t kF16Row = 144;   // bytes of an fp16-section row
-__host__ __device__ inline int64_t f16_max(int64_t kp) { return f16_offset(kp) + kp * kF16Row; }
+constexpr int64_t kF16Row = 144;   // bytes of a row
+__host__ __device__ inline int64_t f16_max(int64_t kp) { return kp * kF16Row; }
 __host__ __device__ inline int64_t f16_exp(int64_t kp) { return f16_max(kp) + 4 * (kp / kChunk); }
 
 __host__ __device__ inline int64_t stage_bytes(int n_codes)

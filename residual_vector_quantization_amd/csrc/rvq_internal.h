@@ -36,15 +36,12 @@ int64_t prepared_bytes(int n_stages, int n_codes);
 // Writes the prepared codebooks (layout in prepared.h).
 hipError_t launch_prepare(const float *books, int n_stages, int n_codes, void *prepared, hipStream_t stream);
 
-// Split-bf16 encode that stages prepared rows instead of splitting them.
+// Same contract and results, scores on the fp16 matrix cores from prepared
+// codebooks: batches of up to 8,192 frames split each stage's codebook over
+// a workgroup's wavefronts, larger ones tile the frames.
 hipError_t launch_encode_prepared(const float *x, int64_t n_frames, const float *books, const void *prepared,
                                   int n_stages, int n_codes, int32_t *codes, int codes_ld,
                                   float *residual, float *recon, hipStream_t stream);
-
-// fp16-scored encode of many frames from prepared codebooks (their fp16 section).
-hipError_t launch_encode_f16(const float *x, int64_t n_frames, const float *books, const void *prepared,
-                             int n_stages, int n_codes, int32_t *codes, int codes_ld, float *residual,
-                             float *recon, hipStream_t stream);
 
 // Launches the gather-sum decode.
 hipError_t launch_decode(const int32_t *codes, int codes_ld, int64_t n_frames,

@@ -36,10 +36,10 @@ def announce(what, **shape):
 
 SCORINGS = ["default", "fp32", "prepared"]
 
-# Batches of up to 16384 frames (8192 with prepared codebooks) take the
-# split-codebook encode (one 32-frame tile per workgroup); larger ones a wide
-# kernel. widen() embeds a small case into a batch that takes the wide
-# kernel on every path.
+# Batches of up to 16384 frames (8192 with prepared codebooks) take a
+# split-codebook encode (one 32-frame tile per workgroup, the codebook split
+# over its wavefronts); larger ones a wide kernel. widen() embeds a small
+# case into a batch that takes the wide kernel on every path.
 SPLIT_MAX_FRAMES = 16384
 PREPARED_SPLIT_MAX_FRAMES = 8192
 WIDE_FRAMES = SPLIT_MAX_FRAMES + 300

@@ -76,7 +76,8 @@ def test_status_strings(libpath):
 def test_prepared_bytes_shape_rules(libpath):
     import residual_vector_quantization_amd as rvq
     a = rvq.rvq_prepared_bytes(8, 1024, 64)
-    assert a > 8 * 1024 * 256 and a % 256 == 0
+    # per stage: 144-byte rows, one maximum per 256 rows and the scale, in a 256-byte aligned block
+    assert a == 8 * ((1024 * 144 + 4 * 4 + 4 + 255) // 256 * 256)
     assert rvq.rvq_prepared_bytes(8, 1000, 64) == a   # rows are padded to whole chunks
     assert rvq.rvq_prepared_bytes(1, 1, 64) > 0
     with pytest.raises(rvq.RVQError):

@@ -227,18 +227,10 @@ def test_unknown_scoring_rejected():
         m.rvq_encode_scored(torch.zeros((4, 64), device="cuda:0"), torch.zeros((1, 64, 64), device="cuda:0"), "fp8")
 
 
-def _bf16_rne(v):
-    """float32 -> bfloat16 (round to nearest even) as float32, for finite v."""
-    u = v.astype(np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    return r.astype(np.uint32).view(np.float32)
-
-
 def _stage_layout(k):
-    """(Kp, offset of the fp16 section, stage block bytes) of the prepared layout."""
+    """(Kp, stage block bytes) of the prepared layout."""
     kp = (k + 255) // 256 * 256
-    f16 = (kp * 260 + 4 * (kp // 256) + 255) // 256 * 256
-    return kp, f16, (f16 + kp * 144 + 4 * (kp // 256) + 4 + 255) // 256 * 256
+    return kp, (kp * 144 + 4 * (kp // 256) + 4 + 255) // 256 * 256
 
 
 def _stage_exp(book):
@@ -249,41 +241,23 @@ def _stage_exp(book):
 
 @pytest.mark.parametrize("q,k", [(3, 1000), (2, 256), (1, 1)])
 def test_prepared_layout(q, k):
-    """rvq_prepare_codebooks. Split-bf16 section: per stage Kp = roundup(K, 256) rows of 8-dim groups
-    (8 hi, 8 lo bf16), hi = bf16(v) and lo = bf16(v - hi) round to nearest even; Kp fp32 half-norms
-    (FLT_MAX on padding rows, which are zero); the bits of the largest valid half-norm of every 256
-    rows. fp16 section: 144-byte rows of fp16 (round to nearest even) of c' = 2^e c with the stage's
-    power of two e, then the two fp16 parts of 0.5*||c'||^2 and zeros; the largest of those per 256
-    rows; e. Stage blocks 256-byte aligned."""
+    """rvq_prepare_codebooks: per stage Kp = roundup(K, 256) rows of 144 bytes, fp16 (round to
+    nearest even) of c' = 2^e c with the stage's power of two e, then the two fp16 parts of
+    0.5*||c'||^2 and zeros (padding rows all zero); the largest of those per 256 rows; e. Stage
+    blocks 256-byte aligned."""
     m = rvq()
     rng = np.random.default_rng(600 + k)
     books = (rng.standard_normal((q, k, 64)) * 3.0 * 4.0 ** -np.arange(q)[:, None, None]).astype(np.float32)
     books[0, 0] = 0.0
     prep = host(m.rvq_prepare_codebooks(to_dev(books)))
-    kp, f16, sbytes = _stage_layout(k)
+    kp, sbytes = _stage_layout(k)
     assert prep.size >= q * sbytes
     for s in range(q):
         blk = prep[s * sbytes:(s + 1) * sbytes]
-        rows = blk[:kp * 256].view(np.uint16).reshape(kp, 8, 2, 8)   # row, group, hi/lo, element
-        as_f32 = lambda h: (h.astype(np.uint32) << 16).view(np.float32)
-        hi, lo = as_f32(rows[:, :, 0, :]).reshape(kp, 64), as_f32(rows[:, :, 1, :]).reshape(kp, 64)
-        want_hi = _bf16_rne(books[s])
-        np.testing.assert_array_equal(hi[:k], want_hi)
-        np.testing.assert_array_equal(lo[:k], _bf16_rne(books[s] - want_hi))
-        assert not rows[k:].any()
-        norms = blk[kp * 256:kp * 260].view(np.float32)
-        exact = 0.5 * (books[s].astype(np.float64) ** 2).sum(axis=1)
-        np.testing.assert_allclose(norms[:k], exact, rtol=1e-6, atol=0)
-        assert (norms[k:] == np.finfo(np.float32).max).all()
-        maxima = blk[kp * 260:kp * 260 + 4 * (kp // 256)].view(np.uint32)
-        for c in range(kp // 256):
-            valid = norms[256 * c:min(256 * (c + 1), k)]
-            assert maxima[c] == (valid.view(np.uint32).max() if valid.size else 0)
-        # fp16 section
         e = _stage_exp(books[s])
-        assert blk[f16 + kp * 144 + 4 * (kp // 256):][:4].view(np.int32)[0] == e
+        assert blk[kp * 144 + 4 * (kp // 256):][:4].view(np.int32)[0] == e
         scaled = (books[s].astype(np.float64) * 2.0 ** e).astype(np.float32)   # exact: a power of two
-        rows = blk[f16:f16 + kp * 144].view(np.uint16).reshape(kp, 72)
+        rows = blk[:kp * 144].view(np.uint16).reshape(kp, 72)
         rows16 = rows[:, :64]
         np.testing.assert_array_equal(rows16[:k], scaled.astype(np.float16).view(np.uint16))
         assert not rows16[k:].any()
@@ -295,33 +269,33 @@ def test_prepared_layout(q, k):
         # the high part is the fp16 rounding of the sum of both parts
         np.testing.assert_array_equal(parts[:k, 0], got.astype(np.float16).astype(np.float64))
         assert not parts[k:].any()
-        max16 = blk[f16 + kp * 144:f16 + kp * 144 + 4 * (kp // 256)].view(np.float32)
+        max16 = blk[kp * 144:kp * 144 + 4 * (kp // 256)].view(np.float32)
         for c in range(kp // 256):
             w = want[256 * c:min(256 * (c + 1), k)]
             assert max16[c] == pytest.approx(w.max() if w.size else 0.0, rel=2e-6, abs=1e-30)
 
 
 def test_prepared_out_of_fp16_range():
-    """A stage with entries beyond 2^20 is marked by infinite fp16-section maxima; an all-zero stage
-    has e = 0."""
+    """A stage with entries beyond 2^20 is marked by infinite maxima; an all-zero stage has e = 0."""
     m = rvq()
     rng = np.random.default_rng(610)
     books = rng.standard_normal((3, 300, 64)).astype(np.float32)
     books[1] *= 2.0 ** 22
     books[2] = 0.0
     prep = host(m.rvq_prepare_codebooks(to_dev(books)))
-    kp, f16, sbytes = _stage_layout(300)
+    kp, sbytes = _stage_layout(300)
     for s, inf in ((0, False), (1, True), (2, False)):
         blk = prep[s * sbytes:(s + 1) * sbytes]
-        max16 = blk[f16 + kp * 144:f16 + kp * 144 + 4 * (kp // 256)].view(np.float32)
+        max16 = blk[kp * 144:kp * 144 + 4 * (kp // 256)].view(np.float32)
         assert bool(np.isinf(max16).all()) == inf and bool(np.isinf(max16).any()) == inf
-        assert blk[f16 + kp * 144 + 4 * (kp // 256):][:4].view(np.int32)[0] == _stage_exp(books[s])
+        assert blk[kp * 144 + 4 * (kp // 256):][:4].view(np.int32)[0] == _stage_exp(books[s])
 
 
 @pytest.mark.parametrize("case", ["huge_stage", "huge_residual", "some_huge_residuals", "tiny_residual",
                                   "near_duplicates", "clustered"])
-def test_prepared_wide_fp16_edges(case):
-    """Wide batches through the prepared path: a stage out of the fp16 range, residuals out of it
+@pytest.mark.parametrize("wide", [False, True])
+def test_prepared_fp16_edges(case, wide):
+    """Small and wide batches through the prepared path: a stage out of the fp16 range, residuals out of it
     (both resolved by the float64 rescan; for some frames of each wavefront only, the others decided
     as usual), residuals in the fp16 subnormal range, near-duplicate
     rows (re-rank within one key set) and rows clustered so tightly that frames hold many
@@ -344,12 +318,13 @@ def test_prepared_wide_fp16_edges(case):
         centre = rng.standard_normal((4, 1, 64)).astype(np.float32)
         books = (centre + 1e-3 * rng.standard_normal((4, 1024, 64))).astype(np.float32)
         x = (centre[0] + 1e-3 * rng.standard_normal((400, 64))).astype(np.float32)
-    _check(x, books, True, "prepared")
+    _check(x, books, wide, "prepared")
 
 
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("seed", range(6))
-def test_prepared_wide_random_shapes_and_scales(seed):
-    """fp16-scored path under random stage counts, codebook sizes (not multiples of 64), per-stage
+def test_prepared_random_shapes_and_scales(seed, wide):
+    """fp16-scored paths (small and wide batches) under random stage counts, codebook sizes (not multiples of 64), per-stage
     codebook scales from 1e-3 to 1e3 (stage exponents across their range), residual scales, and
     near-duplicate rows; codes, residuals and reconstructions against the oracle."""
     rng = np.random.default_rng(700 + seed)
@@ -362,13 +337,14 @@ def test_prepared_wide_random_shapes_and_scales(seed):
         books[:, j] = books[:, rng.integers(0, k, size=j.size)] * (
             1.0 + 1e-6 * rng.standard_normal((q, j.size, 64))).astype(np.float32)
     x = (rng.standard_normal((300, 64)) * 10.0 ** rng.uniform(-3, 3)).astype(np.float32)
-    _check(x, books, True, "prepared")
+    _check(x, books, wide, "prepared")
 
 
 @pytest.mark.parametrize("case", ["mixed_dims", "subnormal_frames", "clamped_scale_stage", "zero_frames_and_rows",
                                   "sparse_integer"])
-def test_prepared_wide_value_extremes(case):
-    """Wide batches through the fp16-scored path on value patterns the random cases do not reach:
+@pytest.mark.parametrize("wide", [False, True])
+def test_prepared_value_extremes(case, wide):
+    """Small and wide batches through the fp16-scored paths on value patterns the random cases do not reach:
     per-dimension scales spread over eight decades (the bound's norm terms dominated by a few
     dimensions), frames of float32 subnormals (flushed by the fp16 conversion, decided by the
     bound's absolute terms), a stage whose scale exponent is clamped (entries near 1e-12, fp16
@@ -393,7 +369,7 @@ def test_prepared_wide_value_extremes(case):
     else:
         books = (rng.integers(-2, 3, size=(4, k, 64)) * (rng.random((4, k, 64)) < 0.1)).astype(np.float32)
         x = (rng.integers(-3, 4, size=(400, 64)) * (rng.random((400, 64)) < 0.2)).astype(np.float32)
-    _check(x, books, True, "prepared")
+    _check(x, books, wide, "prepared")
 
 
 @pytest.mark.parametrize("wide", [False, True])
