@@ -165,6 +165,30 @@ def test_deterministic_and_batch_invariant():
     np.testing.assert_array_equal(host(rc), host(ra)[perm])
 
 
+@pytest.mark.parametrize("q,k", [(8, 1024), (5, 300), (3, 4096)])
+def test_prepared_batch_invariant_across_kernels(q, k):
+    """The same frames encoded from prepared codebooks inside a batch that takes the wide kernel and
+    alone as batches that take the split-codebook kernel (8,192 frames, its largest, and 333) give the
+    same codes, residuals and reconstructions, all frames compared (both kernels decide every stage
+    exactly, so neither may differ from the other in any frame)."""
+    rng = np.random.default_rng(40 + k)
+    books = _books(rng, q, k)
+    x = rng.standard_normal((20000, 64)).astype(np.float32)
+    x[10000:] = (x[10000:] * 1e-3).astype(np.float32)   # small residuals too
+    m = rvq()
+    bg = to_dev(books)
+    prep = m.rvq_prepare_codebooks(bg)
+    announce("prepared batch invariance", n=20000, q=q, k=k)
+    wc, wr, wres = (host(t) for t in m.rvq_encode_prepared(to_dev(x), bg, prep, recon=True))
+    perm = rng.permutation(20000)
+    for sub in (perm[:8192], perm[8192:8192 + 333]):
+        announce("prepared batch invariance, split kernel", n=sub.size, q=q, k=k)
+        c, r, res = (host(t) for t in m.rvq_encode_prepared(to_dev(x[sub]), bg, prep, recon=True))
+        np.testing.assert_array_equal(c, wc[sub])
+        np.testing.assert_array_equal(res, wres[sub])
+        np.testing.assert_array_equal(r, wr[sub])
+
+
 def test_empty_batch_is_noop():
     import torch
     m = rvq()
