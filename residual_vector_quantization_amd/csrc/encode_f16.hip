@@ -400,6 +400,65 @@ __device__ __forceinline__ double row_distance_f64(const float *row, const float
     return acc;
 }
 
+// kParts wavefronts of a workgroup that resolve the same frame each take
+// every kParts-th codeword and then combine their results through LDS
+// (`xch`, 4 words per wavefront), all in wavefront order, so that every one
+// of them ends with the same values. Every wavefront of the workgroup must
+// call these, equally often; the first barrier keeps a previous exchange's
+// readers ahead of this one's writers.
+template <int kParts>
+__device__ __forceinline__ void exchange_f32(float &f1, float &f2, int &k1, unsigned *xch, int part, int lane)
+{
+    __syncthreads();
+    if (lane == 0) {
+        xch[4 * part] = __float_as_uint(f1);
+        xch[4 * part + 1] = __float_as_uint(f2);
+        xch[4 * part + 2] = static_cast<unsigned>(k1);
+    }
+    __syncthreads();
+    float a1 = __uint_as_float(xch[0]), a2 = __uint_as_float(xch[1]);
+    int ak = static_cast<int>(xch[2]);
+#pragma unroll
+    for (int p = 1; p < kParts; ++p) {
+        const float b1 = __uint_as_float(xch[4 * p]), b2 = __uint_as_float(xch[4 * p + 1]);
+        const int bk = static_cast<int>(xch[4 * p + 2]);
+        const float lo = fminf(a1, b1), hi = fmaxf(a1, b1);
+        ak = a1 < b1 ? ak : (b1 < a1 ? bk : min(ak, bk));
+        a2 = fminf(fminf(a2, b2), hi);
+        a1 = lo;
+    }
+    f1 = a1;
+    f2 = a2;
+    k1 = ak;
+}
+
+template <int kParts>
+__device__ __forceinline__ void exchange_f64(double &bd, int &bk, unsigned *xch, int part, int lane)
+{
+    __syncthreads();
+    if (lane == 0) {
+        const unsigned long long u = __double_as_longlong(bd);
+        xch[4 * part] = static_cast<unsigned>(u);
+        xch[4 * part + 1] = static_cast<unsigned>(u >> 32);
+        xch[4 * part + 2] = static_cast<unsigned>(bk);
+    }
+    __syncthreads();
+    double a = INFINITY;
+    int ak = 0x7fffffff;
+#pragma unroll
+    for (int p = 0; p < kParts; ++p) {
+        const double d = __longlong_as_double(static_cast<long long>(
+            static_cast<unsigned long long>(xch[4 * p]) | (static_cast<unsigned long long>(xch[4 * p + 1]) << 32)));
+        const int k = static_cast<int>(xch[4 * p + 2]);
+        if (d < a || (d == a && k < ak)) {
+            a = d;
+            ak = k;
+        }
+    }
+    bd = a;
+    bk = ak;
+}
+
 // A third candidate inside one or more key sets of frame f (lanes f, f+32):
 // the wavefront takes every codeword of each overflowed set (bit 2h+s of
 // `mask`) and the listed candidates of the other sets (l0 / l1 / cnt0 /
@@ -407,9 +466,12 @@ __device__ __forceinline__ double row_distance_f64(const float *row, const float
 // form for every entry within 2^-16 of the smallest when the two smallest
 // are that close (ties go to the lowest index). Returns the winner on every
 // lane. Every lane must call it; `row` is a 64-float LDS row of this
-// wavefront.
+// wavefront. With kParts > 1, kParts wavefronts holding the same frames
+// share the work (this one is `part`; see exchange_f32).
+template <int kParts>
 __device__ int resolve_sets(const float (&n)[32], float *row, const float *book, int n_codes, int f, int lane,
-                            unsigned mask, const int (&l0)[4], const int (&l1)[4], int cnt0, int ncand)
+                            unsigned mask, const int (&l0)[4], const int (&l1)[4], int cnt0, int ncand,
+                            int part, unsigned *xch)
 {
     const int col = lane & 31, half = lane >> 5;
     if (col == f) {
@@ -451,12 +513,12 @@ __device__ int resolve_sets(const float (&n)[32], float *row, const float *book,
     };
     for (int b = 0; b < 4; ++b) {
         if (!((mask >> b) & 1u)) continue;
-        for (int i = lane; i < span; i += 64) {
+        for (int i = lane + 64 * part; i < span; i += 64 * kParts) {
             const int k = subset_code(i, b >> 1, b & 1);
             if (k < n_codes) take(k);
         }
     }
-    if (extra >= 0) take(extra);
+    if (extra >= 0 && part == 0) take(extra);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
         const float of1 = __shfl_xor(f1, off), of2 = __shfl_xor(f2, off);
@@ -466,6 +528,7 @@ __device__ int resolve_sets(const float (&n)[32], float *row, const float *book,
         f2 = fminf(fminf(f2, of2), hi);
         f1 = lo;
     }
+    if (kParts > 1) exchange_f32<kParts>(f1, f2, k1, xch, part, lane);
     const float thr = f1 * (1.0f + 1.52587890625e-05f) + 1e-30f;
     int win = k1;
     if (f2 <= thr) {   // wave-uniform: float64 for every entry within thr of the smallest
@@ -482,12 +545,12 @@ __device__ int resolve_sets(const float (&n)[32], float *row, const float *book,
         };
         for (int b = 0; b < 4; ++b) {
             if (!((mask >> b) & 1u)) continue;
-            for (int i = lane; i < span; i += 64) {
+            for (int i = lane + 64 * part; i < span; i += 64 * kParts) {
                 const int k = subset_code(i, b >> 1, b & 1);
                 if (k < n_codes) exact(k);
             }
         }
-        if (extra >= 0) exact(extra);
+        if (extra >= 0 && part == 0) exact(extra);
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             const double od = __shfl_xor(bd, off);
@@ -497,6 +560,7 @@ __device__ int resolve_sets(const float (&n)[32], float *row, const float *book,
                 bk = ok;
             }
         }
+        if (kParts > 1) exchange_f64<kParts>(bd, bk, xch, part, lane);
         win = bk;
     }
     // all reads of `row` are done before a later call overwrites it
@@ -513,11 +577,14 @@ __device__ int resolve_sets(const float (&n)[32], float *row, const float *book,
 // sweep of its overflowed sets, fp16 out of range to the full float64
 // rescan. Then the pick is stored (code_out, when not null) and subtracted
 // from the negated residual n (and added to acc for kRecon). Every lane
-// must call it.
-template <bool kRecon>
+// must call it. With kParts > 1 the kParts wavefronts of the workgroup
+// decide the same frames from the same key sets and share each sweep
+// (wavefront `part`, LDS `xch`); they must all call it.
+template <bool kRecon, int kParts = 1>
 __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], const KeySet (&ks)[2],
                                              const float *book, int n_codes, float m16, int e, bool valid,
-                                             int half, int col, int lane, float *frame_row, int32_t *code_out)
+                                             int half, int col, int lane, float *frame_row, int32_t *code_out,
+                                             int part = 0, unsigned *xch = nullptr)
 {
     float r4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -669,9 +736,9 @@ __device__ __forceinline__ void decide_stage(float (&n)[32], float (&acc)[32], c
         pending &= pending - 1;
         const int w = __builtin_amdgcn_readlane(static_cast<int>(bad), f)
                           ? rescan_frame(n, frame_row, book, n_codes, f, lane)
-                          : resolve_sets(n, frame_row, book, n_codes, f, lane,
-                                         static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(ovmask), f)),
-                                         l0, l1, cnt0, ncand);
+                          : resolve_sets<kParts>(n, frame_row, book, n_codes, f, lane,
+                                                 static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(ovmask), f)),
+                                                 l0, l1, cnt0, ncand, part, xch);
         if (col == f) pick = w;
     }
 
@@ -901,6 +968,7 @@ void encode_f16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
     __shared__ __align__(16) _Float16 s_rows[kKsWaves][kChunk * kRowHalfs];   // one chunk per wavefront
     __shared__ __align__(16) float s_frame[kKsWaves][kDim];                    // rescan: one frame's residual
     __shared__ unsigned s_keys[kKsWaves][kKsKeyWords][64];
+    __shared__ unsigned s_xch[kKsWaves * 4];   // the shared sweeps' partial results
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1019,8 +1087,9 @@ void encode_f16_ksplit_kernel(const float *__restrict__ x, int64_t n_frames,
 
         const float *book = books + static_cast<int64_t>(q) * n_codes * kDim;
         const float m16 = wave_max_bits(cmax);
-        decide_stage<kRecon>(n, acc, mk, book, n_codes, m16, e, valid, half, col, lane, s_frame[wave],
-                             (wave == 0 && valid && half == 0) ? codes + frame * codes_ld + q : nullptr);
+        decide_stage<kRecon, kKsWaves>(n, acc, mk, book, n_codes, m16, e, valid, half, col, lane, s_frame[wave],
+                                       (wave == 0 && valid && half == 0) ? codes + frame * codes_ld + q : nullptr,
+                                       wave, s_xch);
     }
 
     if (wave == 0 && valid) {
