@@ -74,6 +74,19 @@ def test_codebook_sizes(k, scoring, wide):
 
 
 @pytest.mark.parametrize("wide", [False, True])
+@pytest.mark.parametrize("k", [16384, 20000])
+@pytest.mark.parametrize("scoring", SCORINGS)
+def test_large_codebooks(k, scoring, wide):
+    """Codebooks of many 1024-codeword index spans (16 and 20, the last one partial, K not a multiple
+    of 256): the keys' span bookkeeping and the split-codebook kernel's chunk-per-wavefront rotation
+    across spans."""
+    rng = np.random.default_rng(250 + k)
+    books = _books(rng, 2, k)
+    x = rng.standard_normal((200, 64)).astype(np.float32)
+    _check(x, books, wide, scoring)
+
+
+@pytest.mark.parametrize("wide", [False, True])
 @pytest.mark.parametrize("q,decay", [(1, 1.0), (32, 0.85), (64, 0.9)])
 @pytest.mark.parametrize("scoring", SCORINGS)
 def test_stage_counts(q, decay, scoring, wide):
