@@ -928,9 +928,11 @@ void encode_f16_kernel(const float *__restrict__ x, int64_t n_frames,
 // key and its codeword, the second smallest of the two sets' four keys,
 // and a lower bound of the third -- and every wavefront takes the same
 // decision from the same merged sets (the decision only reads the
-// codebook), so each keeps the residual without a broadcast; wavefront 0
-// stores codes, residual and reconstruction. The keys, bound and decision
-// are the wide kernel's, so the codes are too.
+// codebook), so each keeps the residual without a broadcast; a set sweep
+// is shared among the four (each takes every fourth codeword, the partial
+// results are combined through LDS). Wavefront 0 stores codes, residual
+// and reconstruction. The keys, bound and decision are the wide kernel's,
+// so the codes are too.
 constexpr int kKsWaves = 4;
 constexpr int kKsThreads = 64 * kKsWaves;
 constexpr int kKsChunkLoads = kChunk * kRowSlots / 64;   // wavefront-wide 16-byte copies per chunk
